@@ -1,0 +1,440 @@
+/*
+ * fp8_oracle.c -- plain, slow, obviously-correct CPU reference for FP8 scaled
+ * quantization and the scaled FP8 GEMM it feeds.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the HIP library is
+ * checked against.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load it.  It shares no source, header, table or
+ * helper with the HIP library, and the library never calls it.
+ *
+ * Built with:  gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fopenmp
+ * (no FMA contraction, IEEE binary32/binary64 arithmetic, OpenMP only across
+ * independent rows/groups so that every per-element result is order-free).
+ *
+ * Sources for what is computed (web pages; see the citations per function):
+ *   [DeepL]  "DeepL bets on FP8: unified-precision training and inference"
+ *            (hmyw.cn/news/121341), sections 2.1, 2.3, 4.2, 5.1.
+ *   [H100]   "H100 FP8 acceleration, measured" (scrxy.com/news/908489),
+ *            paragraph on the FP8 formats (OCP origin, E5M2 range +-57344).
+ *   [Soup]   "FP8 training and QAT: ... with Soup on Hopper GPUs"
+ *            (lbrq.cn/news/198264), table of the three FP8 scaling recipes.
+ * Where the pages are silent (rounding mode, saturation, NaN codes, scale edge
+ * cases, block sizes) this file takes one documented reading; each such
+ * reading is marked "READING:".
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#include <math.h>
+#include <float.h>
+
+enum { OR_E4M3 = 0, OR_E5M2 = 1 };
+enum { OR_GRAN_TENSOR = 0, OR_GRAN_ROW = 1, OR_GRAN_1x128 = 2, OR_GRAN_128x128 = 3 };
+enum { OR_IN_F32 = 0, OR_IN_BF16 = 1 };
+
+/* ------------------------------------------------------------------------ */
+/* Bit-level helpers (IEEE binary32 as stored in memory).                    */
+/* ------------------------------------------------------------------------ */
+static inline uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static inline float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* bf16 is by definition the upper half of a binary32 word. */
+static inline float bf16_to_f32(uint16_t h) { return u2f(((uint32_t)h) << 16); }
+
+static inline float load_in(const void* x, int in_dtype, int64_t idx) {
+    if (in_dtype == OR_IN_F32) return ((const float*)x)[idx];
+    return bf16_to_f32(((const uint16_t*)x)[idx]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1. Decode: the value of every code, from the bit split.                  */
+/* [DeepL] 2.1: E4M3 = 1 sign, 4 exponent, 3 mantissa bits; E5M2 = 1 sign,   */
+/* 5 exponent, 2 mantissa bits.  [H100] formats paragraph: the formats are    */
+/* the jointly defined (OCP) ones and E5M2 reaches +-57344.                   */
+/* READING: OCP "E4M3FN" -- bias 7, no infinities, S.1111.111 is NaN, so the  */
+/* largest finite value is 448; E5M2 -- bias 15, IEEE-style Inf/NaN.          */
+/* ------------------------------------------------------------------------ */
+double or_decode(int fmt, uint8_t code) {
+    int sign = (code >> 7) & 1;
+    double mag;
+    if (fmt == OR_E4M3) {
+        int e = (code >> 3) & 0xF, m = code & 0x7;
+        if (e == 15 && m == 7) return NAN;
+        if (e == 0) mag = ldexp((double)m, -9);            /* m/8 * 2^(1-7) */
+        else        mag = ldexp(1.0 + m / 8.0, e - 7);
+    } else {
+        int e = (code >> 2) & 0x1F, m = code & 0x3;
+        if (e == 31) {
+            if (m != 0) return NAN;
+            mag = INFINITY;
+        } else if (e == 0) mag = ldexp((double)m, -16);   /* m/4 * 2^(1-15) */
+        else               mag = ldexp(1.0 + m / 4.0, e - 15);
+    }
+    return sign ? -mag : mag;
+}
+
+void or_decode_table(int fmt, double* out256) {
+    for (int c = 0; c < 256; ++c) out256[c] = or_decode(fmt, (uint8_t)c);
+}
+
+/* Largest finite magnitude and the code that holds it. */
+static double fmt_max(int fmt) { return fmt == OR_E4M3 ? 448.0 : 57344.0; }
+static int fmt_max_code(int fmt) { return fmt == OR_E4M3 ? 0x7E : 0x7B; }
+
+double or_format_max(int fmt) { return fmt_max(fmt); }
+
+/* ------------------------------------------------------------------------ */
+/* O2. Encode one binary32 value: saturating round-to-nearest-even.          */
+/* READING (the pages name neither rounding nor saturation): the code of the  */
+/* finite FP8 value nearest to v; on an exact tie the code with an even       */
+/* mantissa (LSB 0); |v| >= max finite (Inf included) gives +-max; NaN gives  */
+/* the all-ones-exponent/mantissa NaN code with v's sign; the sign of v is    */
+/* kept on underflow (-tiny -> 0x80).                                         */
+/* Done as a nearest-value search over the decoded positive codes, which are  */
+/* monotone in the code value -- deliberately not a bit manipulation.         */
+/* ------------------------------------------------------------------------ */
+uint8_t or_encode(int fmt, float v) {
+    uint8_t sign = (uint8_t)(signbit(v) ? 0x80 : 0x00);
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    int top = fmt_max_code(fmt);
+    if (a >= fmt_max(fmt)) return (uint8_t)(sign | top);
+    /* largest code lo in [0, top] with decode(lo) <= a */
+    int lo = 0, hi = top;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (or_decode(fmt, (uint8_t)mid) <= a) lo = mid; else hi = mid - 1;
+    }
+    double vlo = or_decode(fmt, (uint8_t)lo);
+    if (vlo == a) return (uint8_t)(sign | lo);
+    double vhi = or_decode(fmt, (uint8_t)(lo + 1));
+    double half = 0.5 * (vlo + vhi);   /* exact: one more mantissa bit */
+    int pick;
+    if (a < half) pick = lo;
+    else if (a > half) pick = lo + 1;
+    else pick = (lo % 2 == 0) ? lo : lo + 1;   /* tie: even code */
+    return (uint8_t)(sign | pick);
+}
+
+void or_encode_array(int fmt, const float* v, int64_t n, uint8_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = or_encode(fmt, v[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3. amax = max |x| over a group ([DeepL] 4.2 names the per-layer maximum  */
+/* absolute value as the statistic behind the scale).                        */
+/* READING for non-finite data: any NaN makes the result NaN (the one with    */
+/* the largest magnitude bits), else any Inf makes it Inf.  For non-negative  */
+/* binary32 values the unsigned order of the bit patterns is the numeric     */
+/* order, and NaN patterns sort above Inf, so the result is the element of    */
+/* largest |bits|.                                                            */
+/* ------------------------------------------------------------------------ */
+static inline uint32_t abs_bits(float v) { return f2u(v) & 0x7FFFFFFFu; }
+
+/* Group geometry for a [rows x cols] matrix with leading dimension ld.
+ * READING (block sizes are not on the pages): 1x128 and 128x128 blocks
+ * aligned at element (0,0); a final partial block covers the remainder.   */
+static void group_dims(int gran, int64_t rows, int64_t cols,
+                       int64_t* gr, int64_t* gc, int64_t* h, int64_t* w) {
+    switch (gran) {
+    case OR_GRAN_TENSOR: *h = rows; *w = cols; break;
+    case OR_GRAN_ROW:    *h = 1;    *w = cols; break;
+    case OR_GRAN_1x128:  *h = 1;    *w = 128;  break;
+    default:             *h = 128;  *w = 128;  break;
+    }
+    *gr = (rows + *h - 1) / *h;
+    *gc = (cols + *w - 1) / *w;
+}
+
+int64_t or_num_groups(int gran, int64_t rows, int64_t cols) {
+    int64_t gr, gc, h, w;
+    group_dims(gran, rows, cols, &gr, &gc, &h, &w);
+    return gr * gc;
+}
+
+/* amax_out[g] for every group g (row-major over the group grid). */
+void or_amax(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+             int gran, float* amax_out) {
+    int64_t gr, gc, h, w;
+    group_dims(gran, rows, cols, &gr, &gc, &h, &w);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t g = 0; g < gr * gc; ++g) {
+        int64_t r0 = (g / gc) * h, c0 = (g % gc) * w;
+        int64_t r1 = r0 + h < rows ? r0 + h : rows;
+        int64_t c1 = c0 + w < cols ? c0 + w : cols;
+        uint32_t best = 0;
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t c = c0; c < c1; ++c) {
+                uint32_t b = abs_bits(load_in(x, in_dtype, r * ld + c));
+                if (b > best) best = b;
+            }
+        amax_out[g] = u2f(best);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O4. Scale from amax.  [DeepL] 2.3: a scaling factor maps the raw values    */
+/* into the interval FP8 can represent.  READING: multiply before the cast    */
+/* by s = fl32(fmax / amax) (no margin); dequantize by s_inv = fl32(1/s).     */
+/* Edge cases (silent on the pages): amax == 0 or non-finite -> s = 1; a      */
+/* quotient that overflows -> FLT_MAX.                                        */
+/* [Soup] recipe table: the rowwise recipe uses power-of-two scales --        */
+/* READING: truncate the binary32 quotient to 2^floor(log2 s) by clearing its */
+/* mantissa bits (FLT_MAX becomes 2^127).                                     */
+/* ------------------------------------------------------------------------ */
+void or_scale(float amax, int fmt, int pow2, float* s_out, float* s_inv_out) {
+    float s;
+    float fmax = (float)fmt_max(fmt);
+    if (!(amax > 0.0f) || isinf(amax) || isnan(amax)) {
+        s = 1.0f;
+    } else {
+        s = fmax / amax;                 /* one IEEE binary32 division */
+        if (isinf(s)) s = FLT_MAX;
+    }
+    if (pow2) s = u2f(f2u(s) & 0xFF800000u);
+    *s_out = s;
+    *s_inv_out = 1.0f / s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O5. Quantize: q = encode(fl32(x * s_group)).                               */
+/* Optional counters: sat = non-NaN products with |x*s| > fmax (Inf inputs     */
+/* included); nonfinite = NaN or Inf inputs; underflow = nonzero, non-NaN      */
+/* inputs whose code is +-0.                                                   */
+/* scales[g] supplies s for group g (row-major over the group grid).          */
+/* ------------------------------------------------------------------------ */
+void or_quantize_with_scales(const void* x, int in_dtype, int64_t rows, int64_t cols,
+                             int64_t ld, int gran, int fmt, const float* scales,
+                             uint8_t* q, int64_t ldq, int64_t* counts3) {
+    int64_t gr, gc, h, w;
+    group_dims(gran, rows, cols, &gr, &gc, &h, &w);
+    double fmax = fmt_max(fmt);
+    int64_t sat = 0, nonfinite = 0, under = 0;
+    #pragma omp parallel for schedule(static) reduction(+:sat, nonfinite, under)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            int64_t g = (r / h) * gc + (c / w);
+            float xv = load_in(x, in_dtype, r * ld + c);
+            float v = xv * scales[g];          /* rounded once to binary32 */
+            uint8_t code = or_encode(fmt, v);
+            q[r * ldq + c] = code;
+            if (!isnan(v) && fabs((double)v) > fmax) ++sat;
+            if (isnan(xv) || isinf(xv)) ++nonfinite;
+            if (!isnan(xv) && xv != 0.0f && (code & 0x7F) == 0) ++under;
+        }
+    }
+    if (counts3) { counts3[0] = sat; counts3[1] = nonfinite; counts3[2] = under; }
+}
+
+/* Just-in-time quantize: amax per group, scale per group, cast. */
+void or_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                 int gran, int fmt, int pow2, uint8_t* q, int64_t ldq,
+                 float* amax_out, float* scale_out, float* scale_inv_out,
+                 int64_t* counts3) {
+    int64_t ng = or_num_groups(gran, rows, cols);
+    or_amax(x, in_dtype, rows, cols, ld, gran, amax_out);
+    for (int64_t g = 0; g < ng; ++g)
+        or_scale(amax_out[g], fmt, pow2, &scale_out[g], &scale_inv_out[g]);
+    or_quantize_with_scales(x, in_dtype, rows, cols, ld, gran, fmt, scale_out, q, ldq, counts3);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O6. Delayed scaling.  [DeepL] 2.3: the factor for this step is predicted   */
+/* from statistics of the previous steps, so no synchronous per-step amax is  */
+/* needed; it lags a sudden change of distribution.                           */
+/* READING: per tensor; the history holds the raw amax of the last            */
+/* min(count, len) steps (len <= 16); this step's scale is                    */
+/* scale(max over the history), the current step excluded; with an empty      */
+/* history (first step) the scale is taken just in time from this step's      */
+/* amax.  After the cast this step's amax is pushed into the ring.            */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    float amax[16];
+    int32_t len, pos, count;
+} or_ring;
+
+void or_ring_init(or_ring* r, int32_t len) {
+    memset(r, 0, sizeof(*r));
+    r->len = len;
+}
+
+float or_ring_window_max(const or_ring* r) {
+    uint32_t best = 0;
+    for (int i = 0; i < r->count; ++i) {
+        uint32_t b = abs_bits(r->amax[i]);
+        if (b > best) best = b;
+    }
+    return u2f(best);
+}
+
+/* One delayed step on a whole tensor.  out4 = {s, s_inv, amax, unused}. */
+void or_delayed_step(or_ring* r, const void* x, int in_dtype, int64_t rows, int64_t cols,
+                     int64_t ld, int fmt, uint8_t* q, int64_t ldq, float* out4,
+                     int64_t* counts3) {
+    float amax_now;
+    or_amax(x, in_dtype, rows, cols, ld, OR_GRAN_TENSOR, &amax_now);
+    float basis = (r->count == 0) ? amax_now : or_ring_window_max(r);
+    float s, s_inv;
+    or_scale(basis, fmt, 0, &s, &s_inv);
+    or_quantize_with_scales(x, in_dtype, rows, cols, ld, OR_GRAN_TENSOR, fmt, &s, q, ldq, counts3);
+    r->amax[r->pos] = amax_now;
+    r->pos = (r->pos + 1) % r->len;
+    if (r->count < r->len) r->count += 1;
+    out4[0] = s; out4[1] = s_inv; out4[2] = amax_now; out4[3] = 0.0f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O7. Scaled GEMM, Y = X . W^T with both operands K-contiguous.             */
+/* Dequantize each operand (A_hat = fl32(decode(q) * s_inv)), then an fp32    */
+/* triple loop accumulating in k order; P = sum_k |A_hat*B_hat| in fp64 is    */
+/* returned for the error floor.  a_per_row / b_per_row select a scalar or   */
+/* one scale per row of A (per output row) / of B (per output column).       */
+/* ------------------------------------------------------------------------ */
+static inline float deq(int fmt, uint8_t code, float s_inv) {
+    return (float)or_decode(fmt, code) * s_inv;
+}
+
+/* Generic sampled form: computes n outputs at (ms[i], ns[i]). */
+void or_gemm_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb, int64_t ldb,
+                     int64_t K, const float* a_inv, int a_per_row, const float* b_inv, int b_per_row,
+                     const int64_t* ms, const int64_t* ns, int64_t n, float* y32, double* p64) {
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t m = ms[i], nn = ns[i];
+        float sa = a_per_row ? a_inv[m] : a_inv[0];
+        float sb = b_per_row ? b_inv[nn] : b_inv[0];
+        float acc = 0.0f;
+        double pabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            float av = deq(fa, A[m * lda + k], sa);
+            float bv = deq(fb, B[nn * ldb + k], sb);
+            float prod = av * bv;
+            acc = acc + prod;
+            pabs += fabs((double)av * (double)bv);
+        }
+        y32[i] = acc;
+        if (p64) p64[i] = pabs;
+    }
+}
+
+void or_gemm(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb, int64_t ldb,
+             int64_t M, int64_t N, int64_t K, const float* a_inv, int a_per_row,
+             const float* b_inv, int b_per_row, float* Y32, int64_t ldy, double* P, int64_t ldp) {
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        float sa = a_per_row ? a_inv[m] : a_inv[0];
+        for (int64_t nn = 0; nn < N; ++nn) {
+            float sb = b_per_row ? b_inv[nn] : b_inv[0];
+            float acc = 0.0f;
+            double pabs = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                float av = deq(fa, A[m * lda + k], sa);
+                float bv = deq(fb, B[nn * ldb + k], sb);
+                float prod = av * bv;
+                acc = acc + prod;
+                pabs += fabs((double)av * (double)bv);
+            }
+            Y32[m * ldy + nn] = acc;
+            if (P) P[m * ldp + nn] = pabs;
+        }
+    }
+}
+
+/* Block-scaled GEMM ([DeepL] 2.3, per-block scaling): A has one scale per
+ * (row, 128-wide K block), a_inv[m*(K/128)+kb]; B one per (128-row block,
+ * 128-wide K block), b_inv[(n/128)*(K/128)+kb].  Same fp32 k-order loop with
+ * each element dequantized by its own block scale.  Requires K % 128 == 0. */
+void or_blockgemm_sampled(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t K,
+                          const float* a_inv, const float* b_inv,
+                          const int64_t* ms, const int64_t* ns, int64_t n, float* y32, double* p64) {
+    int64_t kb_n = K / 128;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t m = ms[i], nn = ns[i];
+        float acc = 0.0f;
+        double pabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t kb = k / 128;
+            float av = deq(OR_E4M3, A[m * lda + k], a_inv[m * kb_n + kb]);
+            float bv = deq(OR_E4M3, B[nn * ldb + k], b_inv[(nn / 128) * kb_n + kb]);
+            float prod = av * bv;
+            acc = acc + prod;
+            pabs += fabs((double)av * (double)bv);
+        }
+        y32[i] = acc;
+        if (p64) p64[i] = pabs;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact pin for O7: every finite E4M3 value is an integer multiple of 2^-9   */
+/* and every finite E5M2 value of 2^-16, so each product and the whole K sum  */
+/* are exact integers at scale 2^-(ea+eb).  D is accumulated in __int128.     */
+/* Returns Y_exact = s_a * s_b * D * 2^-(ea+eb) in fp64 (long double product  */
+/* for the final scaling).  Block mode sums per K block with its own scales.  */
+/* Non-finite codes are not allowed here (the caller filters them).           */
+/* ------------------------------------------------------------------------ */
+static inline int64_t code_to_int(int fmt, uint8_t code) {
+    /* decode(code) * 2^9 (E4M3) or * 2^16 (E5M2); exact integer */
+    double v = or_decode(fmt, code) * (fmt == OR_E4M3 ? 512.0 : 65536.0);
+    return (int64_t)v;
+}
+
+void or_gemm_exact_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb,
+                           int64_t ldb, int64_t K, const float* a_inv, int a_per_row,
+                           const float* b_inv, int b_per_row, int block_mode,
+                           const int64_t* ms, const int64_t* ns, int64_t n, double* y_exact) {
+    int64_t kb_n = K / 128;
+    int shift = (fa == OR_E4M3 ? 9 : 16) + (fb == OR_E4M3 ? 9 : 16);
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t m = ms[i], nn = ns[i];
+        long double total = 0.0L;
+        if (!block_mode) {
+            __int128 d = 0;
+            for (int64_t k = 0; k < K; ++k)
+                d += (__int128)code_to_int(fa, A[m * lda + k]) * (__int128)code_to_int(fb, B[nn * ldb + k]);
+            float sa = a_per_row ? a_inv[m] : a_inv[0];
+            float sb = b_per_row ? b_inv[nn] : b_inv[0];
+            total = (long double)d * (long double)sa * (long double)sb;
+        } else {
+            for (int64_t kb = 0; kb < kb_n; ++kb) {
+                __int128 d = 0;
+                for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
+                    d += (__int128)code_to_int(fa, A[m * lda + k]) * (__int128)code_to_int(fb, B[nn * ldb + k]);
+                total += (long double)d * (long double)a_inv[m * kb_n + kb]
+                         * (long double)b_inv[(nn / 128) * kb_n + kb];
+            }
+        }
+        y_exact[i] = (double)ldexpl(total, -shift);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O8. Output rounding to bfloat16, round-to-nearest-even (NaN stays NaN).    */
+/* Done as the nearest-value rule on the two bf16 neighbours of v, ties to   */
+/* the even one -- written out rather than as an add-and-shift trick.         */
+/* ------------------------------------------------------------------------ */
+uint16_t or_f32_to_bf16(float v) {
+    uint32_t b = f2u(v);
+    if (isnan(v)) return (uint16_t)((b >> 16) | 0x0040);   /* quiet NaN, sign kept */
+    uint32_t down = b & 0xFFFF0000u;                        /* toward zero */
+    float lo = u2f(down);
+    if (lo == v) return (uint16_t)(down >> 16);
+    uint32_t up = down + 0x00010000u;                       /* next magnitude */
+    float hi = u2f(up);                                     /* may be Inf */
+    double dv = fabs((double)v), dlo = fabs((double)lo);
+    double dhi = isinf(hi) ? ldexp(1.0, 128) : fabs((double)hi);
+    double half = 0.5 * (dlo + dhi);
+    uint32_t pick;
+    if (dv < half) pick = down;
+    else if (dv > half) pick = up;
+    else pick = ((down >> 16) & 1u) ? up : down;
+    return (uint16_t)(pick >> 16);
+}
+
+void or_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = or_f32_to_bf16(v[i]);
+}
