@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 hot path on one MI355X.
+
+One step = the whole path over one batch of seeded synthetic input already
+resident in HBM: amax + scale + saturating RNE cast of both GEMM operands,
+then the scaled FP8 GEMM with fp32 accumulation and its dequantizing
+epilogue.  Default workload: the 8B-style MLP up-projection
+(X [4096 x 4096] bf16 with 0.1% outlier columns x50, W [14336 x 4096] bf16
+N(0, 0.02), per-tensor dynamic E4M3 scaling, Y bf16).
+
+Prints ONE JSON line.  `value` = whole-step throughput in TFLOP/s
+(2MNK / step time); the GEMM kernel's own TFLOP/s and % of the FP8 MFMA peak,
+and the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.
+
+    python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+# rocprofv3 HBM traffic of the GEMM kernel on the mlp8b workload (FETCH_SIZE +
+# WRITE_SIZE per dispatch, scaled by the copy-kernel calibration factor);
+# None until measured for the current kernel.
+GEMM_TRAFFIC_BYTES = None
+
+WORKLOADS = {
+    "tiny": "tiny: X, W [256 x 256] fp32 N(0,1); per-tensor E4M3; Y fp32",
+    "mlp8b": ("mlp8b: X [4096 x 4096] bf16 N(0,1) with 0.1% outlier columns x50, "
+              "W [14336 x 4096] bf16 N(0,0.02); per-tensor dynamic E4M3; Y bf16"),
+    "qkv": ("qkv: X [8192 x 4096] bf16 with outlier columns, W [6144 x 4096] bf16; "
+            "row-wise power-of-two scales, E4M3; Y bf16"),
+    "mlp70b": ("mlp70b: X [2048 x 8192] bf16 Student-t(4) 1x128 blocks, W [28672 x 8192] bf16 "
+               "N(0,0.015) 128x128 blocks, E4M3; block-scaled GEMM; Y bf16"),
+    "wgrad": ("wgrad: dY [8192 x 4096] bf16 1e-3*t(3) -> E5M2, X [8192 x 4096] bf16 N(0,1) -> E4M3, "
+              "delayed scaling (16-step history), transposed casts; dW = dY^T X [4096 x 4096] fp32"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="X rows in the CPU-baseline sample")
+    ap.add_argument("--cpu-cols", type=int, default=4096, help="W rows in the CPU-baseline sample")
+    return ap.parse_args()
+
+
+class Step:
+    """Device buffers and the callable that runs one step."""
+
+    def __init__(self, workload: str, torch, fp8, synth):
+        self.torch, self.fp8 = torch, fp8
+        self.workload = workload
+        dev = torch.device("cuda:0")
+        self.dev = dev
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        if workload == "tiny":
+            X, W = synth.tiny()
+            xs, ws = [torch.from_numpy(X).to(dev)], [torch.from_numpy(W).to(dev)]
+            self.M, self.N, self.K = 256, 256, 256
+            self.in_bytes = 4
+        elif workload in ("mlp8b", "qkv", "mlp70b"):
+            X, W = getattr(synth, workload)()
+            self.M, self.K = X.shape
+            self.N = W.shape[0]
+            x0, w0 = bf16(X), bf16(W)
+            del X, W
+            # rotate input copies so that no quantize input is still in the
+            # 256 MB Infinity Cache from the previous step
+            per = (x0.numel() + w0.numel()) * 2
+            copies = max(1, min(4, -(-600 * 2 ** 20 // per)))
+            xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+            ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+            self.in_bytes = 2
+        else:  # wgrad
+            dy, x = synth.wgrad_step(0)
+            self.M = self.N = dy.shape[1]
+            self.K = dy.shape[0]
+            xs = [bf16(dy)] + [bf16(synth.wgrad_step(t)[0]) for t in (1, 2)]
+            ws = [bf16(x)] + [bf16(synth.wgrad_step(t)[1]) for t in (1, 2)]
+            self.in_bytes = 2
+            self.h_dy, self.h_x = fp8.AmaxHistory(16), fp8.AmaxHistory(16)
+        self.xs, self.ws = xs, ws
+        self.i = 0
+        M, N, K = self.M, self.N, self.K
+        T = torch
+        # outputs, allocated once
+        if workload == "wgrad":
+            self.xq = T.empty((M, K), dtype=T.uint8, device=dev)
+            self.wq = T.empty((N, K), dtype=T.uint8, device=dev)
+        else:
+            self.xq = T.empty((M, K), dtype=T.uint8, device=dev)
+            self.wq = T.empty((N, K), dtype=T.uint8, device=dev)
+        gx = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "1x128", "wgrad": "tensor"}[workload]
+        gw = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "128x128", "wgrad": "tensor"}[workload]
+        self.gx, self.gw = gx, gw
+        rows_x, cols_x = xs[0].shape
+        rows_w, cols_w = ws[0].shape
+        self.sx = T.empty(fp8.group_grid(gx, rows_x, cols_x), dtype=T.float32, device=dev)
+        self.ax = T.empty_like(self.sx)
+        self.sw = T.empty(fp8.group_grid(gw, rows_w, cols_w), dtype=T.float32, device=dev)
+        self.aw = T.empty_like(self.sw)
+        out_dt = T.float32 if workload in ("tiny", "wgrad") else T.bfloat16
+        self.y = T.empty((M, N), dtype=out_dt, device=dev)
+        self.elems = xs[0].numel() + ws[0].numel()
+
+    def quantize(self):
+        fp8, i = self.fp8, self.i
+        x, w = self.xs[i % len(self.xs)], self.ws[i % len(self.ws)]
+        if self.workload == "wgrad":
+            fp8.quantize(x, "e5m2", "tensor", history=self.h_dy, transpose=True, out=self.xq,
+                         scale_inv_out=self.sx, amax_out=self.ax)
+            fp8.quantize(w, "e4m3", "tensor", history=self.h_x, transpose=True, out=self.wq,
+                         scale_inv_out=self.sw, amax_out=self.aw)
+        else:
+            pow2 = self.workload == "qkv"
+            fp8.quantize(x, "e4m3", self.gx, pow2=pow2, out=self.xq, scale_inv_out=self.sx, amax_out=self.ax)
+            fp8.quantize(w, "e4m3", self.gw, pow2=pow2, out=self.wq, scale_inv_out=self.sw, amax_out=self.aw)
+
+    def gemm(self):
+        fp8 = self.fp8
+        if self.workload == "mlp70b":
+            fp8.blockscaled_gemm(self.xq, self.wq, self.sx, self.sw, out=self.y)
+        elif self.workload == "wgrad":
+            fp8.scaled_gemm(self.xq, self.wq, self.sx, self.sw, "e5m2", "e4m3", out=self.y)
+        else:
+            fp8.scaled_gemm(self.xq, self.wq, self.sx.reshape(-1), self.sw.reshape(-1), out=self.y)
+        self.i += 1
+
+    def quant_bytes(self) -> float:
+        """Algorithmic HBM bytes of the two casts of one step."""
+        e = self.elems
+        if self.workload in ("tiny", "mlp8b"):
+            return e * (2 * self.in_bytes + 1)      # amax pass + cast pass
+        if self.workload == "wgrad":
+            return e * (self.in_bytes + 1)          # delayed: one pass
+        return e * (self.in_bytes + 1)              # row / block: one pass (scales negligible)
+
+
+def cpu_baseline(args, workload, synth):
+    """The oracle, untuned, on a bounded sample of the same step: quantize the
+    first `cpu_rows` rows of X and `cpu_cols` rows of W, then the GEMM block
+    Y[:cpu_rows, :cpu_cols] with the full K."""
+    import oracle
+    if workload not in ("mlp8b", "tiny"):
+        return None
+    if workload == "tiny":
+        X, W = synth.tiny()
+        r, c = 256, 256
+    else:
+        r, c = args.cpu_rows, args.cpu_cols
+        X, W = synth.mlp8b()
+        X, W = np.ascontiguousarray(X[:r]), np.ascontiguousarray(W[:c])
+    K = X.shape[1]
+    t0 = time.perf_counter()
+    qx = oracle.quantize(X, oracle.E4M3, "tensor")
+    qw = oracle.quantize(W, oracle.E4M3, "tensor")
+    y, _ = oracle.gemm(qx["q"], 0, qw["q"], 0, qx["scale_inv"], qw["scale_inv"], with_p=True)
+    dt = time.perf_counter() - t0
+    threads = oracle.num_threads()
+    return {"value": 2.0 * r * c * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "quantize X[:%d], W[:%d] (per-tensor E4M3) + GEMM Y[:%d, :%d] with K=%d: %.1f s"
+                      % (r, c, r, c, K, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_precision_quantization_amd as fp8
+    import synth
+
+    st = Step(args.workload, torch, fp8, synth)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        st.quantize()
+        st.gemm()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        ev[s][0].record()
+        st.quantize()
+        ev[s][1].record()
+        st.gemm()
+        ev[s][2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    q_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    g_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms = total_ms / K
+    flops = 2.0 * st.M * st.N * st.K
+    gemm_tflops = flops / (g_ms.mean() * 1e-3) / 1e12
+    qbytes = st.quant_bytes()
+    q_gbs = qbytes / (q_ms.mean() * 1e-3) / 1e9
+    roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": GEMM_TRAFFIC_BYTES if args.workload == "mlp8b" else None}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, args.workload, synth)
+    out = {
+        "metric": "FP8 scaled-GEMM TFLOPS (% of FP8 MFMA peak); quantize GB/s (% HBM peak)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (e4m3/e5m2 operands, fp32 accumulate)",
+        "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": WORKLOADS[args.workload], "M": st.M, "N": st.N, "K": st.K},
+        "kernels": {
+            "gemm_ms": round(float(g_ms.mean()), 4),
+            "gemm_tflops": round(gemm_tflops, 2),
+            "gemm_pct_fp8_peak": round(100 * gemm_tflops / PEAK_FP8_TFLOPS, 2),
+            "quantize_ms": round(float(q_ms.mean()), 4),
+            "quantize_gbs": round(q_gbs, 1),
+            "quantize_pct_hbm_peak": round(100 * q_gbs / PEAK_HBM_GBS, 2),
+            "quantize_bytes": int(qbytes),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+"""FP8 scaled quantization and scaled FP8 GEMM for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/fp8mi.h (libfp8mi.so).  torch
+tensors serve only as device memory and streams: every step of the
+computation runs in the library's HIP kernels.  There is no CPU path; every
+call raises if the library is missing or the device is not gfx950.
+
+    import fp8_precision_quantization_amd as fp8
+    xq = fp8.quantize(x, "e4m3", "tensor")          # x: bf16/fp32 [rows, cols] on cuda
+    wq = fp8.quantize(w, "e4m3", "tensor")
+    y = fp8.scaled_gemm(xq.q, wq.q, xq.scale_inv, wq.scale_inv)   # y = x w^T, bf16
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import Fp8Error  # noqa: F401
+
+__all__ = ["quantize", "amax", "scaled_gemm", "blockscaled_gemm", "AmaxHistory", "Diag",
+           "QuantResult", "Fp8Error", "FORMATS", "GRANULARITIES", "group_grid"]
+
+FORMATS = {"e4m3": _lib.FP8_E4M3, "e5m2": _lib.FP8_E5M2}
+GRANULARITIES = {"tensor": _lib.FP8_GRAN_TENSOR, "row": _lib.FP8_GRAN_ROW,
+                 "1x128": _lib.FP8_GRAN_BLOCK_1x128, "128x128": _lib.FP8_GRAN_BLOCK_128x128}
+TORCH_FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def _fmt(f) -> int:
+    if isinstance(f, str):
+        return FORMATS[f]
+    return int(f)
+
+
+def _gran(g) -> int:
+    if isinstance(g, str):
+        return GRANULARITIES[g]
+    return int(g)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _matrix(x: torch.Tensor, name: str):
+    if x.dim() != 2:
+        raise ValueError("%s must be 2-D, got shape %s" % (name, tuple(x.shape)))
+    if not x.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if x.stride(1) != 1 and x.shape[1] > 1:
+        raise ValueError("%s must have a contiguous last dimension" % name)
+    return x.shape[0], x.shape[1], max(x.stride(0), 1) if x.shape[0] > 1 else max(x.shape[1], 1)
+
+
+def group_grid(granularity, rows: int, cols: int):
+    g = _gran(granularity)
+    if g == _lib.FP8_GRAN_TENSOR:
+        return (1,)
+    if g == _lib.FP8_GRAN_ROW:
+        return (rows,)
+    if g == _lib.FP8_GRAN_BLOCK_1x128:
+        return (rows, (cols + 127) // 128)
+    return ((rows + 127) // 128, (cols + 127) // 128)
+
+
+class Diag:
+    """Device counters (sat, nonfinite, underflow); the library adds to them."""
+
+    def __init__(self, device="cuda"):
+        self.buf = torch.zeros(4, dtype=torch.int32, device=device)
+
+    def zero_(self):
+        self.buf.zero_()
+        return self
+
+    def read(self) -> dict:
+        v = self.buf.cpu().tolist()
+        return {"sat": v[0], "nonfinite": v[1], "underflow": v[2]}
+
+
+class AmaxHistory:
+    """Delayed-scaling state: a 128-byte device struct (fp8_amax_history)."""
+
+    def __init__(self, length: int = 16, device="cuda"):
+        self.buf = torch.empty(_lib.HISTORY_BYTES // 4, dtype=torch.int32, device=device)
+        self.length = length
+        self.reset()
+
+    def reset(self):
+        dev = self.buf.device
+        _lib.check(_lib.lib().fp8_history_init(self.buf.data_ptr(), self.length, _stream(dev)),
+                   "fp8_history_init")
+
+    def state(self) -> dict:
+        w = self.buf.cpu()
+        f = w.view(torch.float32)
+        return {"amax": f[:16].clone(), "len": int(w[16]), "pos": int(w[17]), "count": int(w[18]),
+                "scale": float(f[21]), "scale_inv": float(f[22]), "steps": int(w[23])}
+
+    def save(self) -> torch.Tensor:
+        return self.buf.clone()
+
+    def load(self, saved: torch.Tensor):
+        self.buf.copy_(saved)
+
+
+@dataclass
+class QuantResult:
+    q: torch.Tensor            # uint8 codes
+    scale_inv: torch.Tensor    # fp32, group grid
+    amax: torch.Tensor         # fp32, group grid
+    fmt: str
+
+    def as_float8(self) -> torch.Tensor:
+        return self.q.view(TORCH_FP8[self.fmt])
+
+
+def quantize(x: torch.Tensor, fmt="e4m3", granularity="tensor", pow2: bool = False,
+             history: Optional[AmaxHistory] = None, transpose: bool = False,
+             diag: Optional[Diag] = None, out: Optional[torch.Tensor] = None,
+             scale_inv_out: Optional[torch.Tensor] = None,
+             amax_out: Optional[torch.Tensor] = None) -> QuantResult:
+    rows, cols, ld = _matrix(x, "x")
+    if x.dtype == torch.bfloat16:
+        in_dt = _lib.FP8_IN_BF16
+    elif x.dtype == torch.float32:
+        in_dt = _lib.FP8_IN_F32
+    else:
+        raise TypeError("x must be bfloat16 or float32, got %s" % x.dtype)
+    fmt_name = fmt if isinstance(fmt, str) else ("e4m3" if fmt == 0 else "e5m2")
+    grid = group_grid(granularity, rows, cols)
+    dev = x.device
+    if out is None:
+        out = torch.empty((cols, rows) if transpose else (rows, cols), dtype=torch.uint8, device=dev)
+    ldq = max(out.stride(0), 1) if out.shape[0] > 1 else max(out.shape[1], 1)
+    if scale_inv_out is None:
+        scale_inv_out = torch.empty(grid, dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty(grid, dtype=torch.float32, device=dev)
+    flags = (_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_TRANSPOSE_OUT if transpose else 0)
+    st = _lib.lib().fp8_quantize(
+        x.data_ptr(), in_dt, rows, cols, ld, _fmt(fmt), _gran(granularity), flags,
+        _ptr(history.buf) if history is not None else None, out.data_ptr(), ldq,
+        scale_inv_out.data_ptr(), amax_out.data_ptr(), _ptr(diag.buf) if diag is not None else None,
+        _stream(dev))
+    _lib.check(st, "fp8_quantize")
+    return QuantResult(out, scale_inv_out, amax_out, fmt_name)
+
+
+def amax(x: torch.Tensor, granularity="tensor", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    rows, cols, ld = _matrix(x, "x")
+    in_dt = _lib.FP8_IN_BF16 if x.dtype == torch.bfloat16 else _lib.FP8_IN_F32
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty(group_grid(granularity, rows, cols), dtype=torch.float32, device=x.device)
+    st = _lib.lib().fp8_amax(x.data_ptr(), in_dt, rows, cols, ld, _gran(granularity), out.data_ptr(),
+                             _stream(x.device))
+    _lib.check(st, "fp8_amax")
+    return out
+
+
+def _out_dtype(dt) -> int:
+    if dt == torch.bfloat16:
+        return _lib.FP8_OUT_BF16
+    if dt == torch.float32:
+        return _lib.FP8_OUT_F32
+    raise TypeError("out dtype must be bfloat16 or float32")
+
+
+def scaled_gemm(a_q: torch.Tensor, b_q: torch.Tensor, a_scale_inv: torch.Tensor,
+                b_scale_inv: torch.Tensor, fa="e4m3", fb="e4m3", out_dtype=torch.bfloat16,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = (A_q . B_q^T) * sa * sb with A_q [M, K], B_q [N, K] uint8 codes."""
+    M, K, lda = _matrix(a_q, "a_q")
+    N, K2, ldb = _matrix(b_q, "b_q")
+    if K != K2:
+        raise ValueError("K mismatch: %d vs %d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    ldc = max(out.stride(0), 1) if out.shape[0] > 1 else max(N, 1)
+    a_row = 0 if a_scale_inv.numel() == 1 else 1
+    b_row = 0 if b_scale_inv.numel() == 1 else 1
+    if a_row and a_scale_inv.numel() != M:
+        raise ValueError("a_scale_inv must hold 1 or M=%d values" % M)
+    if b_row and b_scale_inv.numel() != N:
+        raise ValueError("b_scale_inv must hold 1 or N=%d values" % N)
+    st = _lib.lib().fp8_scaled_gemm(a_q.data_ptr(), _fmt(fa), lda, b_q.data_ptr(), _fmt(fb), ldb, M, N, K,
+                                    a_scale_inv.data_ptr(), a_row, b_scale_inv.data_ptr(), b_row,
+                                    out.data_ptr(), _out_dtype(out.dtype), ldc, _stream(a_q.device))
+    _lib.check(st, "fp8_scaled_gemm")
+    return out
+
+
+def blockscaled_gemm(a_q: torch.Tensor, b_q: torch.Tensor, a_scale_inv: torch.Tensor,
+                     b_scale_inv: torch.Tensor, out_dtype=torch.bfloat16,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """E4M3 block-scaled GEMM: a_scale_inv [M, K/128], b_scale_inv [N/128, K/128]."""
+    M, K, lda = _matrix(a_q, "a_q")
+    N, K2, ldb = _matrix(b_q, "b_q")
+    if K != K2:
+        raise ValueError("K mismatch: %d vs %d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    ldc = max(out.stride(0), 1) if out.shape[0] > 1 else max(N, 1)
+    st = _lib.lib().fp8_blockscaled_gemm(a_q.data_ptr(), lda, b_q.data_ptr(), ldb, M, N, K,
+                                         a_scale_inv.data_ptr(), b_scale_inv.data_ptr(), out.data_ptr(),
+                                         _out_dtype(out.dtype), ldc, _stream(a_q.device))
+    _lib.check(st, "fp8_blockscaled_gemm")
+    return out

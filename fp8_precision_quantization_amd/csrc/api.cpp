@@ -1,0 +1,275 @@
+// api.cpp -- the C ABI of libfp8mi.so: argument validation, device check and
+// dispatch to the gfx950 kernels.  Every invalid combination is rejected
+// before anything is launched, with a message naming the argument (the
+// up-front rejection convention of [Soup, lbrq.cn], list of configuration
+// errors caught at load time, including the explicit "needs hardware X").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "fp8mi.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fp8_status fail(fp8_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+fp8_status ok() {
+    g_last_error.clear();
+    return FP8_OK;
+}
+
+struct DeviceInfo {
+    std::atomic<int> state{0};   // 0 unknown, 1 gfx950, 2 other
+    int num_cus = 0;
+    char arch[64] = {0};
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_dev_mutex;
+
+// Current device must be gfx950; returns its CU count through *cus.
+fp8_status check_device(int* cus) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FP8_ERR_UNSUPPORTED_DEVICE, "device index %d out of range", dev);
+    DeviceInfo& d = g_devices[dev];
+    if (d.state.load(std::memory_order_acquire) == 0) {
+        std::lock_guard<std::mutex> lock(g_dev_mutex);
+        if (d.state.load(std::memory_order_relaxed) == 0) {
+            hipDeviceProp_t prop;
+            e = hipGetDeviceProperties(&prop, dev);
+            if (e != hipSuccess)
+                return fail(FP8_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+            std::strncpy(d.arch, prop.gcnArchName, sizeof(d.arch) - 1);
+            d.num_cus = prop.multiProcessorCount;
+            const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            d.state.store(is950 ? 1 : 2, std::memory_order_release);
+        }
+    }
+    if (d.state.load(std::memory_order_acquire) != 1)
+        return fail(FP8_ERR_UNSUPPORTED_DEVICE,
+                    "device %d is %s; this library needs gfx950 (MI355X / MI350X): FP8 MFMA and OCP FP8 conversion",
+                    dev, d.arch);
+    *cus = d.num_cus;
+    return FP8_OK;
+}
+
+fp8_status launch_result(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool is_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+fp8_status check_matrix_in(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ld) {
+    if (x == nullptr && rows > 0 && cols > 0) return fail(FP8_ERR_INVALID_ARG, "x is NULL");
+    if (in_dtype != FP8_IN_F32 && in_dtype != FP8_IN_BF16)
+        return fail(FP8_ERR_INVALID_ARG, "in_dtype %d is not FP8_IN_F32 or FP8_IN_BF16", in_dtype);
+    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size rows=%lld cols=%lld",
+                                          (long long)rows, (long long)cols);
+    if (ld < cols || ld < 1) return fail(FP8_ERR_INVALID_ARG, "ld=%lld must be >= max(cols, 1)=%lld",
+                                         (long long)ld, (long long)(cols > 1 ? cols : 1));
+    const int esz = in_dtype == FP8_IN_F32 ? 4 : 2;
+    if (!is_aligned(x, esz)) return fail(FP8_ERR_MISALIGNED, "x is not aligned to its %d-byte element", esz);
+    if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows and cols must each be <= 2^31");
+    if ((rows * ((cols + 7) / 8)) > fp8mi::kMaxUnits)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "tensor too large: more than 2^34 elements");
+    return FP8_OK;
+}
+
+bool valid_gran(int g) {
+    return g == FP8_GRAN_TENSOR || g == FP8_GRAN_ROW || g == FP8_GRAN_BLOCK_1x128 ||
+           g == FP8_GRAN_BLOCK_128x128;
+}
+
+int64_t num_groups(int gran, int64_t rows, int64_t cols) {
+    switch (gran) {
+    case FP8_GRAN_TENSOR: return 1;
+    case FP8_GRAN_ROW: return rows;
+    case FP8_GRAN_BLOCK_1x128: return rows * ((cols + 127) / 128);
+    default: return ((rows + 127) / 128) * ((cols + 127) / 128);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_abi_version(void) { return FP8MI_ABI_VERSION; }
+
+const char* fp8_status_string(fp8_status s) {
+    switch (s) {
+    case FP8_OK: return "FP8_OK";
+    case FP8_ERR_INVALID_ARG: return "FP8_ERR_INVALID_ARG";
+    case FP8_ERR_UNSUPPORTED_SHAPE: return "FP8_ERR_UNSUPPORTED_SHAPE";
+    case FP8_ERR_MISALIGNED: return "FP8_ERR_MISALIGNED";
+    case FP8_ERR_UNSUPPORTED_DEVICE: return "FP8_ERR_UNSUPPORTED_DEVICE";
+    case FP8_ERR_HIP: return "FP8_ERR_HIP";
+    }
+    return "FP8_ERR_UNKNOWN";
+}
+
+const char* fp8_last_error(void) { return g_last_error.c_str(); }
+
+fp8_status fp8_history_init(fp8_amax_history* hist, int32_t len, void* stream) {
+    if (hist == nullptr) return fail(FP8_ERR_INVALID_ARG, "hist is NULL");
+    if (len < 1 || len > 16) return fail(FP8_ERR_INVALID_ARG, "history length %d not in 1..16", len);
+    if (!is_aligned(hist, 16)) return fail(FP8_ERR_MISALIGNED, "hist must be 16-byte aligned");
+    int cus = 0;
+    fp8_status st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    return launch_result(fp8mi::launch_history_init(hist, len, (hipStream_t)stream), "fp8_history_init");
+}
+
+fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                    fp8_granularity gran, float* amax_out, void* stream) {
+    fp8_status st = check_matrix_in(x, in_dtype, rows, cols, ld);
+    if (st != FP8_OK) return st;
+    if (!valid_gran(gran)) return fail(FP8_ERR_INVALID_ARG, "granularity %d is not a fp8_granularity", (int)gran);
+    if (amax_out == nullptr && num_groups(gran, rows, cols) > 0)
+        return fail(FP8_ERR_INVALID_ARG, "amax_out is NULL");
+    if (!is_aligned(amax_out, 4)) return fail(FP8_ERR_MISALIGNED, "amax_out is not 4-byte aligned");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    if (num_groups(gran, rows, cols) == 0) return ok();
+    fp8mi::QuantArgs a;
+    a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
+    a.gran = gran; a.write_q = false; a.amax = amax_out; a.ldq = cols;
+    a.stream = (hipStream_t)stream; a.num_cus = cus;
+    return launch_result(fp8mi::launch_quantize(a), "fp8_amax");
+}
+
+fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                        fp8_format fmt, fp8_granularity gran, uint32_t flags, fp8_amax_history* hist,
+                        uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out, fp8_diag* diag,
+                        void* stream) {
+    fp8_status st = check_matrix_in(x, in_dtype, rows, cols, ld);
+    if (st != FP8_OK) return st;
+    if (fmt != FP8_E4M3 && fmt != FP8_E5M2)
+        return fail(FP8_ERR_INVALID_ARG, "format %d is not FP8_E4M3 or FP8_E5M2", (int)fmt);
+    if (!valid_gran(gran)) return fail(FP8_ERR_INVALID_ARG, "granularity %d is not a fp8_granularity", (int)gran);
+    if (flags & ~(FP8_SCALE_POW2 | FP8_TRANSPOSE_OUT))
+        return fail(FP8_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~(FP8_SCALE_POW2 | FP8_TRANSPOSE_OUT));
+    const bool transpose = (flags & FP8_TRANSPOSE_OUT) != 0;
+    if (transpose && gran != FP8_GRAN_TENSOR)
+        return fail(FP8_ERR_INVALID_ARG, "FP8_TRANSPOSE_OUT needs FP8_GRAN_TENSOR");
+    if (hist != nullptr && gran != FP8_GRAN_TENSOR)
+        return fail(FP8_ERR_INVALID_ARG, "delayed scaling (hist != NULL) needs FP8_GRAN_TENSOR");
+    if (hist != nullptr && !is_aligned(hist, 16)) return fail(FP8_ERR_MISALIGNED, "hist must be 16-byte aligned");
+    if (q == nullptr && rows > 0 && cols > 0) return fail(FP8_ERR_INVALID_ARG, "q is NULL");
+    const int64_t qcols = transpose ? rows : cols;
+    if (ldq < qcols || ldq < 1)
+        return fail(FP8_ERR_INVALID_ARG, "ldq=%lld must be >= %s=%lld", (long long)ldq,
+                    transpose ? "rows (transposed output)" : "cols", (long long)qcols);
+    const int64_t ng = num_groups(gran, rows, cols);
+    if (scale_inv_out == nullptr && ng > 0) return fail(FP8_ERR_INVALID_ARG, "scale_inv_out is NULL");
+    if (amax_out == nullptr && ng > 0) return fail(FP8_ERR_INVALID_ARG, "amax_out is NULL");
+    if (!is_aligned(scale_inv_out, 4) || !is_aligned(amax_out, 4))
+        return fail(FP8_ERR_MISALIGNED, "scale_inv_out and amax_out must be 4-byte aligned");
+    if (diag != nullptr && !is_aligned(diag, 4)) return fail(FP8_ERR_MISALIGNED, "diag must be 4-byte aligned");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    if (num_groups(gran, rows, cols) == 0) return ok();
+    fp8mi::QuantArgs a;
+    a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
+    a.fmt = fmt; a.gran = gran; a.pow2 = (flags & FP8_SCALE_POW2) != 0; a.transpose = transpose;
+    a.write_q = true; a.hist = hist; a.q = q; a.ldq = ldq; a.scale_inv = scale_inv_out;
+    a.amax = amax_out; a.diag = diag; a.stream = (hipStream_t)stream; a.num_cus = cus;
+    return launch_result(fp8mi::launch_quantize(a), "fp8_quantize");
+}
+
+static fp8_status check_gemm_common(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M,
+                                    int64_t N, int64_t K, const float* sa, const float* sb, void* C,
+                                    int out_dtype, int64_t ldc) {
+    if ((A == nullptr && M > 0 && K > 0) || (B == nullptr && N > 0 && K > 0))
+        return fail(FP8_ERR_INVALID_ARG, "A or B is NULL");
+    if (C == nullptr && M > 0 && N > 0) return fail(FP8_ERR_INVALID_ARG, "C is NULL");
+    if ((sa == nullptr || sb == nullptr) && M > 0 && N > 0)
+        return fail(FP8_ERR_INVALID_ARG, "a_scale_inv or b_scale_inv is NULL");
+    if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16)
+        return fail(FP8_ERR_INVALID_ARG, "out_dtype %d is not FP8_OUT_F32 or FP8_OUT_BF16", out_dtype);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(FP8_ERR_INVALID_ARG, "negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                    (long long)K);
+    if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M, N and K must each be < 2^31");
+    if (K % 16 != 0) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld must be a multiple of 16", (long long)K);
+    if (K > 0) {
+        if (lda < K || ldb < K) return fail(FP8_ERR_INVALID_ARG, "lda and ldb must be >= K");
+        if (!is_aligned(A, 16) || !is_aligned(B, 16))
+            return fail(FP8_ERR_MISALIGNED, "A and B must be 16-byte aligned");
+        if (lda % 16 != 0 || ldb % 16 != 0) return fail(FP8_ERR_MISALIGNED, "lda and ldb must be multiples of 16");
+    }
+    if (ldc < N || ldc < 1) return fail(FP8_ERR_INVALID_ARG, "ldc=%lld must be >= N", (long long)ldc);
+    if (!is_aligned(C, out_dtype == FP8_OUT_F32 ? 4 : 2))
+        return fail(FP8_ERR_MISALIGNED, "C is not aligned to its element size");
+    if (!is_aligned(sa, 4) || !is_aligned(sb, 4)) return fail(FP8_ERR_MISALIGNED, "scale arrays must be 4-byte aligned");
+    const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    if (tiles >= (int64_t(1) << 31)) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "too many output tiles");
+    return FP8_OK;
+}
+
+fp8_status fp8_scaled_gemm(const uint8_t* A, fp8_format fa, int64_t lda, const uint8_t* B, fp8_format fb,
+                           int64_t ldb, int64_t M, int64_t N, int64_t K, const float* a_scale_inv,
+                           int a_per_row, const float* b_scale_inv, int b_per_row, void* C,
+                           fp8_out_dtype out_dtype, int64_t ldc, void* stream) {
+    if ((fa != FP8_E4M3 && fa != FP8_E5M2) || (fb != FP8_E4M3 && fb != FP8_E5M2))
+        return fail(FP8_ERR_INVALID_ARG, "formats fa=%d fb=%d must be FP8_E4M3 or FP8_E5M2", (int)fa, (int)fb);
+    if ((a_per_row != 0 && a_per_row != 1) || (b_per_row != 0 && b_per_row != 1))
+        return fail(FP8_ERR_INVALID_ARG, "a_per_row and b_per_row must be 0 or 1");
+    fp8_status st = check_gemm_common(A, lda, B, ldb, M, N, K, a_scale_inv, b_scale_inv, C, out_dtype, ldc);
+    if (st != FP8_OK) return st;
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    fp8mi::GemmArgs g;
+    g.A = A; g.B = B; g.fa = fa; g.fb = fb; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N; g.K = K;
+    g.sa = a_scale_inv; g.sb = b_scale_inv; g.sa_per_row = a_per_row; g.sb_per_row = b_per_row;
+    g.C = C; g.out_bf16 = out_dtype == FP8_OUT_BF16; g.ldc = ldc; g.stream = (hipStream_t)stream;
+    g.num_cus = cus;
+    return launch_result(fp8mi::launch_scaled_gemm(g), "fp8_scaled_gemm");
+}
+
+fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M, int64_t N,
+                                int64_t K, const float* a_scale_inv, const float* b_scale_inv, void* C,
+                                fp8_out_dtype out_dtype, int64_t ldc, void* stream) {
+    fp8_status st = check_gemm_common(A, lda, B, ldb, M, N, K, a_scale_inv, b_scale_inv, C, out_dtype, ldc);
+    if (st != FP8_OK) return st;
+    if (K == 0 || K % 128 != 0 || N % 128 != 0)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "block-scaled GEMM needs K > 0, K %% 128 == 0 and N %% 128 == 0 (K=%lld N=%lld)",
+                    (long long)K, (long long)N);
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    fp8mi::GemmArgs g;
+    g.A = A; g.B = B; g.fa = FP8_E4M3; g.fb = FP8_E4M3; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N; g.K = K;
+    g.sa = a_scale_inv; g.sb = b_scale_inv; g.sa_per_row = true; g.sb_per_row = true;
+    g.C = C; g.out_bf16 = out_dtype == FP8_OUT_BF16; g.ldc = ldc; g.stream = (hipStream_t)stream;
+    g.num_cus = cus;
+    return launch_result(fp8mi::launch_blockscaled_gemm(g), "fp8_blockscaled_gemm");
+}
+
+}  // extern "C"

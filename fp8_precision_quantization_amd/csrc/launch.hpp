@@ -1,0 +1,56 @@
+// launch.hpp -- internal host-side interface between the C-ABI layer
+// (api.cpp) and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8mi.h"
+
+namespace fp8mi {
+
+struct QuantArgs {
+    const void* x = nullptr;
+    bool in_bf16 = true;
+    int64_t rows = 0, cols = 0, ld = 0;
+    int fmt = 0;                 // 0 = E4M3, 1 = E5M2
+    int gran = 0;                // fp8_granularity
+    bool pow2 = false;
+    bool transpose = false;
+    bool write_q = true;         // false: amax only (fp8_amax)
+    fp8_amax_history* hist = nullptr;
+    uint8_t* q = nullptr;
+    int64_t ldq = 0;
+    float* scale_inv = nullptr;
+    float* amax = nullptr;
+    fp8_diag* diag = nullptr;
+    hipStream_t stream = nullptr;
+    int num_cus = 256;
+};
+
+struct GemmArgs {
+    const uint8_t* A = nullptr;
+    const uint8_t* B = nullptr;
+    int fa = 0, fb = 0;
+    int64_t lda = 0, ldb = 0;
+    int64_t M = 0, N = 0, K = 0;
+    const float* sa = nullptr;
+    const float* sb = nullptr;
+    bool sa_per_row = false, sb_per_row = false;
+    void* C = nullptr;
+    bool out_bf16 = true;
+    int64_t ldc = 0;
+    hipStream_t stream = nullptr;
+    int num_cus = 256;
+    int tile_override = -1;      // -1: heuristic; otherwise a tile-config id
+};
+
+hipError_t launch_quantize(const QuantArgs& a);
+hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream);
+hipError_t launch_scaled_gemm(const GemmArgs& a);
+hipError_t launch_blockscaled_gemm(const GemmArgs& a);
+
+// Unit count of the element-wise tensor kernels must fit in 31 bits.
+constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;
+
+}  // namespace fp8mi

@@ -1,0 +1,755 @@
+// quantize.hip -- amax reduction, scale and saturating RNE cast to E4M3/E5M2
+// on gfx950, at tensor / row / 1x128 / 128x128 granularity, just in time or
+// delayed from an amax-history ring, optionally written transposed.
+//
+// Method ([DeepL bets on FP8, hmyw.cn] 2.3): a scaling factor per tensor, per
+// row or per block maps the values into FP8's range; delayed scaling takes the
+// factor from previous steps' statistics instead of a synchronous amax.
+// [Soup, lbrq.cn] recipe table: rowwise scales are powers of two.
+//
+// All kernels stream HBM with 16-byte loads along rows: a "unit" is 8
+// consecutive elements of one row (16 B of bf16, 32 B of fp32) that becomes
+// 8 code bytes.  amax is a max over binary32 magnitude bits (exact, order
+// free).  Every kernel is memory bound; the per-element ALU work is a bf16
+// unpack, one multiply, a 4-instruction saturation clamp and half a packed
+// convert.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8mi {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------ data units --
+template <typename InT> struct Pack;
+
+template <> struct Pack<uint16_t> {          // 8 bf16 values packed in 4 words
+    uint32_t w[4];
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t v = w[i >> 1];
+        return __uint_as_float((i & 1) ? (v & 0xFFFF0000u) : (v << 16));
+    }
+    __device__ __forceinline__ uint32_t abs_max() const {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t hi = w[i] & 0x7FFF0000u;
+            const uint32_t lo = (w[i] << 16) & 0x7FFF0000u;
+            m = max(m, max(hi, lo));
+        }
+        return m;
+    }
+};
+
+template <> struct Pack<float> {             // 8 fp32 values
+    uint32_t w[8];
+    __device__ __forceinline__ float get(int i) const { return __uint_as_float(w[i]); }
+    __device__ __forceinline__ uint32_t abs_max() const {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = max(m, w[i] & 0x7FFFFFFFu);
+        return m;
+    }
+};
+
+// Load `nvalid` (0..8) elements starting at x + off; missing ones are 0.
+// `vec`: x + off is 16-byte aligned and the unit is whole.
+template <typename InT>
+__device__ __forceinline__ Pack<InT> load_unit(const InT* __restrict__ x, int64_t off, int nvalid,
+                                               bool vec) {
+    Pack<InT> p;
+    if constexpr (sizeof(InT) == 2) {
+        if (vec && nvalid == 8) {
+            const uint4 r = *reinterpret_cast<const uint4*>(x + off);
+            p.w[0] = r.x; p.w[1] = r.y; p.w[2] = r.z; p.w[3] = r.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = (2 * i < nvalid) ? (uint32_t)x[off + 2 * i] : 0u;
+                const uint32_t hi = (2 * i + 1 < nvalid) ? (uint32_t)x[off + 2 * i + 1] : 0u;
+                p.w[i] = lo | (hi << 16);
+            }
+        }
+    } else {
+        if (vec && nvalid == 8) {
+            const uint4 r0 = *reinterpret_cast<const uint4*>(x + off);
+            const uint4 r1 = *reinterpret_cast<const uint4*>(x + off + 4);
+            p.w[0] = r0.x; p.w[1] = r0.y; p.w[2] = r0.z; p.w[3] = r0.w;
+            p.w[4] = r1.x; p.w[5] = r1.y; p.w[6] = r1.z; p.w[7] = r1.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p.w[i] = (i < nvalid) ? __float_as_uint(x[off + i]) : 0u;
+        }
+    }
+    return p;
+}
+
+struct Counters {
+    uint32_t sat = 0, nonfinite = 0, under = 0;
+};
+
+// Encode a unit with scale s; optionally count the diagnostics.
+template <int FMT, bool DIAG, typename InT>
+__device__ __forceinline__ uint2 encode_unit(const Pack<InT>& p, float s, Counters& cnt) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p.get(i) * s;
+    uint2 out;
+    out.x = encode4<FMT>(v[0], v[1], v[2], v[3]);
+    out.y = encode4<FMT>(v[4], v[5], v[6], v[7]);
+    // The convert instructions give every NaN one canonical code (E4M3 0xFF,
+    // E5M2 0xFE) whatever its sign, and after the clamp no other input can
+    // produce that byte.  A has-zero-byte test on code ^ canonical finds them
+    // (about one instruction per element); the rare fix-up writes the NaN
+    // code 0x7F with the input's sign.
+    constexpr uint32_t kHwNaN = FMT == kE4M3 ? 0xFFFFFFFFu : 0xFEFEFEFEu;
+    const uint32_t nx = out.x ^ kHwNaN, ny = out.y ^ kHwNaN;
+    if (__builtin_expect(((((nx - 0x01010101u) & ~nx) | ((ny - 0x01010101u) & ~ny)) & 0x80808080u) != 0u, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t bx = __float_as_uint(p.get(i));
+            if ((bx & 0x7FFFFFFFu) > kInfBits) {
+                const uint32_t code = 0x7Fu | ((bx >> 24) & 0x80u);
+                const int sh = 8 * (i & 3);
+                uint32_t& w = (i < 4) ? out.x : out.y;
+                w = (w & ~(0xFFu << sh)) | (code << sh);
+            }
+        }
+    }
+    if constexpr (DIAG) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t ax = __float_as_uint(p.get(i)) & 0x7FFFFFFFu;
+            const uint32_t av = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+            const uint32_t code = ((i < 4 ? out.x : out.y) >> (8 * (i & 3))) & 0xFFu;
+            cnt.nonfinite += (ax >= kInfBits) ? 1u : 0u;
+            cnt.sat += (av > FmtTraits<FMT>::kMaxBits && av <= kInfBits) ? 1u : 0u;
+            cnt.under += (ax != 0u && ax <= kInfBits && (code & 0x7Fu) == 0u) ? 1u : 0u;
+        }
+    }
+    return out;
+}
+
+__device__ __forceinline__ void store_unit(uint8_t* __restrict__ q, int64_t off, int nvalid,
+                                           bool vec, uint2 codes) {
+    if (vec && nvalid == 8) {
+        *reinterpret_cast<uint2*>(q + off) = codes;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nvalid) q[off + i] = (uint8_t)(((i < 4 ? codes.x : codes.y) >> (8 * (i & 3))) & 0xFFu);
+    }
+}
+
+// Unit u of a [rows x cols] matrix: rows == 1 is the flat (contiguous) case.
+struct UnitGeom {
+    int64_t rows, cols, ld, ldq;
+    uint32_t upr;      // units per row
+    uint32_t units;    // rows * upr
+    __device__ __forceinline__ void locate(uint32_t u, int64_t& off, int64_t& qoff, int& nvalid) const {
+        int64_t r, c;
+        if (rows == 1) {
+            r = 0;
+            c = (int64_t)u * 8;
+        } else {
+            const uint32_t rr = u / upr;
+            r = rr;
+            c = (int64_t)(u - rr * upr) * 8;
+        }
+        off = r * ld + c;
+        qoff = r * ldq + c;
+        const int64_t rem = cols - c;
+        nvalid = rem >= 8 ? 8 : (int)rem;
+    }
+};
+
+// Block-wide max / sums into thread 0 (256 threads = 4 waves).
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
+    v = wave_max_u32(v);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();
+    if (lane == 0) lds[w] = v;
+    __syncthreads();
+    uint32_t r = 0;
+    if (threadIdx.x == 0) r = max(max(lds[0], lds[1]), max(lds[2], lds[3]));
+    return r;
+}
+
+__device__ __forceinline__ void block_add_diag(Counters c, uint32_t* lds, fp8_diag* diag) {
+    c.sat = wave_sum_u32(c.sat);
+    c.nonfinite = wave_sum_u32(c.nonfinite);
+    c.under = wave_sum_u32(c.under);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();
+    if (lane == 0) { lds[4 + w] = c.sat; lds[8 + w] = c.nonfinite; lds[12 + w] = c.under; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t s = lds[4] + lds[5] + lds[6] + lds[7];
+        const uint32_t n = lds[8] + lds[9] + lds[10] + lds[11];
+        const uint32_t u = lds[12] + lds[13] + lds[14] + lds[15];
+        if (s) atomicAdd(&diag->sat_count, s);
+        if (n) atomicAdd(&diag->nonfinite_count, n);
+        if (u) atomicAdd(&diag->underflow_count, u);
+    }
+}
+
+__device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Delayed scale ([DeepL] 2.3): max over the history window; with an empty
+// history the bootstrap amax of the current step (already reduced into
+// cur_amax_bits by the preceding kernel).
+template <int FMT>
+__device__ __forceinline__ float delayed_scale(fp8_amax_history* h, bool pow2) {
+    const int32_t count = (int32_t)load_relaxed(reinterpret_cast<const uint32_t*>(&h->count));
+    uint32_t basis = 0;
+    if (count <= 0) {
+        basis = load_relaxed(&h->cur_amax_bits);
+    } else {
+        const int n = count > 16 ? 16 : count;
+        for (int i = 0; i < n; ++i)
+            basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
+    }
+    return scale_from_amax_bits<FMT>(basis, pow2);
+}
+
+// The last block of a delayed cast pushes the step's amax into the ring and
+// precomputes the next scale.  Every other block has read the ring before its
+// atomicAdd on blocks_done, so the update cannot race with those reads.
+template <int FMT>
+__device__ void delayed_finish(fp8_amax_history* h, uint32_t block_amax, bool pow2,
+                               float* amax_out, uint32_t* lds) {
+    __shared__ bool is_last;
+    if (threadIdx.x == 0) {
+        atomicMax(&h->cur_amax_bits, block_amax);
+        __threadfence();
+        const uint32_t prev = atomicAdd(&h->blocks_done, 1u);
+        is_last = (prev == gridDim.x * gridDim.y - 1);
+    }
+    __syncthreads();
+    if (is_last && threadIdx.x == 0) {
+        __threadfence();
+        const uint32_t cur = atomicAdd(&h->cur_amax_bits, 0u);
+        const float amax_now = __uint_as_float(cur);
+        amax_out[0] = amax_now;
+        int32_t len = h->len;
+        len = len < 1 ? 1 : (len > 16 ? 16 : len);
+        int32_t pos = h->pos;
+        pos = (pos < 0 || pos >= len) ? 0 : pos;
+        h->amax[pos] = amax_now;
+        h->pos = (pos + 1) % len;
+        const int32_t count = h->count < len ? h->count + 1 : len;
+        h->count = count;
+        uint32_t basis = 0;
+        for (int i = 0; i < count; ++i) basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
+        const float s = scale_from_amax_bits<FMT>(basis, pow2);
+        h->scale = s;
+        h->scale_inv = 1.0f / s;
+        h->steps = h->steps + 1;
+        h->cur_amax_bits = 0u;
+        h->blocks_done = 0u;
+        __threadfence();
+    }
+}
+
+// ------------------------------------------------------------------ kernels --
+__global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ void k_history_init(fp8_amax_history* h, int32_t len) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(h);
+    const int i = threadIdx.x;
+    if (i < (int)(sizeof(fp8_amax_history) / 4)) w[i] = 0u;
+    __syncthreads();
+    if (i == 0) {
+        h->len = len;
+        h->scale = 1.0f;
+        h->scale_inv = 1.0f;
+    }
+}
+
+constexpr int kUnroll = 4;
+
+// Per-tensor amax: grid-stride over units, one atomicMax per block.
+// `gate` non-null: run only while the history is empty (delayed bootstrap).
+template <typename InT>
+__global__ __launch_bounds__(kThreads) void k_amax_tensor(const InT* __restrict__ x, UnitGeom g,
+                                                          bool vec_in, uint32_t* out,
+                                                          const fp8_amax_history* gate) {
+    __shared__ uint32_t lds[16];
+    if (gate != nullptr &&
+        load_relaxed(reinterpret_cast<const uint32_t*>(&gate->count)) != 0u)
+        return;
+    const uint32_t stride = gridDim.x * kThreads;
+    uint32_t m = 0;
+    for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < g.units; u0 += stride * kUnroll) {
+        Pack<InT> p[kUnroll];
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const uint32_t u = u0 + i * stride;
+            if (u < g.units) {
+                int64_t off, qoff; int nv;
+                g.locate(u, off, qoff, nv);
+                p[i] = load_unit<InT>(x, off, nv, vec_in);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i)
+            if (u0 + i * stride < g.units) m = max(m, p[i].abs_max());
+    }
+    const uint32_t bm = block_max(m, lds);
+    if (threadIdx.x == 0 && bm != 0u) atomicMax(out, bm);
+}
+
+// Per-tensor cast.  JIT: s from the reduced amax (amax_bits_in).  DELAYED:
+// s from the history; the block's amax is folded into the ring at the end.
+template <typename InT, int FMT, bool DELAYED, bool DIAG>
+__global__ __launch_bounds__(kThreads) void k_cast_tensor(
+    const InT* __restrict__ x, UnitGeom g, bool vec_in, uint8_t* __restrict__ q, bool vec_out,
+    const uint32_t* amax_bits_in, fp8_amax_history* hist, bool pow2,
+    float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag) {
+    __shared__ uint32_t lds[16];
+    float s;
+    if constexpr (DELAYED) s = delayed_scale<FMT>(hist, pow2);
+    else s = scale_from_amax_bits<FMT>(load_relaxed(amax_bits_in), pow2);
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
+
+    const uint32_t stride = gridDim.x * kThreads;
+    uint32_t m = 0;
+    Counters cnt;
+    for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < g.units; u0 += stride * kUnroll) {
+        Pack<InT> p[kUnroll];
+        int64_t qo[kUnroll];
+        int nv[kUnroll];
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const uint32_t u = u0 + i * stride;
+            nv[i] = 0;
+            qo[i] = 0;
+            if (u < g.units) {
+                int64_t off;
+                g.locate(u, off, qo[i], nv[i]);
+                p[i] = load_unit<InT>(x, off, nv[i], vec_in);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            if (nv[i] > 0) {
+                if constexpr (DELAYED) m = max(m, p[i].abs_max());
+                store_unit(q, qo[i], nv[i], vec_out, encode_unit<FMT, DIAG>(p[i], s, cnt));
+            }
+        }
+    }
+    if constexpr (DIAG) block_add_diag(cnt, lds, diag);
+    if constexpr (DELAYED) {
+        const uint32_t bm = block_max(m, lds);
+        delayed_finish<FMT>(hist, bm, pow2, amax_out, lds);
+    }
+}
+
+// Per-tensor cast written transposed: q[c][r] (the wgrad operands).  One
+// 128x128 tile per block; codes go through LDS with a 16-chunk XOR swizzle so
+// that both the row-wise writes and the column gathers are conflict free,
+// and each output row segment leaves as 16-byte stores (128 B per 8 lanes).
+template <typename InT, int FMT, bool DELAYED, bool DIAG>
+__global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
+    const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
+    uint8_t* __restrict__ q, int64_t ldq, bool vec_out16, const uint32_t* amax_bits_in,
+    fp8_amax_history* hist, bool pow2, float* __restrict__ scale_inv_out,
+    float* __restrict__ amax_out, fp8_diag* diag) {
+    __shared__ uint32_t lds[16];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 128];
+    float s;
+    if constexpr (DELAYED) s = delayed_scale<FMT>(hist, pow2);
+    else s = scale_from_amax_bits<FMT>(load_relaxed(amax_bits_in), pow2);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
+
+    const int t = threadIdx.x;
+    const int cu = t & 15, rr = t >> 4;
+    const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+    const int64_t c = c0 + cu * 8;
+    const int nvc = (int)(cols - c >= 8 ? 8 : (cols - c > 0 ? cols - c : 0));
+    uint32_t m = 0;
+    Counters cnt;
+    Pack<InT> p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + rr + 16 * i;
+        const int nv = (r < rows) ? nvc : 0;
+        if (nv > 0) p[i] = load_unit<InT>(x, r * ld + c, nv, vec_in);
+        else {
+#pragma unroll
+            for (int k = 0; k < (int)(sizeof(p[i].w) / 4); ++k) p[i].w[k] = 0u;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = rr + 16 * i;
+        if constexpr (DELAYED) m = max(m, p[i].abs_max());
+        const uint2 codes = encode_unit<FMT, DIAG>(p[i], s, cnt);
+        const int pos = cu ^ ((r >> 4) & 15);
+        *reinterpret_cast<uint2*>(&tile[r * 128 + pos * 8]) = codes;
+    }
+    __syncthreads();
+    // gather: chunk = (output row cl in 0..127, input-row segment rs in 0..7)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int chunk = t + 256 * j;
+        const int cl = chunk >> 3, rs = chunk & 7;
+        const int pos = (cl >> 3) ^ rs;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int r = rs * 16 + k * 4 + b;
+                acc |= (uint32_t)tile[r * 128 + pos * 8 + (cl & 7)] << (8 * b);
+            }
+            w[k] = acc;
+        }
+        const int64_t orow = c0 + cl;
+        const int64_t ocol = r0 + rs * 16;
+        if (orow < cols && ocol < rows) {
+            uint8_t* dst = q + orow * ldq + ocol;
+            const int64_t remr = rows - ocol;
+            if (vec_out16 && remr >= 16) {
+                *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                for (int b = 0; b < 16 && b < remr; ++b) dst[b] = (uint8_t)((w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+            }
+        }
+    }
+    if constexpr (DIAG) block_add_diag(cnt, lds, diag);
+    if constexpr (DELAYED) {
+        const uint32_t bm = block_max(m, lds);
+        delayed_finish<FMT>(hist, bm, pow2, amax_out, lds);
+    }
+}
+
+// Row-wise: one wave per row, the row held in registers when it has at most
+// 64*NU units (a second read otherwise).  [DeepL] 2.3 (per-row scaling of
+// activations); [Soup] rowwise recipe (power-of-two scales).
+template <typename InT, int FMT, bool DIAG, bool WRITE_Q, int NU = 8>
+__global__ __launch_bounds__(kThreads) void k_cast_rows(
+    const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
+    uint8_t* __restrict__ q, int64_t ldq, bool vec_out, bool pow2,
+    float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag) {
+    __shared__ uint32_t lds[16];
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const bool active = r < rows;
+    const int64_t upr = (cols + 7) / 8;
+    const InT* xr = x + (active ? r : 0) * ld;
+    uint8_t* qr = q + (active ? r : 0) * ldq;
+    Counters cnt;
+    if (upr <= 64 * NU) {
+        Pack<InT> p[NU];
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int64_t u = lane + 64 * i;
+            if (active && u < upr) {
+                const int64_t c = u * 8;
+                const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
+                p[i] = load_unit<InT>(xr, c, nv, vec_in);
+                m = max(m, p[i].abs_max());
+            }
+        }
+        m = wave_max_u32(m);
+        const float s = scale_from_amax_bits<FMT>(m, pow2);
+        if (active && lane == 0) {
+            amax_out[r] = __uint_as_float(m);
+            if (WRITE_Q) scale_inv_out[r] = recip_rn(s);
+        }
+        if constexpr (WRITE_Q) {
+#pragma unroll
+            for (int i = 0; i < NU; ++i) {
+                const int64_t u = lane + 64 * i;
+                if (active && u < upr) {
+                    const int64_t c = u * 8;
+                    const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
+                    store_unit(qr, c, nv, vec_out, encode_unit<FMT, DIAG>(p[i], s, cnt));
+                }
+            }
+        }
+    } else {
+        uint32_t m = 0;
+        for (int64_t u = lane; active && u < upr; u += 64) {
+            const int64_t c = u * 8;
+            const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
+            m = max(m, load_unit<InT>(xr, c, nv, vec_in).abs_max());
+        }
+        m = wave_max_u32(m);
+        const float s = scale_from_amax_bits<FMT>(m, pow2);
+        if (active && lane == 0) {
+            amax_out[r] = __uint_as_float(m);
+            if (WRITE_Q) scale_inv_out[r] = recip_rn(s);
+        }
+        if constexpr (WRITE_Q) {
+            for (int64_t u = lane; active && u < upr; u += 64) {
+                const int64_t c = u * 8;
+                const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
+                store_unit(qr, c, nv, vec_out,
+                           encode_unit<FMT, DIAG>(load_unit<InT>(xr, c, nv, vec_in), s, cnt));
+            }
+        }
+    }
+    if constexpr (DIAG) block_add_diag(cnt, lds, diag);
+}
+
+// 1x128 blocks: 16 lanes per block of 128 elements, UNR blocks per lane in
+// flight.  amax/scale arrays are [rows x ceil(cols/128)].
+template <typename InT, int FMT, bool DIAG, bool WRITE_Q>
+__global__ __launch_bounds__(kThreads) void k_cast_1x128(
+    const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
+    uint8_t* __restrict__ q, int64_t ldq, bool vec_out, bool pow2,
+    float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag) {
+    __shared__ uint32_t lds[16];
+    const int64_t gc = (cols + 127) / 128;
+    const int64_t G = rows * gc;
+    const int slot = threadIdx.x >> 4, j = threadIdx.x & 15;
+    const int64_t stride = (int64_t)gridDim.x * 16;
+    Counters cnt;
+    for (int64_t g0 = (int64_t)blockIdx.x * 16 + slot; g0 - slot < G; g0 += stride * kUnroll) {
+        Pack<InT> p[kUnroll];
+        uint32_t m[kUnroll];
+        int nv[kUnroll];
+        int64_t xo[kUnroll], qo[kUnroll];
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const int64_t g = g0 + i * stride;
+            m[i] = 0; nv[i] = 0; xo[i] = 0; qo[i] = 0;
+            if (g < G) {
+                const int64_t r = g / gc, kb = g - r * gc;
+                const int64_t c = kb * 128 + j * 8;
+                nv[i] = cols - c >= 8 ? 8 : (cols - c > 0 ? (int)(cols - c) : 0);
+                xo[i] = r * ld + c;
+                qo[i] = r * ldq + c;
+                if (nv[i] > 0) {
+                    p[i] = load_unit<InT>(x, xo[i], nv[i], vec_in);
+                    m[i] = p[i].abs_max();
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const uint32_t gm = group_max_u32<16>(m[i]);
+            const int64_t g = g0 + i * stride;
+            if (g < G) {
+                const float s = scale_from_amax_bits<FMT>(gm, pow2);
+                if (j == 0) {
+                    amax_out[g] = __uint_as_float(gm);
+                    if (WRITE_Q) scale_inv_out[g] = recip_rn(s);
+                }
+                if constexpr (WRITE_Q) {
+                    if (nv[i] > 0) store_unit(q, qo[i], nv[i], vec_out, encode_unit<FMT, DIAG>(p[i], s, cnt));
+                }
+            }
+        }
+    }
+    if constexpr (DIAG) block_add_diag(cnt, lds, diag);
+}
+
+// 128x128 blocks: one workgroup per block, 8 units per thread held in
+// registers.  amax/scale arrays are [ceil(rows/128) x ceil(cols/128)].
+template <typename InT, int FMT, bool DIAG, bool WRITE_Q>
+__global__ __launch_bounds__(kThreads) void k_cast_128x128(
+    const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
+    uint8_t* __restrict__ q, int64_t ldq, bool vec_out, bool pow2,
+    float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag) {
+    __shared__ uint32_t lds[16];
+    const int t = threadIdx.x;
+    const int cu = t & 15, rr = t >> 4;
+    const int64_t r0 = (int64_t)blockIdx.y * 128;
+    const int64_t c = (int64_t)blockIdx.x * 128 + cu * 8;
+    const int nvc = (int)(cols - c >= 8 ? 8 : (cols - c > 0 ? cols - c : 0));
+    Pack<InT> p[8];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + rr + 16 * i;
+        if (r < rows && nvc > 0) {
+            p[i] = load_unit<InT>(x, r * ld + c, nvc, vec_in);
+            m = max(m, p[i].abs_max());
+        }
+    }
+    const uint32_t bm0 = block_max(m, lds);
+    __shared__ uint32_t bcast;
+    if (t == 0) bcast = bm0;
+    __syncthreads();
+    const uint32_t bm = bcast;
+    const float s = scale_from_amax_bits<FMT>(bm, pow2);
+    const int64_t g = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    if (t == 0) {
+        amax_out[g] = __uint_as_float(bm);
+        if (WRITE_Q) scale_inv_out[g] = recip_rn(s);
+    }
+    Counters cnt;
+    if constexpr (WRITE_Q) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + rr + 16 * i;
+            if (r < rows && nvc > 0)
+                store_unit(q, r * ldq + c, nvc, vec_out, encode_unit<FMT, DIAG>(p[i], s, cnt));
+        }
+    }
+    if constexpr (DIAG) block_add_diag(cnt, lds, diag);
+}
+
+// ---------------------------------------------------------------- host side --
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
+    int64_t b = (work_items + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > cap) b = cap;
+    return (unsigned)b;
+}
+
+template <typename InT, int FMT>
+hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz);
+
+template <typename InT, int FMT>
+hipError_t quantize_typed(const QuantArgs& a) {
+    const InT* x = static_cast<const InT*>(a.x);
+    const int esz = (int)sizeof(InT);
+    // an empty tensor still yields its scale (1) and amax (0) through the flat path
+    QuantArgs a_eff = a;
+    if (a.rows == 0 || a.cols == 0) a_eff.transpose = false;
+    return quantize_geom<InT, FMT>(a_eff, x, esz);
+}
+
+template <typename InT, int FMT>
+hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
+    const bool diag = a.diag != nullptr;
+    const bool contiguous_in = a.ld == a.cols;
+    const bool contiguous_out = !a.write_q || a.transpose || a.ldq == a.cols;
+    // 2-D geometry, or the flat view of a contiguous matrix
+    UnitGeom g;
+    if (contiguous_in && contiguous_out && !a.transpose) {
+        g.rows = 1; g.cols = a.rows * a.cols; g.ld = g.cols; g.ldq = g.cols;
+    } else {
+        g.rows = a.rows; g.cols = a.cols; g.ld = a.ld; g.ldq = a.ldq;
+    }
+    g.upr = (uint32_t)((g.cols + 7) / 8);
+    g.units = (uint32_t)(g.rows * (int64_t)g.upr);
+    const bool vec_in = aligned(x, 16) && (g.rows == 1 || (g.ld * esz) % 16 == 0);
+    const bool vec_out = a.q != nullptr && aligned(a.q, 8) && (g.rows == 1 || g.ldq % 8 == 0);
+    const unsigned cap = (unsigned)(a.num_cus * 8);
+    hipStream_t st = a.stream;
+
+    if (a.gran == FP8_GRAN_TENSOR) {
+        const unsigned grid = grid_for(g.units, (int64_t)kThreads * kUnroll, cap);
+        if (a.hist == nullptr) {
+            uint32_t* amax_bits = reinterpret_cast<uint32_t*>(a.amax);
+            hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, amax_bits, 0u, 1);
+            hipLaunchKernelGGL(k_amax_tensor<InT>, dim3(grid), dim3(kThreads), 0, st, x, g, vec_in,
+                               amax_bits, (const fp8_amax_history*)nullptr);
+            if (!a.write_q) return hipGetLastError();
+            if (a.transpose) {
+                dim3 tg((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
+                const bool v16 = aligned(a.q, 16) && a.ldq % 16 == 0;
+                if (diag)
+                    hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, false, true>), tg, dim3(kThreads), 0, st,
+                                       x, a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, amax_bits,
+                                       a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
+                else
+                    hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, false, false>), tg, dim3(kThreads), 0, st,
+                                       x, a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, amax_bits,
+                                       a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
+            } else {
+                if (diag)
+                    hipLaunchKernelGGL((k_cast_tensor<InT, FMT, false, true>), dim3(grid), dim3(kThreads), 0,
+                                       st, x, g, vec_in, a.q, vec_out, amax_bits, a.hist, a.pow2,
+                                       a.scale_inv, a.amax, a.diag);
+                else
+                    hipLaunchKernelGGL((k_cast_tensor<InT, FMT, false, false>), dim3(grid), dim3(kThreads), 0,
+                                       st, x, g, vec_in, a.q, vec_out, amax_bits, a.hist, a.pow2,
+                                       a.scale_inv, a.amax, a.diag);
+            }
+            return hipGetLastError();
+        }
+        // delayed: bootstrap amax only while the history is empty, then one pass
+        hipLaunchKernelGGL(k_amax_tensor<InT>, dim3(grid), dim3(kThreads), 0, st, x, g, vec_in,
+                           &a.hist->cur_amax_bits, (const fp8_amax_history*)a.hist);
+        if (a.transpose) {
+            dim3 tg((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
+            const bool v16 = aligned(a.q, 16) && a.ldq % 16 == 0;
+            if (diag)
+                hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, true, true>), tg, dim3(kThreads), 0, st, x,
+                                   a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, (const uint32_t*)nullptr,
+                                   a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
+            else
+                hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, true, false>), tg, dim3(kThreads), 0, st, x,
+                                   a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, (const uint32_t*)nullptr,
+                                   a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
+        } else {
+            if (diag)
+                hipLaunchKernelGGL((k_cast_tensor<InT, FMT, true, true>), dim3(grid), dim3(kThreads), 0, st,
+                                   x, g, vec_in, a.q, vec_out, (const uint32_t*)nullptr, a.hist, a.pow2,
+                                   a.scale_inv, a.amax, a.diag);
+            else
+                hipLaunchKernelGGL((k_cast_tensor<InT, FMT, true, false>), dim3(grid), dim3(kThreads), 0, st,
+                                   x, g, vec_in, a.q, vec_out, (const uint32_t*)nullptr, a.hist, a.pow2,
+                                   a.scale_inv, a.amax, a.diag);
+        }
+        return hipGetLastError();
+    }
+
+    // group granularities: the 2-D geometry always
+    const bool gvec_in = aligned(x, 16) && (a.ld * esz) % 16 == 0;
+    const bool gvec_out = a.q != nullptr && aligned(a.q, 8) && a.ldq % 8 == 0;
+#define FP8MI_GROUP_LAUNCH(KERNEL, GRID)                                                          \
+    do {                                                                                          \
+        if (!a.write_q)                                                                           \
+            hipLaunchKernelGGL((KERNEL<InT, FMT, false, false>), GRID, dim3(kThreads), 0, st, x,  \
+                               a.rows, a.cols, a.ld, gvec_in, a.q, a.ldq, gvec_out, a.pow2,       \
+                               a.scale_inv, a.amax, a.diag);                                      \
+        else if (diag)                                                                            \
+            hipLaunchKernelGGL((KERNEL<InT, FMT, true, true>), GRID, dim3(kThreads), 0, st, x,    \
+                               a.rows, a.cols, a.ld, gvec_in, a.q, a.ldq, gvec_out, a.pow2,       \
+                               a.scale_inv, a.amax, a.diag);                                      \
+        else                                                                                      \
+            hipLaunchKernelGGL((KERNEL<InT, FMT, false, true>), GRID, dim3(kThreads), 0, st, x,   \
+                               a.rows, a.cols, a.ld, gvec_in, a.q, a.ldq, gvec_out, a.pow2,       \
+                               a.scale_inv, a.amax, a.diag);                                      \
+    } while (0)
+
+    if (a.gran == FP8_GRAN_ROW) {
+        const dim3 grid((unsigned)((a.rows + 3) / 4));
+        // rows up to 4096 elements are held in registers
+        FP8MI_GROUP_LAUNCH(k_cast_rows, grid);
+    } else if (a.gran == FP8_GRAN_BLOCK_1x128) {
+        const int64_t G = a.rows * ((a.cols + 127) / 128);
+        const dim3 grid(grid_for(G, 16 * kUnroll, (int64_t)a.num_cus * 8));
+        FP8MI_GROUP_LAUNCH(k_cast_1x128, grid);
+    } else {
+        const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
+        FP8MI_GROUP_LAUNCH(k_cast_128x128, grid);
+    }
+#undef FP8MI_GROUP_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a) {
+    if (a.in_bf16) {
+        return a.fmt == 0 ? quantize_typed<uint16_t, kE4M3>(a) : quantize_typed<uint16_t, kE5M2>(a);
+    }
+    return a.fmt == 0 ? quantize_typed<float, kE4M3>(a) : quantize_typed<float, kE5M2>(a);
+}
+
+hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream) {
+    hipLaunchKernelGGL(k_history_init, dim3(1), dim3(64), 0, stream, h, len);
+    return hipGetLastError();
+}
+
+}  // namespace fp8mi

@@ -1,0 +1,204 @@
+/*
+ * fp8mi.h -- C ABI of the MI355X (gfx950) FP8 scaled-quantization and
+ * scaled-GEMM library (libfp8mi.so).
+ *
+ * The operations follow these web pages (cited by title, site and section):
+ *   [DeepL] "DeepL bets on FP8: unified-precision training and inference"
+ *           (hmyw.cn/news/121341): 2.1 format roles and bit splits, 2.2 cast of
+ *           the high-precision master weights to FP8 before every GEMM, 2.3
+ *           scaling factors at tensor / row / block granularity and delayed
+ *           scaling from previous steps' statistics, 4.2 per-layer max-abs and
+ *           scale diagnostics, 5.1 E5M2 gradient overflow, 5.3 FP8 GEMMs not
+ *           bit-identical across tilings.
+ *   [H100]  "H100 FP8 acceleration, measured" (scrxy.com/news/908489):
+ *           paragraph on the FP8 formats (jointly defined formats, E5M2 range
+ *           +-57344) and on FP8 matrix multiply-add in hardware.
+ *   [Soup]  "FP8 training and QAT ... with Soup on Hopper GPUs"
+ *           (lbrq.cn/news/198264): table of the tensorwise / rowwise (power-of-
+ *           two scales) recipes; configuration errors rejected up front with
+ *           an explicit message.
+ *   [Swift] "FP8 quantization support in ms-swift" (maplevalley.com.cn/news/
+ *           598486): E4M3 / E5M2 and the dynamic per-tensor method.
+ *
+ * Conventions for every entry point:
+ *   - All pointers except the ones documented as host pointers are DEVICE
+ *     pointers on the current HIP device.  The caller owns every buffer; the
+ *     library allocates and frees nothing and never synchronizes the stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call is asynchronous: it returns after host-side validation and
+ *     the kernel launches.  A fault inside a kernel surfaces at the caller's
+ *     next synchronization.
+ *   - Validation runs before any launch.  On any error nothing is launched
+ *     and no output is touched; fp8_last_error() returns a message that names
+ *     the offending argument (thread-local, valid until the next call).
+ *   - Only gfx950 is supported; any other device gives
+ *     FP8_ERR_UNSUPPORTED_DEVICE.
+ *   - Matrices are row-major with an explicit leading dimension (elements
+ *     between consecutive rows, >= the number of columns).
+ *   - Scale convention: dequantized value = decode(q) * scale_inv.
+ *   - Reentrant; the only global state is a per-device architecture cache.
+ */
+#ifndef FP8MI_H
+#define FP8MI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8MI_ABI_VERSION 1
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_INVALID_ARG = 1,        /* bad enum, NULL pointer, size <= 0, ld < cols, bad flags */
+    FP8_ERR_UNSUPPORTED_SHAPE = 2,  /* shape the operation does not support (e.g. K % 16 != 0) */
+    FP8_ERR_MISALIGNED = 3,         /* pointer or leading dimension misaligned */
+    FP8_ERR_UNSUPPORTED_DEVICE = 4, /* current device is not gfx950 */
+    FP8_ERR_HIP = 5                 /* a HIP runtime call or launch failed */
+} fp8_status;
+
+/* [DeepL] 2.1: E4M3 (1/4/3 bits) for forward weights and activations, E5M2
+ * (1/5/2 bits) for gradients.  Both are the OCP formats ([H100], formats
+ * paragraph): E4M3 has no infinities, max finite 448, NaN = S.1111.111;
+ * E5M2 has IEEE-style Inf/NaN, max finite 57344. */
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
+
+typedef enum { FP8_IN_F32 = 0, FP8_IN_BF16 = 1 } fp8_in_dtype;
+typedef enum { FP8_OUT_F32 = 0, FP8_OUT_BF16 = 1 } fp8_out_dtype;
+
+/* [DeepL] 2.3: one factor per tensor, per row, or per block.  Blocks are
+ * 1x128 (one row, 128 consecutive columns) or 128x128, aligned at (0,0); a
+ * final partial block covers the remainder.  Group grids (row-major):
+ *   TENSOR: 1;  ROW: rows;  BLOCK_1x128: rows x ceil(cols/128);
+ *   BLOCK_128x128: ceil(rows/128) x ceil(cols/128). */
+typedef enum {
+    FP8_GRAN_TENSOR = 0,
+    FP8_GRAN_ROW = 1,
+    FP8_GRAN_BLOCK_1x128 = 2,
+    FP8_GRAN_BLOCK_128x128 = 3
+} fp8_granularity;
+
+/* [Soup] rowwise recipe: round every scale down to a power of two
+ * (s = 2^floor(log2(448/amax)), so scale_inv is exact). */
+#define FP8_SCALE_POW2 1u
+/* Write q transposed: q is [cols x rows] with leading dimension ldq >= rows.
+ * Only with FP8_GRAN_TENSOR (the wgrad operands X^T and dY^T). */
+#define FP8_TRANSPOSE_OUT 2u
+
+/* Data-dependent conditions are counted on the device, never returned as a
+ * status ([DeepL] 4.2 and 6.2: watch max-abs, scale and overflow).  Device
+ * memory; the library ADDS to the counters, so the caller zeroes them.
+ *   sat_count:        non-NaN products |x*s| > max finite (saturated, Inf incl.)
+ *   nonfinite_count:  NaN or Inf inputs
+ *   underflow_count:  nonzero, non-NaN inputs whose code is +-0 */
+typedef struct fp8_diag {
+    uint32_t sat_count;
+    uint32_t nonfinite_count;
+    uint32_t underflow_count;
+    uint32_t reserved;
+} fp8_diag;
+
+/* Delayed scaling ([DeepL] 2.3): this step's scale comes from the raw amax of
+ * the previous min(count, len) steps: s = fmax / max(history).  The current
+ * step is excluded; with an empty history the call scales just in time from
+ * the current amax.  After the cast the current amax enters the ring.
+ * Device memory, 128 bytes, caller-owned; initialize with
+ * fp8_history_init().  Saving and restoring the 128 bytes (a device copy)
+ * checkpoints the state.  `scale`/`scale_inv` hold the scale the NEXT call
+ * will use (for inspection).  Calls sharing one history must be ordered on
+ * one stream. */
+typedef struct fp8_amax_history {
+    float amax[16];         /* raw amax of past steps; slot `pos` is written next */
+    int32_t len;            /* window length, 1..16 */
+    int32_t pos;            /* next slot to write */
+    int32_t count;          /* valid entries, 0..len */
+    uint32_t blocks_done;   /* internal: zero between calls */
+    uint32_t cur_amax_bits; /* internal: zero between calls */
+    float scale;            /* scale the next call will use (count > 0) */
+    float scale_inv;
+    uint32_t steps;         /* calls completed */
+    uint32_t reserved[8];
+} fp8_amax_history;
+
+/* Library version of this header (FP8MI_ABI_VERSION). */
+int fp8_abi_version(void);
+
+/* Static description of a status code. */
+const char* fp8_status_string(fp8_status status);
+
+/* Thread-local message for the last error returned on this thread ("" after
+ * a successful call). */
+const char* fp8_last_error(void);
+
+/* Zero a history and set its window length (1..16) on `stream`. */
+fp8_status fp8_history_init(fp8_amax_history* hist, int32_t len, void* stream);
+
+/* amax = max |x| per group ([DeepL] 4.2: the per-layer maximum absolute value
+ * behind the scale).  x: [rows x cols], element type in_dtype, leading
+ * dimension ld.  amax_out: fp32 array of the group grid (see
+ * fp8_granularity).  A NaN anywhere in a group gives NaN, else an Inf gives
+ * Inf.  Any pointer alignment is accepted; 16-byte-aligned rows are fastest. */
+fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                    fp8_granularity gran, float* amax_out, void* stream);
+
+/* Scaled quantization ([DeepL] 2.1, 2.3; [Soup] recipes; [Swift] dynamic
+ * per-tensor):
+ *   per group:  amax, s = fl32(fmax / amax) (amax = 0 or non-finite -> 1,
+ *               overflow -> FLT_MAX; FP8_SCALE_POW2 truncates s to a power
+ *               of two), s_inv = fl32(1 / s);
+ *   per element: q = saturating round-to-nearest-even of fl32(x * s) into
+ *               `fmt`; NaN -> 0x7F|sign; the sign survives underflow.
+ * x: [rows x cols] (ld).  q: uint8 codes [rows x cols] (ldq >= cols), or
+ * [cols x rows] (ldq >= rows) with FP8_TRANSPOSE_OUT.
+ * scale_inv_out, amax_out: fp32 arrays of the group grid, both required.
+ * hist: NULL = just in time; non-NULL = delayed scaling (FP8_GRAN_TENSOR
+ * only); amax_out then receives the current step's amax and scale_inv_out
+ * the inverse of the scale actually used.
+ * diag: optional counters (NULL to skip the counting). */
+fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols,
+                        int64_t ld, fp8_format fmt, fp8_granularity gran, uint32_t flags,
+                        fp8_amax_history* hist, uint8_t* q, int64_t ldq, float* scale_inv_out,
+                        float* amax_out, fp8_diag* diag, void* stream);
+
+/* Scaled FP8 GEMM ([H100] FP8 matrix multiply-add in hardware; [Soup]
+ * tensorwise and rowwise GEMMs; [DeepL] 2.2 results return to high
+ * precision):
+ *   C[m,n] = (sum_k decode(A[m,k]) * decode(B[n,k])) * fl32(sa(m) * sb(n))
+ * accumulated in fp32 on the FP8 matrix cores, i.e. C = A_hat . B_hat^T with
+ * both operands K-contiguous (Y = X W^T; the wgrad dW = dY^T X takes the
+ * transposed casts of dY and X).  A: uint8 [M x K] codes of format fa (lda);
+ * B: uint8 [N x K] codes of format fb (ldb).  sa = a_scale_inv[0] if
+ * a_per_row == 0, else a_scale_inv[m] ([M]); likewise sb with [N].
+ * C: [M x N] fp32 or bf16 (round-to-nearest-even), leading dimension ldc.
+ * Requirements: K % 16 == 0; A, B 16-byte aligned; lda, ldb multiples of 16;
+ * C aligned to its element size.  Results are bit-reproducible run to run
+ * (no split-K, no atomics); they may differ from another tiling in the last
+ * bits of the fp32 sum ([DeepL] 5.3). */
+fp8_status fp8_scaled_gemm(const uint8_t* A, fp8_format fa, int64_t lda,
+                           const uint8_t* B, fp8_format fb, int64_t ldb,
+                           int64_t M, int64_t N, int64_t K,
+                           const float* a_scale_inv, int a_per_row,
+                           const float* b_scale_inv, int b_per_row,
+                           void* C, fp8_out_dtype out_dtype, int64_t ldc, void* stream);
+
+/* Block-scaled FP8 GEMM ([DeepL] 2.3, per-block scaling): E4M3 operands,
+ * A with one scale per (row, 128-wide K block), B with one per (128x128
+ * block):
+ *   C[m,n] = sum_kb  fl32(a_scale_inv[m, kb] * b_scale_inv[n/128, kb])
+ *                    * (sum_{k in kb} decode(A[m,k]) * decode(B[n,k]))
+ * Each K block's partial sum is formed in fp32 on the matrix cores and then
+ * promoted into the fp32 accumulator with its scale product.
+ * a_scale_inv: [M x K/128] row-major; b_scale_inv: [N/128 x K/128].
+ * Requirements: K % 128 == 0 and N % 128 == 0 (else
+ * FP8_ERR_UNSUPPORTED_SHAPE); alignment as fp8_scaled_gemm. */
+fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                int64_t M, int64_t N, int64_t K,
+                                const float* a_scale_inv, const float* b_scale_inv,
+                                void* C, fp8_out_dtype out_dtype, int64_t ldc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MI_H */

@@ -82,8 +82,14 @@ def lib():
         L.or_f32_to_bf16.restype = ctypes.c_uint16
         L.or_f32_to_bf16.argtypes = [f32]
         L.or_f32_to_bf16_array.argtypes = [P, i64, P]
+        L.or_num_threads.restype = i32
+        L.or_num_threads.argtypes = []
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    return int(lib().or_num_threads())
 
 
 def _p(a: np.ndarray):

@@ -27,6 +27,7 @@
 #include <string.h>
 #include <math.h>
 #include <float.h>
+#include <omp.h>
 
 enum { OR_E4M3 = 0, OR_E5M2 = 1 };
 enum { OR_GRAN_TENSOR = 0, OR_GRAN_ROW = 1, OR_GRAN_1x128 = 2, OR_GRAN_128x128 = 3 };
@@ -137,14 +138,16 @@ static inline uint32_t abs_bits(float v) { return f2u(v) & 0x7FFFFFFFu; }
  * aligned at element (0,0); a final partial block covers the remainder.   */
 static void group_dims(int gran, int64_t rows, int64_t cols,
                        int64_t* gr, int64_t* gc, int64_t* h, int64_t* w) {
+    /* an empty tensor (or an empty row) is still one group, of amax 0 */
+    int64_t r1 = rows > 0 ? rows : 1, c1 = cols > 0 ? cols : 1;
     switch (gran) {
-    case OR_GRAN_TENSOR: *h = rows; *w = cols; break;
-    case OR_GRAN_ROW:    *h = 1;    *w = cols; break;
-    case OR_GRAN_1x128:  *h = 1;    *w = 128;  break;
-    default:             *h = 128;  *w = 128;  break;
+    case OR_GRAN_TENSOR: *h = r1; *w = c1;  break;
+    case OR_GRAN_ROW:    *h = 1;  *w = c1;  break;
+    case OR_GRAN_1x128:  *h = 1;  *w = 128; break;
+    default:             *h = 128; *w = 128; break;
     }
-    *gr = (rows + *h - 1) / *h;
-    *gc = (cols + *w - 1) / *w;
+    *gr = (gran == OR_GRAN_TENSOR) ? 1 : (rows + *h - 1) / *h;
+    *gc = (gran == OR_GRAN_TENSOR || gran == OR_GRAN_ROW) ? 1 : (cols + *w - 1) / *w;
 }
 
 int64_t or_num_groups(int gran, int64_t rows, int64_t cols) {
@@ -438,3 +441,6 @@ void or_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out) {
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = or_f32_to_bf16(v[i]);
 }
+
+/* Threads the OpenMP loops above use (reported with CPU timings). */
+int or_num_threads(void) { return omp_get_max_threads(); }

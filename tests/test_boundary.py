@@ -1,0 +1,152 @@
+"""Boundary checks that run without a GPU: the C-ABI library loads, exports
+every function include/fp8mi.h declares, and rejects invalid arguments
+before any device call (validation precedes the device check, so these
+calls never touch HIP).  Pointer values here are fake and never
+dereferenced: every call fails validation first."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from fp8_precision_quantization_amd import _lib
+
+L = _lib
+
+
+def test_library_exports_every_header_function():
+    lib = L.lib()
+    declared = L.header_functions()
+    assert set(declared) == set(L.SIGNATURES), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+
+
+def test_library_is_gfx950_only_code_object():
+    out = subprocess.run(["strings", "-n", "8", L.LIB_PATH], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+    for other in ("gfx942", "gfx90a", "gfx1100", "sm_"):
+        assert "amdgcn-amd-amdhsa--" + other not in out
+
+
+def test_abi_version_and_status_strings():
+    lib = L.lib()
+    assert lib.fp8_abi_version() == 1
+    for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARG"), (2, "FP8_ERR_UNSUPPORTED_SHAPE"),
+                       (3, "FP8_ERR_MISALIGNED"), (4, "FP8_ERR_UNSUPPORTED_DEVICE"), (5, "FP8_ERR_HIP")]:
+        assert L.status_name(code) == name
+
+
+FAKE = 0x10000          # 64 KiB-aligned fake device address, never dereferenced
+
+
+def q(**kw):
+    a = dict(x=FAKE, in_dt=L.FP8_IN_BF16, rows=64, cols=64, ld=64, fmt=L.FP8_E4M3,
+             gran=L.FP8_GRAN_TENSOR, flags=0, hist=None, q=FAKE, ldq=64, sinv=FAKE, amax=FAKE,
+             diag=None)
+    a.update(kw)
+    st = L.lib().fp8_quantize(a["x"], a["in_dt"], a["rows"], a["cols"], a["ld"], a["fmt"], a["gran"],
+                              a["flags"], a["hist"], a["q"], a["ldq"], a["sinv"], a["amax"], a["diag"],
+                              None)
+    return st, L.lib().fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), 1, "x is NULL"),
+    (dict(in_dt=7), 1, "in_dtype"),
+    (dict(rows=-1), 1, "negative"),
+    (dict(ld=32), 1, "ld="),
+    (dict(fmt=3), 1, "format"),
+    (dict(gran=9), 1, "granularity"),
+    (dict(flags=8), 1, "flag"),
+    (dict(flags=2, gran=1), 1, "TRANSPOSE"),
+    (dict(hist=FAKE, gran=2), 1, "delayed"),
+    (dict(q=None), 1, "q is NULL"),
+    (dict(ldq=10), 1, "ldq"),
+    (dict(flags=2, rows=100, ldq=64), 1, "ldq"),
+    (dict(sinv=None), 1, "scale_inv_out"),
+    (dict(amax=None), 1, "amax_out"),
+    (dict(x=FAKE + 1), 3, "aligned"),
+    (dict(in_dt=L.FP8_IN_F32, x=FAKE + 2), 3, "aligned"),
+    (dict(hist=FAKE + 4), 3, "hist"),
+    (dict(amax=FAKE + 2), 3, "aligned"),
+    (dict(rows=2 ** 32), 2, "2^31"),
+])
+def test_quantize_validation(kw, status, needle):
+    st, msg = q(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def gemm(**kw):
+    a = dict(A=FAKE, fa=0, lda=256, B=FAKE, fb=0, ldb=256, M=256, N=256, K=256, sa=FAKE, ar=0,
+             sb=FAKE, br=0, C=FAKE, out=L.FP8_OUT_BF16, ldc=256)
+    a.update(kw)
+    st = L.lib().fp8_scaled_gemm(a["A"], a["fa"], a["lda"], a["B"], a["fb"], a["ldb"], a["M"], a["N"],
+                                 a["K"], a["sa"], a["ar"], a["sb"], a["br"], a["C"], a["out"], a["ldc"],
+                                 None)
+    return st, L.lib().fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(fa=2), 1, "formats"),
+    (dict(ar=2), 1, "per_row"),
+    (dict(A=None), 1, "NULL"),
+    (dict(C=None), 1, "C is NULL"),
+    (dict(sa=None), 1, "scale"),
+    (dict(out=5), 1, "out_dtype"),
+    (dict(M=-1), 1, "negative"),
+    (dict(K=200, lda=256, ldb=256), 2, "multiple of 16"),
+    (dict(lda=128), 1, "lda"),
+    (dict(ldc=100), 1, "ldc"),
+    (dict(A=FAKE + 8), 3, "16-byte"),
+    (dict(lda=272 + 8), 3, "multiples of 16"),
+    (dict(C=FAKE + 1), 3, "C is not aligned"),
+    (dict(out=L.FP8_OUT_F32, C=FAKE + 2), 3, "C is not aligned"),
+    (dict(M=2 ** 31), 2, "2^31"),
+])
+def test_gemm_validation(kw, status, needle):
+    st, msg = gemm(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_blockgemm_validation():
+    lib = L.lib()
+    for (M, N, K), needle in [((256, 200, 256), "N % 128"), ((256, 256, 192), "K % 128"),
+                              ((256, 256, 0), "K > 0")]:
+        st = lib.fp8_blockscaled_gemm(FAKE, 256, FAKE, 256, M, N, K, FAKE, FAKE, FAKE, 1, 256, None)
+        assert st == L.FP8_ERR_UNSUPPORTED_SHAPE
+        assert needle.split()[0] in lib.fp8_last_error().decode()
+
+
+def test_history_and_amax_validation():
+    lib = L.lib()
+    assert lib.fp8_history_init(None, 16, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_history_init(FAKE, 0, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_history_init(FAKE, 17, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_history_init(FAKE + 8, 16, None) == L.FP8_ERR_MISALIGNED
+    assert lib.fp8_amax(FAKE, 1, 4, 4, 4, 5, FAKE, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_amax(FAKE, 1, 4, 4, 4, 0, None, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_amax(FAKE + 1, 1, 4, 4, 4, 0, FAKE, None) == L.FP8_ERR_MISALIGNED
+
+
+def test_history_struct_is_128_bytes():
+    text = open(L.HEADER).read()
+    body = text[text.index("typedef struct fp8_amax_history"):]
+    body = body[:body.index("} fp8_amax_history;")]
+    words = 16 + 3 + 2 + 2 + 1 + 8   # amax, len/pos/count, internals, scale pair, steps, reserved
+    assert "float amax[16]" in body and "uint32_t reserved[8]" in body
+    assert words * 4 == L.HISTORY_BYTES
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(ImportError):
+        L.lib()
