@@ -9,8 +9,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
+#include <utility>
 
 #include "fp8mi.h"
 #include "launch.hpp"
@@ -69,6 +71,32 @@ fp8_status check_device(int* cus) {
                     "device %d is %s; this library needs gfx950 (MI355X / MI350X): FP8 MFMA and OCP FP8 conversion",
                     dev, d.arch);
     *cus = d.num_cus;
+    return FP8_OK;
+}
+
+// Scratch for the per-tensor reductions: one buffer per (device, stream),
+// allocated on the first quantize/amax call that uses the pair and kept for
+// the life of the process.  Calls on one stream are ordered, so they can
+// share it; calls on different streams never do.
+std::mutex g_scratch_mutex;
+std::map<std::pair<int, uintptr_t>, uint32_t*> g_scratch;
+
+fp8_status get_scratch(hipStream_t stream, uint32_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    auto key = std::make_pair(dev, (uintptr_t)stream);
+    auto it = g_scratch.find(key);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return FP8_OK;
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, sizeof(uint32_t) * fp8mi::kScratchWords);
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "scratch allocation failed: %s", hipGetErrorString(e));
+    g_scratch[key] = static_cast<uint32_t*>(p);
+    *out = static_cast<uint32_t*>(p);
     return FP8_OK;
 }
 
@@ -152,9 +180,11 @@ fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t 
     st = check_device(&cus);
     if (st != FP8_OK) return st;
     if (num_groups(gran, rows, cols) == 0) return ok();
+    uint32_t* scratch = nullptr;
+    if (gran == FP8_GRAN_TENSOR && (st = get_scratch((hipStream_t)stream, &scratch)) != FP8_OK) return st;
     fp8mi::QuantArgs a;
     a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
-    a.gran = gran; a.write_q = false; a.amax = amax_out; a.ldq = cols;
+    a.gran = gran; a.write_q = false; a.amax = amax_out; a.ldq = cols; a.scratch = scratch;
     a.stream = (hipStream_t)stream; a.num_cus = cus;
     return launch_result(fp8mi::launch_quantize(a), "fp8_amax");
 }
@@ -191,7 +221,10 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
     st = check_device(&cus);
     if (st != FP8_OK) return st;
     if (num_groups(gran, rows, cols) == 0) return ok();
+    uint32_t* scratch = nullptr;
+    if (gran == FP8_GRAN_TENSOR && (st = get_scratch((hipStream_t)stream, &scratch)) != FP8_OK) return st;
     fp8mi::QuantArgs a;
+    a.scratch = scratch;
     a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
     a.fmt = fmt; a.gran = gran; a.pow2 = (flags & FP8_SCALE_POW2) != 0; a.transpose = transpose;
     a.write_q = true; a.hist = hist; a.q = q; a.ldq = ldq; a.scale_inv = scale_inv_out;

@@ -24,6 +24,7 @@ struct QuantArgs {
     float* scale_inv = nullptr;
     float* amax = nullptr;
     fp8_diag* diag = nullptr;
+    uint32_t* scratch = nullptr;  // library scratch of kScratchWords words, owned per (device, stream)
     hipStream_t stream = nullptr;
     int num_cus = 256;
 };
@@ -49,6 +50,9 @@ hipError_t launch_quantize(const QuantArgs& a);
 hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream);
 hipError_t launch_scaled_gemm(const GemmArgs& a);
 hipError_t launch_blockscaled_gemm(const GemmArgs& a);
+
+// Per-(device, stream) scratch the library allocates once (uint32 words).
+constexpr int kScratchWords = 16384;
 
 // Unit count of the element-wise tensor kernels must fit in 31 bits.
 constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;

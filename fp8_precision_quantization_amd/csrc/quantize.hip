@@ -166,7 +166,7 @@ struct UnitGeom {
     }
 };
 
-// Block-wide max / sums into thread 0 (256 threads = 4 waves).
+// Block-wide max into thread 0 (256 threads = 4 waves).
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
     v = wave_max_u32(v);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -178,6 +178,26 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* lds) {
     return r;
 }
 
+// Max over partials[0..n) computed by the whole block, returned to every
+// thread.  This is how per-tensor maxima are combined: each producer block
+// stores its own partial with a plain store and the consumer reduces them,
+// so no kernel issues same-address device-scope atomics (those serialize
+// across the 8 XCDs).
+__device__ __forceinline__ uint32_t reduce_partials(const uint32_t* __restrict__ partials, int n,
+                                                    uint32_t* lds) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) m = max(m, partials[i]);
+    m = wave_max_u32(m);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();
+    if (lane == 0) lds[w] = m;
+    __syncthreads();
+    m = max(max(lds[0], lds[1]), max(lds[2], lds[3]));
+    __syncthreads();
+    return m;
+}
+
+// Diagnostics are the only atomics left, and only when a caller asks for them.
 __device__ __forceinline__ void block_add_diag(Counters c, uint32_t* lds, fp8_diag* diag) {
     c.sat = wave_sum_u32(c.sat);
     c.nonfinite = wave_sum_u32(c.nonfinite);
@@ -196,72 +216,23 @@ __device__ __forceinline__ void block_add_diag(Counters c, uint32_t* lds, fp8_di
     }
 }
 
-__device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Delayed scale ([DeepL] 2.3): max over the history window; with an empty
-// history the bootstrap amax of the current step (already reduced into
-// cur_amax_bits by the preceding kernel).
+// history, the just-in-time amax of the current step (bootstrap partials).
 template <int FMT>
-__device__ __forceinline__ float delayed_scale(fp8_amax_history* h, bool pow2) {
-    const int32_t count = (int32_t)load_relaxed(reinterpret_cast<const uint32_t*>(&h->count));
+__device__ __forceinline__ float delayed_scale(const fp8_amax_history* h, const uint32_t* boot, int n_boot,
+                                               bool pow2, uint32_t* lds) {
+    const int32_t count = h->count;
     uint32_t basis = 0;
     if (count <= 0) {
-        basis = load_relaxed(&h->cur_amax_bits);
+        basis = reduce_partials(boot, n_boot, lds);
     } else {
         const int n = count > 16 ? 16 : count;
-        for (int i = 0; i < n; ++i)
-            basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
+        for (int i = 0; i < n; ++i) basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
     }
     return scale_from_amax_bits<FMT>(basis, pow2);
 }
 
-// The last block of a delayed cast pushes the step's amax into the ring and
-// precomputes the next scale.  Every other block has read the ring before its
-// atomicAdd on blocks_done, so the update cannot race with those reads.
-template <int FMT>
-__device__ void delayed_finish(fp8_amax_history* h, uint32_t block_amax, bool pow2,
-                               float* amax_out, uint32_t* lds) {
-    __shared__ bool is_last;
-    if (threadIdx.x == 0) {
-        atomicMax(&h->cur_amax_bits, block_amax);
-        __threadfence();
-        const uint32_t prev = atomicAdd(&h->blocks_done, 1u);
-        is_last = (prev == gridDim.x * gridDim.y - 1);
-    }
-    __syncthreads();
-    if (is_last && threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t cur = atomicAdd(&h->cur_amax_bits, 0u);
-        const float amax_now = __uint_as_float(cur);
-        amax_out[0] = amax_now;
-        int32_t len = h->len;
-        len = len < 1 ? 1 : (len > 16 ? 16 : len);
-        int32_t pos = h->pos;
-        pos = (pos < 0 || pos >= len) ? 0 : pos;
-        h->amax[pos] = amax_now;
-        h->pos = (pos + 1) % len;
-        const int32_t count = h->count < len ? h->count + 1 : len;
-        h->count = count;
-        uint32_t basis = 0;
-        for (int i = 0; i < count; ++i) basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
-        const float s = scale_from_amax_bits<FMT>(basis, pow2);
-        h->scale = s;
-        h->scale_inv = 1.0f / s;
-        h->steps = h->steps + 1;
-        h->cur_amax_bits = 0u;
-        h->blocks_done = 0u;
-        __threadfence();
-    }
-}
-
 // ------------------------------------------------------------------ kernels --
-__global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
-}
-
 __global__ void k_history_init(fp8_amax_history* h, int32_t len) {
     uint32_t* w = reinterpret_cast<uint32_t*>(h);
     const int i = threadIdx.x;
@@ -276,16 +247,14 @@ __global__ void k_history_init(fp8_amax_history* h, int32_t len) {
 
 constexpr int kUnroll = 4;
 
-// Per-tensor amax: grid-stride over units, one atomicMax per block.
+// Per-tensor amax, pass 1: grid-stride over units, one partial per block.
 // `gate` non-null: run only while the history is empty (delayed bootstrap).
 template <typename InT>
-__global__ __launch_bounds__(kThreads) void k_amax_tensor(const InT* __restrict__ x, UnitGeom g,
-                                                          bool vec_in, uint32_t* out,
-                                                          const fp8_amax_history* gate) {
+__global__ __launch_bounds__(kThreads) void k_amax_partials(const InT* __restrict__ x, UnitGeom g,
+                                                            bool vec_in, uint32_t* __restrict__ partials,
+                                                            const fp8_amax_history* gate) {
     __shared__ uint32_t lds[16];
-    if (gate != nullptr &&
-        load_relaxed(reinterpret_cast<const uint32_t*>(&gate->count)) != 0u)
-        return;
+    if (gate != nullptr && gate->count != 0) return;
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t m = 0;
     for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < g.units; u0 += stride * kUnroll) {
@@ -304,20 +273,63 @@ __global__ __launch_bounds__(kThreads) void k_amax_tensor(const InT* __restrict_
             if (u0 + i * stride < g.units) m = max(m, p[i].abs_max());
     }
     const uint32_t bm = block_max(m, lds);
-    if (threadIdx.x == 0 && bm != 0u) atomicMax(out, bm);
+    if (threadIdx.x == 0) partials[blockIdx.x] = bm;
 }
 
-// Per-tensor cast.  JIT: s from the reduced amax (amax_bits_in).  DELAYED:
-// s from the history; the block's amax is folded into the ring at the end.
+// Pass 2 of the standalone per-tensor amax.
+__global__ __launch_bounds__(kThreads) void k_reduce_amax(const uint32_t* __restrict__ partials, int n,
+                                                          float* amax_out) {
+    __shared__ uint32_t lds[16];
+    const uint32_t m = reduce_partials(partials, n, lds);
+    if (threadIdx.x == 0) amax_out[0] = __uint_as_float(m);
+}
+
+// After a delayed cast: combine the cast blocks' partials into this step's
+// amax, push it into the ring and precompute the next scale (one block).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h,
+                                                             const uint32_t* __restrict__ partials, int n,
+                                                             bool pow2, float* amax_out) {
+    __shared__ uint32_t lds[16];
+    const uint32_t cur = reduce_partials(partials, n, lds);
+    if (threadIdx.x != 0) return;
+    const float amax_now = __uint_as_float(cur);
+    amax_out[0] = amax_now;
+    int32_t len = h->len;
+    len = len < 1 ? 1 : (len > 16 ? 16 : len);
+    int32_t pos = h->pos;
+    pos = (pos < 0 || pos >= len) ? 0 : pos;
+    h->amax[pos] = amax_now;
+    h->pos = (pos + 1) % len;
+    const int32_t count = h->count < len ? h->count + 1 : len;
+    h->count = count;
+    uint32_t basis = 0;
+    for (int i = 0; i < count; ++i) basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
+    const float s = scale_from_amax_bits<FMT>(basis, pow2);
+    h->scale = s;
+    h->scale_inv = 1.0f / s;
+    h->steps = h->steps + 1;
+}
+
+// Per-tensor cast.  JIT: s from the amax partials of pass 1 (block 0 also
+// writes amax_out).  DELAYED: s from the history (or the bootstrap partials
+// while it is empty); each block stores its own amax partial for the finish
+// kernel.
 template <typename InT, int FMT, bool DELAYED, bool DIAG>
 __global__ __launch_bounds__(kThreads) void k_cast_tensor(
     const InT* __restrict__ x, UnitGeom g, bool vec_in, uint8_t* __restrict__ q, bool vec_out,
-    const uint32_t* amax_bits_in, fp8_amax_history* hist, bool pow2,
-    float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag) {
+    const uint32_t* __restrict__ partials_in, int n_in, const fp8_amax_history* hist, bool pow2,
+    float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag,
+    uint32_t* __restrict__ partials_out) {
     __shared__ uint32_t lds[16];
     float s;
-    if constexpr (DELAYED) s = delayed_scale<FMT>(hist, pow2);
-    else s = scale_from_amax_bits<FMT>(load_relaxed(amax_bits_in), pow2);
+    if constexpr (DELAYED) {
+        s = delayed_scale<FMT>(hist, partials_in, n_in, pow2, lds);
+    } else {
+        const uint32_t am = reduce_partials(partials_in, n_in, lds);
+        s = scale_from_amax_bits<FMT>(am, pow2);
+        if (blockIdx.x == 0 && threadIdx.x == 0) amax_out[0] = __uint_as_float(am);
+    }
     if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
 
     const uint32_t stride = gridDim.x * kThreads;
@@ -349,87 +361,100 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
     if constexpr (DIAG) block_add_diag(cnt, lds, diag);
     if constexpr (DELAYED) {
         const uint32_t bm = block_max(m, lds);
-        delayed_finish<FMT>(hist, bm, pow2, amax_out, lds);
+        if (threadIdx.x == 0) partials_out[blockIdx.x] = bm;
     }
 }
 
-// Per-tensor cast written transposed: q[c][r] (the wgrad operands).  One
-// 128x128 tile per block; codes go through LDS with a 16-chunk XOR swizzle so
-// that both the row-wise writes and the column gathers are conflict free,
-// and each output row segment leaves as 16-byte stores (128 B per 8 lanes).
+// Per-tensor cast written transposed: q[c][r] (the wgrad operands).  Blocks
+// walk 128x128 tiles grid-stride; codes go through LDS with a 16-chunk XOR
+// swizzle so that both the row-wise writes and the column gathers are
+// conflict free, and each output row segment leaves as 16-byte stores
+// (128 B per 8 lanes).
 template <typename InT, int FMT, bool DELAYED, bool DIAG>
 __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
     const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
-    uint8_t* __restrict__ q, int64_t ldq, bool vec_out16, const uint32_t* amax_bits_in,
-    fp8_amax_history* hist, bool pow2, float* __restrict__ scale_inv_out,
-    float* __restrict__ amax_out, fp8_diag* diag) {
+    uint8_t* __restrict__ q, int64_t ldq, bool vec_out16, const uint32_t* __restrict__ partials_in,
+    int n_in, const fp8_amax_history* hist, bool pow2, float* __restrict__ scale_inv_out,
+    float* __restrict__ amax_out, fp8_diag* diag, uint32_t* __restrict__ partials_out) {
     __shared__ uint32_t lds[16];
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 128];
     float s;
-    if constexpr (DELAYED) s = delayed_scale<FMT>(hist, pow2);
-    else s = scale_from_amax_bits<FMT>(load_relaxed(amax_bits_in), pow2);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
+    if constexpr (DELAYED) {
+        s = delayed_scale<FMT>(hist, partials_in, n_in, pow2, lds);
+    } else {
+        const uint32_t am = reduce_partials(partials_in, n_in, lds);
+        s = scale_from_amax_bits<FMT>(am, pow2);
+        if (blockIdx.x == 0 && threadIdx.x == 0) amax_out[0] = __uint_as_float(am);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
 
     const int t = threadIdx.x;
     const int cu = t & 15, rr = t >> 4;
-    const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
-    const int64_t c = c0 + cu * 8;
-    const int nvc = (int)(cols - c >= 8 ? 8 : (cols - c > 0 ? cols - c : 0));
+    const int64_t tiles_c = (cols + 127) / 128;
+    const int64_t tiles = ((rows + 127) / 128) * tiles_c;
     uint32_t m = 0;
     Counters cnt;
-    Pack<InT> p[8];
+    for (int64_t tl = blockIdx.x; tl < tiles; tl += gridDim.x) {
+        const int64_t r0 = (tl / tiles_c) * 128, c0 = (tl % tiles_c) * 128;
+        const int64_t c = c0 + cu * 8;
+        const int nvc = (int)(cols - c >= 8 ? 8 : (cols - c > 0 ? cols - c : 0));
+        Pack<InT> p[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t r = r0 + rr + 16 * i;
-        const int nv = (r < rows) ? nvc : 0;
-        if (nv > 0) p[i] = load_unit<InT>(x, r * ld + c, nv, vec_in);
-        else {
-#pragma unroll
-            for (int k = 0; k < (int)(sizeof(p[i].w) / 4); ++k) p[i].w[k] = 0u;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = rr + 16 * i;
-        if constexpr (DELAYED) m = max(m, p[i].abs_max());
-        const uint2 codes = encode_unit<FMT, DIAG>(p[i], s, cnt);
-        const int pos = cu ^ ((r >> 4) & 15);
-        *reinterpret_cast<uint2*>(&tile[r * 128 + pos * 8]) = codes;
-    }
-    __syncthreads();
-    // gather: chunk = (output row cl in 0..127, input-row segment rs in 0..7)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int chunk = t + 256 * j;
-        const int cl = chunk >> 3, rs = chunk & 7;
-        const int pos = (cl >> 3) ^ rs;
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int r = rs * 16 + k * 4 + b;
-                acc |= (uint32_t)tile[r * 128 + pos * 8 + (cl & 7)] << (8 * b);
-            }
-            w[k] = acc;
-        }
-        const int64_t orow = c0 + cl;
-        const int64_t ocol = r0 + rs * 16;
-        if (orow < cols && ocol < rows) {
-            uint8_t* dst = q + orow * ldq + ocol;
-            const int64_t remr = rows - ocol;
-            if (vec_out16 && remr >= 16) {
-                *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + rr + 16 * i;
+            const int nv = (r < rows) ? nvc : 0;
+            if (nv > 0) {
+                p[i] = load_unit<InT>(x, r * ld + c, nv, vec_in);
             } else {
-                for (int b = 0; b < 16 && b < remr; ++b) dst[b] = (uint8_t)((w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+#pragma unroll
+                for (int k = 0; k < (int)(sizeof(p[i].w) / 4); ++k) p[i].w[k] = 0u;
+            }
+        }
+        __syncthreads();   // the previous tile's gathers are done with `tile`
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = rr + 16 * i;
+            if constexpr (DELAYED) m = max(m, p[i].abs_max());
+            const uint2 codes = encode_unit<FMT, DIAG>(p[i], s, cnt);
+            const int pos = cu ^ ((r >> 4) & 15);
+            *reinterpret_cast<uint2*>(&tile[r * 128 + pos * 8]) = codes;
+        }
+        __syncthreads();
+        // gather: chunk = (output row cl in 0..127, input-row segment rs in 0..7)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int chunk = t + 256 * j;
+            const int cl = chunk >> 3, rs = chunk & 7;
+            const int pos = (cl >> 3) ^ rs;
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t acc = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int r = rs * 16 + k * 4 + b;
+                    acc |= (uint32_t)tile[r * 128 + pos * 8 + (cl & 7)] << (8 * b);
+                }
+                w[k] = acc;
+            }
+            const int64_t orow = c0 + cl;
+            const int64_t ocol = r0 + rs * 16;
+            if (orow < cols && ocol < rows) {
+                uint8_t* dst = q + orow * ldq + ocol;
+                const int64_t remr = rows - ocol;
+                if (vec_out16 && remr >= 16) {
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+                } else {
+                    for (int b = 0; b < 16 && b < remr; ++b)
+                        dst[b] = (uint8_t)((w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+                }
             }
         }
     }
     if constexpr (DIAG) block_add_diag(cnt, lds, diag);
     if constexpr (DELAYED) {
         const uint32_t bm = block_max(m, lds);
-        delayed_finish<FMT>(hist, bm, pow2, amax_out, lds);
+        if (threadIdx.x == 0) partials_out[blockIdx.x] = bm;
     }
 }
 
@@ -606,6 +631,13 @@ __global__ __launch_bounds__(kThreads) void k_cast_128x128(
 // ---------------------------------------------------------------- host side --
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Scratch layout (uint32 words of the per-stream scratch, kScratchWords).
+constexpr int kScratchCastPartials = 0;      // <= kMaxCastBlocks partials of a delayed cast
+constexpr int kScratchAmaxPartials = 4096;   // <= kMaxAmaxBlocks partials of pass 1
+constexpr int64_t kMaxCastBlocks = 4096;
+constexpr int64_t kMaxAmaxBlocks = 512;
+static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchWords, "scratch too small");
+
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
     int64_t b = (work_items + per_block - 1) / per_block;
     if (b < 1) b = 1;
@@ -646,60 +678,47 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
     hipStream_t st = a.stream;
 
     if (a.gran == FP8_GRAN_TENSOR) {
-        const unsigned grid = grid_for(g.units, (int64_t)kThreads * kUnroll, cap);
-        if (a.hist == nullptr) {
-            uint32_t* amax_bits = reinterpret_cast<uint32_t*>(a.amax);
-            hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, amax_bits, 0u, 1);
-            hipLaunchKernelGGL(k_amax_tensor<InT>, dim3(grid), dim3(kThreads), 0, st, x, g, vec_in,
-                               amax_bits, (const fp8_amax_history*)nullptr);
-            if (!a.write_q) return hipGetLastError();
-            if (a.transpose) {
-                dim3 tg((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
-                const bool v16 = aligned(a.q, 16) && a.ldq % 16 == 0;
-                if (diag)
-                    hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, false, true>), tg, dim3(kThreads), 0, st,
-                                       x, a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, amax_bits,
-                                       a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
-                else
-                    hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, false, false>), tg, dim3(kThreads), 0, st,
-                                       x, a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, amax_bits,
-                                       a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
-            } else {
-                if (diag)
-                    hipLaunchKernelGGL((k_cast_tensor<InT, FMT, false, true>), dim3(grid), dim3(kThreads), 0,
-                                       st, x, g, vec_in, a.q, vec_out, amax_bits, a.hist, a.pow2,
-                                       a.scale_inv, a.amax, a.diag);
-                else
-                    hipLaunchKernelGGL((k_cast_tensor<InT, FMT, false, false>), dim3(grid), dim3(kThreads), 0,
-                                       st, x, g, vec_in, a.q, vec_out, amax_bits, a.hist, a.pow2,
-                                       a.scale_inv, a.amax, a.diag);
-            }
+        uint32_t* cast_partials = a.scratch + kScratchCastPartials;
+        uint32_t* amax_partials = a.scratch + kScratchAmaxPartials;
+        const unsigned agrid = grid_for(g.units, (int64_t)kThreads * kUnroll, kMaxAmaxBlocks);
+        const unsigned cgrid = grid_for(g.units, (int64_t)kThreads * kUnroll, cap);
+        const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 127) / 128);
+        const unsigned tgrid = grid_for(tiles, 1, kMaxCastBlocks);
+        const bool v16 = a.q != nullptr && aligned(a.q, 16) && a.ldq % 16 == 0;
+        const bool delayed = a.hist != nullptr;
+        // pass 1: amax partials (JIT), or the bootstrap partials of an empty history
+        hipLaunchKernelGGL(k_amax_partials<InT>, dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in, amax_partials,
+                           (const fp8_amax_history*)a.hist);
+        if (!a.write_q) {
+            hipLaunchKernelGGL(k_reduce_amax, dim3(1), dim3(kThreads), 0, st, (const uint32_t*)amax_partials,
+                               (int)agrid, a.amax);
             return hipGetLastError();
         }
-        // delayed: bootstrap amax only while the history is empty, then one pass
-        hipLaunchKernelGGL(k_amax_tensor<InT>, dim3(grid), dim3(kThreads), 0, st, x, g, vec_in,
-                           &a.hist->cur_amax_bits, (const fp8_amax_history*)a.hist);
-        if (a.transpose) {
-            dim3 tg((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
-            const bool v16 = aligned(a.q, 16) && a.ldq % 16 == 0;
-            if (diag)
-                hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, true, true>), tg, dim3(kThreads), 0, st, x,
-                                   a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, (const uint32_t*)nullptr,
-                                   a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
-            else
-                hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, true, false>), tg, dim3(kThreads), 0, st, x,
-                                   a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16, (const uint32_t*)nullptr,
-                                   a.hist, a.pow2, a.scale_inv, a.amax, a.diag);
+#define FP8MI_TENSOR_CAST(DEL, DG)                                                                        \
+    do {                                                                                                  \
+        if (a.transpose)                                                                                  \
+            hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, DEL, DG>), dim3(tgrid), dim3(kThreads), 0, st, x,  \
+                               a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16,                             \
+                               (const uint32_t*)amax_partials, (int)agrid,                                \
+                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, a.diag,      \
+                               cast_partials);                                                            \
+        else                                                                                              \
+            hipLaunchKernelGGL((k_cast_tensor<InT, FMT, DEL, DG>), dim3(cgrid), dim3(kThreads), 0, st, x, g, \
+                               vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,          \
+                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, a.diag,      \
+                               cast_partials);                                                            \
+    } while (0)
+        if (delayed) {
+            if (diag) FP8MI_TENSOR_CAST(true, true);
+            else FP8MI_TENSOR_CAST(true, false);
+            const int nparts = (int)(a.transpose ? tgrid : cgrid);
+            hipLaunchKernelGGL(k_delayed_finish<FMT>, dim3(1), dim3(kThreads), 0, st, a.hist,
+                               (const uint32_t*)cast_partials, nparts, a.pow2, a.amax);
         } else {
-            if (diag)
-                hipLaunchKernelGGL((k_cast_tensor<InT, FMT, true, true>), dim3(grid), dim3(kThreads), 0, st,
-                                   x, g, vec_in, a.q, vec_out, (const uint32_t*)nullptr, a.hist, a.pow2,
-                                   a.scale_inv, a.amax, a.diag);
-            else
-                hipLaunchKernelGGL((k_cast_tensor<InT, FMT, true, false>), dim3(grid), dim3(kThreads), 0, st,
-                                   x, g, vec_in, a.q, vec_out, (const uint32_t*)nullptr, a.hist, a.pow2,
-                                   a.scale_inv, a.amax, a.diag);
+            if (diag) FP8MI_TENSOR_CAST(false, true);
+            else FP8MI_TENSOR_CAST(false, false);
         }
+#undef FP8MI_TENSOR_CAST
         return hipGetLastError();
     }
 

@@ -22,8 +22,12 @@
  *
  * Conventions for every entry point:
  *   - All pointers except the ones documented as host pointers are DEVICE
- *     pointers on the current HIP device.  The caller owns every buffer; the
- *     library allocates and frees nothing and never synchronizes the stream.
+ *     pointers on the current HIP device.  The caller owns every input and
+ *     output buffer.  The library never synchronizes the stream; its only
+ *     allocation is a 64 KiB scratch buffer per (device, stream) pair, made
+ *     with hipMalloc by the first per-tensor fp8_quantize / fp8_amax call on
+ *     that pair and kept until the process ends (calls on one stream are
+ *     ordered and share it; different streams never share one).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call is asynchronous: it returns after host-side validation and
  *     the kernel launches.  A fault inside a kernel surfaces at the caller's
@@ -36,7 +40,8 @@
  *   - Matrices are row-major with an explicit leading dimension (elements
  *     between consecutive rows, >= the number of columns).
  *   - Scale convention: dequantized value = decode(q) * scale_inv.
- *   - Reentrant; the only global state is a per-device architecture cache.
+ *   - Reentrant; the global state is a per-device architecture cache and the
+ *     per-(device, stream) scratch buffers.
  */
 #ifndef FP8MI_H
 #define FP8MI_H
@@ -113,8 +118,7 @@ typedef struct fp8_amax_history {
     int32_t len;            /* window length, 1..16 */
     int32_t pos;            /* next slot to write */
     int32_t count;          /* valid entries, 0..len */
-    uint32_t blocks_done;   /* internal: zero between calls */
-    uint32_t cur_amax_bits; /* internal: zero between calls */
+    uint32_t internal[2];   /* reserved, zero */
     float scale;            /* scale the next call will use (count > 0) */
     float scale_inv;
     uint32_t steps;         /* calls completed */

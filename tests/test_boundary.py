@@ -140,8 +140,8 @@ def test_history_struct_is_128_bytes():
     text = open(L.HEADER).read()
     body = text[text.index("typedef struct fp8_amax_history"):]
     body = body[:body.index("} fp8_amax_history;")]
-    words = 16 + 3 + 2 + 2 + 1 + 8   # amax, len/pos/count, internals, scale pair, steps, reserved
-    assert "float amax[16]" in body and "uint32_t reserved[8]" in body
+    words = 16 + 3 + 2 + 2 + 1 + 8   # amax, len/pos/count, internal, scale pair, steps, reserved
+    assert "float amax[16]" in body and "uint32_t internal[2]" in body and "uint32_t reserved[8]" in body
     assert words * 4 == L.HISTORY_BYTES
 
 
