@@ -253,6 +253,9 @@ static fp8_status check_gemm_common(const uint8_t* A, int64_t lda, const uint8_t
         if (!is_aligned(A, 16) || !is_aligned(B, 16))
             return fail(FP8_ERR_MISALIGNED, "A and B must be 16-byte aligned");
         if (lda % 16 != 0 || ldb % 16 != 0) return fail(FP8_ERR_MISALIGNED, "lda and ldb must be multiples of 16");
+        // the loads address one 256-row tile through a 32-bit byte offset
+        if (lda > (int64_t(1) << 23) || ldb > (int64_t(1) << 23))
+            return fail(FP8_ERR_UNSUPPORTED_SHAPE, "lda and ldb must be <= 2^23 bytes");
     }
     if (ldc < N || ldc < 1) return fail(FP8_ERR_INVALID_ARG, "ldc=%lld must be >= N", (long long)ldc);
     if (!is_aligned(C, out_dtype == FP8_OUT_F32 ? 4 : 2))

@@ -13,16 +13,28 @@
 // A [M x K] and B [N x K] both K-contiguous (Y = X W^T).
 //
 // Design for CDNA4 (gfx950):
-//   * v_mfma_f32_32x32x64_f8f6f4 (E4M3/E5M2 per operand), 4 waves of 64 as a
-//     2x2 grid, each wave a (BM/2) x (BN/2) tile of 32x32 MFMA blocks;
-//   * K tiles of 128 bytes staged global -> registers -> LDS, two LDS stages
-//     so the next tile's loads are in flight during the current MFMAs; one
-//     barrier per K tile;
-//   * LDS rows of 128 B with the 16-byte chunk index XORed by (row & 7) so
-//     that the MFMA operand reads (8 rows at the same chunk per LDS cycle)
-//     hit distinct banks;
-//   * blockIdx -> tile mapping that keeps each XCD (blocks are dealt round
-//     robin over 8 XCDs) on a contiguous, M-grouped range of tiles so that
+//   * v_mfma_f32_32x32x64_f8f6f4 (E4M3/E5M2 chosen per operand).  Four waves
+//     as a 2x2 grid over a BM x BN block tile; each wave owns (BM/2) x (BN/2)
+//     in 32x32 MFMA blocks.  B is the instruction's first operand, so a lane
+//     ends up holding 4 consecutive output columns of one output row: the
+//     epilogue stores 8/16-byte vectors and needs one row scale per lane.
+//   * K advances 64 bytes per stage through a 4-stage LDS ring filled by
+//     buffer-load-to-LDS DMA (no staging registers): loads run three stages
+//     ahead of the MFMAs, each stage is released by one s_waitcnt vmcnt(N)
+//     plus one s_barrier.  The DMA is issued from inline asm (it has no
+//     register results), so the compiler neither tracks nor waits for it:
+//     the explicit vmcnt + barrier is the only ordering, and the asm's memory
+//     clobber keeps every LDS read below it.  Operand fragments are
+//     double-buffered in registers so the LDS reads of stage k+1 overlap the
+//     MFMAs of stage k.
+//   * Rows of 64 bytes in LDS with the 16-byte chunk index XORed by
+//     ((row >> 1) ^ (row >> 3)) & 3: conflict free for 8 or 16 lanes per LDS
+//     cycle.  The swizzle is applied by choosing which global chunk each DMA
+//     lane fetches.
+//   * Ragged M/N and a K tail are zero-filled by the buffer unit itself: the
+//     lanes that fall outside get an out-of-range offset and return zeros.
+//   * blockIdx -> tile mapping keeps each XCD (blocks are dealt round robin
+//     over 8 XCDs) on a contiguous, M-grouped range of tiles so that
 //     concurrently running tiles share A and B panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
@@ -36,9 +48,23 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 128;          // K bytes per tile
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kBK = 64;               // K bytes per stage
+constexpr int kStages = 5;            // LDS ring slots; DMA runs 4 stages ahead
 constexpr int kGemmThreads = 256;
+constexpr uint32_t kOOB = 0x80000000u; // offset past every descriptor's range
+
+// One LDS ring of kStages stages of (BM + BN) x 64 bytes (A rows, then B
+// rows); block scaling adds a 4-slot ring of A's per-row scales.  The ring
+// is sized per kernel: 5 x 32 KiB = 160 KiB for 256x256 tiles.
+template <int BM, int BN>
+struct Ring {
+    static constexpr int kStageBytes = (BM + BN) * 64;
+};
+extern __shared__ __attribute__((aligned(1024))) uint8_t g_ring[];
 
 struct GemmParams {
     const uint8_t* A;
@@ -52,16 +78,53 @@ struct GemmParams {
     int64_t ldc;
     int tiles_m, tiles_n;
     int group_m;
+    int vec_out;          // C rows allow 4-element vector stores
 };
 
-template <int FA, int FB>
-__device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b, const v16f& c) {
+template <int FX, int FY>
+__device__ __forceinline__ v16f mfma32(const v8i& x, const v8i& y, const v16f& c) {
     // cbsz / blgp select the operand formats: 0 = E4M3, 1 = E5M2.  Zero scale
     // operands select the unscaled instruction.
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, gfx9 data format),
+// made wave-uniform so that it lives in SGPRs.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 64 lanes x 16 bytes from rsrc + voff[lane] into LDS [lds, lds + 1024).
+// No register result: nothing in flight targets a VGPR.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, v4i rsrc) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// 64 lanes x 4 bytes into LDS [lds, lds + 256).
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, v4i rsrc) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in
+// flight, then meet the other waves; also a compiler barrier for memory.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // blockIdx -> (tile_m, tile_n)
 __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& tn) {
@@ -77,206 +140,305 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
     tn = in_group / gsize;
 }
 
+// DMA plan of one operand tile (ROWS x 64 bytes per stage): wave w fills
+// rows [w*ROWS/4, (w+1)*ROWS/4) with ROWS/64 instructions of 16 rows each;
+// lane l of instruction i lands at LDS row (w*ROWS/4 + 16i + l/4), physical
+// chunk l%4, and fetches the logical chunk (l%4) ^ swz(row).  Rows past the
+// matrix and chunks past K get an out-of-range offset: the buffer unit
+// returns zeros for them.
 template <int ROWS>
-struct TileLoader {
-    static constexpr int kChunks = ROWS * (kBK / 16) / kGemmThreads;   // 16-byte chunks per thread
-    uint4 r[kChunks];
+struct Dma {
+    static constexpr int kInst = ROWS / 64;
+    v4i rsrc;
+    uint32_t off[kInst];   // byte offset at k = 0, or kOOB
+    int col[kInst];        // logical byte column of this lane's chunk
 
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int row0, int rows_valid,
-                                         int k0, int K) {
+    __device__ __forceinline__ void init(const uint8_t* base, int64_t ld, int row0, int rows_valid) {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int rows_here = max(0, min(ROWS, rows_valid - row0));
+        rsrc = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)((int64_t)rows_here * ld));
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = threadIdx.x + kGemmThreads * i;
-            const int row = c >> 3, cc = c & 7;
-            const int k = k0 + cc * 16;
-            if (row0 + row < rows_valid && k < K)
-                r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(row0 + row) * ld + k);
-            else
-                r[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < kInst; ++i) {
+            const int row = w * (ROWS / 4) + 16 * i + (lane >> 2);
+            const int c = ((lane & 3) ^ swz(row)) * 16;
+            col[i] = c;
+            off[i] = (row < rows_here) ? (uint32_t)((int64_t)row * ld + c) : kOOB;
         }
     }
-    __device__ __forceinline__ void store(uint8_t* lds) const {
+    __device__ __forceinline__ void issue(uint32_t dst, int k0, int K) const {
+        const int w = threadIdx.x >> 6;
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = threadIdx.x + kGemmThreads * i;
-            const int row = c >> 3, cc = c & 7;
-            *reinterpret_cast<uint4*>(lds + swz(row, cc)) = r[i];
+        for (int i = 0; i < kInst; ++i) {
+            const uint32_t o = (off[i] != kOOB && k0 + col[i] < K) ? off[i] + (uint32_t)k0 : kOOB;
+            dma16(dst + (uint32_t)((w * (ROWS / 4) + 16 * i) * kBK), o, rsrc);
         }
     }
 };
 
-// Operand fragment of one 32-row block for K step ks (64 bytes): lane l
-// takes row (l & 31) and 32 bytes at K offset ks*64 + (l >> 5)*32.  A and B
-// use the same lane->K assignment, so the K order inside an MFMA cannot
-// change the dot product.
-__device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row, int ks) {
+// Fragment of one 32-row block: lane l takes row (l & 31) and the 32 bytes
+// at logical chunks 2*(l>>5), 2*(l>>5)+1.
+__device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row) {
     const int lane = threadIdx.x & 63;
-    const int c0 = ks * 4 + (lane >> 5) * 2;
-    const uint4 lo = *reinterpret_cast<const uint4*>(lds + swz(row, c0));
-    const uint4 hi = *reinterpret_cast<const uint4*>(lds + swz(row, c0 + 1));
+    const int c0 = (lane >> 5) * 2;
+    const int s = swz(row);
+    const uint4 lo = *reinterpret_cast<const uint4*>(lds + row * kBK + ((c0 ^ s) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(lds + row * kBK + (((c0 + 1) ^ s) << 4));
     v8i f;
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
     f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
     return f;
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
     const uint32_t b = __float_as_uint(v);
-    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x0040u);   // quiet NaN
-    const uint32_t rounded = b + 0x7FFFu + ((b >> 16) & 1u);
-    return (uint16_t)(rounded >> 16);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x0040u;   // quiet NaN
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// BLOCK: sa is [M x K/128], sb is [N/128 x K/128]; each K tile is one scale
-// block whose MFMA partial sum is promoted into acc with fl32(sa*sb).
+template <int BM, int BN>
+struct Frags {
+    v8i a[BM / 64];
+    v8i b[BN / 64];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void load_frags(Frags<BM, BN>& f, const uint8_t* stage, int wm, int wn) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < BM / 64; ++i) f.a[i] = read_frag(stage, wm * (BM / 2) + i * 32 + (lane & 31));
+#pragma unroll
+    for (int j = 0; j < BN / 64; ++j) f.b[j] = read_frag(stage + BM * kBK, wn * (BN / 2) + j * 32 + (lane & 31));
+}
+
+// The MFMAs of one stage from `cur` (acc[j][i] (+)= B_j . A_i^T: output rows
+// n, columns m) and, when LOAD, the LDS reads of the next stage's fragments
+// into `nxt`.  The scheduler is asked to alternate them (one MFMA, one
+// 16-byte LDS read) so that the matrix pipe has work queued while the
+// reads are in flight; register allocation stays free.
+template <int BM, int BN, int FA, int FB, bool FRESH, bool LOAD>
+__device__ __forceinline__ void mma_stage(v16f (&acc)[BN / 64][BM / 64], const Frags<BM, BN>& cur,
+                                          Frags<BM, BN>& nxt, const uint8_t* nxt_stage, int wm, int wn) {
+    constexpr int TM = BM / 64, TN = BN / 64;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (FRESH) {
+                const v16f z = {};
+                acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], z);
+            } else {
+                acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], acc[j][i]);
+            }
+        }
+    if constexpr (LOAD) {
+        load_frags<BM, BN>(nxt, nxt_stage, wm, wn);
+        constexpr int kReads = 2 * (TM + TN), kMfma = TM * TN;
+#pragma unroll
+        for (int q = 0; q < kMfma; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            const int r = ((q + 1) * kReads) / kMfma - (q * kReads) / kMfma;
+            if (r == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // LDS reads
+            else if (r == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else if (r == 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+    }
+}
+
+// BLOCK: sa is [M x K/128], sb is [N/128 x K/128] (K % 128 == 0, N % 128 == 0,
+// BN <= 128 so that the tile's columns lie in one 128-row block of B).
+//
+// Pipeline, per K stage kt (slot = kt mod 5):
+//   1. s_waitcnt for this wave's DMA of stage kt+1, s_barrier: stage kt+1 is
+//      in LDS for every wave, and every wave is done with stage kt-1's slot;
+//   2. DMA of stage kt+4 into stage kt-1's slot;
+//   3. MFMAs of stage kt from registers, interleaved by the compiler with
+//      the LDS reads of stage kt+1's fragments.
 template <int BM, int BN, int FA, int FB, bool OUT_BF16, bool BLOCK>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int kStageBytes = (BM + BN) * kBK;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    float* sa_lds = reinterpret_cast<float*>(smem + 2 * kStageBytes);   // BLOCK: [2][BM]
+    constexpr int TM = BM / 64, TN = BN / 64;
+    constexpr int kSB = (BM + BN) * kBK;                     // bytes per stage
+    constexpr int kPer = Dma<BM>::kInst + Dma<BN>::kInst;    // DMA ops per stage
+    constexpr int kEven = BLOCK ? 1 : 0;                     // extra op on even stages
+    static_assert(!BLOCK || BN <= 128, "block scaling needs BN <= 128");
 
     int tile_m, tile_n;
     tile_coords(p, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int nk = (p.K + kBK - 1) / kBK;
-    const int nkb = p.K / kBK;   // BLOCK only (K % 128 == 0)
+    const int K = p.K;
+    const int nk = (K + kBK - 1) / kBK;
+    const uint32_t ring = lds_addr(g_ring);
+    float* sa_ring = reinterpret_cast<float*>(g_ring + kStages * kSB);   // [4][BM], block scaling
 
-    v16f acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    Dma<BM> da;
+    Dma<BN> db;
+    da.init(p.A, p.lda, m0, p.M);
+    db.init(p.B, p.ldb, n0, p.N);
 
-    TileLoader<BM> la;
-    TileLoader<BN> lb;
-    float sa_reg = 0.0f;
-    la.load(p.A, p.lda, m0, p.M, 0, p.K);
-    lb.load(p.B, p.ldb, n0, p.N, 0, p.K);
+    // block scaling: wave w DMAs the scales of A rows [64w, 64w+64) of K
+    // block kb into sa_ring[kb & 3] together with stage 2kb.
+    v4i sa_rsrc = {0, 0, 0, 0};
+    uint32_t sa_off = kOOB;
+    const int nkb = K / 128;
     if constexpr (BLOCK) {
-        if (threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
-            sa_reg = p.sa[(int64_t)(m0 + threadIdx.x) * nkb];
+        const int rows_here = max(0, min(BM, p.M - m0));
+        sa_rsrc = make_rsrc(p.sa + (int64_t)m0 * nkb, (uint32_t)((int64_t)rows_here * nkb * 4));
+        const int row = wave * 64 + lane;
+        sa_off = row < rows_here ? (uint32_t)(row * nkb * 4) : kOOB;
     }
-    la.store(smem);
-    lb.store(smem + BM * kBK);
-    if constexpr (BLOCK) {
-        if (threadIdx.x < BM) sa_lds[threadIdx.x] = sa_reg;
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
-        const uint8_t* As = smem + st * kStageBytes;
-        const uint8_t* Bs = As + BM * kBK;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(p.A, p.lda, m0, p.M, (kt + 1) * kBK, p.K);
-            lb.load(p.B, p.ldb, n0, p.N, (kt + 1) * kBK, p.K);
-            if constexpr (BLOCK) {
-                if (threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
-                    sa_reg = p.sa[(int64_t)(m0 + threadIdx.x) * nkb + kt + 1];
-            }
+    auto issue_stage = [&](int ks, int slot) {
+        const uint32_t dst = ring + (uint32_t)(slot * kSB);
+        da.issue(dst, ks * kBK, K);
+        db.issue(dst + BM * kBK, ks * kBK, K);
+        if constexpr (BLOCK) {
+            if ((ks & 1) == 0)
+                dma4(lds_addr(sa_ring) + (uint32_t)((((ks >> 1) & 3) * BM + wave * 64) * 4),
+                     sa_off == kOOB ? kOOB : sa_off + (uint32_t)((ks >> 1) * 4), sa_rsrc);
         }
-        if constexpr (!BLOCK) {
+    };
+
+    v16f acc[TN][TM];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                v8i af[TM], bf[TN];
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int i = 0; i < TM; ++i) af[i] = read_frag(As, wm * WM + i * 32 + (lane & 31), ks);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) bf[j] = read_frag(Bs, wn * WN + j * 32 + (lane & 31), ks);
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<FA, FB>(af[i], bf[j], acc[i][j]);
-            }
-        } else {
-            v16f part[TM][TN];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                v8i af[TM], bf[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i) af[i] = read_frag(As, wm * WM + i * 32 + (lane & 31), ks);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) bf[j] = read_frag(Bs, wn * WN + j * 32 + (lane & 31), ks);
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        if (ks == 0) {
-                            const v16f z = {};
-                            part[i][j] = mfma32<FA, FB>(af[i], bf[j], z);
-                        } else {
-                            part[i][j] = mfma32<FA, FB>(af[i], bf[j], part[i][j]);
-                        }
-                    }
-            }
-            // promotion: acc += part * fl32(sa[row] * sb[col block])
-            const float sbv = p.sb[(int64_t)((n0 + wn * WN) / 128) * nkb + kt];
-            const float* sa_st = sa_lds + st * BM;
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+    v16f part[BLOCK ? TN : 1][BLOCK ? TM : 1];
+
+    // block scaling: acc += part * fl32(sa[m, kb] * sb[n/128, kb])
+    // ([DeepL bets on FP8] 2.3, per-block scaling)
+    auto promote = [&](int kb) {
+        if constexpr (BLOCK) {
+            const float sbv = p.sb[(int64_t)(n0 / 128) * nkb + kb];
+            const float* sa_l = sa_ring + (kb & 3) * BM;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                float sc[16];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 s4 = *reinterpret_cast<const float4*>(
-                        sa_st + wm * WM + i * 32 + g * 8 + (lane >> 5) * 4);
-                    sc[4 * g + 0] = s4.x * sbv;
-                    sc[4 * g + 1] = s4.y * sbv;
-                    sc[4 * g + 2] = s4.z * sbv;
-                    sc[4 * g + 3] = s4.w * sbv;
-                }
+                const float s = sa_l[wm * (BM / 2) + i * 32 + (lane & 31)] * sbv;
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(part[i][j][r], sc[r], acc[i][j][r]);
+                    for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], s, acc[j][i][r]);
             }
         }
-        if (more) {
-            uint8_t* nxt = smem + (st ^ 1) * kStageBytes;
-            la.store(nxt);
-            lb.store(nxt + BM * kBK);
-            if constexpr (BLOCK) {
-                if (threadIdx.x < BM) sa_lds[(st ^ 1) * BM + threadIdx.x] = sa_reg;
-            }
-        }
-        __syncthreads();
+        (void)kb;
+    };
+
+    Frags<BM, BN> f0, f1;
+    if (nk > 0) {
+        for (int s = 0; s < 4 && s < nk; ++s) issue_stage(s, s);
+        // wait for stage 0 while stages 1..3 stay in flight
+        if (nk >= 4) wait_and_barrier<3 * kPer + kEven>();
+        else if (nk == 3) wait_and_barrier<2 * kPer + kEven>();
+        else if (nk == 2) wait_and_barrier<kPer>();
+        else wait_and_barrier<0>();
+        load_frags<BM, BN>(f0, g_ring, wm, wn);
     }
 
-    // epilogue: lane holds column (lane & 31) and rows (r/4)*8 + (lane>>5)*4 + r%4
-    float sa_t = 1.0f, sb_t = 1.0f;
+    // MFMAs of stage KT (parity EVEN) from CUR, with the reads of the next
+    // stage into NXT when LOAD; BLOCK partial handling
+#define FP8MI_MMA(KT, CUR, NXT, PTR, EVEN, LOAD)                                                   \
+    do {                                                                                         \
+        if constexpr (!BLOCK) {                                                                  \
+            mma_stage<BM, BN, FA, FB, false, LOAD>(acc, CUR, NXT, PTR, wm, wn);                  \
+        } else if constexpr (EVEN) {                                                             \
+            mma_stage<BM, BN, FA, FB, true, LOAD>(part, CUR, NXT, PTR, wm, wn);                  \
+            if ((KT) + 1 == nk) promote((KT) >> 1);                                              \
+        } else {                                                                                 \
+            mma_stage<BM, BN, FA, FB, false, LOAD>(part, CUR, NXT, PTR, wm, wn);                 \
+            promote((KT) >> 1);                                                                  \
+        }                                                                                        \
+    } while (0)
+
+    // steady state (kt + 4 < nk): straight-line body
+#define FP8MI_FULL(KT, CUR, NXT, EVEN)                                                               \
+    do {                                                                                         \
+        wait_and_barrier<2 * kPer + kEven>();           /* stage KT+1 ready */                   \
+        int s_issue = s_cur + 4; if (s_issue >= kStages) s_issue -= kStages;                     \
+        issue_stage((KT) + 4, s_issue);                                                          \
+        int s_nxt = s_cur + 1; if (s_nxt >= kStages) s_nxt -= kStages;                           \
+        FP8MI_MMA(KT, CUR, NXT, g_ring + s_nxt * kSB, EVEN, true);                               \
+        s_cur = s_nxt;                                                                           \
+    } while (0)
+    int kt = 0, s_cur = 0;
+    for (; kt + 5 < nk; kt += 2) {
+        FP8MI_FULL(kt, f0, f1, true);
+        FP8MI_FULL(kt + 1, f1, f0, false);
+    }
+#undef FP8MI_FULL
+    // the last stages: nothing left to issue
+#define FP8MI_TAIL(KT, CUR, NXT, EVEN)                                                               \
+    do {                                                                                         \
+        const int kt_ = (KT);                                                                    \
+        if (kt_ + 1 < nk) {                                                                      \
+            if (kt_ + 3 < nk) wait_and_barrier<2 * kPer + kEven>();                              \
+            else if (kt_ + 2 < nk) wait_and_barrier<kPer + ((EVEN) ? kEven : 0)>();              \
+            else wait_and_barrier<0>();                                                          \
+        }                                                                                        \
+        int s_nxt = s_cur + 1; if (s_nxt >= kStages) s_nxt -= kStages;                           \
+        if (kt_ + 4 < nk) {                                                                      \
+            int s_issue = s_cur + 4; if (s_issue >= kStages) s_issue -= kStages;                 \
+            issue_stage(kt_ + 4, s_issue);                                                       \
+        }                                                                                        \
+        FP8MI_MMA(kt_, CUR, NXT, g_ring + s_nxt * kSB, EVEN, false);                             \
+        if (kt_ + 1 < nk) load_frags<BM, BN>(NXT, g_ring + s_nxt * kSB, wm, wn);                 \
+        s_cur = s_nxt;                                                                           \
+    } while (0)
+    for (; kt < nk; kt += 2) {
+        FP8MI_TAIL(kt, f0, f1, true);
+        if (kt + 1 < nk) FP8MI_TAIL(kt + 1, f1, f0, false);
+    }
+#undef FP8MI_TAIL
+#undef FP8MI_MMA
+
+    // epilogue: lane holds C[m][n..n+3] with m = row of A, 4 consecutive n
+    float st_scale = 1.0f;
     if constexpr (!BLOCK) {
-        if (!p.sa_row) sa_t = p.sa[0];
-        if (!p.sb_row) sb_t = p.sb[0];
+        if (!p.sa_row && !p.sb_row) st_scale = p.sa[0] * p.sb[0];
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + (lane & 31);
-        if (n >= p.N) continue;
-        float sbn = sb_t;
-        if constexpr (!BLOCK) {
-            if (p.sb_row) sbn = p.sb[n];
-        }
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * (BM / 2) + i * 32 + (lane & 31);
+        if (m >= p.M) continue;
+        float sam = 1.0f;
+        if constexpr (!BLOCK) sam = p.sa_row ? p.sa[m] : p.sa[0];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int j = 0; j < TN; ++j) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (m >= p.M) continue;
-                float v = acc[i][j][r];
-                if constexpr (!BLOCK) {
-                    const float sam = p.sa_row ? p.sa[m] : sa_t;
-                    v = v * (sam * sbn);
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * (BN / 2) + j * 32 + g * 8 + (lane >> 5) * 4;
+                if (n >= p.N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float s = 1.0f;
+                    if constexpr (!BLOCK) {
+                        if (!p.sa_row && !p.sb_row) s = st_scale;
+                        else s = sam * (p.sb_row ? p.sb[min(n + e, p.N - 1)] : p.sb[0]);
+                    }
+                    v[e] = BLOCK ? acc[j][i][4 * g + e] : acc[j][i][4 * g + e] * s;
                 }
-                if constexpr (OUT_BF16) {
-                    reinterpret_cast<uint16_t*>(p.C)[(int64_t)m * p.ldc + n] = f32_to_bf16_rne(v);
+                const int64_t off = (int64_t)m * p.ldc + n;
+                if (p.vec_out && n + 3 < p.N) {
+                    if constexpr (OUT_BF16) {
+                        uint2 w;
+                        w.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+                        w.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + off) = w;
+                    } else {
+                        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                    }
                 } else {
-                    reinterpret_cast<float*>(p.C)[(int64_t)m * p.ldc + n] = v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (n + e >= p.N) break;
+                        if constexpr (OUT_BF16)
+                            reinterpret_cast<uint16_t*>(p.C)[off + e] = (uint16_t)f32_to_bf16_rne(v[e]);
+                        else
+                            reinterpret_cast<float*>(p.C)[off + e] = v[e];
+                    }
                 }
             }
         }
@@ -286,10 +448,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
 // ---------------------------------------------------------------- host side --
 template <int BM, int BN, int FA, int FB, bool OUT_BF16, bool BLOCK>
 hipError_t launch_tile(const GemmArgs& a) {
-    constexpr size_t smem = 2 * (size_t)(BM + BN) * kBK + (BLOCK ? 2 * BM * sizeof(float) : 0);
+    constexpr size_t smem = (size_t)kStages * (BM + BN) * kBK + (BLOCK ? 4 * BM * sizeof(float) : 0);
+    static_assert(smem <= 160 * 1024, "LDS budget of one CU");
+    auto kern = k_gemm<BM, BN, FA, FB, OUT_BF16, BLOCK>;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
-    auto kern = k_gemm<BM, BN, FA, FB, OUT_BF16, BLOCK>;
     std::call_once(once, [&] {
         attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -303,6 +466,8 @@ hipError_t launch_tile(const GemmArgs& a) {
     p.tiles_m = (int)((a.M + BM - 1) / BM);
     p.tiles_n = (int)((a.N + BN - 1) / BN);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
+    const int esz = a.out_bf16 ? 2 : 4;
+    p.vec_out = (a.ldc % 4 == 0) && ((uintptr_t)a.C % (4 * esz) == 0);
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, a.stream, p);
     return hipGetLastError();

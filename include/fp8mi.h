@@ -175,8 +175,8 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
  * B: uint8 [N x K] codes of format fb (ldb).  sa = a_scale_inv[0] if
  * a_per_row == 0, else a_scale_inv[m] ([M]); likewise sb with [N].
  * C: [M x N] fp32 or bf16 (round-to-nearest-even), leading dimension ldc.
- * Requirements: K % 16 == 0; A, B 16-byte aligned; lda, ldb multiples of 16;
- * C aligned to its element size.  Results are bit-reproducible run to run
+ * Requirements: K % 16 == 0; A, B 16-byte aligned; lda, ldb multiples of 16
+ * and <= 2^23; C aligned to its element size.  Results are bit-reproducible run to run
  * (no split-K, no atomics); they may differ from another tiling in the last
  * bits of the fp32 sum ([DeepL] 5.3). */
 fp8_status fp8_scaled_gemm(const uint8_t* A, fp8_format fa, int64_t lda,
