@@ -16,8 +16,9 @@
 //   * v_mfma_f32_32x32x64_f8f6f4 (E4M3/E5M2 chosen per operand).  Four waves
 //     as a 2x2 grid over a BM x BN block tile; each wave owns (BM/2) x (BN/2)
 //     in 32x32 MFMA blocks.  B is the instruction's first operand, so a lane
-//     ends up holding 4 consecutive output columns of one output row: the
-//     epilogue stores 8/16-byte vectors and needs one row scale per lane.
+//     ends up holding 4 consecutive output columns of one output row (one
+//     row scale per lane).  The epilogue stages the scaled, converted tile
+//     in LDS and stores full 256-byte row segments, 16 bytes per lane.
 //   * K advances 64 bytes per stage through a 4-stage LDS ring filled by
 //     buffer-load-to-LDS DMA (no staging registers): loads run three stages
 //     ahead of the MFMAs, each stage is released by one s_waitcnt vmcnt(N)
@@ -28,9 +29,9 @@
 //     double-buffered in registers so the LDS reads of stage k+1 overlap the
 //     MFMAs of stage k.
 //   * Rows of 64 bytes in LDS with the 16-byte chunk index XORed by
-//     ((row >> 1) ^ (row >> 3)) & 3: conflict free for 8 or 16 lanes per LDS
-//     cycle.  The swizzle is applied by choosing which global chunk each DMA
-//     lane fetches.
+//     (row >> 2) & 3, which measures conflict free for the fragment reads.
+//     The swizzle is applied by choosing which global chunk each DMA lane
+//     fetches.
 //   * Ragged M/N and a K tail are zero-filled by the buffer unit itself: the
 //     lanes that fall outside get an out-of-range offset and return zeros.
 //   * blockIdx -> tile mapping keeps each XCD (blocks are dealt round robin
@@ -78,7 +79,7 @@ struct GemmParams {
     int64_t ldc;
     int tiles_m, tiles_n;
     int group_m;
-    int vec_out;          // C rows allow 4-element vector stores
+    int vec_out;          // C rows allow 16-byte vector stores
 };
 
 template <int FX, int FY>
@@ -88,7 +89,10 @@ __device__ __forceinline__ v16f mfma32(const v8i& x, const v8i& y, const v16f& c
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 16-byte chunk swizzle of 64-byte LDS rows.  Measured on gfx950: with this
+// XOR the 32-rows-by-16-bytes fragment reads of ds_read_b128 take 4 LDS
+// cycles per instruction (256 B/clk, no bank conflict); without it 16.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
@@ -165,13 +169,14 @@ struct Dma {
             off[i] = (row < rows_here) ? (uint32_t)((int64_t)row * ld + c) : kOOB;
         }
     }
-    __device__ __forceinline__ void issue(uint32_t dst, int k0, int K) const {
+    __device__ __forceinline__ void issue_one(uint32_t dst, int k0, int K, int i) const {
         const int w = threadIdx.x >> 6;
+        const uint32_t o = (off[i] != kOOB && k0 + col[i] < K) ? off[i] + (uint32_t)k0 : kOOB;
+        dma16(dst + (uint32_t)((w * (ROWS / 4) + 16 * i) * kBK), o, rsrc);
+    }
+    __device__ __forceinline__ void issue(uint32_t dst, int k0, int K) const {
 #pragma unroll
-        for (int i = 0; i < kInst; ++i) {
-            const uint32_t o = (off[i] != kOOB && k0 + col[i] < K) ? off[i] + (uint32_t)k0 : kOOB;
-            dma16(dst + (uint32_t)((w * (ROWS / 4) + 16 * i) * kBK), o, rsrc);
-        }
+        for (int i = 0; i < kInst; ++i) issue_one(dst, k0, K, i);
     }
 };
 
@@ -210,39 +215,124 @@ __device__ __forceinline__ void load_frags(Frags<BM, BN>& f, const uint8_t* stag
     for (int j = 0; j < BN / 64; ++j) f.b[j] = read_frag(stage + BM * kBK, wn * (BN / 2) + j * 32 + (lane & 31));
 }
 
+// One 16-byte half of a fragment: half h of the 32-row block at `row`.
+__device__ __forceinline__ uint4 read_half(const uint8_t* lds, int row, int h) {
+    const int lane = threadIdx.x & 63;
+    const int c = (lane >> 5) * 2 + h;
+    return *reinterpret_cast<const uint4*>(lds + row * kBK + ((c ^ swz(row)) << 4));
+}
+
+__device__ __forceinline__ void set_half(v8i& f, int h, uint4 v) {
+    f[4 * h + 0] = (int)v.x; f[4 * h + 1] = (int)v.y; f[4 * h + 2] = (int)v.z; f[4 * h + 3] = (int)v.w;
+}
+
+struct NoDma {
+    static constexpr int kCount = 0;
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
 // The MFMAs of one stage from `cur` (acc[j][i] (+)= B_j . A_i^T: output rows
-// n, columns m) and, when LOAD, the LDS reads of the next stage's fragments
-// into `nxt`.  The scheduler is asked to alternate them (one MFMA, one
-// 16-byte LDS read) so that the matrix pipe has work queued while the
-// reads are in flight; register allocation stays free.
-template <int BM, int BN, int FA, int FB, bool FRESH, bool LOAD>
+// n, columns m) as an explicit program: after each MFMA, the 16-byte LDS
+// reads of the next stage's fragments that are due (LOAD), and the share of
+// the DMA instructions of a later stage that is due (dma(d), d < kCount).
+// sched_barrier(0) pins the order, so the matrix pipe always has work
+// queued and the vector-memory unit sees the DMA spread over the stage.
+template <int BM, int BN, int FA, int FB, bool FRESH, bool LOAD, typename DMA>
 __device__ __forceinline__ void mma_stage(v16f (&acc)[BN / 64][BM / 64], const Frags<BM, BN>& cur,
-                                          Frags<BM, BN>& nxt, const uint8_t* nxt_stage, int wm, int wn) {
+                                          Frags<BM, BN>& nxt, const uint8_t* nxt_stage, int wm, int wn,
+                                          const DMA& dma) {
     constexpr int TM = BM / 64, TN = BN / 64;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (FRESH) {
-                const v16f z = {};
-                acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], z);
-            } else {
-                acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], acc[j][i]);
-            }
+    constexpr int kReads = 2 * (TM + TN), kMfma = TM * TN;
+    const int lane = threadIdx.x & 63;
+    const uint8_t* As = nxt_stage;
+    const uint8_t* Bs = nxt_stage + BM * kBK;
+    // read r (0..kReads-1): a0, b0..b{TN-1}, a1..a{TM-1}, two halves each
+    auto one_read = [&](int r) {
+        const int f = r >> 1, h = r & 1;
+        if (f == 0) {
+            set_half(nxt.a[0], h, read_half(As, wm * (BM / 2) + (lane & 31), h));
+        } else if (f <= TN) {
+            const int j = f - 1;
+            set_half(nxt.b[j], h, read_half(Bs, wn * (BN / 2) + j * 32 + (lane & 31), h));
+        } else {
+            const int i = f - TN;
+            set_half(nxt.a[i], h, read_half(As, wm * (BM / 2) + i * 32 + (lane & 31), h));
         }
-    if constexpr (LOAD) {
-        load_frags<BM, BN>(nxt, nxt_stage, wm, wn);
-        constexpr int kReads = 2 * (TM + TN), kMfma = TM * TN;
+    };
 #pragma unroll
-        for (int q = 0; q < kMfma; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-            const int r = ((q + 1) * kReads) / kMfma - (q * kReads) / kMfma;
-            if (r == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // LDS reads
-            else if (r == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            else if (r == 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    for (int q = 0; q < kMfma; ++q) {
+        const int i = q / TN, j = q % TN;
+        if constexpr (FRESH) {
+            const v16f z = {};
+            acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], z);
+        } else {
+            acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], acc[j][i]);
+        }
+        if constexpr (LOAD || DMA::kCount > 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (LOAD) {
+                const int lo = (q * kReads) / kMfma, hi = ((q + 1) * kReads) / kMfma;
+#pragma unroll
+                for (int r = 0; r < kReads; ++r)
+                    if (r >= lo && r < hi) one_read(r);
+            }
+            {
+                // DMA ops [q*kCount/kMfma, (q+1)*kCount/kMfma) after MFMA q: all
+                // kCount of them are issued, spread evenly over the stage
+                const int d0 = (q * DMA::kCount) / kMfma, d1 = ((q + 1) * DMA::kCount) / kMfma;
+#pragma unroll
+                for (int d = 0; d < DMA::kCount; ++d)
+                    if (d >= d0 && d < d1) dma(d);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
+
+// Epilogue staging geometry: each wave stages its (BM/2) x (BN/2) tile in
+// passes of up to 256 bytes per row, rows padded by 16 bytes.
+template <int BM, int BN, bool OUT_BF16>
+struct Epi {
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int kEsz = OUT_BF16 ? 2 : 4;
+    static constexpr int kCols = (256 / kEsz) < WN ? (256 / kEsz) : WN;   // columns per pass
+    static constexpr int kPasses = WN / kCols;
+    static constexpr int kPitch = kCols * kEsz + 16;                      // bytes per staged row
+    static constexpr int kBytes = 4 * WM * kPitch;                        // all four waves
+};
+
+// Dynamic LDS of a kernel: the pipeline ring (+ block-scale ring), or the
+// epilogue staging, whichever is larger.
+template <int BM, int BN, bool OUT_BF16, bool BLOCK>
+constexpr size_t gemm_lds_bytes() {
+    const size_t ring = (size_t)kStages * (BM + BN) * kBK + (BLOCK ? 4 * BM * sizeof(float) : 0);
+    const size_t epi = (size_t)Epi<BM, BN, OUT_BF16>::kBytes;
+    return ring > epi ? ring : epi;
+}
+
+// The DMA instructions of one stage as a functor for mma_stage: d in
+// [0, kInst(A)) issues A's instruction d, then B's; block scaling adds the
+// 4-byte scale load of an even stage as the last one.
+template <int BM, int BN, bool BLOCK>
+struct StageDma {
+    static constexpr int kCount = Dma<BM>::kInst + Dma<BN>::kInst + (BLOCK ? 1 : 0);
+    const Dma<BM>* da;
+    const Dma<BN>* db;
+    uint32_t dst;
+    int k0, K;
+    bool even_issue;      // the stage being issued is even (carries a scale load)
+    uint32_t sa_lds, sa_voff;
+    v4i sa_rsrc;
+    __device__ __forceinline__ void operator()(int d) const {
+        if (d < Dma<BM>::kInst) {
+            da->issue_one(dst, k0, K, d);
+        } else if (d < Dma<BM>::kInst + Dma<BN>::kInst) {
+            db->issue_one(dst + BM * kBK, k0, K, d - Dma<BM>::kInst);
+        } else if (BLOCK && even_issue) {
+            dma4(sa_lds, sa_voff, sa_rsrc);
+        }
+    }
+};
 
 // BLOCK: sa is [M x K/128], sb is [N/128 x K/128] (K % 128 == 0, N % 128 == 0,
 // BN <= 128 so that the tile's columns lie in one 128-row block of B).
@@ -287,6 +377,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
         const int row = wave * 64 + lane;
         sa_off = row < rows_here ? (uint32_t)(row * nkb * 4) : kOOB;
     }
+    auto sa_ring_addr = [&](int kb) -> uint32_t {
+        return lds_addr(sa_ring) + (uint32_t)(((kb & 3) * BM + wave * 64) * 4);
+    };
+    auto sa_voff = [&](int kb) -> uint32_t { return sa_off == kOOB ? kOOB : sa_off + (uint32_t)(kb * 4); };
     auto issue_stage = [&](int ks, int slot) {
         const uint32_t dst = ring + (uint32_t)(slot * kSB);
         da.issue(dst, ks * kBK, K);
@@ -338,15 +432,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
 
     // MFMAs of stage KT (parity EVEN) from CUR, with the reads of the next
     // stage into NXT when LOAD; BLOCK partial handling
-#define FP8MI_MMA(KT, CUR, NXT, PTR, EVEN, LOAD)                                                   \
+#define FP8MI_MMA(KT, CUR, NXT, PTR, EVEN, LOAD, DMAF)                                             \
     do {                                                                                         \
         if constexpr (!BLOCK) {                                                                  \
-            mma_stage<BM, BN, FA, FB, false, LOAD>(acc, CUR, NXT, PTR, wm, wn);                  \
+            mma_stage<BM, BN, FA, FB, false, LOAD>(acc, CUR, NXT, PTR, wm, wn, DMAF);            \
         } else if constexpr (EVEN) {                                                             \
-            mma_stage<BM, BN, FA, FB, true, LOAD>(part, CUR, NXT, PTR, wm, wn);                  \
+            mma_stage<BM, BN, FA, FB, true, LOAD>(part, CUR, NXT, PTR, wm, wn, DMAF);            \
             if ((KT) + 1 == nk) promote((KT) >> 1);                                              \
         } else {                                                                                 \
-            mma_stage<BM, BN, FA, FB, false, LOAD>(part, CUR, NXT, PTR, wm, wn);                 \
+            mma_stage<BM, BN, FA, FB, false, LOAD>(part, CUR, NXT, PTR, wm, wn, DMAF);           \
             promote((KT) >> 1);                                                                  \
         }                                                                                        \
     } while (0)
@@ -356,9 +450,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
     do {                                                                                         \
         wait_and_barrier<2 * kPer + kEven>();           /* stage KT+1 ready */                   \
         int s_issue = s_cur + 4; if (s_issue >= kStages) s_issue -= kStages;                     \
-        issue_stage((KT) + 4, s_issue);                                                          \
+        const StageDma<BM, BN, BLOCK> sdma{&da, &db, ring + (uint32_t)(s_issue * kSB), ((KT) + 4) * kBK, K, \
+                                           ((KT) & 1) == 0, sa_ring_addr(((KT) + 4) >> 1), sa_voff(((KT) + 4) >> 1), sa_rsrc}; \
         int s_nxt = s_cur + 1; if (s_nxt >= kStages) s_nxt -= kStages;                           \
-        FP8MI_MMA(KT, CUR, NXT, g_ring + s_nxt * kSB, EVEN, true);                               \
+        FP8MI_MMA(KT, CUR, NXT, g_ring + s_nxt * kSB, EVEN, true, sdma);                         \
         s_cur = s_nxt;                                                                           \
     } while (0)
     int kt = 0, s_cur = 0;
@@ -381,7 +476,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
             int s_issue = s_cur + 4; if (s_issue >= kStages) s_issue -= kStages;                 \
             issue_stage(kt_ + 4, s_issue);                                                       \
         }                                                                                        \
-        FP8MI_MMA(kt_, CUR, NXT, g_ring + s_nxt * kSB, EVEN, false);                             \
+        FP8MI_MMA(kt_, CUR, NXT, g_ring + s_nxt * kSB, EVEN, false, NoDma{});                    \
         if (kt_ + 1 < nk) load_frags<BM, BN>(NXT, g_ring + s_nxt * kSB, wm, wn);                 \
         s_cur = s_nxt;                                                                           \
     } while (0)
@@ -392,55 +487,93 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
 #undef FP8MI_TAIL
 #undef FP8MI_MMA
 
-    // epilogue: lane holds C[m][n..n+3] with m = row of A, 4 consecutive n
+    // epilogue: scale, convert, and stage the wave's (BM/2) x (BN/2) tile in
+    // LDS (the ring is free once every wave is past its last MFMA), then
+    // store full row segments: 16 bytes per lane, 16 lanes per 256-byte row.
+    using E = Epi<BM, BN, OUT_BF16>;
+    constexpr int WM = E::WM, WN = E::WN;
+    constexpr int kEsz = E::kEsz, kCols = E::kCols, kPasses = E::kPasses, kPitch = E::kPitch;
+    __syncthreads();
+    uint8_t* stage = g_ring + wave * (WM * kPitch);
     float st_scale = 1.0f;
     if constexpr (!BLOCK) {
         if (!p.sa_row && !p.sb_row) st_scale = p.sa[0] * p.sb[0];
     }
+    const int mw = m0 + wm * WM, nw = n0 + wn * WN;   // wave tile origin
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * (BM / 2) + i * 32 + (lane & 31);
-        if (m >= p.M) continue;
-        float sam = 1.0f;
-        if constexpr (!BLOCK) sam = p.sa_row ? p.sa[m] : p.sa[0];
+    for (int pass = 0; pass < kPasses; ++pass) {
+        // 1. registers -> LDS: lane holds row (i*32 + lane%32), columns
+        //    j*32 + g*8 + (lane/32)*4 + 0..3 of the wave tile
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int i = 0; i < TM; ++i) {
+            const int row = i * 32 + (lane & 31);
+            float sam = 1.0f;
+            if constexpr (!BLOCK) {
+                if (p.sa_row) sam = p.sa[min(mw + row, p.M - 1)];
+            }
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * (BN / 2) + j * 32 + g * 8 + (lane >> 5) * 4;
-                if (n >= p.N) continue;
-                float v[4];
+            for (int jj = 0; jj < kCols / 32; ++jj) {
+                const int j = pass * (kCols / 32) + jj;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float s = 1.0f;
-                    if constexpr (!BLOCK) {
-                        if (!p.sa_row && !p.sb_row) s = st_scale;
-                        else s = sam * (p.sb_row ? p.sb[min(n + e, p.N - 1)] : p.sb[0]);
-                    }
-                    v[e] = BLOCK ? acc[j][i][4 * g + e] : acc[j][i][4 * g + e] * s;
-                }
-                const int64_t off = (int64_t)m * p.ldc + n;
-                if (p.vec_out && n + 3 < p.N) {
-                    if constexpr (OUT_BF16) {
-                        uint2 w;
-                        w.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-                        w.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + off) = w;
-                    } else {
-                        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + off) =
-                            make_float4(v[0], v[1], v[2], v[3]);
-                    }
-                } else {
+                for (int g = 0; g < 4; ++g) {
+                    const int col = jj * 32 + g * 8 + (lane >> 5) * 4;   // within the pass
+                    float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        if (n + e >= p.N) break;
-                        if constexpr (OUT_BF16)
-                            reinterpret_cast<uint16_t*>(p.C)[off + e] = (uint16_t)f32_to_bf16_rne(v[e]);
-                        else
-                            reinterpret_cast<float*>(p.C)[off + e] = v[e];
+                        float sc = 1.0f;
+                        if constexpr (!BLOCK) {
+                            if (!p.sa_row && !p.sb_row) sc = st_scale;
+                            else sc = sam * (p.sb_row ? p.sb[min(nw + j * 32 + g * 8 + (lane >> 5) * 4 + e, p.N - 1)]
+                                                      : p.sb[0]);
+                        }
+                        v[e] = acc[j][i][4 * g + e] * sc;
+                    }
+                    uint8_t* dst = stage + row * kPitch + col * kEsz;
+                    if constexpr (OUT_BF16) {
+                        typedef float f2 __attribute__((ext_vector_type(2)));
+                        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                        const f2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+                        const b2 blo = __builtin_convertvector(lo, b2), bhi = __builtin_convertvector(hi, b2);
+                        uint2 w;
+                        w.x = __builtin_bit_cast(uint32_t, blo);
+                        w.y = __builtin_bit_cast(uint32_t, bhi);
+                        *reinterpret_cast<uint2*>(dst) = w;
+                    } else {
+                        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
                     }
                 }
             }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 2. LDS -> global: chunk c = 16 bytes of row c / kChunks
+        constexpr int kChunks = kCols * kEsz / 16;                  // 16-byte chunks per row
+        constexpr int kPerLane = WM * kChunks / 64;
+        const int ncol0 = nw + pass * kCols;
+#pragma unroll
+        for (int t = 0; t < kPerLane; ++t) {
+            const int c = lane + 64 * t;
+            const int row = c / kChunks, ch = c % kChunks;
+            const uint4 w = *reinterpret_cast<const uint4*>(stage + row * kPitch + ch * 16);
+            const int m = mw + row;
+            const int n = ncol0 + ch * (16 / kEsz);
+            if (m >= p.M || n >= p.N) continue;
+            uint8_t* dstg = reinterpret_cast<uint8_t*>(p.C) + ((int64_t)m * p.ldc + n) * kEsz;
+            if (p.vec_out && n + 16 / kEsz <= p.N) {
+                *reinterpret_cast<uint4*>(dstg) = w;
+            } else {
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                for (int e = 0; e < 16 / kEsz && n + e < p.N; ++e) {
+                    if constexpr (OUT_BF16)
+                        reinterpret_cast<uint16_t*>(dstg)[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+                    else
+                        reinterpret_cast<uint32_t*>(dstg)[e] = ww[e];
+                }
+            }
+        }
+        if (pass + 1 < kPasses) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -448,7 +581,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
 // ---------------------------------------------------------------- host side --
 template <int BM, int BN, int FA, int FB, bool OUT_BF16, bool BLOCK>
 hipError_t launch_tile(const GemmArgs& a) {
-    constexpr size_t smem = (size_t)kStages * (BM + BN) * kBK + (BLOCK ? 4 * BM * sizeof(float) : 0);
+    constexpr size_t smem = gemm_lds_bytes<BM, BN, OUT_BF16, BLOCK>();
     static_assert(smem <= 160 * 1024, "LDS budget of one CU");
     auto kern = k_gemm<BM, BN, FA, FB, OUT_BF16, BLOCK>;
     static std::once_flag once;
@@ -467,7 +600,7 @@ hipError_t launch_tile(const GemmArgs& a) {
     p.tiles_n = (int)((a.N + BN - 1) / BN);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     const int esz = a.out_bf16 ? 2 : 4;
-    p.vec_out = (a.ldc % 4 == 0) && ((uintptr_t)a.C % (4 * esz) == 0);
+    p.vec_out = ((a.ldc * esz) % 16 == 0) && ((uintptr_t)a.C % 16 == 0);   // 16-byte row chunks
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, a.stream, p);
     return hipGetLastError();
