@@ -29,10 +29,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
-# rocprofv3 HBM traffic of the GEMM kernel on the mlp8b workload (FETCH_SIZE +
-# WRITE_SIZE per dispatch, scaled by the copy-kernel calibration factor);
-# None until measured for the current kernel.
-GEMM_TRAFFIC_BYTES = None
+# rocprofv3 HBM traffic of the GEMM kernel on the mlp8b workload: FETCH_SIZE x
+# 2.0 + WRITE_SIZE x 1.0 per dispatch (factors from a plain 512 MiB copy, see
+# profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None whenever k_gemm changes
+# until the counters are taken again.
+GEMM_TRAFFIC_BYTES = 488179577
 
 WORKLOADS = {
     "tiny": "tiny: X, W [256 x 256] fp32 N(0,1); per-tensor E4M3; Y fp32",
@@ -56,7 +57,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512, help="X rows in the CPU-baseline sample")
     ap.add_argument("--cpu-cols", type=int, default=4096, help="W rows in the CPU-baseline sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """A plain device-to-device copy of known size: read mib MiB, write mib MiB.
+    Under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the factor that
+    turns those counters into bytes."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
 class Step:
@@ -186,6 +203,9 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import torch
     import fp8_precision_quantization_amd as fp8
     import synth
