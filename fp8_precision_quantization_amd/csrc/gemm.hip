@@ -19,8 +19,8 @@
 //     ends up holding 4 consecutive output columns of one output row (one
 //     row scale per lane).  The epilogue stages the scaled, converted tile
 //     in LDS and stores full 256-byte row segments, 16 bytes per lane.
-//   * K advances 64 bytes per stage through a 4-stage LDS ring filled by
-//     buffer-load-to-LDS DMA (no staging registers): loads run three stages
+//   * K advances 64 bytes per stage through a 5-slot LDS ring filled by
+//     buffer-load-to-LDS DMA (no staging registers): loads run four stages
 //     ahead of the MFMAs, each stage is released by one s_waitcnt vmcnt(N)
 //     plus one s_barrier.  The DMA is issued from inline asm (it has no
 //     register results), so the compiler neither tracks nor waits for it:
@@ -110,11 +110,12 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
     return r;
 }
 
-// 64 lanes x 16 bytes from rsrc + voff[lane] into LDS [lds, lds + 1024).
-// No register result: nothing in flight targets a VGPR.
-__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, v4i rsrc) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
+// 64 lanes x 16 bytes from rsrc + voff[lane] + soff into LDS [lds, lds + 1024).
+// No register result: nothing in flight targets a VGPR.  A lane whose voff
+// is past the descriptor's range reads zeros whatever soff is.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, v4i rsrc, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
 // 64 lanes x 4 bytes into LDS [lds, lds + 256).
@@ -148,35 +149,50 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
 // rows [w*ROWS/4, (w+1)*ROWS/4) with ROWS/64 instructions of 16 rows each;
 // lane l of instruction i lands at LDS row (w*ROWS/4 + 16i + l/4), physical
 // chunk l%4, and fetches the logical chunk (l%4) ^ swz(row).  Rows past the
-// matrix and chunks past K get an out-of-range offset: the buffer unit
-// returns zeros for them.
+// matrix get an out-of-range offset, and so do chunks past K in a ragged
+// last stage: the buffer unit returns zeros for them.
+//
+// A full stage (k0 + 64 <= K) passes k0 as the instruction's scalar offset
+// with the per-lane offsets fixed for the whole loop: no vector arithmetic
+// per DMA.  Only a ragged last stage takes the per-lane K check.
 template <int ROWS>
 struct Dma {
     static constexpr int kInst = ROWS / 64;
     v4i rsrc;
     uint32_t off[kInst];   // byte offset at k = 0, or kOOB
     int col[kInst];        // logical byte column of this lane's chunk
+    uint32_t lds0;         // LDS byte offset of this wave's first row within a stage (wave-uniform)
 
-    __device__ __forceinline__ void init(const uint8_t* base, int64_t ld, int row0, int rows_valid) {
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __device__ __forceinline__ void init(const uint8_t* base, int64_t ld, int row0, int rows_valid, int wave) {
+        const int lane = threadIdx.x & 63;
         const int rows_here = max(0, min(ROWS, rows_valid - row0));
         rsrc = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)((int64_t)rows_here * ld));
+        lds0 = (uint32_t)(wave * (ROWS / 4) * kBK);
 #pragma unroll
         for (int i = 0; i < kInst; ++i) {
-            const int row = w * (ROWS / 4) + 16 * i + (lane >> 2);
+            const int row = wave * (ROWS / 4) + 16 * i + (lane >> 2);
             const int c = ((lane & 3) ^ swz(row)) * 16;
             col[i] = c;
             off[i] = (row < rows_here) ? (uint32_t)((int64_t)row * ld + c) : kOOB;
         }
     }
-    __device__ __forceinline__ void issue_one(uint32_t dst, int k0, int K, int i) const {
-        const int w = threadIdx.x >> 6;
+    // full stage: k0 + kBK <= K
+    __device__ __forceinline__ void issue_full(uint32_t dst, int k0, int i) const {
+        dma16(dst + lds0 + (uint32_t)(16 * i * kBK), off[i], rsrc, (uint32_t)k0);
+    }
+    // any stage, with the per-lane K range check
+    __device__ __forceinline__ void issue_checked(uint32_t dst, int k0, int K, int i) const {
         const uint32_t o = (off[i] != kOOB && k0 + col[i] < K) ? off[i] + (uint32_t)k0 : kOOB;
-        dma16(dst + (uint32_t)((w * (ROWS / 4) + 16 * i) * kBK), o, rsrc);
+        dma16(dst + lds0 + (uint32_t)(16 * i * kBK), o, rsrc, 0u);
     }
     __device__ __forceinline__ void issue(uint32_t dst, int k0, int K) const {
+        if (k0 + kBK <= K) {
 #pragma unroll
-        for (int i = 0; i < kInst; ++i) issue_one(dst, k0, K, i);
+            for (int i = 0; i < kInst; ++i) issue_full(dst, k0, i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kInst; ++i) issue_checked(dst, k0, K, i);
+        }
     }
 };
 
@@ -206,13 +222,16 @@ struct Frags {
     v8i b[BN / 64];
 };
 
+// Same order as the reads inside mma_stage (a0, b0..b{TN-1}, a1..), so that
+// the first MFMAs of the next stage wait only for the reads they use.
 template <int BM, int BN>
 __device__ __forceinline__ void load_frags(Frags<BM, BN>& f, const uint8_t* stage, int wm, int wn) {
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < BM / 64; ++i) f.a[i] = read_frag(stage, wm * (BM / 2) + i * 32 + (lane & 31));
+    f.a[0] = read_frag(stage, wm * (BM / 2) + (lane & 31));
 #pragma unroll
     for (int j = 0; j < BN / 64; ++j) f.b[j] = read_frag(stage + BM * kBK, wn * (BN / 2) + j * 32 + (lane & 31));
+#pragma unroll
+    for (int i = 1; i < BM / 64; ++i) f.a[i] = read_frag(stage, wm * (BM / 2) + i * 32 + (lane & 31));
 }
 
 // One 16-byte half of a fragment: half h of the 32-row block at `row`.
@@ -310,7 +329,7 @@ constexpr size_t gemm_lds_bytes() {
     return ring > epi ? ring : epi;
 }
 
-// The DMA instructions of one stage as a functor for mma_stage: d in
+// The DMA instructions of one full stage as a functor for mma_stage: d in
 // [0, kInst(A)) issues A's instruction d, then B's; block scaling adds the
 // 4-byte scale load of an even stage as the last one.
 template <int BM, int BN, bool BLOCK>
@@ -319,15 +338,15 @@ struct StageDma {
     const Dma<BM>* da;
     const Dma<BN>* db;
     uint32_t dst;
-    int k0, K;
+    int k0;               // a full stage: k0 + kBK <= K
     bool even_issue;      // the stage being issued is even (carries a scale load)
     uint32_t sa_lds, sa_voff;
     v4i sa_rsrc;
     __device__ __forceinline__ void operator()(int d) const {
         if (d < Dma<BM>::kInst) {
-            da->issue_one(dst, k0, K, d);
+            da->issue_full(dst, k0, d);
         } else if (d < Dma<BM>::kInst + Dma<BN>::kInst) {
-            db->issue_one(dst + BM * kBK, k0, K, d - Dma<BM>::kInst);
+            db->issue_full(dst + BM * kBK, k0, d - Dma<BM>::kInst);
         } else if (BLOCK && even_issue) {
             dma4(sa_lds, sa_voff, sa_rsrc);
         }
@@ -354,7 +373,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
     int tile_m, tile_n;
     tile_coords(p, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = p.K;
     const int nk = (K + kBK - 1) / kBK;
@@ -363,8 +382,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
 
     Dma<BM> da;
     Dma<BN> db;
-    da.init(p.A, p.lda, m0, p.M);
-    db.init(p.B, p.ldb, n0, p.N);
+    da.init(p.A, p.lda, m0, p.M, wave);
+    db.init(p.B, p.ldb, n0, p.N, wave);
 
     // block scaling: wave w DMAs the scales of A rows [64w, 64w+64) of K
     // block kb into sa_ring[kb & 3] together with stage 2kb.
@@ -445,19 +464,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
         }                                                                                        \
     } while (0)
 
-    // steady state (kt + 4 < nk): straight-line body
+    // steady state: both stages issued per iteration (kt + 4, kt + 5) are
+    // below the last one, hence full; the last six stages go to the tail
 #define FP8MI_FULL(KT, CUR, NXT, EVEN)                                                               \
     do {                                                                                         \
         wait_and_barrier<2 * kPer + kEven>();           /* stage KT+1 ready */                   \
         int s_issue = s_cur + 4; if (s_issue >= kStages) s_issue -= kStages;                     \
-        const StageDma<BM, BN, BLOCK> sdma{&da, &db, ring + (uint32_t)(s_issue * kSB), ((KT) + 4) * kBK, K, \
-                                           ((KT) & 1) == 0, sa_ring_addr(((KT) + 4) >> 1), sa_voff(((KT) + 4) >> 1), sa_rsrc}; \
+        const StageDma<BM, BN, BLOCK> sdma{&da, &db, ring + (uint32_t)(s_issue * kSB), ((KT) + 4) * kBK, \
+                                           ((KT) & 1) == 0,                                          \
+                                           sa_ring_addr(((KT) + 4) >> 1), sa_voff(((KT) + 4) >> 1), sa_rsrc}; \
         int s_nxt = s_cur + 1; if (s_nxt >= kStages) s_nxt -= kStages;                           \
         FP8MI_MMA(KT, CUR, NXT, g_ring + s_nxt * kSB, EVEN, true, sdma);                         \
         s_cur = s_nxt;                                                                           \
     } while (0)
     int kt = 0, s_cur = 0;
-    for (; kt + 5 < nk; kt += 2) {
+    // settle every LDS / scalar load of the prologue here, so that the loop
+    // head waits only for the fragment reads of the previous stage
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    for (; kt + 6 < nk; kt += 2) {
         FP8MI_FULL(kt, f0, f1, true);
         FP8MI_FULL(kt + 1, f1, f0, false);
     }
