@@ -19,19 +19,22 @@
 //     ends up holding 4 consecutive output columns of one output row (one
 //     row scale per lane).  The epilogue stages the scaled, converted tile
 //     in LDS and stores full 256-byte row segments, 16 bytes per lane.
-//   * K advances 64 bytes per stage through a 5-slot LDS ring filled by
-//     buffer-load-to-LDS DMA (no staging registers): loads run four stages
-//     ahead of the MFMAs, each stage is released by one s_waitcnt vmcnt(N)
-//     plus one s_barrier.  The DMA is issued from inline asm (it has no
-//     register results), so the compiler neither tracks nor waits for it:
-//     the explicit vmcnt + barrier is the only ordering, and the asm's memory
-//     clobber keeps every LDS read below it.  Operand fragments are
-//     double-buffered in registers so the LDS reads of stage k+1 overlap the
-//     MFMAs of stage k.
-//   * Rows of 64 bytes in LDS with the 16-byte chunk index XORed by
-//     (row >> 2) & 3, which measures conflict free for the fragment reads.
-//     The swizzle is applied by choosing which global chunk each DMA lane
-//     fetches.
+//   * Operands reach LDS by buffer-load-to-LDS DMA (no staging registers)
+//     issued from inline asm (it has no register results), so the compiler
+//     neither tracks nor waits for it: explicit s_waitcnt vmcnt(N) plus
+//     s_barrier is the only ordering, and the asm's memory clobber keeps
+//     every LDS read below it.  Operand fragments are double-buffered in
+//     registers so the LDS reads of the next step overlap the MFMAs.
+//   * The scaled GEMM (k_gemm128, 256 x 256 tiles) moves K in stages of 128
+//     bytes, so that 8 lanes of a DMA instruction read one whole 128-byte
+//     line per row (measured: 64-byte row pieces cost about twice the
+//     vector-memory time), through a ring of five 32 KiB slots: A two stages
+//     ahead, B one stage ahead, one barrier per stage.
+//   * The block-scaled GEMM (k_gemm, 256 x 128 tiles) moves K in stages of 64
+//     bytes through a 5-stage ring, four stages ahead, one barrier per stage.
+//   * LDS rows carry an XOR swizzle of their 16-byte chunks that makes the
+//     32-rows-by-16-bytes fragment reads conflict free.  The swizzle is
+//     applied by choosing which global chunk each DMA lane fetches.
 //   * Ragged M/N and a K tail are zero-filled by the buffer unit itself: the
 //     lanes that fall outside get an out-of-range offset and return zeros.
 //   * blockIdx -> tile mapping keeps each XCD (blocks are dealt round robin
@@ -115,7 +118,8 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 // is past the descriptor's range reads zeros whatever soff is.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, v4i rsrc, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                    "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 
 // 64 lanes x 4 bytes into LDS [lds, lds + 256).
@@ -353,6 +357,101 @@ struct StageDma {
     }
 };
 
+// Epilogue: scale, convert, and stage the wave's (BM/2) x (BN/2) tile in
+// LDS (the ring is free once every wave is past its last MFMA), then store
+// full row segments: 16 bytes per lane, 16 lanes per 256-byte row.
+template <int BM, int BN, bool OUT_BF16, bool BLOCK>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const v16f (&acc)[BN / 64][BM / 64], int m0,
+                                              int n0, int wm, int wn, int wave, int lane) {
+    constexpr int TM = BM / 64;
+    using E = Epi<BM, BN, OUT_BF16>;
+    constexpr int WM = E::WM, WN = E::WN;
+    constexpr int kEsz = E::kEsz, kCols = E::kCols, kPasses = E::kPasses, kPitch = E::kPitch;
+    __syncthreads();
+    uint8_t* stage = g_ring + wave * (WM * kPitch);
+    float st_scale = 1.0f;
+    if constexpr (!BLOCK) {
+        if (!p.sa_row && !p.sb_row) st_scale = p.sa[0] * p.sb[0];
+    }
+    const int mw = m0 + wm * WM, nw = n0 + wn * WN;   // wave tile origin
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+        // 1. registers -> LDS: lane holds row (i*32 + lane%32), columns
+        //    j*32 + g*8 + (lane/32)*4 + 0..3 of the wave tile
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = i * 32 + (lane & 31);
+            float sam = 1.0f;
+            if constexpr (!BLOCK) {
+                if (p.sa_row) sam = p.sa[min(mw + row, p.M - 1)];
+            }
+#pragma unroll
+            for (int jj = 0; jj < kCols / 32; ++jj) {
+                const int j = pass * (kCols / 32) + jj;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = jj * 32 + g * 8 + (lane >> 5) * 4;   // within the pass
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float sc = 1.0f;
+                        if constexpr (!BLOCK) {
+                            if (!p.sa_row && !p.sb_row) sc = st_scale;
+                            else sc = sam * (p.sb_row ? p.sb[min(nw + j * 32 + g * 8 + (lane >> 5) * 4 + e, p.N - 1)]
+                                                      : p.sb[0]);
+                        }
+                        v[e] = acc[j][i][4 * g + e] * sc;
+                    }
+                    uint8_t* dst = stage + row * kPitch + col * kEsz;
+                    if constexpr (OUT_BF16) {
+                        typedef float f2 __attribute__((ext_vector_type(2)));
+                        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                        const f2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+                        const b2 blo = __builtin_convertvector(lo, b2), bhi = __builtin_convertvector(hi, b2);
+                        uint2 w;
+                        w.x = __builtin_bit_cast(uint32_t, blo);
+                        w.y = __builtin_bit_cast(uint32_t, bhi);
+                        *reinterpret_cast<uint2*>(dst) = w;
+                    } else {
+                        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 2. LDS -> global: chunk c = 16 bytes of row c / kChunks
+        constexpr int kChunks = kCols * kEsz / 16;                  // 16-byte chunks per row
+        constexpr int kPerLane = WM * kChunks / 64;
+        const int ncol0 = nw + pass * kCols;
+#pragma unroll
+        for (int t = 0; t < kPerLane; ++t) {
+            const int c = lane + 64 * t;
+            const int row = c / kChunks, ch = c % kChunks;
+            const uint4 w = *reinterpret_cast<const uint4*>(stage + row * kPitch + ch * 16);
+            const int m = mw + row;
+            const int n = ncol0 + ch * (16 / kEsz);
+            if (m >= p.M || n >= p.N) continue;
+            uint8_t* dstg = reinterpret_cast<uint8_t*>(p.C) + ((int64_t)m * p.ldc + n) * kEsz;
+            if (p.vec_out && n + 16 / kEsz <= p.N) {
+                *reinterpret_cast<uint4*>(dstg) = w;
+            } else {
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                for (int e = 0; e < 16 / kEsz && n + e < p.N; ++e) {
+                    if constexpr (OUT_BF16)
+                        reinterpret_cast<uint16_t*>(dstg)[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+                    else
+                        reinterpret_cast<uint32_t*>(dstg)[e] = ww[e];
+                }
+            }
+        }
+        if (pass + 1 < kPasses) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 // BLOCK: sa is [M x K/128], sb is [N/128 x K/128] (K % 128 == 0, N % 128 == 0,
 // BN <= 128 so that the tile's columns lie in one 128-row block of B).
 //
@@ -511,95 +610,258 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
 #undef FP8MI_TAIL
 #undef FP8MI_MMA
 
-    // epilogue: scale, convert, and stage the wave's (BM/2) x (BN/2) tile in
-    // LDS (the ring is free once every wave is past its last MFMA), then
-    // store full row segments: 16 bytes per lane, 16 lanes per 256-byte row.
-    using E = Epi<BM, BN, OUT_BF16>;
-    constexpr int WM = E::WM, WN = E::WN;
-    constexpr int kEsz = E::kEsz, kCols = E::kCols, kPasses = E::kPasses, kPitch = E::kPitch;
-    __syncthreads();
-    uint8_t* stage = g_ring + wave * (WM * kPitch);
-    float st_scale = 1.0f;
-    if constexpr (!BLOCK) {
-        if (!p.sa_row && !p.sb_row) st_scale = p.sa[0] * p.sb[0];
+    gemm_epilogue<BM, BN, OUT_BF16, BLOCK>(p, acc, m0, n0, wm, wn, wave, lane);
+}
+
+// ------------------------------------------------------------------------
+// Scaled GEMM with 128-byte K stages (256 x 256 tiles).
+//
+// A stage holds K = 128 bytes of every A and B row of the tile, so each DMA
+// lane group reads whole 128-byte lines (8 lanes per row).  The A rows of
+// stage s live in ring slot (2s) mod 5 and the B rows in slot (2s+1) mod 5
+// (slots of 32 KiB).  A stage is consumed in two MFMA steps of K = 64:
+//   even step 2s:   MFMAs of step 2s; LDS reads of step 2s+1 (stage s,
+//                   second half); DMA of A(s+2) into B(s-1)'s slot;
+//   odd step 2s+1:  after the first MFMA, s_waitcnt for A(s+1), B(s+1)
+//                   (only A(s+2) may still be in flight) and for this wave's
+//                   LDS reads, then s_barrier: stage s+1 is in LDS and every
+//                   wave is done reading stage s; then the LDS reads of step
+//                   2s+2 (stage s+1, first half) and the DMA of B(s+2) into
+//                   A(s)'s slot.
+// So A runs two stages ahead and B one, with one barrier per 128 K.
+// ------------------------------------------------------------------------
+constexpr int kBK2 = 128;                 // K bytes per stage
+constexpr int kSlot2 = 256 * kBK2;        // one operand of one stage: 32 KiB
+
+// 16-byte chunk swizzle of 128-byte LDS rows.  A ds_read_b128 serves 16
+// lanes per LDS cycle; lanes 0-15 read 16 consecutive rows at one logical
+// chunk, whose 16 bank quads (8 * (row & 1) + physical chunk) are distinct
+// under this XOR.
+__device__ __forceinline__ int swz2(int row) { return (row >> 1) & 7; }
+
+// DMA plan of one operand for one stage (256 rows x 128 bytes): wave w fills
+// rows [64w, 64w + 64) with 8 instructions of 8 rows; lane l of instruction
+// i lands at LDS row (64w + 8i + l/8), physical chunk l%8, and fetches the
+// logical chunk (l%8) ^ swz2(row).
+struct Dma2 {
+    static constexpr int kInst = 8;
+    v4i rsrc;
+    uint32_t off[kInst];   // byte offset at k = 0, or kOOB
+    uint32_t lds0;         // LDS offset of this wave's first row within a slot
+
+    // logical byte column of this lane's chunk in instruction i: row bits
+    // 1..3 are (8i + lane/8) bits 1..3, since a wave's first row is a
+    // multiple of 64
+    __device__ __forceinline__ static int col_of(int i) {
+        const int lane = threadIdx.x & 63;
+        return ((lane & 7) ^ (((8 * i + (lane >> 3)) >> 1) & 7)) * 16;
     }
-    const int mw = m0 + wm * WM, nw = n0 + wn * WN;   // wave tile origin
+
+    __device__ __forceinline__ void init(const uint8_t* base, int64_t ld, int row0, int rows_valid, int wave) {
+        const int lane = threadIdx.x & 63;
+        const int rows_here = max(0, min(256, rows_valid - row0));
+        rsrc = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)((int64_t)rows_here * ld));
+        lds0 = (uint32_t)(wave * 64 * kBK2);
 #pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass) {
-        // 1. registers -> LDS: lane holds row (i*32 + lane%32), columns
-        //    j*32 + g*8 + (lane/32)*4 + 0..3 of the wave tile
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = i * 32 + (lane & 31);
-            float sam = 1.0f;
-            if constexpr (!BLOCK) {
-                if (p.sa_row) sam = p.sa[min(mw + row, p.M - 1)];
-            }
-#pragma unroll
-            for (int jj = 0; jj < kCols / 32; ++jj) {
-                const int j = pass * (kCols / 32) + jj;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = jj * 32 + g * 8 + (lane >> 5) * 4;   // within the pass
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float sc = 1.0f;
-                        if constexpr (!BLOCK) {
-                            if (!p.sa_row && !p.sb_row) sc = st_scale;
-                            else sc = sam * (p.sb_row ? p.sb[min(nw + j * 32 + g * 8 + (lane >> 5) * 4 + e, p.N - 1)]
-                                                      : p.sb[0]);
-                        }
-                        v[e] = acc[j][i][4 * g + e] * sc;
-                    }
-                    uint8_t* dst = stage + row * kPitch + col * kEsz;
-                    if constexpr (OUT_BF16) {
-                        typedef float f2 __attribute__((ext_vector_type(2)));
-                        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-                        const f2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
-                        const b2 blo = __builtin_convertvector(lo, b2), bhi = __builtin_convertvector(hi, b2);
-                        uint2 w;
-                        w.x = __builtin_bit_cast(uint32_t, blo);
-                        w.y = __builtin_bit_cast(uint32_t, bhi);
-                        *reinterpret_cast<uint2*>(dst) = w;
-                    } else {
-                        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-        // 2. LDS -> global: chunk c = 16 bytes of row c / kChunks
-        constexpr int kChunks = kCols * kEsz / 16;                  // 16-byte chunks per row
-        constexpr int kPerLane = WM * kChunks / 64;
-        const int ncol0 = nw + pass * kCols;
-#pragma unroll
-        for (int t = 0; t < kPerLane; ++t) {
-            const int c = lane + 64 * t;
-            const int row = c / kChunks, ch = c % kChunks;
-            const uint4 w = *reinterpret_cast<const uint4*>(stage + row * kPitch + ch * 16);
-            const int m = mw + row;
-            const int n = ncol0 + ch * (16 / kEsz);
-            if (m >= p.M || n >= p.N) continue;
-            uint8_t* dstg = reinterpret_cast<uint8_t*>(p.C) + ((int64_t)m * p.ldc + n) * kEsz;
-            if (p.vec_out && n + 16 / kEsz <= p.N) {
-                *reinterpret_cast<uint4*>(dstg) = w;
-            } else {
-                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-                for (int e = 0; e < 16 / kEsz && n + e < p.N; ++e) {
-                    if constexpr (OUT_BF16)
-                        reinterpret_cast<uint16_t*>(dstg)[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
-                    else
-                        reinterpret_cast<uint32_t*>(dstg)[e] = ww[e];
-                }
-            }
-        }
-        if (pass + 1 < kPasses) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            __builtin_amdgcn_wave_barrier();
+        for (int i = 0; i < kInst; ++i) {
+            const int row = wave * 64 + 8 * i + (lane >> 3);
+            off[i] = (row < rows_here) ? (uint32_t)((int64_t)row * ld + col_of(i)) : kOOB;
         }
     }
+    __device__ __forceinline__ void issue_full(uint32_t slot, int k0, int i) const {
+        dma16(slot + lds0 + (uint32_t)(8 * i * kBK2), off[i], rsrc, (uint32_t)k0);
+    }
+    __device__ __forceinline__ void issue_checked(uint32_t slot, int k0, int K, int i) const {
+        const uint32_t o = (off[i] != kOOB && k0 + col_of(i) < K) ? off[i] + (uint32_t)k0 : kOOB;
+        dma16(slot + lds0 + (uint32_t)(8 * i * kBK2), o, rsrc, 0u);
+    }
+    __device__ __forceinline__ void issue(uint32_t slot, int k0, int K) const {
+        if (k0 + kBK2 <= K) {
+#pragma unroll
+            for (int i = 0; i < kInst; ++i) issue_full(slot, k0, i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kInst; ++i) issue_checked(slot, k0, K, i);
+        }
+    }
+};
+
+// The 8 DMA instructions of one operand of one full stage, as a functor.
+struct FullDma {
+    static constexpr int kCount = Dma2::kInst;
+    const Dma2* d;
+    uint32_t slot;
+    int k0;
+    __device__ __forceinline__ void operator()(int i) const { d->issue_full(slot, k0, i); }
+};
+
+// The same for the last stages: `on` and `full` are wave-uniform.
+struct TailDma {
+    static constexpr int kCount = Dma2::kInst;
+    const Dma2* d;
+    uint32_t slot;
+    int k0, K;
+    bool on, full;
+    __device__ __forceinline__ void operator()(int i) const {
+        if (on) {
+            if (full) d->issue_full(slot, k0, i);
+            else d->issue_checked(slot, k0, K, i);
+        }
+    }
+};
+
+// Half e of the 32-byte K piece of step h for the 32-row block at `row`.
+__device__ __forceinline__ uint4 read_half2(const uint8_t* slot, int row, int h, int e) {
+    const int lane = threadIdx.x & 63;
+    const int c = 4 * h + 2 * (lane >> 5) + e;
+    return *reinterpret_cast<const uint4*>(slot + row * kBK2 + ((c ^ swz2(row)) << 4));
+}
+
+// All fragments of step h of a stage, in the order mma_step reads them.
+__device__ __forceinline__ void load_frags2(Frags<256, 256>& f, const uint8_t* As, const uint8_t* Bs, int h,
+                                            int wm, int wn) {
+    const int lane = threadIdx.x & 63;
+    set_half(f.a[0], 0, read_half2(As, wm * 128 + (lane & 31), h, 0));
+    set_half(f.a[0], 1, read_half2(As, wm * 128 + (lane & 31), h, 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        set_half(f.b[j], 0, read_half2(Bs, wn * 128 + j * 32 + (lane & 31), h, 0));
+        set_half(f.b[j], 1, read_half2(Bs, wn * 128 + j * 32 + (lane & 31), h, 1));
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+        set_half(f.a[i], 0, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, 0));
+        set_half(f.a[i], 1, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, 1));
+    }
+}
+
+// The 16 MFMAs of one K = 64 step from `cur`, as an explicit program.
+// BAR: after the first MFMA, s_waitcnt vmcnt(8 if vm8 else 0) lgkmcnt(0)
+// and s_barrier.  The 16 LDS reads of the next step's fragments (step h of
+// the stage in As/Bs) are spread over the MFMAs after the barrier, and so
+// are the DMA functor's kCount instructions.
+template <int FA, int FB, bool BAR, typename DMA>
+__device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const Frags<256, 256>& cur, Frags<256, 256>& nxt,
+                                         const uint8_t* As, const uint8_t* Bs, int h, int wm, int wn,
+                                         const DMA& dma, bool vm8) {
+    constexpr int kReads = 16, kMfma = 16;
+    constexpr int q0 = BAR ? 1 : 0;             // first MFMA followed by reads / DMA
+    constexpr int kSlots = kMfma - q0;
+    const int lane = threadIdx.x & 63;
+    auto one_read = [&](int r) {
+        const int f = r >> 1, e = r & 1;
+        if (f == 0) {
+            set_half(nxt.a[0], e, read_half2(As, wm * 128 + (lane & 31), h, e));
+        } else if (f <= 4) {
+            const int j = f - 1;
+            set_half(nxt.b[j], e, read_half2(Bs, wn * 128 + j * 32 + (lane & 31), h, e));
+        } else {
+            const int i = f - 4;
+            set_half(nxt.a[i], e, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, e));
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+        const int i = q / 4, j = q % 4;
+        acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], acc[j][i]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (BAR) {
+            if (q == 0) {
+                if (vm8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+        }
+        if (q >= q0) {
+            const int t = q - q0;
+            {
+                const int lo = (t * kReads) / kSlots, hi = ((t + 1) * kReads) / kSlots;
+#pragma unroll
+                for (int r = 0; r < kReads; ++r)
+                    if (r >= lo && r < hi) one_read(r);
+            }
+            const int d0 = (t * DMA::kCount) / kSlots, d1 = ((t + 1) * DMA::kCount) / kSlots;
+#pragma unroll
+            for (int d = 0; d < DMA::kCount; ++d)
+                if (d >= d0 && d < d1) dma(d);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm128(GemmParams p) {
+    int tile_m, tile_n;
+    tile_coords(p, tile_m, tile_n);
+    const int m0 = tile_m * 256, n0 = tile_n * 256;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int K = p.K;
+    const int nsteps = (K + 63) / 64;            // K = 64 MFMA steps
+    const int nks = (nsteps + 1) / 2;            // K = 128 stages
+    const uint32_t ring = lds_addr(g_ring);
+    // slot of A(s) = 2s mod 5, of B(s) = 2s+1 mod 5; `sl` tracks 2s mod 5
+    auto wrap = [](int x) { return x >= 5 ? x - 5 : x; };
+    auto addr = [&](int slot) { return ring + (uint32_t)(slot * kSlot2); };
+    auto ptr = [&](int slot) { return g_ring + slot * kSlot2; };
+
+    Dma2 da, db;
+    da.init(p.A, p.lda, m0, p.M, wave);
+    db.init(p.B, p.ldb, n0, p.N, wave);
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+    Frags<256, 256> f0, f1;
+    if (nks > 0) {
+        da.issue(addr(0), 0, K);
+        db.issue(addr(1), 0, K);
+        if (nks > 1) {
+            da.issue(addr(2), kBK2, K);
+            db.issue(addr(3), kBK2, K);
+            wait_and_barrier<2 * Dma2::kInst>();
+        } else {
+            wait_and_barrier<0>();
+        }
+        load_frags2(f0, ptr(0), ptr(1), 0, wm, wn);
+    }
+    // settle the prologue's LDS / scalar loads so that the loop head waits
+    // only for the reads of the previous step
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+
+    int s = 0, sl = 0;   // sl = 2s mod 5: A(s) in slot sl, B(s) in sl+1, A(s+1) in sl+2,
+                         // B(s+1) in sl+3, A(s+2) in sl+4, B(s+2) in sl (mod 5)
+    // steady state: the stage s+2 issued here is below the last one, hence
+    // full, and A(s+2) is in flight at the odd step's wait
+    for (; s + 3 < nks; ++s) {
+        const int s1 = wrap(sl + 1), s2 = wrap(sl + 2), s3 = wrap(sl + 3), s4 = wrap(sl + 4);
+        const FullDma dA{&da, addr(s4), (s + 2) * kBK2};
+        mma_step<FA, FB, false>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, true);
+        const FullDma dB{&db, addr(sl), (s + 2) * kBK2};
+        mma_step<FA, FB, true>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, true);
+        sl = s2;
+    }
+    // the last (up to three) stages, one body: the DMA of stage s+2 runs
+    // while that stage exists (the per-lane K check for a ragged last stage),
+    // and the odd step's wait lets A(s+2) stay in flight while it was issued.
+    // A stage's second step always runs: when K ends inside its first half,
+    // the DMA filled the second half with zeros.  The odd step of the last
+    // stage reads a stale slot into registers that are never used.
+    for (; s < nks; ++s) {
+        const int s1 = wrap(sl + 1), s2 = wrap(sl + 2), s3 = wrap(sl + 3), s4 = wrap(sl + 4);
+        const bool issue = s + 2 < nks;
+        const bool full = (s + 3) * kBK2 <= K;
+        const TailDma dA{&da, addr(s4), (s + 2) * kBK2, K, issue, full};
+        mma_step<FA, FB, false>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, false);
+        const TailDma dB{&db, addr(sl), (s + 2) * kBK2, K, issue, full};
+        mma_step<FA, FB, true>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, issue);
+        sl = s2;
+    }
+    gemm_epilogue<256, 256, OUT_BF16, false>(p, acc, m0, n0, wm, wn, wave, lane);
 }
 
 // ---------------------------------------------------------------- host side --
@@ -607,7 +869,12 @@ template <int BM, int BN, int FA, int FB, bool OUT_BF16, bool BLOCK>
 hipError_t launch_tile(const GemmArgs& a) {
     constexpr size_t smem = gemm_lds_bytes<BM, BN, OUT_BF16, BLOCK>();
     static_assert(smem <= 160 * 1024, "LDS budget of one CU");
-    auto kern = k_gemm<BM, BN, FA, FB, OUT_BF16, BLOCK>;
+    static_assert(BLOCK || (BM == 256 && BN == 256), "the scaled GEMM runs 256 x 256 tiles");
+    static_assert(BLOCK || (size_t)5 * kSlot2 <= smem, "ring of the 128-byte-stage kernel");
+    // the scaled GEMM: 128-byte K stages; the block-scaled GEMM: 64-byte stages
+    void (*kern)(GemmParams);
+    if constexpr (BLOCK) kern = k_gemm<BM, BN, FA, FB, OUT_BF16, true>;
+    else kern = k_gemm128<FA, FB, OUT_BF16>;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {

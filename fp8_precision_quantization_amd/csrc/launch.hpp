@@ -43,7 +43,6 @@ struct GemmArgs {
     int64_t ldc = 0;
     hipStream_t stream = nullptr;
     int num_cus = 256;
-    int tile_override = -1;      // -1: heuristic; otherwise a tile-config id
 };
 
 hipError_t launch_quantize(const QuantArgs& a);
