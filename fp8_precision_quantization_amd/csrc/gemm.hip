@@ -25,11 +25,14 @@
 //     s_barrier is the only ordering, and the asm's memory clobber keeps
 //     every LDS read below it.  Operand fragments are double-buffered in
 //     registers so the LDS reads of the next step overlap the MFMAs.
-//   * The scaled GEMM (k_gemm128, 256 x 256 tiles) moves K in stages of 128
+//   * The scaled GEMM (k_gemm_p, 256 x 256 tiles) moves K in stages of 128
 //     bytes, so that 8 lanes of a DMA instruction read one whole 128-byte
 //     line per row (measured: 64-byte row pieces cost about twice the
 //     vector-memory time), through a ring of five 32 KiB slots: A two stages
-//     ahead, B one stage ahead, one barrier per stage.
+//     ahead, B one stage ahead, one barrier per stage.  It is persistent
+//     (one block per CU when tiles outnumber CUs): the next tile's first
+//     stages stream in during the current tile's last ones, and the
+//     epilogue's stores overlap the next tile's first stage.
 //   * The block-scaled GEMM (k_gemm, 256 x 128 tiles) moves K in stages of 64
 //     bytes through a 5-stage ring, four stages ahead, one barrier per stage.
 //   * LDS rows carry an XOR swizzle of their 16-byte chunks that makes the
@@ -642,37 +645,40 @@ __device__ __forceinline__ int swz2(int row) { return (row >> 1) & 7; }
 // DMA plan of one operand for one stage (256 rows x 128 bytes): wave w fills
 // rows [64w, 64w + 64) with 8 instructions of 8 rows; lane l of instruction
 // i lands at LDS row (64w + 8i + l/8), physical chunk l%8, and fetches the
-// logical chunk (l%8) ^ swz2(row).
+// logical chunk (l%8) ^ swz2(row).  The swizzle depends on the row only
+// through (8i + l/8) bits 1..3, i.e. on the parity of i, so the per-lane
+// offset of instruction i is base[i & 1] + 8i * ld.  The descriptor covers
+// exactly the tile's valid rows, so a row past them is out of range and
+// reads zeros.
 struct Dma2 {
     static constexpr int kInst = 8;
     v4i rsrc;
-    uint32_t off[kInst];   // byte offset at k = 0, or kOOB
+    uint32_t base[2];      // byte offset of instruction 0 / 1 at k = 0, minus 8 * ld for 1
+    uint32_t ld8;          // 8 * ld (wave-uniform)
     uint32_t lds0;         // LDS offset of this wave's first row within a slot
 
-    // logical byte column of this lane's chunk in instruction i: row bits
-    // 1..3 are (8i + lane/8) bits 1..3, since a wave's first row is a
-    // multiple of 64
+    // logical byte column of this lane's chunk in instruction i
     __device__ __forceinline__ static int col_of(int i) {
         const int lane = threadIdx.x & 63;
         return ((lane & 7) ^ (((8 * i + (lane >> 3)) >> 1) & 7)) * 16;
     }
+    __device__ __forceinline__ uint32_t off(int i) const { return base[i & 1] + (uint32_t)i * ld8; }
 
-    __device__ __forceinline__ void init(const uint8_t* base, int64_t ld, int row0, int rows_valid, int wave) {
+    __device__ __forceinline__ void init(const uint8_t* base_ptr, int64_t ld, int row0, int rows_valid, int wave) {
         const int lane = threadIdx.x & 63;
         const int rows_here = max(0, min(256, rows_valid - row0));
-        rsrc = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)((int64_t)rows_here * ld));
+        rsrc = make_rsrc(base_ptr + (int64_t)row0 * ld, (uint32_t)((int64_t)rows_here * ld));
         lds0 = (uint32_t)(wave * 64 * kBK2);
-#pragma unroll
-        for (int i = 0; i < kInst; ++i) {
-            const int row = wave * 64 + 8 * i + (lane >> 3);
-            off[i] = (row < rows_here) ? (uint32_t)((int64_t)row * ld + col_of(i)) : kOOB;
-        }
+        ld8 = (uint32_t)(8 * ld);
+        const uint32_t r0 = (uint32_t)((wave * 64 + (lane >> 3)) * ld);
+        base[0] = r0 + (uint32_t)col_of(0);
+        base[1] = r0 + (uint32_t)col_of(1);
     }
     __device__ __forceinline__ void issue_full(uint32_t slot, int k0, int i) const {
-        dma16(slot + lds0 + (uint32_t)(8 * i * kBK2), off[i], rsrc, (uint32_t)k0);
+        dma16(slot + lds0 + (uint32_t)(8 * i * kBK2), off(i), rsrc, (uint32_t)k0);
     }
     __device__ __forceinline__ void issue_checked(uint32_t slot, int k0, int K, int i) const {
-        const uint32_t o = (off[i] != kOOB && k0 + col_of(i) < K) ? off[i] + (uint32_t)k0 : kOOB;
+        const uint32_t o = (k0 + col_of(i) < K) ? off(i) + (uint32_t)k0 : kOOB;
         dma16(slot + lds0 + (uint32_t)(8 * i * kBK2), o, rsrc, 0u);
     }
     __device__ __forceinline__ void issue(uint32_t slot, int k0, int K) const {
@@ -736,14 +742,14 @@ __device__ __forceinline__ void load_frags2(Frags<256, 256>& f, const uint8_t* A
 }
 
 // The 16 MFMAs of one K = 64 step from `cur`, as an explicit program.
-// BAR: after the first MFMA, s_waitcnt vmcnt(8 if vm8 else 0) lgkmcnt(0)
-// and s_barrier.  The 16 LDS reads of the next step's fragments (step h of
-// the stage in As/Bs) are spread over the MFMAs after the barrier, and so
-// are the DMA functor's kCount instructions.
-template <int FA, int FB, bool BAR, typename DMA>
+// BAR: after the first MFMA, s_waitcnt vmcnt(N) lgkmcnt(0) and s_barrier,
+// with N = 0, 8 or VM2 for vmsel = 0, 1, 2.  The 16 LDS reads of the next
+// step's fragments (step h of the stage in As/Bs) are spread over the MFMAs
+// after the barrier, and so are the DMA functor's kCount instructions.
+template <int FA, int FB, bool BAR, int VM2, typename DMA>
 __device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const Frags<256, 256>& cur, Frags<256, 256>& nxt,
                                          const uint8_t* As, const uint8_t* Bs, int h, int wm, int wn,
-                                         const DMA& dma, bool vm8) {
+                                         const DMA& dma, int vmsel) {
     constexpr int kReads = 16, kMfma = 16;
     constexpr int q0 = BAR ? 1 : 0;             // first MFMA followed by reads / DMA
     constexpr int kSlots = kMfma - q0;
@@ -767,7 +773,8 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const Frags<256, 256
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (BAR) {
             if (q == 0) {
-                if (vm8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (vmsel == 1) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else if (vmsel == 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM2) : "memory");
                 else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             }
         }
@@ -788,25 +795,167 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const Frags<256, 256
     }
 }
 
-template <int FA, int FB, bool OUT_BF16>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm128(GemmParams p) {
-    int tile_m, tile_n;
-    tile_coords(p, tile_m, tile_n);
-    const int m0 = tile_m * 256, n0 = tile_n * 256;
+// Epilogue of one 256 x 256 tile staged through one 32 KiB ring slot: each
+// wave owns 8 KiB = 32 rows x 256 bytes of it, so it writes its 128 x 128
+// tile in passes of one 32-row MFMA block (bf16: all 128 columns, 4 passes;
+// fp32: 64 columns, 8 passes).  A pass writes the scaled, converted values
+// (row r's 16-byte chunk c at physical chunk c ^ (r & 15)), reads them back
+// as 16-byte row chunks (16 lanes per 256-byte row segment) and stores them.
+// An interior tile with 16-byte aligned rows issues exactly kStores vector
+// stores per wave, unconditionally (the persistent loop's vmcnt accounting
+// relies on it).
+template <bool OUT_BF16>
+struct Epi2 {
+    static constexpr int kEsz = OUT_BF16 ? 2 : 4;
+    static constexpr int kCols = 256 / kEsz;            // columns per pass
+    static constexpr int kJ = kCols / 32;               // MFMA column blocks per pass
+    static constexpr int kPasses = 4 * (4 / kJ);
+    static constexpr int kStores = kPasses * 8;         // 8 KiB per pass, 1 KiB per store
+};
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void epilogue_slot(const GemmParams& p, const v16f (&acc)[4][4], int m0, int n0, int wm,
+                                              int wn, int wave, int lane_in, uint8_t* slot, bool interior) {
+    using E = Epi2<OUT_BF16>;
+    // an opaque copy of the lane id: the per-lane address arithmetic below
+    // stays here instead of being hoisted out of the tile loop (where it
+    // would hold registers across the whole K loop)
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    constexpr int kEsz = E::kEsz, kJ = E::kJ;
+    uint8_t* stage = slot + wave * 8192;
+    const float st_scale = (!p.sa_row && !p.sb_row) ? p.sa[0] * p.sb[0] : 1.0f;
+    const int mw = m0 + wm * 128, nw = n0 + wn * 128;      // wave tile origin
+    const int r_w = lane & 31;                              // row of this lane in a 32-row block
+#pragma unroll
+    for (int pass = 0; pass < E::kPasses; ++pass) {
+        const int i = pass / (4 / kJ);                      // 32-row block
+        const int jb = (pass % (4 / kJ)) * kJ;              // first MFMA column block
+        float sam = 1.0f;
+        if (p.sa_row) sam = p.sa[min(mw + i * 32 + r_w, p.M - 1)];
+        // 1. registers -> LDS: lane holds columns j*32 + g*8 + (lane/32)*4 + 0..3
+#pragma unroll
+        for (int jj = 0; jj < kJ; ++jj) {
+            const int j = jb + jj;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = jj * 32 + g * 8 + (lane >> 5) * 4;     // within the pass
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float sc;
+                    if (!p.sa_row && !p.sb_row) sc = st_scale;
+                    else sc = sam * (p.sb_row ? p.sb[min(nw + j * 32 + g * 8 + (lane >> 5) * 4 + e, p.N - 1)] : p.sb[0]);
+                    v[e] = acc[j][i][4 * g + e] * sc;
+                }
+                const int byte = col * kEsz;                           // logical byte in the 256-byte row
+                uint8_t* dst = stage + r_w * 256 + ((((byte >> 4) ^ (r_w & 15)) << 4) | (byte & 15));
+                if constexpr (OUT_BF16) {
+                    typedef float f2 __attribute__((ext_vector_type(2)));
+                    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                    const f2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+                    const b2 blo = __builtin_convertvector(lo, b2), bhi = __builtin_convertvector(hi, b2);
+                    uint2 w;
+                    w.x = __builtin_bit_cast(uint32_t, blo);
+                    w.y = __builtin_bit_cast(uint32_t, bhi);
+                    *reinterpret_cast<uint2*>(dst) = w;
+                } else {
+                    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 2. LDS -> global: store t covers rows 4t .. 4t+3, lane -> row 4t + lane/16, chunk lane%16
+        const int ncol0 = nw + jb * 32;
+        const int ch = lane & 15;
+        uint4 w[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = 4 * t + (lane >> 4);
+            w[t] = *reinterpret_cast<const uint4*>(stage + row * 256 + ((ch ^ (row & 15)) << 4));
+        }
+        const int n = ncol0 + ch * (16 / kEsz);
+        if (interior) {
+            // exactly 8 vector stores per pass
+            uint8_t* dst0 = reinterpret_cast<uint8_t*>(p.C) +
+                            ((int64_t)(mw + i * 32 + (lane >> 4)) * p.ldc + n) * kEsz;
+            const int64_t step = (int64_t)4 * p.ldc * kEsz;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) *reinterpret_cast<uint4*>(dst0 + t * step) = w[t];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int m = mw + i * 32 + 4 * t + (lane >> 4);
+                uint8_t* dstg = reinterpret_cast<uint8_t*>(p.C) + ((int64_t)m * p.ldc + n) * kEsz;
+                if (m < p.M && p.vec_out && n + 16 / kEsz <= p.N) {
+                    *reinterpret_cast<uint4*>(dstg) = w[t];
+                } else if (m < p.M && n < p.N) {
+                    const uint32_t ww[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
+                    for (int e = 0; e < 16 / kEsz && n + e < p.N; ++e) {
+                        if constexpr (OUT_BF16)
+                            reinterpret_cast<uint16_t*>(dstg)[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+                        else
+                            reinterpret_cast<uint32_t*>(dstg)[e] = ww[e];
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // the reads of this pass are done before the next writes
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Linear tile of block b in round r (persistent grid of G blocks): the
+// blocks of one round take G consecutive tiles, each XCD a contiguous range
+// of them; the linear index is then grouped along M as in tile_coords.
+__device__ __forceinline__ bool tile_of_round(const GemmParams& p, int r, int& tm, int& tn) {
+    const int G = gridDim.x;
+    int b = blockIdx.x;
+    if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+    const int t = r * G + b;
+    if (t >= p.tiles_m * p.tiles_n) return false;
+    const int per_group = p.group_m * p.tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * p.group_m;
+    const int gsize = min(p.tiles_m - first_m, p.group_m);
+    const int in_group = t - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+    return true;
+}
+
+// Persistent scaled GEMM over 256 x 256 tiles with 128-byte K stages.
+// Stages are numbered globally over this block's tiles; the ring schedule
+// of each stage is the one described above, so the first two stages of the
+// next tile stream in during the last two stages of the current one.  The
+// epilogue stages through B(last)'s slot, which the schedule leaves free
+// until the next tile's first even step, and its stores overlap the next
+// tile's first stage: the first odd-step wait of a tile counts them as in
+// flight (vector-memory operations complete in issue order).
+// Needs K > 256 (three stages) when a block runs more than one tile.
+template <int FA, int FB, bool OUT_BF16, bool RAGGED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
+    using E = Epi2<OUT_BF16>;
+    constexpr int kVm2 = 8 + E::kStores < 63 ? 8 + E::kStores : 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = p.K;
     const int nsteps = (K + 63) / 64;            // K = 64 MFMA steps
-    const int nks = (nsteps + 1) / 2;            // K = 128 stages
+    const int nks = (nsteps + 1) / 2;            // K = 128 stages per tile
     const uint32_t ring = lds_addr(g_ring);
-    // slot of A(s) = 2s mod 5, of B(s) = 2s+1 mod 5; `sl` tracks 2s mod 5
     auto wrap = [](int x) { return x >= 5 ? x - 5 : x; };
     auto addr = [&](int slot) { return ring + (uint32_t)(slot * kSlot2); };
     auto ptr = [&](int slot) { return g_ring + slot * kSlot2; };
 
+    int tm, tn;
+    if (!tile_of_round(p, 0, tm, tn)) return;
+    int tm_n = 0, tn_n = 0;
+    bool has_next = tile_of_round(p, 1, tm_n, tn_n);
+
     Dma2 da, db;
-    da.init(p.A, p.lda, m0, p.M, wave);
-    db.init(p.B, p.ldb, n0, p.N, wave);
+    da.init(p.A, p.lda, tm * 256, p.M, wave);
+    db.init(p.B, p.ldb, tn * 256, p.N, wave);
 
     v16f acc[4][4];
 #pragma unroll
@@ -833,35 +982,62 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm128(GemmParams p) {
     // only for the reads of the previous step
     __builtin_amdgcn_s_waitcnt(0xC07F);
 
-    int s = 0, sl = 0;   // sl = 2s mod 5: A(s) in slot sl, B(s) in sl+1, A(s+1) in sl+2,
-                         // B(s+1) in sl+3, A(s+2) in sl+4, B(s+2) in sl (mod 5)
-    // steady state: the stage s+2 issued here is below the last one, hence
-    // full, and A(s+2) is in flight at the odd step's wait
-    for (; s + 3 < nks; ++s) {
-        const int s1 = wrap(sl + 1), s2 = wrap(sl + 2), s3 = wrap(sl + 3), s4 = wrap(sl + 4);
-        const FullDma dA{&da, addr(s4), (s + 2) * kBK2};
-        mma_step<FA, FB, false>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, true);
-        const FullDma dB{&db, addr(sl), (s + 2) * kBK2};
-        mma_step<FA, FB, true>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, true);
-        sl = s2;
+    int sl = 0;        // 2g mod 5 for the global stage g: A(g) in slot sl, B(g) in sl+1,
+                       // A(g+1) in sl+2, B(g+1) in sl+3, A(g+2) in sl+4, B(g+2) in sl
+    int first_vm = 1;  // the first odd-step wait of a tile: 8, or 8 + the previous epilogue's stores
+    for (int r = 0;; ++r) {
+        const int m0 = tm * 256, n0 = tn * 256;
+        int s = 0;
+        // stages whose DMA target (s + 2) is in this tile
+        for (; s + 2 < nks; ++s) {
+            const int s1 = wrap(sl + 1), s2 = wrap(sl + 2), s3 = wrap(sl + 3), s4 = wrap(sl + 4);
+            const int vmsel = s == 0 ? first_vm : 1;
+            if constexpr (RAGGED) {
+                const bool full = (s + 3) * kBK2 <= K;
+                const TailDma dA{&da, addr(s4), (s + 2) * kBK2, K, true, full};
+                mma_step<FA, FB, false, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
+                const TailDma dB{&db, addr(sl), (s + 2) * kBK2, K, true, full};
+                mma_step<FA, FB, true, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
+            } else {
+                const FullDma dA{&da, addr(s4), (s + 2) * kBK2};
+                mma_step<FA, FB, false, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
+                const FullDma dB{&db, addr(sl), (s + 2) * kBK2};
+                mma_step<FA, FB, true, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
+            }
+            sl = s2;
+        }
+        // every DMA of this tile is issued: point the descriptors at the next
+        // tile, whose stages 0 and 1 are issued by this tile's last two stages
+        if (has_next) {
+            da.init(p.A, p.lda, tm_n * 256, p.M, wave);
+            db.init(p.B, p.ldb, tn_n * 256, p.N, wave);
+        }
+        for (; s < nks; ++s) {
+            const int s1 = wrap(sl + 1), s2 = wrap(sl + 2), s3 = wrap(sl + 3), s4 = wrap(sl + 4);
+            // odd-step wait: stage s+1 (this tile's, or the next tile's stage 0)
+            // must be in; only the A issued in this even step may still fly
+            const int vmsel = has_next ? 1 : 0;
+            const TailDma dA{&da, addr(s4), (s + 2 - nks) * kBK2, K, has_next, true};
+            mma_step<FA, FB, false, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
+            const TailDma dB{&db, addr(sl), (s + 2 - nks) * kBK2, K, has_next, true};
+            mma_step<FA, FB, true, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
+            sl = s2;
+        }
+        // B(last)'s slot is free until the next tile's first even step
+        const bool interior = p.vec_out && m0 + 256 <= p.M && n0 + 256 <= p.N;
+        epilogue_slot<OUT_BF16>(p, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+        if (!has_next) break;
+        first_vm = interior ? 2 : 1;
+        tm = tm_n; tn = tn_n;
+        has_next = tile_of_round(p, r + 2, tm_n, tn_n);
+        __syncthreads();   // every wave is done with the staging slot
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
     }
-    // the last (up to three) stages, one body: the DMA of stage s+2 runs
-    // while that stage exists (the per-lane K check for a ragged last stage),
-    // and the odd step's wait lets A(s+2) stay in flight while it was issued.
-    // A stage's second step always runs: when K ends inside its first half,
-    // the DMA filled the second half with zeros.  The odd step of the last
-    // stage reads a stale slot into registers that are never used.
-    for (; s < nks; ++s) {
-        const int s1 = wrap(sl + 1), s2 = wrap(sl + 2), s3 = wrap(sl + 3), s4 = wrap(sl + 4);
-        const bool issue = s + 2 < nks;
-        const bool full = (s + 3) * kBK2 <= K;
-        const TailDma dA{&da, addr(s4), (s + 2) * kBK2, K, issue, full};
-        mma_step<FA, FB, false>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, false);
-        const TailDma dB{&db, addr(sl), (s + 2) * kBK2, K, issue, full};
-        mma_step<FA, FB, true>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, issue);
-        sl = s2;
-    }
-    gemm_epilogue<256, 256, OUT_BF16, false>(p, acc, m0, n0, wm, wn, wave, lane);
 }
 
 // ---------------------------------------------------------------- host side --
@@ -874,7 +1050,7 @@ hipError_t launch_tile(const GemmArgs& a) {
     // the scaled GEMM: 128-byte K stages; the block-scaled GEMM: 64-byte stages
     void (*kern)(GemmParams);
     if constexpr (BLOCK) kern = k_gemm<BM, BN, FA, FB, OUT_BF16, true>;
-    else kern = k_gemm128<FA, FB, OUT_BF16>;
+    else kern = (a.K % kBK2 == 0) ? k_gemm_p<FA, FB, OUT_BF16, false> : k_gemm_p<FA, FB, OUT_BF16, true>;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
@@ -892,7 +1068,10 @@ hipError_t launch_tile(const GemmArgs& a) {
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     const int esz = a.out_bf16 ? 2 : 4;
     p.vec_out = ((a.ldc * esz) % 16 == 0) && ((uintptr_t)a.C % 16 == 0);   // 16-byte row chunks
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    // the persistent scaled GEMM runs one block per CU when there are more
+    // tiles than CUs and K has at least three 128-byte stages
+    if (!BLOCK && grid > (unsigned)a.num_cus && a.K > 2 * kBK2) grid = (unsigned)a.num_cus;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, a.stream, p);
     return hipGetLastError();
 }
