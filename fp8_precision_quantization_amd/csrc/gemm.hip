@@ -33,8 +33,10 @@
 //     (one block per CU when tiles outnumber CUs): the next tile's first
 //     stages stream in during the current tile's last ones, and the
 //     epilogue's stores overlap the next tile's first stage.
-//   * The block-scaled GEMM (k_gemm, 256 x 128 tiles) moves K in stages of 64
-//     bytes through a 5-stage ring, four stages ahead, one barrier per stage.
+//   * The block-scaled GEMM (k_gemm_bp, 256 x 128 tiles) also moves K in
+//     stages of 128 bytes, one stage per 128-wide scale block, through three
+//     slots that carry the block's A-row scales too; the promotion of a
+//     block's partial sum is interleaved with the next block's MFMAs.
 //   * LDS rows carry an XOR swizzle of their 16-byte chunks that makes the
 //     32-rows-by-16-bytes fragment reads conflict free.  The swizzle is
 //     applied by choosing which global chunk each DMA lane fetches.
@@ -331,7 +333,9 @@ struct Epi {
 // epilogue staging, whichever is larger.
 template <int BM, int BN, bool OUT_BF16, bool BLOCK>
 constexpr size_t gemm_lds_bytes() {
-    const size_t ring = (size_t)kStages * (BM + BN) * kBK + (BLOCK ? 4 * BM * sizeof(float) : 0);
+    // the scaled GEMM: five 32 KiB slots; the block-scaled GEMM: three
+    // [A | B | scales] slots of 49 KiB
+    const size_t ring = BLOCK ? (size_t)3 * ((size_t)(BM + BN) * 128 + (size_t)BM * 4) : (size_t)5 * (BM + BN) * 64;
     const size_t epi = (size_t)Epi<BM, BN, OUT_BF16>::kBytes;
     return ring > epi ? ring : epi;
 }
@@ -642,16 +646,18 @@ constexpr int kSlot2 = 256 * kBK2;        // one operand of one stage: 32 KiB
 // under this XOR.
 __device__ __forceinline__ int swz2(int row) { return (row >> 1) & 7; }
 
-// DMA plan of one operand for one stage (256 rows x 128 bytes): wave w fills
-// rows [64w, 64w + 64) with 8 instructions of 8 rows; lane l of instruction
-// i lands at LDS row (64w + 8i + l/8), physical chunk l%8, and fetches the
-// logical chunk (l%8) ^ swz2(row).  The swizzle depends on the row only
-// through (8i + l/8) bits 1..3, i.e. on the parity of i, so the per-lane
-// offset of instruction i is base[i & 1] + 8i * ld.  The descriptor covers
-// exactly the tile's valid rows, so a row past them is out of range and
-// reads zeros.
-struct Dma2 {
-    static constexpr int kInst = 8;
+// DMA plan of one operand for one stage (ROWS rows x 128 bytes): wave w
+// fills rows [w*ROWS/4, (w+1)*ROWS/4) with ROWS/32 instructions of 8 rows;
+// lane l of instruction i lands at LDS row (w*ROWS/4 + 8i + l/8), physical
+// chunk l%8, and fetches the logical chunk (l%8) ^ swz2(row).  The swizzle
+// depends on the row only through (8i + l/8) bits 1..3 (ROWS/4 is a
+// multiple of 16), i.e. on the parity of i, so the per-lane offset of
+// instruction i is base[i & 1] + 8i * ld.  The descriptor covers exactly
+// the tile's valid rows, so a row past them is out of range and reads zeros.
+template <int ROWS>
+struct DmaL {
+    static constexpr int kInst = ROWS / 32;
+    static constexpr int kWaveRows = ROWS / 4;
     v4i rsrc;
     uint32_t base[2];      // byte offset of instruction 0 / 1 at k = 0, minus 8 * ld for 1
     uint32_t ld8;          // 8 * ld (wave-uniform)
@@ -666,11 +672,11 @@ struct Dma2 {
 
     __device__ __forceinline__ void init(const uint8_t* base_ptr, int64_t ld, int row0, int rows_valid, int wave) {
         const int lane = threadIdx.x & 63;
-        const int rows_here = max(0, min(256, rows_valid - row0));
+        const int rows_here = max(0, min(ROWS, rows_valid - row0));
         rsrc = make_rsrc(base_ptr + (int64_t)row0 * ld, (uint32_t)((int64_t)rows_here * ld));
-        lds0 = (uint32_t)(wave * 64 * kBK2);
+        lds0 = (uint32_t)(wave * kWaveRows * kBK2);
         ld8 = (uint32_t)(8 * ld);
-        const uint32_t r0 = (uint32_t)((wave * 64 + (lane >> 3)) * ld);
+        const uint32_t r0 = (uint32_t)((wave * kWaveRows + (lane >> 3)) * ld);
         base[0] = r0 + (uint32_t)col_of(0);
         base[1] = r0 + (uint32_t)col_of(1);
     }
@@ -691,6 +697,7 @@ struct Dma2 {
         }
     }
 };
+using Dma2 = DmaL<256>;
 
 // The 8 DMA instructions of one operand of one full stage, as a functor.
 struct FullDma {
@@ -1040,16 +1047,227 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
     }
 }
 
+// ------------------------------------------------------------------------
+// Block-scaled GEMM with 128-byte K stages: one stage is one 128-wide K
+// block.  256 x 128 tiles (wave tile 128 x 64), a ring of three slots of
+// [A 256 x 128 B | B 128 x 128 B | the block's 256 A-row scales], DMA three
+// stages ahead (stage s+3 into stage s's slot once every wave is done with
+// it).  The MFMAs of a block accumulate into `part` (fresh at the block's
+// first step); `acc` += part * sa[m, kb] * sb[n/128, kb] is done element by
+// element just before the next block's fresh MFMA overwrites that part, so
+// the promotion's vector instructions issue between matrix instructions
+// ([DeepL bets on FP8] 2.3, per-block scaling).
+// ------------------------------------------------------------------------
+constexpr int kBSlotA = 256 * kBK2;
+constexpr int kBSlotB = 128 * kBK2;
+constexpr int kBSlot = kBSlotA + kBSlotB + 256 * 4;
+constexpr int kBRing = 3 * kBSlot;
+constexpr int kBPer = DmaL<256>::kInst + DmaL<128>::kInst + 1;   // DMA ops per stage per wave
+
+struct FragsB {
+    v8i a[4];
+    v8i b[2];
+};
+
+// All fragments of step h of a stage, in the order mma_step_b reads them.
+__device__ __forceinline__ void load_frags_b(FragsB& f, const uint8_t* As, const uint8_t* Bs, int h, int wm, int wn) {
+    const int lane = threadIdx.x & 63;
+    set_half(f.a[0], 0, read_half2(As, wm * 128 + (lane & 31), h, 0));
+    set_half(f.a[0], 1, read_half2(As, wm * 128 + (lane & 31), h, 1));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        set_half(f.b[j], 0, read_half2(Bs, wn * 64 + j * 32 + (lane & 31), h, 0));
+        set_half(f.b[j], 1, read_half2(Bs, wn * 64 + j * 32 + (lane & 31), h, 1));
+    }
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+        set_half(f.a[i], 0, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, 0));
+        set_half(f.a[i], 1, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, 1));
+    }
+}
+
+// The DMA instructions of one full stage of the block-scaled GEMM: A's 8,
+// B's 4, and one 4-byte load of the block's A-row scales.
+struct BlockStageDma {
+    static constexpr int kCount = kBPer;
+    const DmaL<256>* da;
+    const DmaL<128>* db;
+    uint32_t slot;          // LDS address of the slot
+    int k0;
+    uint32_t sa_voff;       // this lane's scale offset for the stage, or kOOB
+    v4i sa_rsrc;
+    uint32_t sa_lds;        // LDS address of this wave's 64 scales
+    __device__ __forceinline__ void operator()(int d) const {
+        if (d < DmaL<256>::kInst) da->issue_full(slot, k0, d);
+        else if (d < DmaL<256>::kInst + DmaL<128>::kInst) db->issue_full(slot + kBSlotA, k0, d - DmaL<256>::kInst);
+        else dma4(sa_lds, sa_voff, sa_rsrc);
+    }
+};
+
+// The 8 MFMAs of one K = 64 step of the block-scaled GEMM.  FRESH (a block's
+// first step): before MFMA q overwrites part[q] with a fresh product, the
+// previous block's part[q] is promoted into acc with the per-row scales sc.
+// Otherwise the MFMAs accumulate into part.  BAR, the reads of the next
+// step and the DMA are as in mma_step (vmcnt kBPer or 0 for vmsel 1 / 0).
+template <int FA, int FB, bool FRESH, bool BAR, typename DMA>
+__device__ __forceinline__ void mma_step_b(v16f (&part)[2][4], v16f (&acc)[2][4], const float (&sc)[4],
+                                           const FragsB& cur, FragsB& nxt, const uint8_t* As, const uint8_t* Bs,
+                                           int h, int wm, int wn, const DMA& dma, int vmsel) {
+    constexpr int kReads = 12, kMfma = 8;
+    constexpr int q0 = BAR ? 1 : 0;
+    constexpr int kSlots = kMfma - q0;
+    const int lane = threadIdx.x & 63;
+    auto one_read = [&](int r) {
+        const int f = r >> 1, e = r & 1;
+        if (f == 0) {
+            set_half(nxt.a[0], e, read_half2(As, wm * 128 + (lane & 31), h, e));
+        } else if (f <= 2) {
+            const int j = f - 1;
+            set_half(nxt.b[j], e, read_half2(Bs, wn * 64 + j * 32 + (lane & 31), h, e));
+        } else {
+            const int i = f - 2;
+            set_half(nxt.a[i], e, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, e));
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+        const int i = q / 2, j = q % 2;
+        if constexpr (FRESH) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], sc[i], acc[j][i][r]);
+            const v16f z = {};
+            part[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], z);
+        } else {
+            part[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], part[j][i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (BAR) {
+            if (q == 0) {
+                if (vmsel == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kBPer) : "memory");
+                else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+        }
+        if (q >= q0) {
+            const int t = q - q0;
+            {
+                const int lo = (t * kReads) / kSlots, hi = ((t + 1) * kReads) / kSlots;
+#pragma unroll
+                for (int r = 0; r < kReads; ++r)
+                    if (r >= lo && r < hi) one_read(r);
+            }
+            const int d0 = (t * DMA::kCount) / kSlots, d1 = ((t + 1) * DMA::kCount) / kSlots;
+#pragma unroll
+            for (int d = 0; d < DMA::kCount; ++d)
+                if (d >= d0 && d < d1) dma(d);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// sa is [M x K/128], sb is [N/128 x K/128]; K % 128 == 0, N % 128 == 0.
+template <int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bp(GemmParams p) {
+    int tile_m, tile_n;
+    tile_coords(p, tile_m, tile_n);
+    const int m0 = tile_m * 256, n0 = tile_n * 128;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int K = p.K;
+    const int nks = K / kBK2;                    // 128-wide K blocks = stages
+    const uint32_t ring = lds_addr(g_ring);
+    auto addr = [&](int slot) { return ring + (uint32_t)(slot * kBSlot); };
+    auto ptr = [&](int slot) { return g_ring + slot * kBSlot; };
+    auto wrap3 = [](int x) { return x >= 3 ? x - 3 : x; };
+
+    DmaL<256> da;
+    DmaL<128> db;
+    da.init(p.A, p.lda, m0, p.M, wave);
+    db.init(p.B, p.ldb, n0, p.N, wave);
+    // A-row scales: wave w loads the scales of rows [64w, 64w + 64) of the
+    // stage's K block into the slot's scale area
+    const int rows_here = max(0, min(256, p.M - m0));
+    const v4i sa_rsrc = make_rsrc(p.sa + (int64_t)m0 * nks, (uint32_t)((int64_t)rows_here * nks * 4));
+    const int srow = wave * 64 + lane;
+    const uint32_t sa_off0 = srow < rows_here ? (uint32_t)(srow * nks * 4) : kOOB;
+    auto stage_dma = [&](int st, int slot) {
+        return BlockStageDma{&da, &db, addr(slot), st * kBK2, sa_off0 == kOOB ? kOOB : sa_off0 + (uint32_t)(st * 4),
+                             sa_rsrc, addr(slot) + (uint32_t)(kBSlotA + kBSlotB + wave * 256)};
+    };
+    const float* sb_row = p.sb + (int64_t)(n0 / 128) * nks;
+
+    v16f acc[2][4], part[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { acc[j][i][r] = 0.0f; part[j][i][r] = 0.0f; }
+    float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};     // scales of the block whose part awaits promotion
+
+    FragsB f0, f1;
+    // prologue: stages 0, 1, 2 into slots 0, 1, 2
+    const int npro = nks < 3 ? nks : 3;
+    for (int st = 0; st < npro; ++st) {
+        const BlockStageDma d = stage_dma(st, st);
+#pragma unroll
+        for (int q = 0; q < kBPer; ++q) d(q);
+    }
+    if (npro == 3) wait_and_barrier<2 * kBPer>();
+    else if (npro == 2) wait_and_barrier<kBPer>();
+    else wait_and_barrier<0>();
+    load_frags_b(f0, ptr(0), ptr(0) + kBSlotA, 0, wm, wn);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+
+    int sl = 0;                                  // slot of stage s
+    auto block_scales = [&](int st, int slot) {  // sa[m, st] * sb[n/128, st] for this lane's 4 rows
+        const float* sa_l = reinterpret_cast<const float*>(ptr(slot) + kBSlotA + kBSlotB);
+        const float sbv = sb_row[st];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = sa_l[wm * 128 + i * 32 + (lane & 31)] * sbv;
+    };
+    int s = 0;
+    for (; s + 3 < nks; ++s) {
+        const int s1 = wrap3(sl + 1);
+        // even step: promote block s-1 while starting block s; read step 2s+1
+        mma_step_b<FA, FB, true, false>(part, acc, sc, f0, f1, ptr(sl), ptr(sl) + kBSlotA, 1, wm, wn, NoDma{}, 0);
+        block_scales(s, sl);
+        // odd step: wait for stage s+1 (stage s+2 may fly), free stage s's slot,
+        // read step 2s+2, DMA stage s+3 into stage s's slot
+        const BlockStageDma d = stage_dma(s + 3, sl);
+        mma_step_b<FA, FB, false, true>(part, acc, sc, f1, f0, ptr(s1), ptr(s1) + kBSlotA, 0, wm, wn, d, 1);
+        sl = s1;
+    }
+    for (; s < nks; ++s) {
+        const int s1 = wrap3(sl + 1);
+        mma_step_b<FA, FB, true, false>(part, acc, sc, f0, f1, ptr(sl), ptr(sl) + kBSlotA, 1, wm, wn, NoDma{}, 0);
+        block_scales(s, sl);
+        // (the last stage's odd step reads a stale slot into registers that
+        // are never used)
+        mma_step_b<FA, FB, false, true>(part, acc, sc, f1, f0, ptr(s1), ptr(s1) + kBSlotA, 0, wm, wn, NoDma{},
+                                        s + 2 < nks ? 1 : 0);
+        sl = s1;
+    }
+    // the last block's promotion
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], sc[i], acc[j][i][r]);
+    gemm_epilogue<256, 128, OUT_BF16, true>(p, acc, m0, n0, wm, wn, wave, lane);
+}
+
 // ---------------------------------------------------------------- host side --
 template <int BM, int BN, int FA, int FB, bool OUT_BF16, bool BLOCK>
 hipError_t launch_tile(const GemmArgs& a) {
     constexpr size_t smem = gemm_lds_bytes<BM, BN, OUT_BF16, BLOCK>();
     static_assert(smem <= 160 * 1024, "LDS budget of one CU");
     static_assert(BLOCK || (BM == 256 && BN == 256), "the scaled GEMM runs 256 x 256 tiles");
-    static_assert(BLOCK || (size_t)5 * kSlot2 <= smem, "ring of the 128-byte-stage kernel");
+    static_assert(BLOCK || (size_t)5 * kSlot2 <= smem, "ring of the scaled GEMM");
+    static_assert(!BLOCK || (BM == 256 && BN == 128 && (size_t)kBRing <= smem), "ring of the block-scaled GEMM");
     // the scaled GEMM: 128-byte K stages; the block-scaled GEMM: 64-byte stages
     void (*kern)(GemmParams);
-    if constexpr (BLOCK) kern = k_gemm<BM, BN, FA, FB, OUT_BF16, true>;
+    if constexpr (BLOCK) kern = k_gemm_bp<FA, FB, OUT_BF16>;
     else kern = (a.K % kBK2 == 0) ? k_gemm_p<FA, FB, OUT_BF16, false> : k_gemm_p<FA, FB, OUT_BF16, true>;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
