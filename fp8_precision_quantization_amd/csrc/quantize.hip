@@ -635,7 +635,7 @@ inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0
 constexpr int kScratchCastPartials = 0;      // <= kMaxCastBlocks partials of a delayed cast
 constexpr int kScratchAmaxPartials = 4096;   // <= kMaxAmaxBlocks partials of pass 1
 constexpr int64_t kMaxCastBlocks = 4096;
-constexpr int64_t kMaxAmaxBlocks = 512;
+constexpr int64_t kMaxAmaxBlocks = 1024;   // a stream needs about 4 workgroups per CU (measured)
 static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchWords, "scratch too small");
 
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
