@@ -61,18 +61,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBK = 64;               // K bytes per stage
-constexpr int kStages = 5;            // LDS ring slots; DMA runs 4 stages ahead
 constexpr int kGemmThreads = 256;
 constexpr uint32_t kOOB = 0x80000000u; // offset past every descriptor's range
 
-// One LDS ring of kStages stages of (BM + BN) x 64 bytes (A rows, then B
-// rows); block scaling adds a 4-slot ring of A's per-row scales.  The ring
-// is sized per kernel: 5 x 32 KiB = 160 KiB for 256x256 tiles.
-template <int BM, int BN>
-struct Ring {
-    static constexpr int kStageBytes = (BM + BN) * 64;
-};
 extern __shared__ __attribute__((aligned(1024))) uint8_t g_ring[];
 
 struct GemmParams {
@@ -96,11 +87,6 @@ __device__ __forceinline__ v16f mfma32(const v8i& x, const v8i& y, const v16f& c
     // operands select the unscaled instruction.
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
 }
-
-// 16-byte chunk swizzle of 64-byte LDS rows.  Measured on gfx950: with this
-// XOR the 32-rows-by-16-bytes fragment reads of ds_read_b128 take 4 LDS
-// cycles per instruction (256 B/clk, no bank conflict); without it 16.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
@@ -154,101 +140,11 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
     tn = in_group / gsize;
 }
 
-// DMA plan of one operand tile (ROWS x 64 bytes per stage): wave w fills
-// rows [w*ROWS/4, (w+1)*ROWS/4) with ROWS/64 instructions of 16 rows each;
-// lane l of instruction i lands at LDS row (w*ROWS/4 + 16i + l/4), physical
-// chunk l%4, and fetches the logical chunk (l%4) ^ swz(row).  Rows past the
-// matrix get an out-of-range offset, and so do chunks past K in a ragged
-// last stage: the buffer unit returns zeros for them.
-//
-// A full stage (k0 + 64 <= K) passes k0 as the instruction's scalar offset
-// with the per-lane offsets fixed for the whole loop: no vector arithmetic
-// per DMA.  Only a ragged last stage takes the per-lane K check.
-template <int ROWS>
-struct Dma {
-    static constexpr int kInst = ROWS / 64;
-    v4i rsrc;
-    uint32_t off[kInst];   // byte offset at k = 0, or kOOB
-    int col[kInst];        // logical byte column of this lane's chunk
-    uint32_t lds0;         // LDS byte offset of this wave's first row within a stage (wave-uniform)
-
-    __device__ __forceinline__ void init(const uint8_t* base, int64_t ld, int row0, int rows_valid, int wave) {
-        const int lane = threadIdx.x & 63;
-        const int rows_here = max(0, min(ROWS, rows_valid - row0));
-        rsrc = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)((int64_t)rows_here * ld));
-        lds0 = (uint32_t)(wave * (ROWS / 4) * kBK);
-#pragma unroll
-        for (int i = 0; i < kInst; ++i) {
-            const int row = wave * (ROWS / 4) + 16 * i + (lane >> 2);
-            const int c = ((lane & 3) ^ swz(row)) * 16;
-            col[i] = c;
-            off[i] = (row < rows_here) ? (uint32_t)((int64_t)row * ld + c) : kOOB;
-        }
-    }
-    // full stage: k0 + kBK <= K
-    __device__ __forceinline__ void issue_full(uint32_t dst, int k0, int i) const {
-        dma16(dst + lds0 + (uint32_t)(16 * i * kBK), off[i], rsrc, (uint32_t)k0);
-    }
-    // any stage, with the per-lane K range check
-    __device__ __forceinline__ void issue_checked(uint32_t dst, int k0, int K, int i) const {
-        const uint32_t o = (off[i] != kOOB && k0 + col[i] < K) ? off[i] + (uint32_t)k0 : kOOB;
-        dma16(dst + lds0 + (uint32_t)(16 * i * kBK), o, rsrc, 0u);
-    }
-    __device__ __forceinline__ void issue(uint32_t dst, int k0, int K) const {
-        if (k0 + kBK <= K) {
-#pragma unroll
-            for (int i = 0; i < kInst; ++i) issue_full(dst, k0, i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kInst; ++i) issue_checked(dst, k0, K, i);
-        }
-    }
-};
-
-// Fragment of one 32-row block: lane l takes row (l & 31) and the 32 bytes
-// at logical chunks 2*(l>>5), 2*(l>>5)+1.
-__device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row) {
-    const int lane = threadIdx.x & 63;
-    const int c0 = (lane >> 5) * 2;
-    const int s = swz(row);
-    const uint4 lo = *reinterpret_cast<const uint4*>(lds + row * kBK + ((c0 ^ s) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(lds + row * kBK + (((c0 + 1) ^ s) << 4));
-    v8i f;
-    f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
-    f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
-    return f;
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
-    const uint32_t b = __float_as_uint(v);
-    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x0040u;   // quiet NaN
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 template <int BM, int BN>
 struct Frags {
     v8i a[BM / 64];
     v8i b[BN / 64];
 };
-
-// Same order as the reads inside mma_stage (a0, b0..b{TN-1}, a1..), so that
-// the first MFMAs of the next stage wait only for the reads they use.
-template <int BM, int BN>
-__device__ __forceinline__ void load_frags(Frags<BM, BN>& f, const uint8_t* stage, int wm, int wn) {
-    const int lane = threadIdx.x & 63;
-    f.a[0] = read_frag(stage, wm * (BM / 2) + (lane & 31));
-#pragma unroll
-    for (int j = 0; j < BN / 64; ++j) f.b[j] = read_frag(stage + BM * kBK, wn * (BN / 2) + j * 32 + (lane & 31));
-#pragma unroll
-    for (int i = 1; i < BM / 64; ++i) f.a[i] = read_frag(stage, wm * (BM / 2) + i * 32 + (lane & 31));
-}
-
-// One 16-byte half of a fragment: half h of the 32-row block at `row`.
-__device__ __forceinline__ uint4 read_half(const uint8_t* lds, int row, int h) {
-    const int lane = threadIdx.x & 63;
-    const int c = (lane >> 5) * 2 + h;
-    return *reinterpret_cast<const uint4*>(lds + row * kBK + ((c ^ swz(row)) << 4));
-}
 
 __device__ __forceinline__ void set_half(v8i& f, int h, uint4 v) {
     f[4 * h + 0] = (int)v.x; f[4 * h + 1] = (int)v.y; f[4 * h + 2] = (int)v.z; f[4 * h + 3] = (int)v.w;
@@ -258,64 +154,6 @@ struct NoDma {
     static constexpr int kCount = 0;
     __device__ __forceinline__ void operator()(int) const {}
 };
-
-// The MFMAs of one stage from `cur` (acc[j][i] (+)= B_j . A_i^T: output rows
-// n, columns m) as an explicit program: after each MFMA, the 16-byte LDS
-// reads of the next stage's fragments that are due (LOAD), and the share of
-// the DMA instructions of a later stage that is due (dma(d), d < kCount).
-// sched_barrier(0) pins the order, so the matrix pipe always has work
-// queued and the vector-memory unit sees the DMA spread over the stage.
-template <int BM, int BN, int FA, int FB, bool FRESH, bool LOAD, typename DMA>
-__device__ __forceinline__ void mma_stage(v16f (&acc)[BN / 64][BM / 64], const Frags<BM, BN>& cur,
-                                          Frags<BM, BN>& nxt, const uint8_t* nxt_stage, int wm, int wn,
-                                          const DMA& dma) {
-    constexpr int TM = BM / 64, TN = BN / 64;
-    constexpr int kReads = 2 * (TM + TN), kMfma = TM * TN;
-    const int lane = threadIdx.x & 63;
-    const uint8_t* As = nxt_stage;
-    const uint8_t* Bs = nxt_stage + BM * kBK;
-    // read r (0..kReads-1): a0, b0..b{TN-1}, a1..a{TM-1}, two halves each
-    auto one_read = [&](int r) {
-        const int f = r >> 1, h = r & 1;
-        if (f == 0) {
-            set_half(nxt.a[0], h, read_half(As, wm * (BM / 2) + (lane & 31), h));
-        } else if (f <= TN) {
-            const int j = f - 1;
-            set_half(nxt.b[j], h, read_half(Bs, wn * (BN / 2) + j * 32 + (lane & 31), h));
-        } else {
-            const int i = f - TN;
-            set_half(nxt.a[i], h, read_half(As, wm * (BM / 2) + i * 32 + (lane & 31), h));
-        }
-    };
-#pragma unroll
-    for (int q = 0; q < kMfma; ++q) {
-        const int i = q / TN, j = q % TN;
-        if constexpr (FRESH) {
-            const v16f z = {};
-            acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], z);
-        } else {
-            acc[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], acc[j][i]);
-        }
-        if constexpr (LOAD || DMA::kCount > 0) {
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (LOAD) {
-                const int lo = (q * kReads) / kMfma, hi = ((q + 1) * kReads) / kMfma;
-#pragma unroll
-                for (int r = 0; r < kReads; ++r)
-                    if (r >= lo && r < hi) one_read(r);
-            }
-            {
-                // DMA ops [q*kCount/kMfma, (q+1)*kCount/kMfma) after MFMA q: all
-                // kCount of them are issued, spread evenly over the stage
-                const int d0 = (q * DMA::kCount) / kMfma, d1 = ((q + 1) * DMA::kCount) / kMfma;
-#pragma unroll
-                for (int d = 0; d < DMA::kCount; ++d)
-                    if (d >= d0 && d < d1) dma(d);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-}
 
 // Epilogue staging geometry: each wave stages its (BM/2) x (BN/2) tile in
 // passes of up to 256 bytes per row, rows padded by 16 bytes.
@@ -327,41 +165,6 @@ struct Epi {
     static constexpr int kPasses = WN / kCols;
     static constexpr int kPitch = kCols * kEsz + 16;                      // bytes per staged row
     static constexpr int kBytes = 4 * WM * kPitch;                        // all four waves
-};
-
-// Dynamic LDS of a kernel: the pipeline ring (+ block-scale ring), or the
-// epilogue staging, whichever is larger.
-template <int BM, int BN, bool OUT_BF16, bool BLOCK>
-constexpr size_t gemm_lds_bytes() {
-    // the scaled GEMM: five 32 KiB slots; the block-scaled GEMM: three
-    // [A | B | scales] slots of 49 KiB
-    const size_t ring = BLOCK ? (size_t)3 * ((size_t)(BM + BN) * 128 + (size_t)BM * 4) : (size_t)5 * (BM + BN) * 64;
-    const size_t epi = (size_t)Epi<BM, BN, OUT_BF16>::kBytes;
-    return ring > epi ? ring : epi;
-}
-
-// The DMA instructions of one full stage as a functor for mma_stage: d in
-// [0, kInst(A)) issues A's instruction d, then B's; block scaling adds the
-// 4-byte scale load of an even stage as the last one.
-template <int BM, int BN, bool BLOCK>
-struct StageDma {
-    static constexpr int kCount = Dma<BM>::kInst + Dma<BN>::kInst + (BLOCK ? 1 : 0);
-    const Dma<BM>* da;
-    const Dma<BN>* db;
-    uint32_t dst;
-    int k0;               // a full stage: k0 + kBK <= K
-    bool even_issue;      // the stage being issued is even (carries a scale load)
-    uint32_t sa_lds, sa_voff;
-    v4i sa_rsrc;
-    __device__ __forceinline__ void operator()(int d) const {
-        if (d < Dma<BM>::kInst) {
-            da->issue_full(dst, k0, d);
-        } else if (d < Dma<BM>::kInst + Dma<BN>::kInst) {
-            db->issue_full(dst + BM * kBK, k0, d - Dma<BM>::kInst);
-        } else if (BLOCK && even_issue) {
-            dma4(sa_lds, sa_voff, sa_rsrc);
-        }
-    }
 };
 
 // Epilogue: scale, convert, and stage the wave's (BM/2) x (BN/2) tile in
@@ -457,167 +260,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const v16f (&
             __builtin_amdgcn_wave_barrier();
         }
     }
-}
-
-// BLOCK: sa is [M x K/128], sb is [N/128 x K/128] (K % 128 == 0, N % 128 == 0,
-// BN <= 128 so that the tile's columns lie in one 128-row block of B).
-//
-// Pipeline, per K stage kt (slot = kt mod 5):
-//   1. s_waitcnt for this wave's DMA of stage kt+1, s_barrier: stage kt+1 is
-//      in LDS for every wave, and every wave is done with stage kt-1's slot;
-//   2. DMA of stage kt+4 into stage kt-1's slot;
-//   3. MFMAs of stage kt from registers, interleaved by the compiler with
-//      the LDS reads of stage kt+1's fragments.
-template <int BM, int BN, int FA, int FB, bool OUT_BF16, bool BLOCK>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(GemmParams p) {
-    constexpr int TM = BM / 64, TN = BN / 64;
-    constexpr int kSB = (BM + BN) * kBK;                     // bytes per stage
-    constexpr int kPer = Dma<BM>::kInst + Dma<BN>::kInst;    // DMA ops per stage
-    constexpr int kEven = BLOCK ? 1 : 0;                     // extra op on even stages
-    static_assert(!BLOCK || BN <= 128, "block scaling needs BN <= 128");
-
-    int tile_m, tile_n;
-    tile_coords(p, tile_m, tile_n);
-    const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int K = p.K;
-    const int nk = (K + kBK - 1) / kBK;
-    const uint32_t ring = lds_addr(g_ring);
-    float* sa_ring = reinterpret_cast<float*>(g_ring + kStages * kSB);   // [4][BM], block scaling
-
-    Dma<BM> da;
-    Dma<BN> db;
-    da.init(p.A, p.lda, m0, p.M, wave);
-    db.init(p.B, p.ldb, n0, p.N, wave);
-
-    // block scaling: wave w DMAs the scales of A rows [64w, 64w+64) of K
-    // block kb into sa_ring[kb & 3] together with stage 2kb.
-    v4i sa_rsrc = {0, 0, 0, 0};
-    uint32_t sa_off = kOOB;
-    const int nkb = K / 128;
-    if constexpr (BLOCK) {
-        const int rows_here = max(0, min(BM, p.M - m0));
-        sa_rsrc = make_rsrc(p.sa + (int64_t)m0 * nkb, (uint32_t)((int64_t)rows_here * nkb * 4));
-        const int row = wave * 64 + lane;
-        sa_off = row < rows_here ? (uint32_t)(row * nkb * 4) : kOOB;
-    }
-    auto sa_ring_addr = [&](int kb) -> uint32_t {
-        return lds_addr(sa_ring) + (uint32_t)(((kb & 3) * BM + wave * 64) * 4);
-    };
-    auto sa_voff = [&](int kb) -> uint32_t { return sa_off == kOOB ? kOOB : sa_off + (uint32_t)(kb * 4); };
-    auto issue_stage = [&](int ks, int slot) {
-        const uint32_t dst = ring + (uint32_t)(slot * kSB);
-        da.issue(dst, ks * kBK, K);
-        db.issue(dst + BM * kBK, ks * kBK, K);
-        if constexpr (BLOCK) {
-            if ((ks & 1) == 0)
-                dma4(lds_addr(sa_ring) + (uint32_t)((((ks >> 1) & 3) * BM + wave * 64) * 4),
-                     sa_off == kOOB ? kOOB : sa_off + (uint32_t)((ks >> 1) * 4), sa_rsrc);
-        }
-    };
-
-    v16f acc[TN][TM];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
-    v16f part[BLOCK ? TN : 1][BLOCK ? TM : 1];
-
-    // block scaling: acc += part * fl32(sa[m, kb] * sb[n/128, kb])
-    // ([DeepL bets on FP8] 2.3, per-block scaling)
-    auto promote = [&](int kb) {
-        if constexpr (BLOCK) {
-            const float sbv = p.sb[(int64_t)(n0 / 128) * nkb + kb];
-            const float* sa_l = sa_ring + (kb & 3) * BM;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const float s = sa_l[wm * (BM / 2) + i * 32 + (lane & 31)] * sbv;
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], s, acc[j][i][r]);
-            }
-        }
-        (void)kb;
-    };
-
-    Frags<BM, BN> f0, f1;
-    if (nk > 0) {
-        for (int s = 0; s < 4 && s < nk; ++s) issue_stage(s, s);
-        // wait for stage 0 while stages 1..3 stay in flight
-        if (nk >= 4) wait_and_barrier<3 * kPer + kEven>();
-        else if (nk == 3) wait_and_barrier<2 * kPer + kEven>();
-        else if (nk == 2) wait_and_barrier<kPer>();
-        else wait_and_barrier<0>();
-        load_frags<BM, BN>(f0, g_ring, wm, wn);
-    }
-
-    // MFMAs of stage KT (parity EVEN) from CUR, with the reads of the next
-    // stage into NXT when LOAD; BLOCK partial handling
-#define FP8MI_MMA(KT, CUR, NXT, PTR, EVEN, LOAD, DMAF)                                             \
-    do {                                                                                         \
-        if constexpr (!BLOCK) {                                                                  \
-            mma_stage<BM, BN, FA, FB, false, LOAD>(acc, CUR, NXT, PTR, wm, wn, DMAF);            \
-        } else if constexpr (EVEN) {                                                             \
-            mma_stage<BM, BN, FA, FB, true, LOAD>(part, CUR, NXT, PTR, wm, wn, DMAF);            \
-            if ((KT) + 1 == nk) promote((KT) >> 1);                                              \
-        } else {                                                                                 \
-            mma_stage<BM, BN, FA, FB, false, LOAD>(part, CUR, NXT, PTR, wm, wn, DMAF);           \
-            promote((KT) >> 1);                                                                  \
-        }                                                                                        \
-    } while (0)
-
-    // steady state: both stages issued per iteration (kt + 4, kt + 5) are
-    // below the last one, hence full; the last six stages go to the tail
-#define FP8MI_FULL(KT, CUR, NXT, EVEN)                                                               \
-    do {                                                                                         \
-        wait_and_barrier<2 * kPer + kEven>();           /* stage KT+1 ready */                   \
-        int s_issue = s_cur + 4; if (s_issue >= kStages) s_issue -= kStages;                     \
-        const StageDma<BM, BN, BLOCK> sdma{&da, &db, ring + (uint32_t)(s_issue * kSB), ((KT) + 4) * kBK, \
-                                           ((KT) & 1) == 0,                                          \
-                                           sa_ring_addr(((KT) + 4) >> 1), sa_voff(((KT) + 4) >> 1), sa_rsrc}; \
-        int s_nxt = s_cur + 1; if (s_nxt >= kStages) s_nxt -= kStages;                           \
-        FP8MI_MMA(KT, CUR, NXT, g_ring + s_nxt * kSB, EVEN, true, sdma);                         \
-        s_cur = s_nxt;                                                                           \
-    } while (0)
-    int kt = 0, s_cur = 0;
-    // settle every LDS / scalar load of the prologue here, so that the loop
-    // head waits only for the fragment reads of the previous stage
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    for (; kt + 6 < nk; kt += 2) {
-        FP8MI_FULL(kt, f0, f1, true);
-        FP8MI_FULL(kt + 1, f1, f0, false);
-    }
-#undef FP8MI_FULL
-    // the last stages: nothing left to issue
-#define FP8MI_TAIL(KT, CUR, NXT, EVEN)                                                               \
-    do {                                                                                         \
-        const int kt_ = (KT);                                                                    \
-        if (kt_ + 1 < nk) {                                                                      \
-            if (kt_ + 3 < nk) wait_and_barrier<2 * kPer + kEven>();                              \
-            else if (kt_ + 2 < nk) wait_and_barrier<kPer + ((EVEN) ? kEven : 0)>();              \
-            else wait_and_barrier<0>();                                                          \
-        }                                                                                        \
-        int s_nxt = s_cur + 1; if (s_nxt >= kStages) s_nxt -= kStages;                           \
-        if (kt_ + 4 < nk) {                                                                      \
-            int s_issue = s_cur + 4; if (s_issue >= kStages) s_issue -= kStages;                 \
-            issue_stage(kt_ + 4, s_issue);                                                       \
-        }                                                                                        \
-        FP8MI_MMA(kt_, CUR, NXT, g_ring + s_nxt * kSB, EVEN, false, NoDma{});                    \
-        if (kt_ + 1 < nk) load_frags<BM, BN>(NXT, g_ring + s_nxt * kSB, wm, wn);                 \
-        s_cur = s_nxt;                                                                           \
-    } while (0)
-    for (; kt < nk; kt += 2) {
-        FP8MI_TAIL(kt, f0, f1, true);
-        if (kt + 1 < nk) FP8MI_TAIL(kt + 1, f1, f0, false);
-    }
-#undef FP8MI_TAIL
-#undef FP8MI_MMA
-
-    gemm_epilogue<BM, BN, OUT_BF16, BLOCK>(p, acc, m0, n0, wm, wn, wave, lane);
 }
 
 // ------------------------------------------------------------------------
@@ -1062,7 +704,9 @@ constexpr int kBSlotA = 256 * kBK2;
 constexpr int kBSlotB = 128 * kBK2;
 constexpr int kBSlot = kBSlotA + kBSlotB + 256 * 4;
 constexpr int kBRing = 3 * kBSlot;
-constexpr int kBPer = DmaL<256>::kInst + DmaL<128>::kInst + 1;   // DMA ops per stage per wave
+// DMA ops per stage per wave: A's 8, B's 4 and one 4-byte load of the
+// block's A-row scales
+constexpr int kBPer = DmaL<256>::kInst + DmaL<128>::kInst + 1;
 
 struct FragsB {
     v8i a[4];
@@ -1086,8 +730,8 @@ __device__ __forceinline__ void load_frags_b(FragsB& f, const uint8_t* As, const
     }
 }
 
-// The DMA instructions of one full stage of the block-scaled GEMM: A's 8,
-// B's 4, and one 4-byte load of the block's A-row scales.
+// The DMA instructions of one stage of the block-scaled GEMM: A's 8, B's 4
+// and one 4-byte load of the block's A-row scales.
 struct BlockStageDma {
     static constexpr int kCount = kBPer;
     const DmaL<256>* da;
@@ -1225,24 +869,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bp(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[i] = sa_l[wm * 128 + i * 32 + (lane & 31)] * sbv;
     };
+    // even step: promote block s-1 while starting block s; read step 2s+1.
+    // Odd step: wait for stage s+1 (stage s+2 may fly), free stage s's slot,
+    // read step 2s+2, DMA stage s+3 into stage s's slot.
     int s = 0;
     for (; s + 3 < nks; ++s) {
         const int s1 = wrap3(sl + 1);
-        // even step: promote block s-1 while starting block s; read step 2s+1
         mma_step_b<FA, FB, true, false>(part, acc, sc, f0, f1, ptr(sl), ptr(sl) + kBSlotA, 1, wm, wn, NoDma{}, 0);
         block_scales(s, sl);
-        // odd step: wait for stage s+1 (stage s+2 may fly), free stage s's slot,
-        // read step 2s+2, DMA stage s+3 into stage s's slot
         const BlockStageDma d = stage_dma(s + 3, sl);
         mma_step_b<FA, FB, false, true>(part, acc, sc, f1, f0, ptr(s1), ptr(s1) + kBSlotA, 0, wm, wn, d, 1);
         sl = s1;
     }
+    // the last stages: no DMA left, and the wait shrinks as they run out (the
+    // last stage's odd step reads a stale slot into registers never used)
     for (; s < nks; ++s) {
         const int s1 = wrap3(sl + 1);
         mma_step_b<FA, FB, true, false>(part, acc, sc, f0, f1, ptr(sl), ptr(sl) + kBSlotA, 1, wm, wn, NoDma{}, 0);
         block_scales(s, sl);
-        // (the last stage's odd step reads a stale slot into registers that
-        // are never used)
         mma_step_b<FA, FB, false, true>(part, acc, sc, f1, f0, ptr(s1), ptr(s1) + kBSlotA, 0, wm, wn, NoDma{},
                                         s + 2 < nks ? 1 : 0);
         sl = s1;
@@ -1258,66 +902,95 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bp(GemmParams p) {
 }
 
 // ---------------------------------------------------------------- host side --
-template <int BM, int BN, int FA, int FB, bool OUT_BF16, bool BLOCK>
-hipError_t launch_tile(const GemmArgs& a) {
-    constexpr size_t smem = gemm_lds_bytes<BM, BN, OUT_BF16, BLOCK>();
-    static_assert(smem <= 160 * 1024, "LDS budget of one CU");
-    static_assert(BLOCK || (BM == 256 && BN == 256), "the scaled GEMM runs 256 x 256 tiles");
-    static_assert(BLOCK || (size_t)5 * kSlot2 <= smem, "ring of the scaled GEMM");
-    static_assert(!BLOCK || (BM == 256 && BN == 128 && (size_t)kBRing <= smem), "ring of the block-scaled GEMM");
-    // the scaled GEMM: 128-byte K stages; the block-scaled GEMM: 64-byte stages
-    void (*kern)(GemmParams);
-    if constexpr (BLOCK) kern = k_gemm_bp<FA, FB, OUT_BF16>;
-    else kern = (a.K % kBK2 == 0) ? k_gemm_p<FA, FB, OUT_BF16, false> : k_gemm_p<FA, FB, OUT_BF16, true>;
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    });
-    if (attr_err != hipSuccess) return attr_err;
+// Dynamic LDS of each kernel: its ring, or the epilogue staging if larger.
+template <bool OUT_BF16>
+constexpr size_t lds_scaled() { return (size_t)5 * kSlot2; }          // the epilogue uses one slot
+template <bool OUT_BF16>
+constexpr size_t lds_256x128() {
+    return (size_t)kBRing > (size_t)Epi<256, 128, OUT_BF16>::kBytes ? (size_t)kBRing
+                                                                    : (size_t)Epi<256, 128, OUT_BF16>::kBytes;
+}
+static_assert(lds_scaled<true>() <= 160 * 1024 && lds_256x128<false>() <= 160 * 1024, "LDS budget of one CU");
+
+template <typename KERN>
+hipError_t set_lds(KERN kern, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+GemmParams make_params(const GemmArgs& a, int bm, int bn) {
     GemmParams p;
     p.A = a.A; p.B = a.B; p.lda = a.lda; p.ldb = a.ldb;
     p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K;
     p.sa = a.sa; p.sb = a.sb; p.sa_row = a.sa_per_row; p.sb_row = a.sb_per_row;
     p.C = a.C; p.ldc = a.ldc;
-    p.tiles_m = (int)((a.M + BM - 1) / BM);
-    p.tiles_n = (int)((a.N + BN - 1) / BN);
+    p.tiles_m = (int)((a.M + bm - 1) / bm);
+    p.tiles_n = (int)((a.N + bn - 1) / bn);
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     const int esz = a.out_bf16 ? 2 : 4;
     p.vec_out = ((a.ldc * esz) % 16 == 0) && ((uintptr_t)a.C % 16 == 0);   // 16-byte row chunks
+    return p;
+}
+
+// Scaled GEMM: 256 x 256 tiles, on a persistent grid of one block per CU
+// when there are more tiles than CUs and K has at least three stages.
+// (Measured: a last round left half full costs about half a round, since
+// the busy CUs then run faster; splitting it into half-width tiles does not
+// pay.)
+template <int FA, int FB, bool OUT_BF16>
+hipError_t launch_scaled_typed(const GemmArgs& a) {
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [&] {
+        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false>, lds_scaled<OUT_BF16>());
+        if (attr_err == hipSuccess) attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true>, lds_scaled<OUT_BF16>());
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    const GemmParams p = make_params(a, 256, 256);
     unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    // the persistent scaled GEMM runs one block per CU when there are more
-    // tiles than CUs and K has at least three 128-byte stages
-    if (!BLOCK && grid > (unsigned)a.num_cus && a.K > 2 * kBK2) grid = (unsigned)a.num_cus;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), smem, a.stream, p);
+    if (grid > (unsigned)a.num_cus && a.K > 2 * kBK2) grid = (unsigned)a.num_cus;
+    if (grid == 0) return hipSuccess;
+    if (a.K % kBK2 != 0)
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true>), dim3(grid), dim3(kGemmThreads), lds_scaled<OUT_BF16>(),
+                           a.stream, p);
+    else
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false>), dim3(grid), dim3(kGemmThreads), lds_scaled<OUT_BF16>(),
+                           a.stream, p);
     return hipGetLastError();
 }
 
-template <int BM, int BN, bool BLOCK>
-hipError_t dispatch_formats(const GemmArgs& a) {
-#define FP8MI_FMT_CASE(FA, FB)                                                  \
-    if (a.fa == FA && a.fb == FB)                                               \
-        return a.out_bf16 ? launch_tile<BM, BN, FA, FB, true, BLOCK>(a)        \
-                          : launch_tile<BM, BN, FA, FB, false, BLOCK>(a);
-    FP8MI_FMT_CASE(0, 0)
-    if constexpr (!BLOCK) {
-        FP8MI_FMT_CASE(1, 0)
-        FP8MI_FMT_CASE(0, 1)
-        FP8MI_FMT_CASE(1, 1)
-    }
-#undef FP8MI_FMT_CASE
-    return hipErrorInvalidValue;
+// Block-scaled GEMM (E4M3 x E4M3): 256 x 128 tiles, one block each.
+template <bool OUT_BF16>
+hipError_t launch_block_typed(const GemmArgs& a) {
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [&] { attr_err = set_lds(k_gemm_bp<0, 0, OUT_BF16>, lds_256x128<OUT_BF16>()); });
+    if (attr_err != hipSuccess) return attr_err;
+    const GemmParams p = make_params(a, 256, 128);
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    if (grid > 0)
+        hipLaunchKernelGGL((k_gemm_bp<0, 0, OUT_BF16>), dim3(grid), dim3(kGemmThreads),
+                           lds_256x128<OUT_BF16>(), a.stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_scaled_gemm(const GemmArgs& a) {
-    return dispatch_formats<256, 256, false>(a);
+#define FP8MI_FMT_CASE(FA, FB)                                                              \
+    if (a.fa == FA && a.fb == FB)                                                           \
+        return a.out_bf16 ? launch_scaled_typed<FA, FB, true>(a) : launch_scaled_typed<FA, FB, false>(a);
+    FP8MI_FMT_CASE(0, 0)
+    FP8MI_FMT_CASE(1, 0)
+    FP8MI_FMT_CASE(0, 1)
+    FP8MI_FMT_CASE(1, 1)
+#undef FP8MI_FMT_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_blockscaled_gemm(const GemmArgs& a) {
-    return dispatch_formats<256, 128, true>(a);
+    if (a.fa != 0 || a.fb != 0) return hipErrorInvalidValue;
+    return a.out_bf16 ? launch_block_typed<true>(a) : launch_block_typed<false>(a);
 }
 
 }  // namespace fp8mi

@@ -143,6 +143,43 @@ def test_gemm_deterministic():
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("per_row", [False, True])
+def test_gemm_persistent_ragged(out, per_row):
+    """More tiles than CUs (the persistent path) with M, N and K all ragged
+    (K % 128 != 0), realistic operands; sampled outputs against the oracle."""
+    rng = np.random.default_rng(21 + per_row)
+    M, N, K = 4100, 9000, 1040
+    A, B, sa, sb = _realistic_operands(rng, M, N, K, 0, 0, per_row)
+    say("persistent ragged gemm", M, N, K, out, "per_row" if per_row else "tensor")
+    y = host(_run_gemm(A, 0, B, 0, sa, sb, torch.float32 if out == "f32" else torch.bfloat16))
+    ms = np.concatenate([[0, M - 1, M - 1, 0], rng.integers(0, M, 2000), np.arange(4096, M)])
+    ns = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, 2000), rng.integers(8960, N, M - 4096)])
+    y32, pp = oracle.gemm_sampled(A, 0, B, 0, sa, sb, ms, ns)
+    print(assert_gemm(y[ms, ns], y32, pp, K, out, what="persistent ragged",
+                      exact=exact_checker(A, 0, B, 0, sa, sb, ms, ns)))
+
+
+def test_gemm_column_ranges_bitwise():
+    """The persistent grid (more tiles than CUs) and the one-tile-per-block
+    grid must give every output element bit-identically: the full product
+    against separate calls on two column ranges (each element sums the same
+    MFMA sequence whichever block computes it)."""
+    rng = np.random.default_rng(22)
+    M, N, K = 4096, 14336, 1024              # 16 x 56 tiles: three rounds + 128 tiles
+    A = random_codes(rng, (M, K), 0)
+    B = random_codes(rng, (N, K), 0)
+    a, b = dev_u8(A), dev_u8(B)
+    s = dev_f32(np.float32([0.25]))
+    say("column split bitwise")
+    y = fp8.scaled_gemm(a, b, s, s, out_dtype=torch.float32)
+    y_head = fp8.scaled_gemm(a, b[:12288], s, s, out_dtype=torch.float32)
+    y_tail = fp8.scaled_gemm(a, b[12288:], s, s, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :12288], y_head)
+    assert torch.equal(y[:, 12288:], y_tail)
+
+
 def test_gemm_strided_operands_and_output():
     rng = np.random.default_rng(6)
     M, N, K = 100, 130, 160
