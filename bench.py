@@ -33,7 +33,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 # 2.0 + WRITE_SIZE x 1.0 per dispatch (factors from a plain 512 MiB copy, see
 # profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None whenever k_gemm changes
 # until the counters are taken again.
-GEMM_TRAFFIC_BYTES = None
+GEMM_TRAFFIC_BYTES = 476156704
 
 WORKLOADS = {
     "tiny": "tiny: X, W [256 x 256] fp32 N(0,1); per-tensor E4M3; Y fp32",
