@@ -98,11 +98,18 @@ class AmaxHistory:
         _lib.check(_lib.lib().fp8_history_init(self.buf.data_ptr(), self.length, _stream(dev)),
                    "fp8_history_init")
 
+    def set_guard(self, threshold: float):
+        """Spike threshold for quantize(..., spike_guard=True); <= 0 is off."""
+        dev = self.buf.device
+        _lib.check(_lib.lib().fp8_history_set_guard(self.buf.data_ptr(), float(threshold), _stream(dev)),
+                   "fp8_history_set_guard")
+
     def state(self) -> dict:
         w = self.buf.cpu()
         f = w.view(torch.float32)
         return {"amax": f[:16].clone(), "len": int(w[16]), "pos": int(w[17]), "count": int(w[18]),
-                "scale": float(f[21]), "scale_inv": float(f[22]), "steps": int(w[23])}
+                "scale": float(f[21]), "scale_inv": float(f[22]), "steps": int(w[23]),
+                "spike_threshold": float(f[24]), "spikes": int(w[25]), "last_spiked": int(w[19])}
 
     def save(self) -> torch.Tensor:
         return self.buf.clone()
@@ -125,6 +132,7 @@ class QuantResult:
 def quantize(x: torch.Tensor, fmt="e4m3", granularity="tensor", pow2: bool = False,
              history: Optional[AmaxHistory] = None, transpose: bool = False,
              diag: Optional[Diag] = None, out: Optional[torch.Tensor] = None,
+             spike_guard: bool = False,
              scale_inv_out: Optional[torch.Tensor] = None,
              amax_out: Optional[torch.Tensor] = None) -> QuantResult:
     rows, cols, ld = _matrix(x, "x")
@@ -144,7 +152,8 @@ def quantize(x: torch.Tensor, fmt="e4m3", granularity="tensor", pow2: bool = Fal
         scale_inv_out = torch.empty(grid, dtype=torch.float32, device=dev)
     if amax_out is None:
         amax_out = torch.empty(grid, dtype=torch.float32, device=dev)
-    flags = (_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_TRANSPOSE_OUT if transpose else 0)
+    flags = ((_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_TRANSPOSE_OUT if transpose else 0)
+             | (_lib.FP8_SPIKE_GUARD if spike_guard else 0))
     st = _lib.lib().fp8_quantize(
         x.data_ptr(), in_dt, rows, cols, ld, _fmt(fmt), _gran(granularity), flags,
         _ptr(history.buf) if history is not None else None, out.data_ptr(), ldq,

@@ -27,6 +27,7 @@ FP8_OUT_F32, FP8_OUT_BF16 = 0, 1
 FP8_GRAN_TENSOR, FP8_GRAN_ROW, FP8_GRAN_BLOCK_1x128, FP8_GRAN_BLOCK_128x128 = 0, 1, 2, 3
 FP8_SCALE_POW2 = 1
 FP8_TRANSPOSE_OUT = 2
+FP8_SPIKE_GUARD = 4
 HISTORY_BYTES = 128
 DIAG_BYTES = 16
 
@@ -42,6 +43,7 @@ SIGNATURES = {
     "fp8_status_string": (ctypes.c_char_p, [_INT]),
     "fp8_last_error": (ctypes.c_char_p, []),
     "fp8_history_init": (_INT, [_P, _I32, _P]),
+    "fp8_history_set_guard": (_INT, [_P, ctypes.c_float, _P]),
     "fp8_amax": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P]),
     "fp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U32, _P, _P, _I64, _P, _P, _P, _P]),
     "fp8_scaled_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,

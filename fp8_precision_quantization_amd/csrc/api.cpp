@@ -95,6 +95,13 @@ fp8_status get_scratch(hipStream_t stream, uint32_t** out) {
     void* p = nullptr;
     e = hipMalloc(&p, sizeof(uint32_t) * fp8mi::kScratchWords);
     if (e != hipSuccess) return fail(FP8_ERR_HIP, "scratch allocation failed: %s", hipGetErrorString(e));
+    // zeroed once, in stream order (a kernel, not a memset node): the
+    // guarded delayed cast relies on its diagnostic words starting at zero
+    e = fp8mi::launch_zero_words(static_cast<uint32_t*>(p), fp8mi::kScratchWords, stream);
+    if (e != hipSuccess) {
+        hipFree(p);
+        return fail(FP8_ERR_HIP, "scratch initialization failed: %s", hipGetErrorString(e));
+    }
     g_scratch[key] = static_cast<uint32_t*>(p);
     *out = static_cast<uint32_t*>(p);
     return FP8_OK;
@@ -168,6 +175,16 @@ fp8_status fp8_history_init(fp8_amax_history* hist, int32_t len, void* stream) {
     return launch_result(fp8mi::launch_history_init(hist, len, (hipStream_t)stream), "fp8_history_init");
 }
 
+fp8_status fp8_history_set_guard(fp8_amax_history* hist, float threshold, void* stream) {
+    if (hist == nullptr) return fail(FP8_ERR_INVALID_ARG, "hist is NULL");
+    if (!is_aligned(hist, 16)) return fail(FP8_ERR_MISALIGNED, "hist must be 16-byte aligned");
+    int cus = 0;
+    fp8_status st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    return launch_result(fp8mi::launch_history_set_guard(hist, threshold, (hipStream_t)stream),
+                         "fp8_history_set_guard");
+}
+
 fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
                     fp8_granularity gran, float* amax_out, void* stream) {
     fp8_status st = check_matrix_in(x, in_dtype, rows, cols, ld);
@@ -198,8 +215,10 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
     if (fmt != FP8_E4M3 && fmt != FP8_E5M2)
         return fail(FP8_ERR_INVALID_ARG, "format %d is not FP8_E4M3 or FP8_E5M2", (int)fmt);
     if (!valid_gran(gran)) return fail(FP8_ERR_INVALID_ARG, "granularity %d is not a fp8_granularity", (int)gran);
-    if (flags & ~(FP8_SCALE_POW2 | FP8_TRANSPOSE_OUT))
-        return fail(FP8_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~(FP8_SCALE_POW2 | FP8_TRANSPOSE_OUT));
+    const uint32_t known = FP8_SCALE_POW2 | FP8_TRANSPOSE_OUT | FP8_SPIKE_GUARD;
+    if (flags & ~known) return fail(FP8_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~known);
+    if ((flags & FP8_SPIKE_GUARD) && hist == nullptr)
+        return fail(FP8_ERR_INVALID_ARG, "FP8_SPIKE_GUARD needs delayed scaling (hist != NULL)");
     const bool transpose = (flags & FP8_TRANSPOSE_OUT) != 0;
     if (transpose && gran != FP8_GRAN_TENSOR)
         return fail(FP8_ERR_INVALID_ARG, "FP8_TRANSPOSE_OUT needs FP8_GRAN_TENSOR");
@@ -227,7 +246,8 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
     a.scratch = scratch;
     a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
     a.fmt = fmt; a.gran = gran; a.pow2 = (flags & FP8_SCALE_POW2) != 0; a.transpose = transpose;
-    a.write_q = true; a.hist = hist; a.q = q; a.ldq = ldq; a.scale_inv = scale_inv_out;
+    a.write_q = true; a.hist = hist; a.guard = (flags & FP8_SPIKE_GUARD) != 0; a.q = q; a.ldq = ldq;
+    a.scale_inv = scale_inv_out;
     a.amax = amax_out; a.diag = diag; a.stream = (hipStream_t)stream; a.num_cus = cus;
     return launch_result(fp8mi::launch_quantize(a), "fp8_quantize");
 }

@@ -18,6 +18,7 @@ struct QuantArgs {
     bool pow2 = false;
     bool transpose = false;
     bool write_q = true;         // false: amax only (fp8_amax)
+    bool guard = false;          // FP8_SPIKE_GUARD (delayed only)
     fp8_amax_history* hist = nullptr;
     uint8_t* q = nullptr;
     int64_t ldq = 0;
@@ -47,6 +48,8 @@ struct GemmArgs {
 
 hipError_t launch_quantize(const QuantArgs& a);
 hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream);
+hipError_t launch_history_set_guard(fp8_amax_history* h, float threshold, hipStream_t stream);
+hipError_t launch_zero_words(uint32_t* w, int n, hipStream_t stream);
 hipError_t launch_scaled_gemm(const GemmArgs& a);
 hipError_t launch_blockscaled_gemm(const GemmArgs& a);
 

@@ -233,6 +233,11 @@ __device__ __forceinline__ float delayed_scale(const fp8_amax_history* h, const 
 }
 
 // ------------------------------------------------------------------ kernels --
+// Per-tensor cast modes: just in time (scale from this call's amax pass),
+// delayed (scale from the history), and the spike guard's re-cast (scale
+// recorded by the finish kernel; does nothing unless that kernel saw a spike).
+constexpr int kModeJit = 0, kModeDelayed = 1, kModeRecast = 2;
+
 __global__ void k_history_init(fp8_amax_history* h, int32_t len) {
     uint32_t* w = reinterpret_cast<uint32_t*>(h);
     const int i = threadIdx.x;
@@ -284,12 +289,27 @@ __global__ __launch_bounds__(kThreads) void k_reduce_amax(const uint32_t* __rest
     if (threadIdx.x == 0) amax_out[0] = __uint_as_float(m);
 }
 
+__global__ void k_history_set_guard(fp8_amax_history* h, float threshold) {
+    if (threadIdx.x == 0) h->spike_threshold = threshold;
+}
+
+__global__ void k_zero_words(uint32_t* w, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
+}
+
 // After a delayed cast: combine the cast blocks' partials into this step's
 // amax, push it into the ring and precompute the next scale (one block).
-template <int FMT>
+// GUARD ([DeepL bets on FP8] 2.3, recovery from a distribution jump): when
+// this amax exceeds spike_threshold x the window max (fp32 product; only with
+// a non-empty window and a positive threshold), record the just-in-time
+// scale for the re-cast kernel and give scale_inv_out its inverse.  The
+// first cast counted its diagnostics into `diag_tmp`; they reach `diag` only
+// when that cast stands.
+template <int FMT, bool GUARD>
 __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h,
                                                              const uint32_t* __restrict__ partials, int n,
-                                                             bool pow2, float* amax_out) {
+                                                             bool pow2, float* amax_out, float* scale_inv_out,
+                                                             fp8_diag* diag, fp8_diag* diag_tmp) {
     __shared__ uint32_t lds[16];
     const uint32_t cur = reduce_partials(partials, n, lds);
     if (threadIdx.x != 0) return;
@@ -299,6 +319,30 @@ __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h
     len = len < 1 ? 1 : (len > 16 ? 16 : len);
     int32_t pos = h->pos;
     pos = (pos < 0 || pos >= len) ? 0 : pos;
+    if constexpr (GUARD) {
+        const int32_t count0 = h->count < 0 ? 0 : (h->count > len ? len : h->count);
+        uint32_t wbits = 0;
+        for (int i = 0; i < count0; ++i) wbits = max(wbits, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
+        const float thr = h->spike_threshold;
+        const bool spiked = count0 > 0 && thr > 0.0f && amax_now > thr * __uint_as_float(wbits);
+        h->internal[0] = spiked ? 1u : 0u;
+        if (spiked) {
+            const float sj = scale_from_amax_bits<FMT>(cur, pow2);
+            h->internal[1] = __float_as_uint(sj);
+            scale_inv_out[0] = recip_rn(sj);
+            h->spikes = h->spikes + 1u;
+        }
+        if (diag_tmp != nullptr) {
+            if (!spiked && diag != nullptr) {
+                diag->sat_count += diag_tmp->sat_count;
+                diag->nonfinite_count += diag_tmp->nonfinite_count;
+                diag->underflow_count += diag_tmp->underflow_count;
+            }
+            diag_tmp->sat_count = 0u;
+            diag_tmp->nonfinite_count = 0u;
+            diag_tmp->underflow_count = 0u;
+        }
+    }
     h->amax[pos] = amax_now;
     h->pos = (pos + 1) % len;
     const int32_t count = h->count < len ? h->count + 1 : len;
@@ -314,23 +358,27 @@ __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h
 // Per-tensor cast.  JIT: s from the amax partials of pass 1 (block 0 also
 // writes amax_out).  DELAYED: s from the history (or the bootstrap partials
 // while it is empty); each block stores its own amax partial for the finish
-// kernel.
-template <typename InT, int FMT, bool DELAYED, bool DIAG>
+// kernel.  RECAST: s recorded by a guarded finish kernel, or nothing to do.
+template <typename InT, int FMT, int MODE, bool DIAG>
 __global__ __launch_bounds__(kThreads) void k_cast_tensor(
     const InT* __restrict__ x, UnitGeom g, bool vec_in, uint8_t* __restrict__ q, bool vec_out,
     const uint32_t* __restrict__ partials_in, int n_in, const fp8_amax_history* hist, bool pow2,
     float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag,
     uint32_t* __restrict__ partials_out) {
     __shared__ uint32_t lds[16];
+    constexpr bool DELAYED = MODE == kModeDelayed;
     float s;
-    if constexpr (DELAYED) {
+    if constexpr (MODE == kModeRecast) {
+        if (hist->internal[0] == 0u) return;
+        s = __uint_as_float(hist->internal[1]);
+    } else if constexpr (DELAYED) {
         s = delayed_scale<FMT>(hist, partials_in, n_in, pow2, lds);
     } else {
         const uint32_t am = reduce_partials(partials_in, n_in, lds);
         s = scale_from_amax_bits<FMT>(am, pow2);
         if (blockIdx.x == 0 && threadIdx.x == 0) amax_out[0] = __uint_as_float(am);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
+    if (MODE != kModeRecast && blockIdx.x == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
 
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t m = 0;
@@ -370,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
 // swizzle so that both the row-wise writes and the column gathers are
 // conflict free, and each output row segment leaves as 16-byte stores
 // (128 B per 8 lanes).
-template <typename InT, int FMT, bool DELAYED, bool DIAG>
+template <typename InT, int FMT, int MODE, bool DIAG>
 __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
     const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
     uint8_t* __restrict__ q, int64_t ldq, bool vec_out16, const uint32_t* __restrict__ partials_in,
@@ -378,15 +426,19 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
     float* __restrict__ amax_out, fp8_diag* diag, uint32_t* __restrict__ partials_out) {
     __shared__ uint32_t lds[16];
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 128];
+    constexpr bool DELAYED = MODE == kModeDelayed;
     float s;
-    if constexpr (DELAYED) {
+    if constexpr (MODE == kModeRecast) {
+        if (hist->internal[0] == 0u) return;
+        s = __uint_as_float(hist->internal[1]);
+    } else if constexpr (DELAYED) {
         s = delayed_scale<FMT>(hist, partials_in, n_in, pow2, lds);
     } else {
         const uint32_t am = reduce_partials(partials_in, n_in, lds);
         s = scale_from_amax_bits<FMT>(am, pow2);
         if (blockIdx.x == 0 && threadIdx.x == 0) amax_out[0] = __uint_as_float(am);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
+    if (MODE != kModeRecast && blockIdx.x == 0 && threadIdx.x == 0) scale_inv_out[0] = recip_rn(s);
 
     const int t = threadIdx.x;
     const int cu = t & 15, rr = t >> 4;
@@ -634,9 +686,11 @@ inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0
 // Scratch layout (uint32 words of the per-stream scratch, kScratchWords).
 constexpr int kScratchCastPartials = 0;      // <= kMaxCastBlocks partials of a delayed cast
 constexpr int kScratchAmaxPartials = 4096;   // <= kMaxAmaxBlocks partials of pass 1
+constexpr int kScratchDiag = 8192;           // fp8_diag of a guarded delayed cast (zero between calls)
 constexpr int64_t kMaxCastBlocks = 4096;
 constexpr int64_t kMaxAmaxBlocks = 1024;   // a stream needs about 4 workgroups per CU (measured)
-static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchWords, "scratch too small");
+static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchDiag, "scratch layout");
+static_assert(kScratchDiag + 4 <= kScratchWords, "scratch too small");
 
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
     int64_t b = (work_items + per_block - 1) / per_block;
@@ -694,29 +748,41 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
                                (int)agrid, a.amax);
             return hipGetLastError();
         }
-#define FP8MI_TENSOR_CAST(DEL, DG)                                                                        \
+#define FP8MI_TENSOR_CAST(MODE, DG, DIAGP)                                                                  \
     do {                                                                                                  \
         if (a.transpose)                                                                                  \
-            hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, DEL, DG>), dim3(tgrid), dim3(kThreads), 0, st, x,  \
+            hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, MODE, DG>), dim3(tgrid), dim3(kThreads), 0, st, x,    \
                                a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16,                             \
                                (const uint32_t*)amax_partials, (int)agrid,                                \
-                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, a.diag,      \
+                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
                                cast_partials);                                                            \
         else                                                                                              \
-            hipLaunchKernelGGL((k_cast_tensor<InT, FMT, DEL, DG>), dim3(cgrid), dim3(kThreads), 0, st, x, g, \
+            hipLaunchKernelGGL((k_cast_tensor<InT, FMT, MODE, DG>), dim3(cgrid), dim3(kThreads), 0, st, x, g,   \
                                vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,          \
-                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, a.diag,      \
+                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
                                cast_partials);                                                            \
     } while (0)
         if (delayed) {
-            if (diag) FP8MI_TENSOR_CAST(true, true);
-            else FP8MI_TENSOR_CAST(true, false);
+            // with the guard, the first cast's diagnostics wait in scratch
+            fp8_diag* diag_tmp = a.guard ? reinterpret_cast<fp8_diag*>(a.scratch + kScratchDiag) : nullptr;
+            fp8_diag* d1 = a.guard ? diag_tmp : a.diag;
+            if (diag) FP8MI_TENSOR_CAST(kModeDelayed, true, d1);
+            else FP8MI_TENSOR_CAST(kModeDelayed, false, d1);
             const int nparts = (int)(a.transpose ? tgrid : cgrid);
-            hipLaunchKernelGGL(k_delayed_finish<FMT>, dim3(1), dim3(kThreads), 0, st, a.hist,
-                               (const uint32_t*)cast_partials, nparts, a.pow2, a.amax);
+            if (a.guard) {
+                hipLaunchKernelGGL((k_delayed_finish<FMT, true>), dim3(1), dim3(kThreads), 0, st, a.hist,
+                                   (const uint32_t*)cast_partials, nparts, a.pow2, a.amax, a.scale_inv, a.diag,
+                                   diag ? diag_tmp : nullptr);
+                if (diag) FP8MI_TENSOR_CAST(kModeRecast, true, a.diag);
+                else FP8MI_TENSOR_CAST(kModeRecast, false, a.diag);
+            } else {
+                hipLaunchKernelGGL((k_delayed_finish<FMT, false>), dim3(1), dim3(kThreads), 0, st, a.hist,
+                                   (const uint32_t*)cast_partials, nparts, a.pow2, a.amax, a.scale_inv, a.diag,
+                                   (fp8_diag*)nullptr);
+            }
         } else {
-            if (diag) FP8MI_TENSOR_CAST(false, true);
-            else FP8MI_TENSOR_CAST(false, false);
+            if (diag) FP8MI_TENSOR_CAST(kModeJit, true, a.diag);
+            else FP8MI_TENSOR_CAST(kModeJit, false, a.diag);
         }
 #undef FP8MI_TENSOR_CAST
         return hipGetLastError();
@@ -768,6 +834,16 @@ hipError_t launch_quantize(const QuantArgs& a) {
 
 hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream) {
     hipLaunchKernelGGL(k_history_init, dim3(1), dim3(64), 0, stream, h, len);
+    return hipGetLastError();
+}
+
+hipError_t launch_history_set_guard(fp8_amax_history* h, float threshold, hipStream_t stream) {
+    hipLaunchKernelGGL(k_history_set_guard, dim3(1), dim3(64), 0, stream, h, threshold);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_words(uint32_t* w, int n, hipStream_t stream) {
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, stream, w, n);
     return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP8MI_ABI_VERSION 1
+#define FP8MI_ABI_VERSION 2
 
 typedef enum {
     FP8_OK = 0,
@@ -90,6 +90,15 @@ typedef enum {
 /* Write q transposed: q is [cols x rows] with leading dimension ldq >= rows.
  * Only with FP8_GRAN_TENSOR (the wgrad operands X^T and dY^T). */
 #define FP8_TRANSPOSE_OUT 2u
+/* Spike guard for delayed scaling ([DeepL] 2.3: the delayed scale lags a
+ * sudden change of the distribution; compare the current statistic with the
+ * history and recompute the scale past a threshold).  Needs hist.  When this
+ * step's amax exceeds hist->spike_threshold x the window max (an fp32
+ * product; never with an empty window or a threshold <= 0), the tensor is
+ * cast again just in time, with s = fmax / amax (FP8_SCALE_POW2 applies),
+ * scale_inv_out holds that scale's inverse, diag counts that cast only and
+ * hist->spikes grows by one.  The ring is updated as without the guard. */
+#define FP8_SPIKE_GUARD 4u
 
 /* Data-dependent conditions are counted on the device, never returned as a
  * status ([DeepL] 4.2 and 6.2: watch max-abs, scale and overflow).  Device
@@ -118,11 +127,13 @@ typedef struct fp8_amax_history {
     int32_t len;            /* window length, 1..16 */
     int32_t pos;            /* next slot to write */
     int32_t count;          /* valid entries, 0..len */
-    uint32_t internal[2];   /* reserved, zero */
+    uint32_t internal[2];   /* last guarded call: 1 if it cast again, and that scale's bits */
     float scale;            /* scale the next call will use (count > 0) */
     float scale_inv;
     uint32_t steps;         /* calls completed */
-    uint32_t reserved[8];
+    float spike_threshold;  /* FP8_SPIKE_GUARD threshold, 0 after fp8_history_init (off) */
+    uint32_t spikes;        /* guarded calls that cast again */
+    uint32_t reserved[6];
 } fp8_amax_history;
 
 /* Library version of this header (FP8MI_ABI_VERSION). */
@@ -137,6 +148,10 @@ const char* fp8_last_error(void);
 
 /* Zero a history and set its window length (1..16) on `stream`. */
 fp8_status fp8_history_init(fp8_amax_history* hist, int32_t len, void* stream);
+
+/* Set the spike threshold of a history on `stream` (see FP8_SPIKE_GUARD;
+ * the pages give no value: a ratio such as 10 is the caller's choice). */
+fp8_status fp8_history_set_guard(fp8_amax_history* hist, float threshold, void* stream);
 
 /* amax = max |x| per group ([DeepL] 4.2: the per-layer maximum absolute value
  * behind the scale).  x: [rows x cols], element type in_dtype, leading

@@ -73,7 +73,7 @@ def lib():
         L.or_ring_init.argtypes = [P, ctypes.c_int32]
         L.or_ring_window_max.restype = f32
         L.or_ring_window_max.argtypes = [P]
-        L.or_delayed_step.argtypes = [P, P, i32, i64, i64, i64, i32, P, i64, P, P]
+        L.or_delayed_step.argtypes = [P, P, i32, i64, i64, i64, i32, P, i64, f32, P, P]
         L.or_gemm_sampled.argtypes = [P, i32, i64, P, i32, i64, i64, P, i32, P, i32, P, P, i64, P, P]
         L.or_gemm.argtypes = [P, i32, i64, P, i32, i64, i64, i64, i64, P, i32, P, i32, P, i64, P, i64]
         L.or_blockgemm_sampled.argtypes = [P, i64, P, i64, i64, P, P, P, P, i64, P, P]
@@ -201,11 +201,13 @@ class _Ring(ctypes.Structure):
 
 
 class DelayedScaler:
-    """Amax-history ring for one tensor (see or_delayed_step in the C source)."""
+    """Amax-history ring for one tensor (see or_delayed_step in the C source).
+    spike_threshold > 0 enables the spike guard of or_delayed_step."""
 
-    def __init__(self, fmt, length: int = 16):
+    def __init__(self, fmt, length: int = 16, spike_threshold: float = 0.0):
         assert 1 <= length <= 16
         self.fmt = fmt_code(fmt)
+        self.spike_threshold = float(spike_threshold)
         self.ring = _Ring()
         lib().or_ring_init(ctypes.byref(self.ring), length)
 
@@ -219,9 +221,9 @@ class DelayedScaler:
         out4 = np.zeros(4, dtype=np.float32)
         counts = np.zeros(3, dtype=np.int64)
         lib().or_delayed_step(ctypes.byref(self.ring), _p(x), dt, rows, cols, cols, self.fmt,
-                              _p(q), cols, _p(out4), _p(counts))
+                              _p(q), cols, ctypes.c_float(self.spike_threshold), _p(out4), _p(counts))
         return {"q": q, "scale": out4[0], "scale_inv": out4[1], "amax": out4[2],
-                "sat": int(counts[0]), "nonfinite": int(counts[1]),
+                "spiked": bool(out4[3]), "sat": int(counts[0]), "nonfinite": int(counts[1]),
                 "underflow": int(counts[2])}
 
     def state(self):

@@ -271,20 +271,36 @@ float or_ring_window_max(const or_ring* r) {
     return u2f(best);
 }
 
-/* One delayed step on a whole tensor.  out4 = {s, s_inv, amax, unused}. */
+/* One delayed step on a whole tensor.  out4 = {s, s_inv, amax, spiked}.
+ * [DeepL] 2.3 also describes the recovery from a sudden change of the
+ * distribution that delayed scaling lags behind: compare the current
+ * statistic with the history and recompute the scaling factor past a
+ * threshold.  READING: the statistic is this step's amax, the history's is
+ * the window max, "past a threshold" is amax > threshold * window_max (an
+ * fp32 product), and the recomputed factor is the just-in-time scale of
+ * this step's amax; the ring is updated as without the guard.  A threshold
+ * <= 0 (the default) or an empty window never triggers. */
 void or_delayed_step(or_ring* r, const void* x, int in_dtype, int64_t rows, int64_t cols,
-                     int64_t ld, int fmt, uint8_t* q, int64_t ldq, float* out4,
-                     int64_t* counts3) {
+                     int64_t ld, int fmt, uint8_t* q, int64_t ldq, float spike_threshold,
+                     float* out4, int64_t* counts3) {
     float amax_now;
     or_amax(x, in_dtype, rows, cols, ld, OR_GRAN_TENSOR, &amax_now);
     float basis = (r->count == 0) ? amax_now : or_ring_window_max(r);
+    int spiked = 0;
+    if (r->count > 0 && spike_threshold > 0.0f) {
+        float limit = spike_threshold * or_ring_window_max(r);
+        if (amax_now > limit) {
+            spiked = 1;
+            basis = amax_now;
+        }
+    }
     float s, s_inv;
     or_scale(basis, fmt, 0, &s, &s_inv);
     or_quantize_with_scales(x, in_dtype, rows, cols, ld, OR_GRAN_TENSOR, fmt, &s, q, ldq, counts3);
     r->amax[r->pos] = amax_now;
     r->pos = (r->pos + 1) % r->len;
     if (r->count < r->len) r->count += 1;
-    out4[0] = s; out4[1] = s_inv; out4[2] = amax_now; out4[3] = 0.0f;
+    out4[0] = s; out4[1] = s_inv; out4[2] = amax_now; out4[3] = (float)spiked;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -36,7 +36,7 @@ def test_library_is_gfx950_only_code_object():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.fp8_abi_version() == 1
+    assert lib.fp8_abi_version() == 2
     for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARG"), (2, "FP8_ERR_UNSUPPORTED_SHAPE"),
                        (3, "FP8_ERR_MISALIGNED"), (4, "FP8_ERR_UNSUPPORTED_DEVICE"), (5, "FP8_ERR_HIP")]:
         assert L.status_name(code) == name
@@ -76,6 +76,8 @@ def q(**kw):
     (dict(hist=FAKE + 4), 3, "hist"),
     (dict(amax=FAKE + 2), 3, "aligned"),
     (dict(rows=2 ** 32), 2, "2^31"),
+    (dict(flags=4), 1, "FP8_SPIKE_GUARD"),
+    (dict(flags=16), 1, "flag"),
 ])
 def test_quantize_validation(kw, status, needle):
     st, msg = q(**kw)
@@ -127,6 +129,8 @@ def test_blockgemm_validation():
 
 def test_history_and_amax_validation():
     lib = L.lib()
+    assert lib.fp8_history_set_guard(None, 10.0, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_history_set_guard(FAKE + 4, 10.0, None) == L.FP8_ERR_MISALIGNED
     assert lib.fp8_history_init(None, 16, None) == L.FP8_ERR_INVALID_ARG
     assert lib.fp8_history_init(FAKE, 0, None) == L.FP8_ERR_INVALID_ARG
     assert lib.fp8_history_init(FAKE, 17, None) == L.FP8_ERR_INVALID_ARG
@@ -140,8 +144,10 @@ def test_history_struct_is_128_bytes():
     text = open(L.HEADER).read()
     body = text[text.index("typedef struct fp8_amax_history"):]
     body = body[:body.index("} fp8_amax_history;")]
-    words = 16 + 3 + 2 + 2 + 1 + 8   # amax, len/pos/count, internal, scale pair, steps, reserved
-    assert "float amax[16]" in body and "uint32_t internal[2]" in body and "uint32_t reserved[8]" in body
+    # amax, len/pos/count, internal, scale pair, steps, spike threshold, spikes, reserved
+    words = 16 + 3 + 2 + 2 + 1 + 1 + 1 + 6
+    assert "float amax[16]" in body and "uint32_t internal[2]" in body and "uint32_t reserved[6]" in body
+    assert "float spike_threshold" in body and "uint32_t spikes" in body
     assert words * 4 == L.HISTORY_BYTES
 
 

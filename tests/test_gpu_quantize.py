@@ -241,6 +241,42 @@ def test_delayed_ring_20_steps(transpose):
             assert o_dy.state()["count"] == 13
 
 
+@pytest.mark.parametrize("transpose", [False, True])
+@pytest.mark.parametrize("with_diag", [False, True])
+def test_delayed_spike_guard_20_steps(transpose, with_diag):
+    """The spike guard with threshold 10 on the wgrad recipe, step by step
+    against the oracle: only dY's spike step casts again just in time (codes,
+    scale_inv, saturation count of that cast), everything else and the rings
+    as without the guard; the history counts one re-cast."""
+    tokens, hidden = 512, 384
+    h_dy, h_x = fp8.AmaxHistory(16), fp8.AmaxHistory(16)
+    h_dy.set_guard(10.0)
+    h_x.set_guard(10.0)
+    o_dy = oracle.DelayedScaler(oracle.E5M2, spike_threshold=10.0)
+    o_x = oracle.DelayedScaler(oracle.E4M3, spike_threshold=10.0)
+    for t in range(20):
+        dy, x = synth.wgrad_step(t, tokens=tokens, hidden=hidden)
+        for name, data, h, o, fmt in (("dY", dy, h_dy, o_dy, "e5m2"), ("X", x, h_x, o_x, "e4m3")):
+            say("guarded step", t, name, "transpose" if transpose else "", "diag" if with_diag else "")
+            diag = fp8.Diag() if with_diag else None
+            r = fp8.quantize(dev_input(data), fmt, "tensor", history=h, transpose=transpose, diag=diag,
+                             spike_guard=True)
+            w = o.step(data)
+            assert w["spiked"] == (name == "dY" and t == 12)
+            got = host(r.q)
+            assert np.array_equal(got, w["q"].T if transpose else w["q"]), (t, name)
+            assert host(r.scale_inv)[0] == w["scale_inv"], (t, name)
+            assert host(r.amax)[0] == w["amax"], (t, name)
+            if with_diag:
+                assert diag.read()["sat"] == w["sat"], (t, name)
+            st, os_ = h.state(), o.state()
+            assert (st["count"], st["pos"]) == (os_["count"], os_["pos"])
+            assert np.array_equal(st["amax"].numpy(), os_["amax"])
+            assert st["last_spiked"] == int(w["spiked"])
+    assert h_dy.state()["spikes"] == 1 and h_x.state()["spikes"] == 0
+    assert h_dy.state()["spike_threshold"] == 10.0
+
+
 def test_delayed_save_restore():
     tokens, hidden = 256, 256
     h = fp8.AmaxHistory(16)

@@ -332,6 +332,52 @@ def test_delayed_spike_small_wgrad_run():
         assert 448.0 / 8.0 < res[t][1]["scale"] < 448.0 / 2.0
 
 
+def test_delayed_spike_guard_on_the_wgrad_run():
+    """The spike guard ([DeepL bets on FP8] 2.3, recovery from a distribution
+    jump) with threshold 10: only dY's step 12 trips it; that step equals the
+    independently pinned just-in-time cast of the same tensor (codes, scale,
+    saturation count), every other step and the final rings equal the
+    unguarded run."""
+    plain = (oracle.DelayedScaler(oracle.E5M2), oracle.DelayedScaler(oracle.E4M3))
+    guard = (oracle.DelayedScaler(oracle.E5M2, spike_threshold=10.0),
+             oracle.DelayedScaler(oracle.E4M3, spike_threshold=10.0))
+    for t in range(16):
+        dy, x = synth.wgrad_step(t, tokens=64, hidden=96, spike_step=12)
+        for k, (inp, fmt) in enumerate([(dy, oracle.E5M2), (x, oracle.E4M3)]):
+            a, g = plain[k].step(inp), guard[k].step(inp)
+            spike = (k == 0 and t == 12)
+            assert g["spiked"] == spike, (t, k)
+            assert a["spiked"] is False
+            if spike:
+                jit = oracle.quantize(inp, fmt, "tensor")
+                assert np.array_equal(g["q"], jit["q"])
+                assert g["scale_inv"] == jit["scale_inv"].ravel()[0]
+                assert g["sat"] == jit["sat"] < a["sat"]
+            else:
+                assert np.array_equal(g["q"], a["q"]) and g["scale"] == a["scale"]
+    for k in range(2):
+        assert guard[k].state()["amax"].tolist() == plain[k].state()["amax"].tolist()
+        assert guard[k].state()["count"] == plain[k].state()["count"]
+
+
+def test_delayed_spike_guard_threshold_is_strict():
+    """amax > threshold * window max trips the guard; equality, an empty
+    window and a threshold <= 0 do not."""
+    def step(scaler, m):
+        return scaler.step(np.array([[m, -0.5]], np.float32))
+    for thr, second, want in [(10.0, 10.0, False), (10.0, np.nextafter(np.float32(10), np.float32(20)), True),
+                              (0.0, 1e6, False), (-1.0, 1e6, False), (2.0, 2.5, True)]:
+        sc = oracle.DelayedScaler(oracle.E4M3, spike_threshold=thr)
+        first = step(sc, 1.0)
+        assert first["spiked"] is False                  # empty window
+        r = step(sc, np.float32(second))
+        assert r["spiked"] == want, (thr, second)
+        if want:
+            assert r["scale"] == np.float32(np.float32(448.0) / np.float32(second))
+        else:
+            assert r["scale"] == np.float32(448.0)       # from the window's amax 1.0
+
+
 # ------------------------------------------------------------------- GEMM --
 def _rand_codes(rng, shape, fmt):
     t = oracle.decode_table(fmt)
