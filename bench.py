@@ -12,7 +12,7 @@ Prints ONE JSON line.  `value` = whole-step throughput in TFLOP/s
 (2MNK / step time); the GEMM kernel's own TFLOP/s and % of the FP8 MFMA peak,
 and the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.
 
-    python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|dgrad|tiny]
 """
 from __future__ import annotations
 
@@ -45,6 +45,8 @@ WORKLOADS = {
                "N(0,0.015) 128x128 blocks, E4M3; block-scaled GEMM; Y bf16"),
     "wgrad": ("wgrad: dY [8192 x 4096] bf16 1e-3*t(3) -> E5M2, X [8192 x 4096] bf16 N(0,1) -> E4M3, "
               "delayed scaling (16-step history), transposed casts; dW = dY^T X [4096 x 4096] fp32"),
+    "dgrad": ("dgrad: dY [4096 x 14336] bf16 1e-3*t(3) -> E5M2 delayed, both layouts in one pass; "
+              "W [14336 x 4096] bf16 N(0,0.02) -> E4M3 transposed; dX = dY W [4096 x 4096] bf16"),
 }
 
 
@@ -106,6 +108,18 @@ class Step:
             xs = [x0] + [x0.clone() for _ in range(copies - 1)]
             ws = [w0] + [w0.clone() for _ in range(copies - 1)]
             self.in_bytes = 2
+        elif workload == "dgrad":
+            dy, w = synth.dgrad()
+            self.M, self.K = dy.shape            # tokens, layer outputs (the reduction)
+            self.N = w.shape[1]                  # layer inputs
+            d0, w0 = bf16(dy), bf16(w)
+            del dy, w
+            per = (d0.numel() + w0.numel()) * 2
+            copies = max(1, min(4, -(-600 * 2 ** 20 // per)))
+            xs = [d0] + [d0.clone() for _ in range(copies - 1)]
+            ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+            self.in_bytes = 2
+            self.h_dy = fp8.AmaxHistory(16)
         else:  # wgrad
             dy, x = synth.wgrad_step(0)
             self.M = self.N = dy.shape[1]
@@ -119,14 +133,20 @@ class Step:
         M, N, K = self.M, self.N, self.K
         T = torch
         # outputs, allocated once
-        if workload == "wgrad":
+        if workload == "dgrad":
+            self.xq = T.empty((M, K), dtype=T.uint8, device=dev)        # dY
+            self.xqt = T.empty((K, M), dtype=T.uint8, device=dev)       # dY^T (the wgrad operand)
+            self.wq = T.empty((N, K), dtype=T.uint8, device=dev)        # W^T
+        elif workload == "wgrad":
             self.xq = T.empty((M, K), dtype=T.uint8, device=dev)
             self.wq = T.empty((N, K), dtype=T.uint8, device=dev)
         else:
             self.xq = T.empty((M, K), dtype=T.uint8, device=dev)
             self.wq = T.empty((N, K), dtype=T.uint8, device=dev)
-        gx = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "1x128", "wgrad": "tensor"}[workload]
-        gw = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "128x128", "wgrad": "tensor"}[workload]
+        gx = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "1x128", "wgrad": "tensor",
+              "dgrad": "tensor"}[workload]
+        gw = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "128x128", "wgrad": "tensor",
+              "dgrad": "tensor"}[workload]
         self.gx, self.gw = gx, gw
         rows_x, cols_x = xs[0].shape
         rows_w, cols_w = ws[0].shape
@@ -141,7 +161,12 @@ class Step:
     def quantize(self):
         fp8, i = self.fp8, self.i
         x, w = self.xs[i % len(self.xs)], self.ws[i % len(self.ws)]
-        if self.workload == "wgrad":
+        if self.workload == "dgrad":
+            fp8.quantize_dual(x, "e5m2", history=self.h_dy, out=self.xq, out_t=self.xqt,
+                              scale_inv_out=self.sx, amax_out=self.ax)
+            fp8.quantize(w, "e4m3", "tensor", transpose=True, out=self.wq, scale_inv_out=self.sw,
+                         amax_out=self.aw)
+        elif self.workload == "wgrad":
             fp8.quantize(x, "e5m2", "tensor", history=self.h_dy, transpose=True, out=self.xq,
                          scale_inv_out=self.sx, amax_out=self.ax)
             fp8.quantize(w, "e4m3", "tensor", history=self.h_x, transpose=True, out=self.wq,
@@ -155,8 +180,8 @@ class Step:
         fp8 = self.fp8
         if self.workload == "mlp70b":
             fp8.blockscaled_gemm(self.xq, self.wq, self.sx, self.sw, out=self.y)
-        elif self.workload == "wgrad":
-            fp8.scaled_gemm(self.xq, self.wq, self.sx, self.sw, "e5m2", "e4m3", out=self.y)
+        elif self.workload in ("wgrad", "dgrad"):
+            fp8.scaled_gemm(self.xq, self.wq, self.sx.reshape(-1), self.sw.reshape(-1), "e5m2", "e4m3", out=self.y)
         else:
             fp8.scaled_gemm(self.xq, self.wq, self.sx.reshape(-1), self.sw.reshape(-1), out=self.y)
         self.i += 1
@@ -168,6 +193,9 @@ class Step:
             return e * (2 * self.in_bytes + 1)      # amax pass + cast pass
         if self.workload == "wgrad":
             return e * (self.in_bytes + 1)          # delayed: one pass
+        if self.workload == "dgrad":
+            nd, nw = self.M * self.K, self.N * self.K
+            return nd * (self.in_bytes + 2) + nw * (2 * self.in_bytes + 1)   # dY delayed, 2 outputs; W two-pass
         return e * (self.in_bytes + 1)              # row / block: one pass (scales negligible)
 
 

@@ -163,6 +163,42 @@ def quantize(x: torch.Tensor, fmt="e4m3", granularity="tensor", pow2: bool = Fal
     return QuantResult(out, scale_inv_out, amax_out, fmt_name)
 
 
+def quantize_dual(x: torch.Tensor, fmt="e5m2", pow2: bool = False, history: Optional[AmaxHistory] = None,
+                  diag: Optional[Diag] = None, spike_guard: bool = False,
+                  out: Optional[torch.Tensor] = None, out_t: Optional[torch.Tensor] = None,
+                  scale_inv_out: Optional[torch.Tensor] = None,
+                  amax_out: Optional[torch.Tensor] = None):
+    """Per-tensor quantization into both layouts from one pass over x
+    (fp8_quantize_dual).  Returns (QuantResult with q [rows x cols], qt [cols x rows])."""
+    rows, cols, ld = _matrix(x, "x")
+    if x.dtype == torch.bfloat16:
+        in_dt = _lib.FP8_IN_BF16
+    elif x.dtype == torch.float32:
+        in_dt = _lib.FP8_IN_F32
+    else:
+        raise TypeError("x must be bfloat16 or float32, got %s" % x.dtype)
+    fmt_name = fmt if isinstance(fmt, str) else ("e4m3" if fmt == 0 else "e5m2")
+    dev = x.device
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if out_t is None:
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    ldq = max(out.stride(0), 1) if out.shape[0] > 1 else max(out.shape[1], 1)
+    ldqt = max(out_t.stride(0), 1) if out_t.shape[0] > 1 else max(out_t.shape[1], 1)
+    if scale_inv_out is None:
+        scale_inv_out = torch.empty((1, 1), dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty((1, 1), dtype=torch.float32, device=dev)
+    flags = (_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_SPIKE_GUARD if spike_guard else 0)
+    st = _lib.lib().fp8_quantize_dual(
+        x.data_ptr(), in_dt, rows, cols, ld, _fmt(fmt), flags,
+        _ptr(history.buf) if history is not None else None, out.data_ptr(), ldq, out_t.data_ptr(), ldqt,
+        scale_inv_out.data_ptr(), amax_out.data_ptr(), _ptr(diag.buf) if diag is not None else None,
+        _stream(dev))
+    _lib.check(st, "fp8_quantize_dual")
+    return QuantResult(out, scale_inv_out, amax_out, fmt_name), out_t
+
+
 def amax(x: torch.Tensor, granularity="tensor", out: Optional[torch.Tensor] = None) -> torch.Tensor:
     rows, cols, ld = _matrix(x, "x")
     in_dt = _lib.FP8_IN_BF16 if x.dtype == torch.bfloat16 else _lib.FP8_IN_F32

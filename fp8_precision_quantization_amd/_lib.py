@@ -46,6 +46,7 @@ SIGNATURES = {
     "fp8_history_set_guard": (_INT, [_P, ctypes.c_float, _P]),
     "fp8_amax": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P]),
     "fp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U32, _P, _P, _I64, _P, _P, _P, _P]),
+    "fp8_quantize_dual": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _U32, _P, _P, _I64, _P, _I64, _P, _P, _P, _P]),
     "fp8_scaled_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,
                                _P, _INT, _I64, _P]),
     "fp8_blockscaled_gemm": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _INT, _I64, _P]),

@@ -206,30 +206,40 @@ fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t 
     return launch_result(fp8mi::launch_quantize(a), "fp8_amax");
 }
 
-fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
-                        fp8_format fmt, fp8_granularity gran, uint32_t flags, fp8_amax_history* hist,
-                        uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out, fp8_diag* diag,
-                        void* stream) {
+// fp8_quantize and fp8_quantize_dual (qt != nullptr: q untransposed plus qt
+// transposed, per tensor).
+static fp8_status quantize_impl(const char* what, const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols,
+                                int64_t ld, fp8_format fmt, fp8_granularity gran, uint32_t flags,
+                                fp8_amax_history* hist, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                                bool dual, float* scale_inv_out, float* amax_out, fp8_diag* diag, void* stream) {
     fp8_status st = check_matrix_in(x, in_dtype, rows, cols, ld);
     if (st != FP8_OK) return st;
     if (fmt != FP8_E4M3 && fmt != FP8_E5M2)
         return fail(FP8_ERR_INVALID_ARG, "format %d is not FP8_E4M3 or FP8_E5M2", (int)fmt);
     if (!valid_gran(gran)) return fail(FP8_ERR_INVALID_ARG, "granularity %d is not a fp8_granularity", (int)gran);
-    const uint32_t known = FP8_SCALE_POW2 | FP8_TRANSPOSE_OUT | FP8_SPIKE_GUARD;
+    const uint32_t known = FP8_SCALE_POW2 | FP8_SPIKE_GUARD | (dual ? 0u : FP8_TRANSPOSE_OUT);
     if (flags & ~known) return fail(FP8_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~known);
     if ((flags & FP8_SPIKE_GUARD) && hist == nullptr)
         return fail(FP8_ERR_INVALID_ARG, "FP8_SPIKE_GUARD needs delayed scaling (hist != NULL)");
-    const bool transpose = (flags & FP8_TRANSPOSE_OUT) != 0;
-    if (transpose && gran != FP8_GRAN_TENSOR)
+    const bool transpose = dual || (flags & FP8_TRANSPOSE_OUT) != 0;
+    if (transpose && !dual && gran != FP8_GRAN_TENSOR)
         return fail(FP8_ERR_INVALID_ARG, "FP8_TRANSPOSE_OUT needs FP8_GRAN_TENSOR");
     if (hist != nullptr && gran != FP8_GRAN_TENSOR)
         return fail(FP8_ERR_INVALID_ARG, "delayed scaling (hist != NULL) needs FP8_GRAN_TENSOR");
     if (hist != nullptr && !is_aligned(hist, 16)) return fail(FP8_ERR_MISALIGNED, "hist must be 16-byte aligned");
     if (q == nullptr && rows > 0 && cols > 0) return fail(FP8_ERR_INVALID_ARG, "q is NULL");
-    const int64_t qcols = transpose ? rows : cols;
-    if (ldq < qcols || ldq < 1)
-        return fail(FP8_ERR_INVALID_ARG, "ldq=%lld must be >= %s=%lld", (long long)ldq,
-                    transpose ? "rows (transposed output)" : "cols", (long long)qcols);
+    if (dual) {
+        if (qt == nullptr && rows > 0 && cols > 0) return fail(FP8_ERR_INVALID_ARG, "qt is NULL");
+        if (ldq < cols || ldq < 1)
+            return fail(FP8_ERR_INVALID_ARG, "ldq=%lld must be >= cols=%lld", (long long)ldq, (long long)cols);
+        if (ldqt < rows || ldqt < 1)
+            return fail(FP8_ERR_INVALID_ARG, "ldqt=%lld must be >= rows=%lld", (long long)ldqt, (long long)rows);
+    } else {
+        const int64_t qcols = transpose ? rows : cols;
+        if (ldq < qcols || ldq < 1)
+            return fail(FP8_ERR_INVALID_ARG, "ldq=%lld must be >= %s=%lld", (long long)ldq,
+                        transpose ? "rows (transposed output)" : "cols", (long long)qcols);
+    }
     const int64_t ng = num_groups(gran, rows, cols);
     if (scale_inv_out == nullptr && ng > 0) return fail(FP8_ERR_INVALID_ARG, "scale_inv_out is NULL");
     if (amax_out == nullptr && ng > 0) return fail(FP8_ERR_INVALID_ARG, "amax_out is NULL");
@@ -246,10 +256,31 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
     a.scratch = scratch;
     a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
     a.fmt = fmt; a.gran = gran; a.pow2 = (flags & FP8_SCALE_POW2) != 0; a.transpose = transpose;
-    a.write_q = true; a.hist = hist; a.guard = (flags & FP8_SPIKE_GUARD) != 0; a.q = q; a.ldq = ldq;
+    a.write_q = true; a.hist = hist; a.guard = (flags & FP8_SPIKE_GUARD) != 0;
+    if (dual) {   // the kernel's main output is the transposed one
+        a.q = qt; a.ldq = ldqt; a.q2 = q; a.ldq2 = ldq;
+    } else {
+        a.q = q; a.ldq = ldq;
+    }
     a.scale_inv = scale_inv_out;
     a.amax = amax_out; a.diag = diag; a.stream = (hipStream_t)stream; a.num_cus = cus;
-    return launch_result(fp8mi::launch_quantize(a), "fp8_quantize");
+    return launch_result(fp8mi::launch_quantize(a), what);
+}
+
+fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                        fp8_format fmt, fp8_granularity gran, uint32_t flags, fp8_amax_history* hist,
+                        uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out, fp8_diag* diag,
+                        void* stream) {
+    return quantize_impl("fp8_quantize", x, in_dtype, rows, cols, ld, fmt, gran, flags, hist, q, ldq, nullptr, 0,
+                         false, scale_inv_out, amax_out, diag, stream);
+}
+
+fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                             fp8_format fmt, uint32_t flags, fp8_amax_history* hist, uint8_t* q, int64_t ldq,
+                             uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* amax_out, fp8_diag* diag,
+                             void* stream) {
+    return quantize_impl("fp8_quantize_dual", x, in_dtype, rows, cols, ld, fmt, FP8_GRAN_TENSOR, flags, hist, q,
+                         ldq, qt, ldqt, true, scale_inv_out, amax_out, diag, stream);
 }
 
 static fp8_status check_gemm_common(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M,

@@ -22,6 +22,8 @@ struct QuantArgs {
     fp8_amax_history* hist = nullptr;
     uint8_t* q = nullptr;
     int64_t ldq = 0;
+    uint8_t* q2 = nullptr;       // with transpose: the untransposed codes too (fp8_quantize_dual)
+    int64_t ldq2 = 0;
     float* scale_inv = nullptr;
     float* amax = nullptr;
     fp8_diag* diag = nullptr;

@@ -417,13 +417,16 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
 // walk 128x128 tiles grid-stride; codes go through LDS with a 16-chunk XOR
 // swizzle so that both the row-wise writes and the column gathers are
 // conflict free, and each output row segment leaves as 16-byte stores
-// (128 B per 8 lanes).
+// (128 B per 8 lanes).  q2 != nullptr: the codes also go out untransposed
+// (q2[r][c], ld ldq2) from the same pass, for a gradient that feeds both
+// backward GEMMs.
 template <typename InT, int FMT, int MODE, bool DIAG>
 __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
     const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
     uint8_t* __restrict__ q, int64_t ldq, bool vec_out16, const uint32_t* __restrict__ partials_in,
     int n_in, const fp8_amax_history* hist, bool pow2, float* __restrict__ scale_inv_out,
-    float* __restrict__ amax_out, fp8_diag* diag, uint32_t* __restrict__ partials_out) {
+    float* __restrict__ amax_out, fp8_diag* diag, uint32_t* __restrict__ partials_out,
+    uint8_t* __restrict__ q2, int64_t ldq2, bool vec_out2) {
     __shared__ uint32_t lds[16];
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 128];
     constexpr bool DELAYED = MODE == kModeDelayed;
@@ -470,6 +473,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
             const uint2 codes = encode_unit<FMT, DIAG>(p[i], s, cnt);
             const int pos = cu ^ ((r >> 4) & 15);
             *reinterpret_cast<uint2*>(&tile[r * 128 + pos * 8]) = codes;
+            if (q2 != nullptr && r0 + r < rows && nvc > 0) store_unit(q2, (r0 + r) * ldq2 + c, nvc, vec_out2, codes);
         }
         __syncthreads();
         // gather: chunk = (output row cl in 0..127, input-row segment rs in 0..7)
@@ -739,6 +743,7 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
         const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 127) / 128);
         const unsigned tgrid = grid_for(tiles, 1, kMaxCastBlocks);
         const bool v16 = a.q != nullptr && aligned(a.q, 16) && a.ldq % 16 == 0;
+        const bool v2 = a.q2 != nullptr && aligned(a.q2, 8) && a.ldq2 % 8 == 0;
         const bool delayed = a.hist != nullptr;
         // pass 1: amax partials (JIT), or the bootstrap partials of an empty history
         hipLaunchKernelGGL(k_amax_partials<InT>, dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in, amax_partials,
@@ -755,7 +760,7 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
                                a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16,                             \
                                (const uint32_t*)amax_partials, (int)agrid,                                \
                                (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
-                               cast_partials);                                                            \
+                               cast_partials, a.q2, a.ldq2, v2);                                          \
         else                                                                                              \
             hipLaunchKernelGGL((k_cast_tensor<InT, FMT, MODE, DG>), dim3(cgrid), dim3(kThreads), 0, st, x, g,   \
                                vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,          \

@@ -180,6 +180,17 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
                         fp8_amax_history* hist, uint8_t* q, int64_t ldq, float* scale_inv_out,
                         float* amax_out, fp8_diag* diag, void* stream);
 
+/* Per-tensor quantization with both layouts from one pass over x: q
+ * [rows x cols] (ldq >= cols) and qt [cols x rows] (ldqt >= rows), the same
+ * codes.  A gradient feeds the data-gradient GEMM as dY and the weight-
+ * gradient GEMM as dY^T, both in E5M2 ([DeepL] 2.1), so one read of dY gives
+ * both operands.  Arguments and rules as fp8_quantize with FP8_GRAN_TENSOR;
+ * flags: FP8_SCALE_POW2, FP8_SPIKE_GUARD. */
+fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                             fp8_format fmt, uint32_t flags, fp8_amax_history* hist, uint8_t* q, int64_t ldq,
+                             uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* amax_out, fp8_diag* diag,
+                             void* stream);
+
 /* Scaled FP8 GEMM ([H100] FP8 matrix multiply-add in hardware; [Soup]
  * tensorwise and rowwise GEMMs; [DeepL] 2.2 results return to high
  * precision):

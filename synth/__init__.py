@@ -113,3 +113,13 @@ def wgrad_step(t: int, tokens: int = 8192, hidden: int = 4096,
     rx = np.random.default_rng(600 + t)
     x = normal(rx, tokens, hidden)
     return to_bf16_bits(dy), to_bf16_bits(x)
+
+
+def dgrad(M: int = 4096, N: int = 14336, K: int = 4096, seed: int = 7):
+    """(dY, W) for the data gradient of the 8B-style MLP up-projection
+    Y = X W^T: dY [M x N] = 1e-3 * t(3) (the gradient recipe of wgrad_step),
+    W [N x K] N(0, 0.02); bf16 bit patterns."""
+    rg = np.random.default_rng(seed)
+    dy = student_t(rg, M, N, 3.0, 1e-3)
+    w = normal(rg, N, K, 0.02)
+    return to_bf16_bits(dy), to_bf16_bits(w)

@@ -85,6 +85,32 @@ def test_quantize_validation(kw, status, needle):
     assert needle in msg
 
 
+def qd(**kw):
+    a = dict(x=FAKE, in_dt=L.FP8_IN_BF16, rows=64, cols=96, ld=96, fmt=L.FP8_E5M2, flags=0, hist=None,
+             q=FAKE, ldq=96, qt=FAKE, ldqt=64, sinv=FAKE, amax=FAKE, diag=None)
+    a.update(kw)
+    st = L.lib().fp8_quantize_dual(a["x"], a["in_dt"], a["rows"], a["cols"], a["ld"], a["fmt"], a["flags"],
+                                   a["hist"], a["q"], a["ldq"], a["qt"], a["ldqt"], a["sinv"], a["amax"],
+                                   a["diag"], None)
+    return st, L.lib().fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(qt=None), 1, "qt is NULL"),
+    (dict(ldq=90), 1, "ldq"),
+    (dict(ldqt=60), 1, "ldqt"),
+    (dict(flags=2), 1, "flag"),
+    (dict(flags=4), 1, "FP8_SPIKE_GUARD"),
+    (dict(fmt=5), 1, "format"),
+    (dict(x=FAKE + 1), 3, "aligned"),
+])
+def test_quantize_dual_validation(kw, status, needle):
+    st, msg = qd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
 def gemm(**kw):
     a = dict(A=FAKE, fa=0, lda=256, B=FAKE, fb=0, ldb=256, M=256, N=256, K=256, sa=FAKE, ar=0,
              sb=FAKE, br=0, C=FAKE, out=L.FP8_OUT_BF16, ldc=256)

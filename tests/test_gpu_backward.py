@@ -1,0 +1,121 @@
+"""GPU parity of the backward pass around the scaled GEMM: the dual-layout
+cast of a gradient (fp8_quantize_dual: dY and dY^T from one pass), the data
+gradient dX = dY W (E5M2 x E4M3, W cast transposed) and the weight gradient
+dW = dY^T X, each against the oracle; and the accuracy of the FP8 backward
+GEMMs against the same products in high precision (the bf16/fp32 weight
+gradient of the rowwise_with_gw_hp recipe, as the comparison)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import dev_input, host, say
+from tests.parity import assert_gemm, exact_checker
+
+pytestmark = pytest.mark.gpu
+
+fp8 = pytest.importorskip("fp8_precision_quantization_amd")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu):
+    yield
+
+
+@pytest.mark.parametrize("shape", [(300, 260), (1000, 520), (64, 4096), (4096, 64), (1, 7)])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("in_f32", [False, True])
+def test_quantize_dual_parity(shape, fmt, in_f32):
+    """Both layouts bit-exact against the oracle's cast, just in time."""
+    rows, cols = shape
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = (rng.standard_t(3, size=(rows, cols)) * 1e-3).astype(np.float32)
+    data = x if in_f32 else synth.to_bf16_bits(x)
+    o = oracle.quantize(data, oracle.E4M3 if fmt == "e4m3" else oracle.E5M2, "tensor")
+    say("quantize dual", shape, fmt, "f32" if in_f32 else "bf16")
+    r, qt = fp8.quantize_dual(dev_input(data), fmt)
+    assert np.array_equal(host(r.q), o["q"])
+    assert np.array_equal(host(qt), o["q"].T)
+    assert host(r.scale_inv)[0, 0] == o["scale_inv"].ravel()[0]
+    assert host(r.amax)[0, 0] == o["amax"].ravel()[0]
+
+
+@pytest.mark.parametrize("guard", [False, True])
+def test_quantize_dual_delayed_20_steps(guard):
+    """Delayed scaling through the dual cast, step by step against the oracle
+    ring (the wgrad recipe's dY with its spike at step 12)."""
+    tokens, hidden = 384, 640
+    h = fp8.AmaxHistory(16)
+    if guard:
+        h.set_guard(10.0)
+    o = oracle.DelayedScaler(oracle.E5M2, spike_threshold=10.0 if guard else 0.0)
+    for t in range(20):
+        dy, _ = synth.wgrad_step(t, tokens=tokens, hidden=hidden)
+        say("dual delayed step", t, "guard" if guard else "")
+        r, qt = fp8.quantize_dual(dev_input(dy), "e5m2", history=h, spike_guard=guard)
+        w = o.step(dy)
+        assert np.array_equal(host(r.q), w["q"]), t
+        assert np.array_equal(host(qt), w["q"].T), t
+        assert host(r.scale_inv)[0, 0] == w["scale_inv"], t
+        assert host(r.amax)[0, 0] == w["amax"], t
+
+
+def _rel(y, ref):
+    return float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
+
+
+@pytest.mark.timeout(600)
+def test_backward_gemms_parity_and_accuracy():
+    """dX = dY W and dW = dY^T X through FP8 (dY E5M2 from the dual cast, W and
+    X E4M3 cast transposed): sampled outputs against the oracle within the
+    floored 1e-3 rule, and the normwise error of the whole FP8 results against
+    the same products of the bf16 inputs in fp64."""
+    M, N, K = 1024, 2048, 1024          # tokens, layer outputs, layer inputs
+    rng = np.random.default_rng(31)
+    dy = synth.to_bf16_bits((rng.standard_t(3, size=(M, N)) * 1e-3).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    say("backward quantize")
+    rdy, dyt = fp8.quantize_dual(dev_input(dy), "e5m2")
+    rwt = fp8.quantize(dev_input(w), "e4m3", "tensor", transpose=True)      # W^T [K x N]
+    rxt = fp8.quantize(dev_input(x), "e4m3", "tensor", transpose=True)      # X^T [K x M]
+    ody = oracle.quantize(dy, oracle.E5M2, "tensor")
+    ow = oracle.quantize(w, oracle.E4M3, "tensor")
+    ox = oracle.quantize(x, oracle.E4M3, "tensor")
+    assert np.array_equal(host(rwt.q), ow["q"].T) and np.array_equal(host(rxt.q), ox["q"].T)
+    sdy, sw, sx = (o["scale_inv"].ravel() for o in (ody, ow, ox))
+
+    say("dgrad gemm", M, K, N)
+    dx = host(fp8.scaled_gemm(rdy.q, rwt.q, rdy.scale_inv.reshape(-1), rwt.scale_inv.reshape(-1),
+                              "e5m2", "e4m3", torch.float32))                 # [M x K]
+    wt_q = np.ascontiguousarray(ow["q"].T)
+    ms = np.concatenate([[0, M - 1], rng.integers(0, M, 1500)])
+    ns = np.concatenate([[K - 1, 0], rng.integers(0, K, 1500)])
+    y32, p = oracle.gemm_sampled(ody["q"], oracle.E5M2, wt_q, oracle.E4M3, sdy, sw, ms, ns)
+    print(assert_gemm(dx[ms, ns], y32, p, N, "f32", what="dgrad",
+                      exact=exact_checker(ody["q"], oracle.E5M2, wt_q, oracle.E4M3, sdy, sw, ms, ns)))
+
+    say("wgrad gemm", N, K, M)
+    dw = host(fp8.scaled_gemm(dyt, rxt.q, rdy.scale_inv.reshape(-1), rxt.scale_inv.reshape(-1),
+                              "e5m2", "e4m3", torch.float32))                 # [N x K]
+    dyt_q = np.ascontiguousarray(ody["q"].T)
+    xt_q = np.ascontiguousarray(ox["q"].T)
+    ms = np.concatenate([[0, N - 1], rng.integers(0, N, 1500)])
+    ns = np.concatenate([[K - 1, 0], rng.integers(0, K, 1500)])
+    y32, p = oracle.gemm_sampled(dyt_q, oracle.E5M2, xt_q, oracle.E4M3, sdy, sx, ms, ns)
+    print(assert_gemm(dw[ms, ns], y32, p, M, "f32", what="wgrad",
+                      exact=exact_checker(dyt_q, oracle.E5M2, xt_q, oracle.E4M3, sdy, sx, ms, ns)))
+
+    # accuracy against the high-precision products of the same bf16 inputs
+    dy64 = synth.bf16_bits_to_f32(dy).astype(np.float64)
+    w64 = synth.bf16_bits_to_f32(w).astype(np.float64)
+    x64 = synth.bf16_bits_to_f32(x).astype(np.float64)
+    e_dx = _rel(dx, dy64 @ w64)
+    e_dw = _rel(dw, dy64.T @ x64)
+    print("normwise error vs high precision: dgrad %.4f, wgrad %.4f" % (e_dx, e_dw))
+    # E5M2 keeps 2 mantissa bits, E4M3 3: per product about 2^-4 relative
+    # rounding error, uncorrelated over K terms; a few percent normwise
+    assert e_dx < 0.1 and e_dw < 0.1

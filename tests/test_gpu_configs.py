@@ -9,6 +9,8 @@ that the oracle computes one by one, within the floored 1e-3 rule.
   mlp70b  X [2048 x 8192] 1x128, W [28672 x 8192] 128x128, bf16 out
   wgrad   dY, X [8192 x 4096] delayed (16-step history) E5M2 / E4M3,
           transposed casts, dW = dY^T X [4096 x 4096] fp32, 20 steps
+  dgrad   dY [4096 x 14336] E5M2 in both layouts (one pass), W [14336 x 4096]
+          E4M3 transposed, dX = dY W [4096 x 4096] bf16 (K = 14336)
 """
 from __future__ import annotations
 
@@ -160,3 +162,28 @@ def test_config_wgrad_20_steps():
     # the spike saturates at step 12; step 13 rescales from the spike's amax
     assert sats[12] > 0
     assert sats[13] == 0
+
+
+@pytest.mark.timeout(900)
+def test_config_dgrad():
+    dy, w = synth.dgrad()
+    say("dgrad quantize dY dual", dy.shape)
+    rdy, dyt = fp8.quantize_dual(dev_input(dy), "e5m2")
+    say("dgrad quantize W transposed", w.shape)
+    rwt = fp8.quantize(dev_input(w), "e4m3", "tensor", transpose=True)
+    ody = oracle.quantize(dy, oracle.E5M2, "tensor")
+    ow = oracle.quantize(w, oracle.E4M3, "tensor")
+    assert np.array_equal(host(rdy.q), ody["q"])
+    assert np.array_equal(host(dyt), ody["q"].T)
+    assert np.array_equal(host(rwt.q), ow["q"].T)
+    assert host(rdy.scale_inv)[0, 0] == ody["scale_inv"].ravel()[0]
+    assert host(rwt.scale_inv).ravel()[0] == ow["scale_inv"].ravel()[0]
+    say("dgrad gemm")
+    y = host(fp8.scaled_gemm(rdy.q, rwt.q, rdy.scale_inv.reshape(-1), rwt.scale_inv.reshape(-1),
+                             "e5m2", "e4m3", torch.bfloat16))
+    wt_q = np.ascontiguousarray(ow["q"].T)
+    sdy, sw = ody["scale_inv"].ravel(), ow["scale_inv"].ravel()
+    ms, ns = sample_positions(4096, 4096, seed=5)
+    y32, p = oracle.gemm_sampled(ody["q"], oracle.E5M2, wt_q, oracle.E4M3, sdy, sw, ms, ns)
+    print(assert_gemm(y[ms, ns], y32, p, 14336, "bf16", what="dgrad",
+                      exact=exact_checker(ody["q"], oracle.E5M2, wt_q, oracle.E4M3, sdy, sw, ms, ns)))
