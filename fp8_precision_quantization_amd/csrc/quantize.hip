@@ -476,33 +476,45 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
             if (q2 != nullptr && r0 + r < rows && nvc > 0) store_unit(q2, (r0 + r) * ldq2 + c, nvc, vec_out2, codes);
         }
         __syncthreads();
-        // gather: chunk = (output row cl in 0..127, input-row segment rs in 0..7)
+        // gather: thread (rs = t % 8, cl4 = t / 8) takes input rows rs*16 ..
+        // rs*16+15 of input columns 4*cl4 .. 4*cl4+3 as 16 words (one row
+        // each), transposes the four 4x4 byte blocks with byte permutes and
+        // leaves 16 bytes for each of the 4 output rows; 8 consecutive lanes
+        // write one 128-byte output row segment.
+        {
+            const int rs = t & 7, cl4 = t >> 3;
+            const int chunk = (cl4 >> 1) ^ rs;          // the write swizzle; row >> 4 == rs here
+            uint32_t wv[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int chunk = t + 256 * j;
-            const int cl = chunk >> 3, rs = chunk & 7;
-            const int pos = (cl >> 3) ^ rs;
-            uint32_t w[4];
+            for (int k = 0; k < 16; ++k)
+                wv[k] = *reinterpret_cast<const uint32_t*>(&tile[(rs * 16 + k) * 128 + chunk * 8 + (cl4 & 1) * 4]);
+            uint32_t o[4][4];   // [output row c][input rows 4*blk .. 4*blk+3]
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                uint32_t acc = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int r = rs * 16 + k * 4 + b;
-                    acc |= (uint32_t)tile[r * 128 + pos * 8 + (cl & 7)] << (8 * b);
-                }
-                w[k] = acc;
+            for (int blk = 0; blk < 4; ++blk) {
+                const uint32_t w0 = wv[4 * blk], w1 = wv[4 * blk + 1], w2 = wv[4 * blk + 2], w3 = wv[4 * blk + 3];
+                // byte i of perm(a, b, sel) is byte sel_i of the 8 bytes {b (0..3), a (4..7)}
+                const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);   // w0.0 w1.0 w0.1 w1.1
+                const uint32_t lo23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);   // w2.0 w3.0 w2.1 w3.1
+                const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);   // w0.2 w1.2 w0.3 w1.3
+                const uint32_t hi23 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);   // w2.2 w3.2 w2.3 w3.3
+                o[0][blk] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);          // column 0 of rows 0..3
+                o[1][blk] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+                o[2][blk] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+                o[3][blk] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
             }
-            const int64_t orow = c0 + cl;
             const int64_t ocol = r0 + rs * 16;
-            if (orow < cols && ocol < rows) {
-                uint8_t* dst = q + orow * ldq + ocol;
-                const int64_t remr = rows - ocol;
-                if (vec_out16 && remr >= 16) {
-                    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-                } else {
-                    for (int b = 0; b < 16 && b < remr; ++b)
-                        dst[b] = (uint8_t)((w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+            const int64_t remr = rows - ocol;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t orow = c0 + cl4 * 4 + c;
+                if (orow < cols && remr > 0) {
+                    uint8_t* dst = q + orow * ldq + ocol;
+                    if (vec_out16 && remr >= 16) {
+                        *reinterpret_cast<uint4*>(dst) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+                    } else {
+                        for (int b = 0; b < 16 && b < remr; ++b)
+                            dst[b] = (uint8_t)((o[c][b >> 2] >> (8 * (b & 3))) & 0xFFu);
+                    }
                 }
             }
         }
@@ -738,13 +750,13 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
     if (a.gran == FP8_GRAN_TENSOR) {
         uint32_t* cast_partials = a.scratch + kScratchCastPartials;
         uint32_t* amax_partials = a.scratch + kScratchAmaxPartials;
+        const bool delayed = a.hist != nullptr;
         const unsigned agrid = grid_for(g.units, (int64_t)kThreads * kUnroll, kMaxAmaxBlocks);
         const unsigned cgrid = grid_for(g.units, (int64_t)kThreads * kUnroll, cap);
         const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 127) / 128);
         const unsigned tgrid = grid_for(tiles, 1, kMaxCastBlocks);
         const bool v16 = a.q != nullptr && aligned(a.q, 16) && a.ldq % 16 == 0;
         const bool v2 = a.q2 != nullptr && aligned(a.q2, 8) && a.ldq2 % 8 == 0;
-        const bool delayed = a.hist != nullptr;
         // pass 1: amax partials (JIT), or the bootstrap partials of an empty history
         hipLaunchKernelGGL(k_amax_partials<InT>, dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in, amax_partials,
                            (const fp8_amax_history*)a.hist);
