@@ -28,6 +28,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 E4M3, E5M2 = 0, 1
 GRAN_TENSOR, GRAN_ROW, GRAN_1x128, GRAN_128x128 = 0, 1, 2, 3
 IN_F32, IN_BF16 = 0, 1
+KV_E4M3, KV_E5M2, KV_BF16 = 0, 1, 2
+KV_PER_TOKEN_HEAD, KV_PER_HEAD = 0, 1
 
 GCC_FLAGS = ["-O2", "-std=gnu11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
              "-fPIC", "-shared"]
@@ -82,6 +84,8 @@ def lib():
         L.or_f32_to_bf16.restype = ctypes.c_uint16
         L.or_f32_to_bf16.argtypes = [f32]
         L.or_f32_to_bf16_array.argtypes = [P, i64, P]
+        L.or_kv_store.argtypes = [P, i32, i64, i64, i64, i64, P, i64, i32, i32, i32, P, P, P]
+        L.or_kv_load.argtypes = [P, i32, i32, P, i64, i64, i64, P, i64, i32, P, i64]
         L.or_num_threads.restype = i32
         L.or_num_threads.argtypes = []
         _lib = L
@@ -320,3 +324,57 @@ def f32_to_bf16(v: np.ndarray) -> np.ndarray:
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# -------------------------------------------------------------- KV cache --
+_KV_STORAGE = {"e4m3": KV_E4M3, "e5m2": KV_E5M2, "bf16": KV_BF16}
+_KV_SCALING = {"token_head": KV_PER_TOKEN_HEAD, "head": KV_PER_HEAD}
+
+
+def _slots_arg(slots, n):
+    if slots is None:
+        return None
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    assert slots.shape == (n,)
+    return slots
+
+
+def kv_store(x: np.ndarray, heads: int, head_dim: int, cache: np.ndarray, scale_inv: np.ndarray,
+             storage="e4m3", scaling="token_head", slots=None, pow2: bool = False):
+    """Store n new tokens (x: [n x heads*head_dim], float32 or bf16 bits) into
+    a cache in place (see or_kv_store).  cache: uint8 [capacity x heads x
+    head_dim] (uint16 for bf16 storage); scale_inv: float32 [capacity x heads]
+    (written, token_head) or [heads] (read, head).  Returns the counters."""
+    x, dt = _in_array(x)
+    n = x.shape[0]
+    assert x.shape[1] == heads * head_dim
+    st = _KV_STORAGE[storage]
+    sc = _KV_SCALING[scaling]
+    capacity = cache.shape[0]
+    assert cache.flags.c_contiguous and cache.shape[1:] == (heads, head_dim)
+    assert cache.dtype == (np.uint16 if st == KV_BF16 else np.uint8)
+    assert scale_inv.dtype == np.float32 and scale_inv.flags.c_contiguous
+    sl = _slots_arg(slots, n)
+    counts = np.zeros(3, dtype=np.int64)
+    lib().or_kv_store(_p(x), dt, n, heads, head_dim, x.shape[1], _p(sl) if sl is not None else None,
+                      capacity, st, sc, int(bool(pow2)), _p(cache), _p(scale_inv), _p(counts))
+    return {"sat": int(counts[0]), "nonfinite": int(counts[1]), "underflow": int(counts[2])}
+
+
+def kv_load(cache: np.ndarray, scale_inv: np.ndarray, n: int, storage="e4m3",
+            scaling="token_head", slots=None, out_bf16: bool = True, out=None):
+    """Gather n cache rows and dequantize them (see or_kv_load).  Returns
+    out: [n x heads*head_dim], uint16 bf16 bits or float32."""
+    st = _KV_STORAGE[storage]
+    sc = _KV_SCALING[scaling]
+    capacity, heads, head_dim = cache.shape
+    assert cache.flags.c_contiguous
+    scale_inv = np.ascontiguousarray(scale_inv, dtype=np.float32)
+    if out is None:
+        out = np.zeros((n, heads * head_dim), dtype=np.uint16 if out_bf16 else np.float32)
+    assert out.flags.c_contiguous and out.shape == (n, heads * head_dim)
+    sl = _slots_arg(slots, n)
+    lib().or_kv_load(_p(cache), st, sc, _p(scale_inv), n, heads, head_dim,
+                     _p(sl) if sl is not None else None, capacity, int(bool(out_bf16)),
+                     _p(out), heads * head_dim)
+    return out

@@ -458,5 +458,91 @@ void or_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = or_f32_to_bf16(v[i]);
 }
 
+/* ------------------------------------------------------------------------ */
+/* O9. FP8 KV cache.  [DeepL] 3.1: holding the attention K and V caches in    */
+/* FP8 halves their memory against BF16 (longer contexts, larger batches);   */
+/* K's precision drives the attention scores, V's the mixed output, and      */
+/* keeping a single layer's K cache in BF16 removed a long-sequence error.    */
+/* READING (the page fixes no layout, granularity or scale rule):             */
+/*  - one layer's K (or V) cache is [capacity x heads x head_dim], head_dim   */
+/*    contiguous.  New token t (of n, x row t at x + t*ld) goes to cache row  */
+/*    slots[t]; slots == NULL means row t; a slot outside [0, capacity) is    */
+/*    not stored (padding).                                                   */
+/*  - PER_TOKEN_HEAD: each (token, head) vector of head_dim values is one     */
+/*    group: amax (O3), scale (O4, pow2 optional), cast (O5), and             */
+/*    scale_inv[slot*heads + head] is stored beside the codes.                */
+/*  - PER_HEAD: a fixed, calibrated scale_inv[head] is given; the cast        */
+/*    multiplies by s = fl32(1 / scale_inv[head]).                            */
+/*  - BF16 storage (the per-layer fallback): the values rounded to bf16 (O8), */
+/*    no scale.                                                               */
+/*  - load gathers cache rows slots[t] (NULL: row t) into out row t:          */
+/*    y = fl32(decode(q) * scale_inv), kept in fp32 or rounded to bf16 (O8);   */
+/*    a BF16 cache returns its values.  A slot outside [0, capacity) leaves   */
+/*    out row t untouched.                                                    */
+/* ------------------------------------------------------------------------ */
+enum { OR_KV_E4M3 = 0, OR_KV_E5M2 = 1, OR_KV_BF16 = 2 };
+enum { OR_KV_PER_TOKEN_HEAD = 0, OR_KV_PER_HEAD = 1 };
+
+void or_kv_store(const void* x, int in_dtype, int64_t n, int64_t heads, int64_t head_dim,
+                 int64_t ld, const int64_t* slots, int64_t capacity, int storage, int scaling,
+                 int pow2, void* cache, float* scale_inv, int64_t* counts3) {
+    int64_t sat = 0, nonfinite = 0, under = 0;
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t slot = slots ? slots[t] : t;
+        if (slot < 0 || slot >= capacity) continue;
+        for (int64_t h = 0; h < heads; ++h) {
+            int64_t src = t * ld + h * head_dim;
+            int64_t dst = (slot * heads + h) * head_dim;
+            if (storage == OR_KV_BF16) {
+                for (int64_t c = 0; c < head_dim; ++c)
+                    ((uint16_t*)cache)[dst + c] = or_f32_to_bf16(load_in(x, in_dtype, src + c));
+                continue;
+            }
+            float s, s_inv;
+            if (scaling == OR_KV_PER_TOKEN_HEAD) {
+                /* one row of one group: O3 and O4 as for row-wise scaling */
+                float amax;
+                or_amax((const char*)x + src * (in_dtype == OR_IN_F32 ? 4 : 2), in_dtype,
+                        1, head_dim, head_dim, OR_GRAN_ROW, &amax);
+                or_scale(amax, storage, pow2, &s, &s_inv);
+                scale_inv[slot * heads + h] = s_inv;
+            } else {
+                s = 1.0f / scale_inv[h];
+            }
+            int64_t c3[3];
+            or_quantize_with_scales((const char*)x + src * (in_dtype == OR_IN_F32 ? 4 : 2),
+                                    in_dtype, 1, head_dim, head_dim, OR_GRAN_TENSOR, storage,
+                                    &s, (uint8_t*)cache + dst, head_dim, c3);
+            sat += c3[0]; nonfinite += c3[1]; under += c3[2];
+        }
+    }
+    if (counts3) { counts3[0] = sat; counts3[1] = nonfinite; counts3[2] = under; }
+}
+
+void or_kv_load(const void* cache, int storage, int scaling, const float* scale_inv,
+                int64_t n, int64_t heads, int64_t head_dim, const int64_t* slots,
+                int64_t capacity, int out_bf16, void* out, int64_t ld_out) {
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t slot = slots ? slots[t] : t;
+        if (slot < 0 || slot >= capacity) continue;
+        for (int64_t h = 0; h < heads; ++h) {
+            int64_t src = (slot * heads + h) * head_dim;
+            int64_t dst = t * ld_out + h * head_dim;
+            float sinv = 1.0f;
+            if (storage != OR_KV_BF16)
+                sinv = scaling == OR_KV_PER_TOKEN_HEAD ? scale_inv[slot * heads + h] : scale_inv[h];
+            for (int64_t c = 0; c < head_dim; ++c) {
+                float y;
+                if (storage == OR_KV_BF16)
+                    y = bf16_to_f32(((const uint16_t*)cache)[src + c]);
+                else
+                    y = (float)or_decode(storage, ((const uint8_t*)cache)[src + c]) * sinv;
+                if (out_bf16) ((uint16_t*)out)[dst + c] = or_f32_to_bf16(y);
+                else ((float*)out)[dst + c] = y;
+            }
+        }
+    }
+}
+
 /* Threads the OpenMP loops above use (reported with CPU timings). */
 int or_num_threads(void) { return omp_get_max_threads(); }
