@@ -12,7 +12,12 @@ Prints ONE JSON line.  `value` = whole-step throughput in TFLOP/s
 (2MNK / step time); the GEMM kernel's own TFLOP/s and % of the FP8 MFMA peak,
 and the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.
 
-    python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|dgrad|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|dgrad|kv|tiny]
+
+The kv workload is the memory-bound FP8 KV cache instead (its own JSON line
+in GB/s): one step = one layer's store of a 8192-token chunk of K and V into
+E4M3 caches through a page table, then the gather-dequantize of the whole
+32768-token context to bf16.
 """
 from __future__ import annotations
 
@@ -34,6 +39,9 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 # profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None whenever k_gemm changes
 # until the counters are taken again.
 GEMM_TRAFFIC_BYTES = 476156704
+# The same counters for one fp8_kv_load launch of the kv workload (None until
+# taken for the current kernel).
+KV_LOAD_TRAFFIC_BYTES = None
 
 WORKLOADS = {
     "tiny": "tiny: X, W [256 x 256] fp32 N(0,1); per-tensor E4M3; Y fp32",
@@ -47,6 +55,10 @@ WORKLOADS = {
               "delayed scaling (16-step history), transposed casts; dW = dY^T X [4096 x 4096] fp32"),
     "dgrad": ("dgrad: dY [4096 x 14336] bf16 1e-3*t(3) -> E5M2 delayed, both layouts in one pass; "
               "W [14336 x 4096] bf16 N(0,0.02) -> E4M3 transposed; dX = dY W [4096 x 4096] bf16"),
+    "kv": ("kv: one layer of an 8B-style model, 8 KV heads x 128; K (outlier channels) and V bf16 of a "
+           "8192-token chunk stored as E4M3 with per-(token, head) scales into 32768-row caches through "
+           "a 16-row page table, then all 32768 rows of K and V gathered and dequantized to bf16; "
+           "4 layers rotate"),
 }
 
 
@@ -199,6 +211,140 @@ class Step:
         return e * (self.in_bytes + 1)              # row / block: one pass (scales negligible)
 
 
+class KvStep:
+    """The KV-cache step: store K and V of the new chunk, gather the context."""
+
+    LAYERS = 4     # rotated so that one step's caches are not left in the 256 MB Infinity Cache
+
+    def __init__(self, torch, fp8, synth):
+        cfg = synth.CONFIGS["kv"]
+        self.H, self.D, self.cap, self.n = cfg["heads"], cfg["head_dim"], cfg["capacity"], cfg["new_tokens"]
+        dev = torch.device("cuda:0")
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        pages = synth.kv_pages(self.cap, cfg["page"])
+        self.pt = torch.from_numpy(pages).to(dev)
+        self.new_slots = self.pt[self.cap - self.n:].contiguous()
+        self.k = [bf16(synth.kv_keys(self.n, self.H, self.D, seed=11 + 100 * i)) for i in range(self.LAYERS)]
+        self.v = [bf16(synth.kv_values(self.n, self.H, self.D, seed=12 + 100 * i)) for i in range(self.LAYERS)]
+        self.cache = fp8.KVCache(self.LAYERS, self.cap, self.H, self.D, device=dev)
+        old = bf16(synth.kv_values(self.cap - self.n, self.H, self.D, seed=21))
+        old_slots = self.pt[:self.cap - self.n].contiguous()
+        for layer in range(self.LAYERS):
+            self.cache.store(layer, old, old, old_slots)
+        self.ko = torch.empty((self.cap, self.H * self.D), dtype=torch.bfloat16, device=dev)
+        self.vo = torch.empty_like(self.ko)
+        self.fp8 = fp8
+        self.i = 0
+
+    def store(self):
+        L = self.i % self.LAYERS
+        self.cache.store(L, self.k[L], self.v[L], self.new_slots)
+
+    def load(self):
+        L = self.i % self.LAYERS
+        self.cache.k[L].load(slots=self.pt, out=self.ko)
+        self.cache.v[L].load(slots=self.pt, out=self.vo)
+        self.i += 1
+
+    def store_bytes(self) -> float:
+        """Algorithmic HBM bytes of the two stores: bf16 in, codes and one
+        fp32 scale per (token, head) out, the slot of each token read."""
+        n, H, D = self.n, self.H, self.D
+        return 2 * (n * H * D * (2 + 1) + n * H * 4 + n * 8)
+
+    def load_bytes(self) -> float:
+        """The two gathers: codes and scales in, bf16 out, a slot per row."""
+        c, H, D = self.cap, self.H, self.D
+        return 2 * (c * H * D * (1 + 2) + c * H * 4 + c * 8)
+
+
+def kv_cpu_baseline(synth):
+    """The oracle, untuned, on one whole KV step (one layer): store the 8192
+    new tokens of K and V, gather all 32768 rows of each; GB/s by the same
+    byte count.  Its loops run per (token, head) vector, one row at a time,
+    so one core does the work."""
+    import oracle
+    cfg = synth.CONFIGS["kv"]
+    H, D, cap = cfg["heads"], cfg["head_dim"], cfg["capacity"]
+    n, m = cfg["new_tokens"], cap
+    pages = synth.kv_pages(cap, cfg["page"])
+    k = synth.kv_keys(n, H, D)
+    v = synth.kv_values(n, H, D)
+    ck = np.zeros((cap, H, D), np.uint8)
+    cv = np.zeros((cap, H, D), np.uint8)
+    sk = np.zeros((cap, H), np.float32)
+    sv = np.zeros((cap, H), np.float32)
+    t0 = time.perf_counter()
+    oracle.kv_store(k, H, D, ck, sk, slots=pages[cap - n:])
+    oracle.kv_store(v, H, D, cv, sv, slots=pages[cap - n:])
+    oracle.kv_load(ck, sk, m, slots=pages[:m])
+    oracle.kv_load(cv, sv, m, slots=pages[:m])
+    dt = time.perf_counter() - t0
+    nbytes = 2 * (n * H * D * 3 + n * H * 4 + n * 8) + 2 * (m * H * D * 3 + m * H * 4 + m * 8)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "store %d tokens of K and V (8 heads x 128, E4M3 per token-head) through the page "
+                      "table, gather %d rows of each to bf16: %.1f s" % (n, m, dt)}
+
+
+def kv_main(args, torch, fp8, synth):
+    st = KvStep(torch, fp8, synth)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        st.store()
+        st.load()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        ev[s][0].record()
+        st.store()
+        ev[s][1].record()
+        st.load()
+        ev[s][2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    s_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    l_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    sb, lb = st.store_bytes(), st.load_bytes()
+    s_gbs, l_gbs = sb / (s_ms * 1e-3) / 1e9, lb / (l_ms * 1e-3) / 1e9
+    # the gather kernel dominates; its launches are the two loads of a step
+    per_launch = lb / 2
+    roof = {"bound": "hbm", "achieved": round(l_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(l_gbs / PEAK_HBM_GBS, 4), "traffic": KV_LOAD_TRAFFIC_BYTES,
+            "algorithmic_bytes_per_launch": int(per_launch)}
+    cpu = None if args.no_cpu_baseline else kv_cpu_baseline(synth)
+    out = {
+        "metric": "FP8 KV-cache store + paged gather-dequantize GB/s (% HBM peak)",
+        "value": round((sb + lb) / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 codes + fp32 scales (bf16 in/out)",
+        "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": WORKLOADS["kv"], "heads": st.H, "head_dim": st.D, "capacity": st.cap,
+                   "new_tokens": st.n},
+        "kernels": {
+            "store_ms": round(s_ms, 4), "store_gbs": round(s_gbs, 1),
+            "load_ms": round(l_ms, 4), "load_gbs": round(l_gbs, 1),
+            "store_bytes": int(sb), "load_bytes": int(lb),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(args, workload, synth):
     """The oracle, untuned, on a bounded sample of the same step: quantize the
     first `cpu_rows` rows of X and `cpu_cols` rows of W, then the GEMM block
@@ -238,6 +384,9 @@ def main():
     import fp8_precision_quantization_amd as fp8
     import synth
 
+    if args.workload == "kv":
+        kv_main(args, torch, fp8, synth)
+        return
     st = Step(args.workload, torch, fp8, synth)
     torch.cuda.synchronize()
     for _ in range(args.warmup):

@@ -20,8 +20,9 @@ import torch
 from . import _lib
 from ._lib import Fp8Error  # noqa: F401
 
-__all__ = ["quantize", "amax", "scaled_gemm", "blockscaled_gemm", "AmaxHistory", "Diag",
-           "QuantResult", "Fp8Error", "FORMATS", "GRANULARITIES", "group_grid"]
+__all__ = ["quantize", "quantize_dual", "amax", "scaled_gemm", "blockscaled_gemm", "AmaxHistory", "Diag",
+           "QuantResult", "Fp8Error", "FORMATS", "GRANULARITIES", "group_grid", "kv_store", "kv_load",
+           "KVTensorCache", "KVCache"]
 
 FORMATS = {"e4m3": _lib.FP8_E4M3, "e5m2": _lib.FP8_E5M2}
 GRANULARITIES = {"tensor": _lib.FP8_GRAN_TENSOR, "row": _lib.FP8_GRAN_ROW,
@@ -260,3 +261,147 @@ def blockscaled_gemm(a_q: torch.Tensor, b_q: torch.Tensor, a_scale_inv: torch.Te
                                          _out_dtype(out.dtype), ldc, _stream(a_q.device))
     _lib.check(st, "fp8_blockscaled_gemm")
     return out
+
+
+# ------------------------------------------------------------ FP8 KV cache --
+KV_STORAGE = {"e4m3": _lib.FP8_KV_E4M3, "e5m2": _lib.FP8_KV_E5M2, "bf16": _lib.FP8_KV_BF16}
+KV_SCALING = {"token_head": _lib.FP8_KV_PER_TOKEN_HEAD, "head": _lib.FP8_KV_PER_HEAD}
+
+
+def _kv_rows(x: torch.Tensor, heads: int, head_dim: int, name: str):
+    """(n, ld) of a [n, heads*head_dim] or [n, heads, head_dim] device tensor
+    whose heads are packed back to back within a token."""
+    if not x.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if x.dim() == 3:
+        if tuple(x.shape[1:]) != (heads, head_dim) or x.stride(2) != 1 or (heads > 1 and x.stride(1) != head_dim):
+            raise ValueError("%s [n, heads, head_dim] must have packed heads" % name)
+    elif x.dim() == 2:
+        if x.shape[1] != heads * head_dim or (x.shape[1] > 1 and x.stride(1) != 1):
+            raise ValueError("%s must be [n, %d] with a contiguous last dimension" % (name, heads * head_dim))
+    else:
+        raise ValueError("%s must be 2-D or 3-D" % name)
+    n = x.shape[0]
+    return n, (x.stride(0) if n > 1 else heads * head_dim)
+
+
+def _slots(slots: Optional[torch.Tensor], n: int):
+    if slots is None:
+        return None
+    if slots.dtype != torch.int64 or not slots.is_cuda or slots.shape != (n,) or not slots.is_contiguous():
+        raise ValueError("slots must be a contiguous int64 device tensor of %d entries" % n)
+    return slots.data_ptr()
+
+
+def kv_store(x: torch.Tensor, cache: torch.Tensor, scale_inv: Optional[torch.Tensor], storage="e4m3",
+             scaling="token_head", slots: Optional[torch.Tensor] = None, pow2: bool = False,
+             diag: Optional[Diag] = None) -> None:
+    """Store new tokens' vectors x [n, heads*head_dim] (bf16/fp32) into one
+    layer's cache [capacity, heads, head_dim] (uint8 codes, bf16 for the
+    "bf16" storage) at rows `slots` (None: rows 0..n-1; negative = padding)."""
+    capacity, heads, head_dim = cache.shape
+    n, ld = _kv_rows(x, heads, head_dim, "x")
+    if x.dtype == torch.bfloat16:
+        in_dt = _lib.FP8_IN_BF16
+    elif x.dtype == torch.float32:
+        in_dt = _lib.FP8_IN_F32
+    else:
+        raise TypeError("x must be bfloat16 or float32, got %s" % x.dtype)
+    want = torch.bfloat16 if storage == "bf16" else torch.uint8
+    if cache.dtype != want or not cache.is_contiguous():
+        raise ValueError("cache must be a contiguous %s tensor" % want)
+    st = _lib.lib().fp8_kv_store(
+        x.data_ptr(), in_dt, n, ld, heads, head_dim, _slots(slots, n), KV_STORAGE[storage],
+        KV_SCALING[scaling], _lib.FP8_SCALE_POW2 if pow2 else 0, cache.data_ptr(), _ptr(scale_inv), capacity,
+        _ptr(diag.buf) if diag is not None else None, _stream(cache.device))
+    _lib.check(st, "fp8_kv_store")
+
+
+def kv_load(cache: torch.Tensor, scale_inv: Optional[torch.Tensor], n: Optional[int] = None, storage="e4m3",
+            scaling="token_head", slots: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gather n cache rows (slots, or rows 0..n-1) as dequantized values
+    out [n, heads*head_dim] (bf16 or fp32)."""
+    capacity, heads, head_dim = cache.shape
+    if n is None:
+        n = slots.shape[0] if slots is not None else capacity
+    if out is None:
+        out = torch.empty((n, heads * head_dim), dtype=out_dtype, device=cache.device)
+    n2, ld_out = _kv_rows(out, heads, head_dim, "out")
+    if n2 != n:
+        raise ValueError("out has %d rows, expected %d" % (n2, n))
+    st = _lib.lib().fp8_kv_load(
+        cache.data_ptr(), KV_STORAGE[storage], KV_SCALING[scaling], _ptr(scale_inv), capacity, heads, head_dim,
+        _slots(slots, n), n, _out_dtype(out.dtype), out.data_ptr(), ld_out, _stream(cache.device))
+    _lib.check(st, "fp8_kv_load")
+    return out
+
+
+class KVTensorCache:
+    """One layer's K (or V) cache: `data` [capacity, heads, head_dim] (uint8
+    codes; bf16 for the "bf16" storage) and `scale_inv` ([capacity, heads] for
+    per-(token, head) scales, [heads] fixed scales for "head" scaling)."""
+
+    def __init__(self, capacity: int, heads: int, head_dim: int, storage="e4m3", scaling="token_head",
+                 head_scale_inv: Optional[torch.Tensor] = None, device="cuda"):
+        if storage not in KV_STORAGE or scaling not in KV_SCALING:
+            raise ValueError("storage %r / scaling %r" % (storage, scaling))
+        self.storage, self.scaling = storage, scaling
+        self.capacity, self.heads, self.head_dim = capacity, heads, head_dim
+        dt = torch.bfloat16 if storage == "bf16" else torch.uint8
+        self.data = torch.zeros((capacity, heads, head_dim), dtype=dt, device=device)
+        if storage == "bf16":
+            self.scale_inv = None
+        elif scaling == "token_head":
+            self.scale_inv = torch.zeros((capacity, heads), dtype=torch.float32, device=device)
+        else:
+            if head_scale_inv is None or head_scale_inv.numel() != heads:
+                raise ValueError("'head' scaling needs head_scale_inv with %d entries" % heads)
+            self.scale_inv = head_scale_inv.to(device=device, dtype=torch.float32).contiguous()
+
+    @property
+    def nbytes(self) -> int:
+        n = self.data.numel() * self.data.element_size()
+        return n + (self.scale_inv.numel() * 4 if self.scale_inv is not None else 0)
+
+    def store(self, x: torch.Tensor, slots: Optional[torch.Tensor] = None, pow2: bool = False,
+              diag: Optional[Diag] = None) -> None:
+        kv_store(x, self.data, self.scale_inv, self.storage, self.scaling, slots, pow2, diag)
+
+    def load(self, n: Optional[int] = None, slots: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        return kv_load(self.data, self.scale_inv, n, self.storage, self.scaling, slots, out_dtype, out)
+
+
+class KVCache:
+    """K and V caches of every layer of a model.  Layers listed in
+    `bf16_k_layers` keep their K cache in bf16 (the per-layer fallback of a
+    precision-sensitive layer); `bf16_v_layers` likewise for V."""
+
+    def __init__(self, layers: int, capacity: int, kv_heads: int, head_dim: int, storage="e4m3",
+                 scaling="token_head", bf16_k_layers=(), bf16_v_layers=(), head_scale_inv=None, device="cuda"):
+        bk, bv = set(bf16_k_layers), set(bf16_v_layers)
+        for s in (bk, bv):
+            if any(not 0 <= i < layers for i in s):
+                raise ValueError("fallback layer index out of range 0..%d" % (layers - 1))
+
+        def make(i, fallback, which):
+            st = "bf16" if i in fallback else storage
+            hs = None if head_scale_inv is None else head_scale_inv[which][i]
+            return KVTensorCache(capacity, kv_heads, head_dim, st, scaling, hs, device)
+
+        self.k = [make(i, bk, 0) for i in range(layers)]
+        self.v = [make(i, bv, 1) for i in range(layers)]
+
+    @property
+    def nbytes(self) -> int:
+        return sum(c.nbytes for c in self.k + self.v)
+
+    def store(self, layer: int, k: torch.Tensor, v: torch.Tensor, slots: Optional[torch.Tensor] = None,
+              pow2: bool = False) -> None:
+        self.k[layer].store(k, slots, pow2)
+        self.v[layer].store(v, slots, pow2)
+
+    def load(self, layer: int, n: Optional[int] = None, slots: Optional[torch.Tensor] = None,
+             out_dtype=torch.bfloat16):
+        return (self.k[layer].load(n, slots, out_dtype), self.v[layer].load(n, slots, out_dtype))

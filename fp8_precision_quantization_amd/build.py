@@ -17,8 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8mi.so")
-SOURCES = ["quantize.hip", "gemm.hip", "api.cpp"]
-HEADERS = ["device_common.hpp", "launch.hpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "kvcache.hip", "api.cpp"]
+HEADERS = ["device_common.hpp", "cast_unit.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

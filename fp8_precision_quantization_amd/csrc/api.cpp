@@ -359,4 +359,82 @@ fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B,
     return launch_result(fp8mi::launch_blockscaled_gemm(g), "fp8_blockscaled_gemm");
 }
 
+// Shape and alignment rules shared by fp8_kv_store and fp8_kv_load.
+static fp8_status check_kv_common(const void* cache, int storage, int scaling, const void* scale_inv,
+                                  int64_t capacity, int32_t heads, int32_t head_dim, int64_t n_tokens) {
+    if (storage != FP8_KV_E4M3 && storage != FP8_KV_E5M2 && storage != FP8_KV_BF16)
+        return fail(FP8_ERR_INVALID_ARG, "storage %d is not FP8_KV_E4M3, FP8_KV_E5M2 or FP8_KV_BF16", storage);
+    if (scaling != FP8_KV_PER_TOKEN_HEAD && scaling != FP8_KV_PER_HEAD)
+        return fail(FP8_ERR_INVALID_ARG, "scaling %d is not FP8_KV_PER_TOKEN_HEAD or FP8_KV_PER_HEAD", scaling);
+    if (n_tokens < 0 || capacity < 0 || heads < 0)
+        return fail(FP8_ERR_INVALID_ARG, "negative size n_tokens=%lld capacity=%lld heads=%d",
+                    (long long)n_tokens, (long long)capacity, (int)heads);
+    if (head_dim < 8 || head_dim > 2048 || head_dim % 8 != 0)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "head_dim=%d must be a multiple of 8 in 8..2048", (int)head_dim);
+    if (heads > 0 && n_tokens >= (int64_t(1) << 31) / heads)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "n_tokens * heads must be < 2^31");
+    if (cache == nullptr && capacity > 0 && heads > 0) return fail(FP8_ERR_INVALID_ARG, "cache is NULL");
+    if (!is_aligned(cache, 16)) return fail(FP8_ERR_MISALIGNED, "cache must be 16-byte aligned");
+    if (storage != FP8_KV_BF16) {
+        if (scale_inv == nullptr && heads > 0) return fail(FP8_ERR_INVALID_ARG, "scale_inv is NULL");
+        if (!is_aligned(scale_inv, 4)) return fail(FP8_ERR_MISALIGNED, "scale_inv must be 4-byte aligned");
+    }
+    return FP8_OK;
+}
+
+fp8_status fp8_kv_store(const void* x, fp8_in_dtype in_dtype, int64_t n_tokens, int64_t ld, int32_t heads,
+                        int32_t head_dim, const int64_t* slots, fp8_kv_storage storage, fp8_kv_scaling scaling,
+                        uint32_t flags, void* cache, float* scale_inv, int64_t capacity, fp8_diag* diag,
+                        void* stream) {
+    fp8_status st = check_kv_common(cache, storage, scaling, scale_inv, capacity, heads, head_dim, n_tokens);
+    if (st != FP8_OK) return st;
+    if (in_dtype != FP8_IN_F32 && in_dtype != FP8_IN_BF16)
+        return fail(FP8_ERR_INVALID_ARG, "in_dtype %d is not FP8_IN_F32 or FP8_IN_BF16", (int)in_dtype);
+    if (flags & ~FP8_SCALE_POW2) return fail(FP8_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~FP8_SCALE_POW2);
+    const int64_t width = (int64_t)heads * head_dim;
+    if (ld < width || ld < 1)
+        return fail(FP8_ERR_INVALID_ARG, "ld=%lld must be >= heads*head_dim=%lld", (long long)ld, (long long)width);
+    if (ld % 8 != 0) return fail(FP8_ERR_MISALIGNED, "ld=%lld must be a multiple of 8", (long long)ld);
+    if (x == nullptr && n_tokens > 0 && heads > 0) return fail(FP8_ERR_INVALID_ARG, "x is NULL");
+    if (!is_aligned(x, 16)) return fail(FP8_ERR_MISALIGNED, "x must be 16-byte aligned");
+    if (!is_aligned(slots, 8)) return fail(FP8_ERR_MISALIGNED, "slots must be 8-byte aligned");
+    if (diag != nullptr && !is_aligned(diag, 4)) return fail(FP8_ERR_MISALIGNED, "diag must be 4-byte aligned");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    if (n_tokens == 0 || heads == 0 || capacity == 0) return ok();
+    fp8mi::KvStoreArgs a;
+    a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.n_tokens = n_tokens; a.ld = ld; a.heads = heads;
+    a.head_dim = head_dim; a.slots = slots; a.capacity = capacity; a.storage = storage;
+    a.per_head = scaling == FP8_KV_PER_HEAD; a.pow2 = (flags & FP8_SCALE_POW2) != 0; a.cache = cache;
+    a.scale_inv = scale_inv; a.diag = storage == FP8_KV_BF16 ? nullptr : diag; a.stream = (hipStream_t)stream;
+    return launch_result(fp8mi::launch_kv_store(a), "fp8_kv_store");
+}
+
+fp8_status fp8_kv_load(const void* cache, fp8_kv_storage storage, fp8_kv_scaling scaling, const float* scale_inv,
+                       int64_t capacity, int32_t heads, int32_t head_dim, const int64_t* slots, int64_t n_tokens,
+                       fp8_out_dtype out_dtype, void* out, int64_t ld_out, void* stream) {
+    fp8_status st = check_kv_common(cache, storage, scaling, scale_inv, capacity, heads, head_dim, n_tokens);
+    if (st != FP8_OK) return st;
+    if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16)
+        return fail(FP8_ERR_INVALID_ARG, "out_dtype %d is not FP8_OUT_F32 or FP8_OUT_BF16", (int)out_dtype);
+    const int64_t width = (int64_t)heads * head_dim;
+    if (ld_out < width || ld_out < 1)
+        return fail(FP8_ERR_INVALID_ARG, "ld_out=%lld must be >= heads*head_dim=%lld", (long long)ld_out,
+                    (long long)width);
+    if (ld_out % 8 != 0) return fail(FP8_ERR_MISALIGNED, "ld_out=%lld must be a multiple of 8", (long long)ld_out);
+    if (out == nullptr && n_tokens > 0 && heads > 0) return fail(FP8_ERR_INVALID_ARG, "out is NULL");
+    if (!is_aligned(out, 16)) return fail(FP8_ERR_MISALIGNED, "out must be 16-byte aligned");
+    if (!is_aligned(slots, 8)) return fail(FP8_ERR_MISALIGNED, "slots must be 8-byte aligned");
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    if (n_tokens == 0 || heads == 0 || capacity == 0) return ok();
+    fp8mi::KvLoadArgs a;
+    a.cache = cache; a.storage = storage; a.per_head = scaling == FP8_KV_PER_HEAD; a.scale_inv = scale_inv;
+    a.capacity = capacity; a.heads = heads; a.head_dim = head_dim; a.slots = slots; a.n_tokens = n_tokens;
+    a.out_bf16 = out_dtype == FP8_OUT_BF16; a.out = out; a.ld_out = ld_out; a.stream = (hipStream_t)stream;
+    return launch_result(fp8mi::launch_kv_load(a), "fp8_kv_load");
+}
+
 }  // extern "C"

@@ -48,7 +48,40 @@ struct GemmArgs {
     int num_cus = 256;
 };
 
+struct KvStoreArgs {
+    const void* x = nullptr;
+    bool in_bf16 = true;
+    int64_t n_tokens = 0, ld = 0;
+    int heads = 0, head_dim = 0;
+    const int64_t* slots = nullptr;
+    int64_t capacity = 0;
+    int storage = 0;             // fp8_kv_storage
+    bool per_head = false;       // FP8_KV_PER_HEAD
+    bool pow2 = false;
+    void* cache = nullptr;
+    float* scale_inv = nullptr;
+    fp8_diag* diag = nullptr;
+    hipStream_t stream = nullptr;
+};
+
+struct KvLoadArgs {
+    const void* cache = nullptr;
+    int storage = 0;
+    bool per_head = false;
+    const float* scale_inv = nullptr;
+    int64_t capacity = 0;
+    int heads = 0, head_dim = 0;
+    const int64_t* slots = nullptr;
+    int64_t n_tokens = 0;
+    bool out_bf16 = true;
+    void* out = nullptr;
+    int64_t ld_out = 0;
+    hipStream_t stream = nullptr;
+};
+
 hipError_t launch_quantize(const QuantArgs& a);
+hipError_t launch_kv_store(const KvStoreArgs& a);
+hipError_t launch_kv_load(const KvLoadArgs& a);
 hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream);
 hipError_t launch_history_set_guard(fp8_amax_history* h, float threshold, hipStream_t stream);
 hipError_t launch_zero_words(uint32_t* w, int n, hipStream_t stream);

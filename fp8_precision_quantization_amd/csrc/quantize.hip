@@ -15,6 +15,7 @@
 // convert.
 #include <hip/hip_runtime.h>
 
+#include "cast_unit.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -22,127 +23,7 @@ namespace fp8mi {
 namespace {
 
 constexpr int kThreads = 256;
-
-// ------------------------------------------------------------ data units --
-template <typename InT> struct Pack;
-
-template <> struct Pack<uint16_t> {          // 8 bf16 values packed in 4 words
-    uint32_t w[4];
-    __device__ __forceinline__ float get(int i) const {
-        const uint32_t v = w[i >> 1];
-        return __uint_as_float((i & 1) ? (v & 0xFFFF0000u) : (v << 16));
-    }
-    __device__ __forceinline__ uint32_t abs_max() const {
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t hi = w[i] & 0x7FFF0000u;
-            const uint32_t lo = (w[i] << 16) & 0x7FFF0000u;
-            m = max(m, max(hi, lo));
-        }
-        return m;
-    }
-};
-
-template <> struct Pack<float> {             // 8 fp32 values
-    uint32_t w[8];
-    __device__ __forceinline__ float get(int i) const { return __uint_as_float(w[i]); }
-    __device__ __forceinline__ uint32_t abs_max() const {
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = max(m, w[i] & 0x7FFFFFFFu);
-        return m;
-    }
-};
-
-// Load `nvalid` (0..8) elements starting at x + off; missing ones are 0.
-// `vec`: x + off is 16-byte aligned and the unit is whole.
-template <typename InT>
-__device__ __forceinline__ Pack<InT> load_unit(const InT* __restrict__ x, int64_t off, int nvalid,
-                                               bool vec) {
-    Pack<InT> p;
-    if constexpr (sizeof(InT) == 2) {
-        if (vec && nvalid == 8) {
-            const uint4 r = *reinterpret_cast<const uint4*>(x + off);
-            p.w[0] = r.x; p.w[1] = r.y; p.w[2] = r.z; p.w[3] = r.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = (2 * i < nvalid) ? (uint32_t)x[off + 2 * i] : 0u;
-                const uint32_t hi = (2 * i + 1 < nvalid) ? (uint32_t)x[off + 2 * i + 1] : 0u;
-                p.w[i] = lo | (hi << 16);
-            }
-        }
-    } else {
-        if (vec && nvalid == 8) {
-            const uint4 r0 = *reinterpret_cast<const uint4*>(x + off);
-            const uint4 r1 = *reinterpret_cast<const uint4*>(x + off + 4);
-            p.w[0] = r0.x; p.w[1] = r0.y; p.w[2] = r0.z; p.w[3] = r0.w;
-            p.w[4] = r1.x; p.w[5] = r1.y; p.w[6] = r1.z; p.w[7] = r1.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) p.w[i] = (i < nvalid) ? __float_as_uint(x[off + i]) : 0u;
-        }
-    }
-    return p;
-}
-
-struct Counters {
-    uint32_t sat = 0, nonfinite = 0, under = 0;
-};
-
-// Encode a unit with scale s; optionally count the diagnostics.
-template <int FMT, bool DIAG, typename InT>
-__device__ __forceinline__ uint2 encode_unit(const Pack<InT>& p, float s, Counters& cnt) {
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = p.get(i) * s;
-    uint2 out;
-    out.x = encode4<FMT>(v[0], v[1], v[2], v[3]);
-    out.y = encode4<FMT>(v[4], v[5], v[6], v[7]);
-    // The convert instructions give every NaN one canonical code (E4M3 0xFF,
-    // E5M2 0xFE) whatever its sign, and after the clamp no other input can
-    // produce that byte.  A has-zero-byte test on code ^ canonical finds them
-    // (about one instruction per element); the rare fix-up writes the NaN
-    // code 0x7F with the input's sign.
-    constexpr uint32_t kHwNaN = FMT == kE4M3 ? 0xFFFFFFFFu : 0xFEFEFEFEu;
-    const uint32_t nx = out.x ^ kHwNaN, ny = out.y ^ kHwNaN;
-    if (__builtin_expect(((((nx - 0x01010101u) & ~nx) | ((ny - 0x01010101u) & ~ny)) & 0x80808080u) != 0u, 0)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t bx = __float_as_uint(p.get(i));
-            if ((bx & 0x7FFFFFFFu) > kInfBits) {
-                const uint32_t code = 0x7Fu | ((bx >> 24) & 0x80u);
-                const int sh = 8 * (i & 3);
-                uint32_t& w = (i < 4) ? out.x : out.y;
-                w = (w & ~(0xFFu << sh)) | (code << sh);
-            }
-        }
-    }
-    if constexpr (DIAG) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t ax = __float_as_uint(p.get(i)) & 0x7FFFFFFFu;
-            const uint32_t av = __float_as_uint(v[i]) & 0x7FFFFFFFu;
-            const uint32_t code = ((i < 4 ? out.x : out.y) >> (8 * (i & 3))) & 0xFFu;
-            cnt.nonfinite += (ax >= kInfBits) ? 1u : 0u;
-            cnt.sat += (av > FmtTraits<FMT>::kMaxBits && av <= kInfBits) ? 1u : 0u;
-            cnt.under += (ax != 0u && ax <= kInfBits && (code & 0x7Fu) == 0u) ? 1u : 0u;
-        }
-    }
-    return out;
-}
-
-__device__ __forceinline__ void store_unit(uint8_t* __restrict__ q, int64_t off, int nvalid,
-                                           bool vec, uint2 codes) {
-    if (vec && nvalid == 8) {
-        *reinterpret_cast<uint2*>(q + off) = codes;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < nvalid) q[off + i] = (uint8_t)(((i < 4 ? codes.x : codes.y) >> (8 * (i & 3))) & 0xFFu);
-    }
-}
+using namespace cast;
 
 // Unit u of a [rows x cols] matrix: rows == 1 is the flat (contiguous) case.
 struct UnitGeom {
@@ -195,25 +76,6 @@ __device__ __forceinline__ uint32_t reduce_partials(const uint32_t* __restrict__
     m = max(max(lds[0], lds[1]), max(lds[2], lds[3]));
     __syncthreads();
     return m;
-}
-
-// Diagnostics are the only atomics left, and only when a caller asks for them.
-__device__ __forceinline__ void block_add_diag(Counters c, uint32_t* lds, fp8_diag* diag) {
-    c.sat = wave_sum_u32(c.sat);
-    c.nonfinite = wave_sum_u32(c.nonfinite);
-    c.under = wave_sum_u32(c.under);
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    __syncthreads();
-    if (lane == 0) { lds[4 + w] = c.sat; lds[8 + w] = c.nonfinite; lds[12 + w] = c.under; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t s = lds[4] + lds[5] + lds[6] + lds[7];
-        const uint32_t n = lds[8] + lds[9] + lds[10] + lds[11];
-        const uint32_t u = lds[12] + lds[13] + lds[14] + lds[15];
-        if (s) atomicAdd(&diag->sat_count, s);
-        if (n) atomicAdd(&diag->nonfinite_count, n);
-        if (u) atomicAdd(&diag->underflow_count, u);
-    }
 }
 
 // Delayed scale ([DeepL] 2.3): max over the history window; with an empty

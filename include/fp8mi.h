@@ -19,6 +19,8 @@
  *           an explicit message.
  *   [Swift] "FP8 quantization support in ms-swift" (maplevalley.com.cn/news/
  *           598486): E4M3 / E5M2 and the dynamic per-tensor method.
+ *   [DeepL] 3.1 also: the FP8 KV cache (half of BF16's memory) and the one
+ *           layer whose K cache stayed in BF16.
  *
  * Conventions for every entry point:
  *   - All pointers except the ones documented as host pointers are DEVICE
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP8MI_ABI_VERSION 2
+#define FP8MI_ABI_VERSION 3
 
 typedef enum {
     FP8_OK = 0,
@@ -226,6 +228,52 @@ fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B,
                                 int64_t M, int64_t N, int64_t K,
                                 const float* a_scale_inv, const float* b_scale_inv,
                                 void* C, fp8_out_dtype out_dtype, int64_t ldc, void* stream);
+
+/* FP8 KV cache ([DeepL] 3.1: K and V caches held in FP8 take half of BF16's
+ * memory; K's precision drives the attention scores, V's the mixed output;
+ * keeping one layer's K cache in BF16 removed a long-sequence error, so the
+ * storage is chosen per layer and per tensor).
+ *
+ * One layer's K (or V) cache: `cache` [capacity x heads x head_dim], head_dim
+ * contiguous -- uint8 codes (FP8_KV_E4M3 / FP8_KV_E5M2) or bf16 values
+ * (FP8_KV_BF16, the fallback).  Scales (FP8 storage only), dequantized value
+ * = decode(q) * scale_inv:
+ *   FP8_KV_PER_TOKEN_HEAD: scale_inv [capacity x heads] fp32, written by
+ *     fp8_kv_store: each (token, head) vector of head_dim values is one group
+ *     of the row rule of fp8_quantize (amax, s = fl32(fmax / amax),
+ *     FP8_SCALE_POW2 applies, s_inv = fl32(1 / s));
+ *   FP8_KV_PER_HEAD: scale_inv [heads] fp32, fixed (calibrated) by the
+ *     caller and only read: the cast multiplies by s = fl32(1 / scale_inv[h]),
+ *     saturating what falls outside.  Entries must be finite and > 0.
+ * Token placement: new token t goes to cache row slots[t] (device int64
+ * array of n_tokens; NULL = row t); a slot outside [0, capacity) is padding
+ * and is skipped.  Two new tokens with one slot race.
+ * Requirements (else FP8_ERR_UNSUPPORTED_SHAPE / FP8_ERR_MISALIGNED):
+ * head_dim % 8 == 0 and 8 <= head_dim <= 2048; n_tokens * heads < 2^31;
+ * x, cache and out 16-byte aligned; ld and ld_out multiples of 8. */
+typedef enum { FP8_KV_E4M3 = 0, FP8_KV_E5M2 = 1, FP8_KV_BF16 = 2 } fp8_kv_storage;
+typedef enum { FP8_KV_PER_TOKEN_HEAD = 0, FP8_KV_PER_HEAD = 1 } fp8_kv_scaling;
+
+/* Store n_tokens new vectors: x [n_tokens x (heads*head_dim)] (ld >=
+ * heads*head_dim elements between tokens; head h of token t at
+ * x + t*ld + h*head_dim), fp32 or bf16.  BF16 storage rounds fp32 input to
+ * nearest even and copies bf16 input.  flags: FP8_SCALE_POW2 (per token-head
+ * scales only).  diag: optional counters of the FP8 cast (as fp8_quantize). */
+fp8_status fp8_kv_store(const void* x, fp8_in_dtype in_dtype, int64_t n_tokens, int64_t ld,
+                        int32_t heads, int32_t head_dim, const int64_t* slots,
+                        fp8_kv_storage storage, fp8_kv_scaling scaling, uint32_t flags,
+                        void* cache, float* scale_inv, int64_t capacity, fp8_diag* diag,
+                        void* stream);
+
+/* Gather n_tokens cache rows (slots[t], NULL = row t) and dequantize them:
+ * out row t [heads*head_dim] at out + t*ld_out (ld_out >= heads*head_dim),
+ * y = fl32(decode(q) * scale_inv) as fp32 or rounded to bf16 (nearest even);
+ * a BF16 cache returns its values.  Padding slots leave their out row
+ * untouched. */
+fp8_status fp8_kv_load(const void* cache, fp8_kv_storage storage, fp8_kv_scaling scaling,
+                       const float* scale_inv, int64_t capacity, int32_t heads, int32_t head_dim,
+                       const int64_t* slots, int64_t n_tokens, fp8_out_dtype out_dtype, void* out,
+                       int64_t ld_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,15 @@ Recipe (distribution parameters are standard deviations):
   * wgrad:  per step t in 0..19: dY [8192 x 4096] = 1e-3 * Student-t(df=3)
             from seed 500+t, multiplied by 100 at t = 12; X [8192 x 4096]
             ~ N(0,1) from seed 600+t.  bf16.
+  * kv:     an 8B-style model's attention K/V of one layer: kv_heads 8,
+            head_dim 128, cache capacity 32768 tokens in pages of 16 rows,
+            a prefill chunk of 8192 new tokens.  K [tokens x 8*128] ~ N(0,1)
+            with 4 fixed channels per head (seeded choice) x 16 and every
+            (token, head) vector x a log-uniform gain in [2^-2, 2^2]; V
+            ~ N(0,1).  kv_pages: a seeded permutation of the cache's pages
+            (a page table) mapping logical row i to a cache row; the new
+            tokens are the last 8192 logical rows (a context filled to
+            32768).  Seed 11 (K), 12 (V), 13 (pages).  bf16.
 Values are drawn in float32 (Student-t in float64, then float32) and rounded
 to bf16 with round-to-nearest-even by torch's CPU cast.
 """
@@ -26,7 +35,8 @@ import numpy as np
 
 __all__ = [
     "to_bf16_bits", "bf16_bits_to_f32", "normal", "activation_with_outliers",
-    "student_t", "tiny", "mlp8b", "qkv", "mlp70b", "wgrad_step", "CONFIGS",
+    "student_t", "tiny", "mlp8b", "qkv", "mlp70b", "wgrad_step", "dgrad", "kv_keys", "kv_values",
+    "kv_pages", "CONFIGS",
 ]
 
 CONFIGS = {
@@ -35,6 +45,7 @@ CONFIGS = {
     "qkv": dict(M=8192, N=6144, K=4096),
     "mlp70b": dict(M=2048, N=28672, K=8192),
     "wgrad": dict(tokens=8192, hidden=4096, steps=20, spike_step=12, spike=100.0),
+    "kv": dict(heads=8, head_dim=128, capacity=32768, new_tokens=8192, page=16),
 }
 
 
@@ -123,3 +134,30 @@ def dgrad(M: int = 4096, N: int = 14336, K: int = 4096, seed: int = 7):
     dy = student_t(rg, M, N, 3.0, 1e-3)
     w = normal(rg, N, K, 0.02)
     return to_bf16_bits(dy), to_bf16_bits(w)
+
+
+def kv_keys(tokens: int = 8192, heads: int = 8, head_dim: int = 128, seed: int = 11):
+    """K vectors [tokens x heads*head_dim], bf16 bits: N(0,1), 4 outlier
+    channels per head x 16, a log-uniform per-(token, head) gain in
+    [2^-2, 2^2]."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((tokens, heads, head_dim), dtype=np.float32)
+    for h in range(heads):
+        k[:, h, rng.permutation(head_dim)[:min(4, head_dim)]] *= np.float32(16.0)
+    k *= (2.0 ** rng.uniform(-2.0, 2.0, size=(tokens, heads, 1))).astype(np.float32)
+    return to_bf16_bits(k.reshape(tokens, heads * head_dim))
+
+
+def kv_values(tokens: int = 8192, heads: int = 8, head_dim: int = 128, seed: int = 12):
+    """V vectors [tokens x heads*head_dim], bf16 bits, N(0,1)."""
+    rng = np.random.default_rng(seed)
+    return to_bf16_bits(rng.standard_normal((tokens, heads * head_dim), dtype=np.float32))
+
+
+def kv_pages(capacity: int = 32768, page: int = 16, seed: int = 13):
+    """A page table over the cache: row i of the logical sequence lives in
+    cache row perm[i // page] * page + i % page (int64 [capacity])."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(capacity // page).astype(np.int64)
+    i = np.arange(capacity, dtype=np.int64)
+    return perm[i // page] * page + i % page

@@ -36,7 +36,7 @@ def test_library_is_gfx950_only_code_object():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.fp8_abi_version() == 2
+    assert lib.fp8_abi_version() == 3
     for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARG"), (2, "FP8_ERR_UNSUPPORTED_SHAPE"),
                        (3, "FP8_ERR_MISALIGNED"), (4, "FP8_ERR_UNSUPPORTED_DEVICE"), (5, "FP8_ERR_HIP")]:
         assert L.status_name(code) == name
@@ -107,6 +107,76 @@ def qd(**kw):
 ])
 def test_quantize_dual_validation(kw, status, needle):
     st, msg = qd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def kvs(**kw):
+    a = dict(x=FAKE, in_dt=L.FP8_IN_BF16, n=16, ld=1024, heads=8, hd=128, slots=None, storage=L.FP8_KV_E4M3,
+             scaling=L.FP8_KV_PER_TOKEN_HEAD, flags=0, cache=FAKE, sinv=FAKE, cap=64, diag=None)
+    a.update(kw)
+    st = L.lib().fp8_kv_store(a["x"], a["in_dt"], a["n"], a["ld"], a["heads"], a["hd"], a["slots"], a["storage"],
+                              a["scaling"], a["flags"], a["cache"], a["sinv"], a["cap"], a["diag"], None)
+    return st, L.lib().fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(storage=3), 1, "storage"),
+    (dict(scaling=2), 1, "scaling"),
+    (dict(n=-1), 1, "negative"),
+    (dict(cap=-1), 1, "negative"),
+    (dict(hd=100), 2, "head_dim"),
+    (dict(hd=2056, ld=8 * 2056), 2, "head_dim"),
+    (dict(hd=0), 2, "head_dim"),
+    (dict(n=2 ** 28), 2, "2^31"),
+    (dict(cache=None), 1, "cache is NULL"),
+    (dict(cache=FAKE + 8), 3, "cache"),
+    (dict(sinv=None), 1, "scale_inv is NULL"),
+    (dict(sinv=FAKE + 2), 3, "scale_inv"),
+    (dict(in_dt=4), 1, "in_dtype"),
+    (dict(flags=2), 1, "flag"),
+    (dict(ld=1000), 1, "ld="),
+    (dict(ld=1028), 3, "multiple of 8"),
+    (dict(x=None), 1, "x is NULL"),
+    (dict(x=FAKE + 8), 3, "x must be"),
+    (dict(slots=FAKE + 4), 3, "slots"),
+    (dict(diag=FAKE + 2), 3, "diag"),
+])
+def test_kv_store_validation(kw, status, needle):
+    st, msg = kvs(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_kv_store_bf16_needs_no_scales():
+    """BF16 storage ignores scale_inv: NULL passes validation, which then stops
+    at the device check (no GPU here) or at a later argument."""
+    st, msg = kvs(storage=L.FP8_KV_BF16, sinv=None, x=None)
+    assert st == 1 and "x is NULL" in msg
+
+
+def kvl(**kw):
+    a = dict(cache=FAKE, storage=L.FP8_KV_E4M3, scaling=L.FP8_KV_PER_HEAD, sinv=FAKE, cap=64, heads=8, hd=128,
+             slots=None, n=16, out_dt=L.FP8_OUT_BF16, out=FAKE, ld_out=1024)
+    a.update(kw)
+    st = L.lib().fp8_kv_load(a["cache"], a["storage"], a["scaling"], a["sinv"], a["cap"], a["heads"], a["hd"],
+                             a["slots"], a["n"], a["out_dt"], a["out"], a["ld_out"], None)
+    return st, L.lib().fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(storage=-1), 1, "storage"),
+    (dict(hd=12), 2, "head_dim"),
+    (dict(sinv=None), 1, "scale_inv is NULL"),
+    (dict(out_dt=2), 1, "out_dtype"),
+    (dict(ld_out=512), 1, "ld_out="),
+    (dict(ld_out=1025), 3, "multiple of 8"),
+    (dict(out=None), 1, "out is NULL"),
+    (dict(out=FAKE + 4), 3, "out must be"),
+    (dict(slots=FAKE + 1), 3, "slots"),
+])
+def test_kv_load_validation(kw, status, needle):
+    st, msg = kvl(**kw)
     assert st == status, (st, msg)
     assert needle in msg
 
