@@ -39,9 +39,10 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 # profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None whenever k_gemm changes
 # until the counters are taken again.
 GEMM_TRAFFIC_BYTES = 476156704
-# The same counters for one fp8_kv_load launch of the kv workload (None until
-# taken for the current kernel).
-KV_LOAD_TRAFFIC_BYTES = None
+# The same counters for one fp8_kv_load launch of the kv workload (see
+# profiles/kv_store_gather_8x128_paged_kernel_stats.md); None once k_kv_load
+# changes until they are taken again.
+KV_LOAD_TRAFFIC_BYTES = 104882176
 
 WORKLOADS = {
     "tiny": "tiny: X, W [256 x 256] fp32 N(0,1); per-tensor E4M3; Y fp32",
