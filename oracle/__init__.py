@@ -10,8 +10,10 @@ no FMA contraction).  This module only marshals numpy arrays.  Every function
 cites the passage of the web pages it follows in the C source.
 
 Functions with no pin against something other than themselves: none.  Every
-function here is pinned by ``tests/test_oracle_pins.py`` (library routines,
-closed forms, page constants, exact integer arithmetic, brute force).
+function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_kv_pins.py`` or ``tests/test_oracle_grouped_pins.py``
+(library routines, closed forms, page constants, exact integer arithmetic,
+brute force).
 """
 from __future__ import annotations
 
@@ -378,3 +380,45 @@ def kv_load(cache: np.ndarray, scale_inv: np.ndarray, n: int, storage="e4m3",
                      _p(sl) if sl is not None else None, capacity, int(bool(out_bf16)),
                      _p(out), heads * head_dim)
     return out
+
+
+# ----------------------------------------------------------- grouped GEMM --
+def group_of_rows(offsets, ms) -> np.ndarray:
+    """Route rows to groups ("DeepL bets on FP8" (hmyw.cn) 3.2: the tokens of
+    a batch split into groups by their routing, each group multiplied with
+    its own expert's weight).  READING: group g holds rows [offsets[g],
+    offsets[g+1]) of the token matrix (offsets non-decreasing); a row outside
+    every group gets -1 (no output)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    ms = np.asarray(ms, dtype=np.int64)
+    g = np.searchsorted(offsets, ms, side="right") - 1
+    G = offsets.size - 1
+    inside = (g >= 0) & (g < G)
+    inside &= ms < offsets[np.clip(g + 1, 0, G)]
+    return np.where(inside, g, -1)
+
+
+def grouped_gemm_sampled(A, fa, B, fb, offsets, a_inv, b_inv, ms, ns, exact=False):
+    """Grouped scaled GEMM at sampled outputs: C[m, n] = the scaled GEMM of
+    row m of A with expert g(m)'s weight B[g] ([G, N, K]), its scale b_inv[g]
+    (one per expert, [G]) or b_inv[g, n] ([G, N]); a_inv is one scale or one
+    per row of A.  Each group is the plain sampled GEMM (gemm_sampled, or
+    gemm_exact_sampled with exact=True) on its own rows.  Rows outside every
+    group give NaN."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    G, N, K = B.shape
+    b_inv = np.asarray(b_inv, dtype=np.float32).reshape(G, -1)
+    assert b_inv.shape[1] in (1, N)
+    ms = np.asarray(ms, dtype=np.int64)
+    ns = np.asarray(ns, dtype=np.int64)
+    g = group_of_rows(offsets, ms)
+    y = np.full(ms.size, np.nan, dtype=np.float64 if exact else np.float32)
+    p = np.full(ms.size, np.nan, dtype=np.float64)
+    for gi in np.unique(g[g >= 0]):
+        sel = np.nonzero(g == gi)[0]
+        if exact:
+            y[sel] = gemm_exact_sampled(A, fa, B[gi], fb, a_inv, b_inv[gi], ms[sel], ns[sel])
+        else:
+            y[sel], p[sel] = gemm_sampled(A, fa, B[gi], fb, a_inv, b_inv[gi], ms[sel], ns[sel])
+    return y if exact else (y, p)
