@@ -12,7 +12,7 @@ Prints ONE JSON line.  `value` = whole-step throughput in TFLOP/s
 (2MNK / step time); the GEMM kernel's own TFLOP/s and % of the FP8 MFMA peak,
 and the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.
 
-    python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|dgrad|kv|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|dgrad|moe|kv|tiny]
 
 The kv workload is the memory-bound FP8 KV cache instead (its own JSON line
 in GB/s): one step = one layer's store of a 8192-token chunk of K and V into
@@ -56,6 +56,9 @@ WORKLOADS = {
               "delayed scaling (16-step history), transposed casts; dW = dY^T X [4096 x 4096] fp32"),
     "dgrad": ("dgrad: dY [4096 x 14336] bf16 1e-3*t(3) -> E5M2 delayed, both layouts in one pass; "
               "W [14336 x 4096] bf16 N(0,0.02) -> E4M3 transposed; dX = dY W [4096 x 4096] bf16"),
+    "moe": ("moe: Mixtral-style expert up-projection, 8 experts, 4096 tokens routed top-2 (8192 rows, "
+            "uneven expert loads); routed X [8192 x 4096] bf16 cast row-wise to E4M3 each step; expert W "
+            "[8 x 14336 x 4096] E4M3 per-tensor per expert (cast once); grouped GEMM, Y bf16"),
     "kv": ("kv: one layer of an 8B-style model, 8 KV heads x 128; K (outlier channels) and V bf16 of a "
            "8192-token chunk stored as E4M3 with per-(token, head) scales into 32768-row caches through "
            "a 16-row page table, then all 32768 rows of K and V gathered and dequantized to bf16; "
@@ -121,6 +124,24 @@ class Step:
             xs = [x0] + [x0.clone() for _ in range(copies - 1)]
             ws = [w0] + [w0.clone() for _ in range(copies - 1)]
             self.in_bytes = 2
+        elif workload == "moe":
+            cfg = synth.CONFIGS["moe"]
+            X, offsets, _ = synth.moe_routing(cfg["tokens"], cfg["top_k"], cfg["experts"], cfg["K"])
+            self.M, self.K = X.shape
+            self.N = cfg["N"]
+            E = cfg["experts"]
+            x0 = bf16(X)
+            del X
+            xs = [x0] + [x0.clone() for _ in range(3)]
+            # expert weights: served in FP8, cast once outside the timed steps
+            self.wq_e = torch.empty((E, self.N, self.K), dtype=torch.uint8, device=dev)
+            self.sw_e = torch.empty(E, dtype=torch.float32, device=dev)
+            for e in range(E):
+                fp8.quantize(bf16(synth.moe_weight(e, self.N, self.K)), "e4m3", "tensor", out=self.wq_e[e],
+                             scale_inv_out=self.sw_e[e:e + 1].view(1, 1))
+            self.offs = torch.from_numpy(offsets.astype(np.int32)).to(dev)
+            ws = [self.wq_e]
+            self.in_bytes = 2
         elif workload == "dgrad":
             dy, w = synth.dgrad()
             self.M, self.K = dy.shape            # tokens, layer outputs (the reduction)
@@ -157,19 +178,19 @@ class Step:
             self.xq = T.empty((M, K), dtype=T.uint8, device=dev)
             self.wq = T.empty((N, K), dtype=T.uint8, device=dev)
         gx = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "1x128", "wgrad": "tensor",
-              "dgrad": "tensor"}[workload]
+              "dgrad": "tensor", "moe": "row"}[workload]
         gw = {"tiny": "tensor", "mlp8b": "tensor", "qkv": "row", "mlp70b": "128x128", "wgrad": "tensor",
-              "dgrad": "tensor"}[workload]
+              "dgrad": "tensor", "moe": "tensor"}[workload]
         self.gx, self.gw = gx, gw
         rows_x, cols_x = xs[0].shape
-        rows_w, cols_w = ws[0].shape
+        rows_w, cols_w = ws[0].shape[-2:]
         self.sx = T.empty(fp8.group_grid(gx, rows_x, cols_x), dtype=T.float32, device=dev)
         self.ax = T.empty_like(self.sx)
         self.sw = T.empty(fp8.group_grid(gw, rows_w, cols_w), dtype=T.float32, device=dev)
         self.aw = T.empty_like(self.sw)
         out_dt = T.float32 if workload in ("tiny", "wgrad") else T.bfloat16
         self.y = T.empty((M, N), dtype=out_dt, device=dev)
-        self.elems = xs[0].numel() + ws[0].numel()
+        self.elems = xs[0].numel() + (0 if workload == "moe" else ws[0].numel())
 
     def quantize(self):
         fp8, i = self.fp8, self.i
@@ -184,6 +205,8 @@ class Step:
                          scale_inv_out=self.sx, amax_out=self.ax)
             fp8.quantize(w, "e4m3", "tensor", history=self.h_x, transpose=True, out=self.wq,
                          scale_inv_out=self.sw, amax_out=self.aw)
+        elif self.workload == "moe":
+            fp8.quantize(x, "e4m3", "row", out=self.xq, scale_inv_out=self.sx, amax_out=self.ax)
         else:
             pow2 = self.workload == "qkv"
             fp8.quantize(x, "e4m3", self.gx, pow2=pow2, out=self.xq, scale_inv_out=self.sx, amax_out=self.ax)
@@ -193,6 +216,8 @@ class Step:
         fp8 = self.fp8
         if self.workload == "mlp70b":
             fp8.blockscaled_gemm(self.xq, self.wq, self.sx, self.sw, out=self.y)
+        elif self.workload == "moe":
+            fp8.grouped_gemm(self.xq, self.wq_e, self.offs, self.sx.reshape(-1), self.sw_e, out=self.y)
         elif self.workload in ("wgrad", "dgrad"):
             fp8.scaled_gemm(self.xq, self.wq, self.sx.reshape(-1), self.sw.reshape(-1), "e5m2", "e4m3", out=self.y)
         else:

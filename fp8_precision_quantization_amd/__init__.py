@@ -22,7 +22,7 @@ from ._lib import Fp8Error  # noqa: F401
 
 __all__ = ["quantize", "quantize_dual", "amax", "scaled_gemm", "blockscaled_gemm", "AmaxHistory", "Diag",
            "QuantResult", "Fp8Error", "FORMATS", "GRANULARITIES", "group_grid", "kv_store", "kv_load",
-           "KVTensorCache", "KVCache"]
+           "KVTensorCache", "KVCache", "grouped_gemm"]
 
 FORMATS = {"e4m3": _lib.FP8_E4M3, "e5m2": _lib.FP8_E5M2}
 GRANULARITIES = {"tensor": _lib.FP8_GRAN_TENSOR, "row": _lib.FP8_GRAN_ROW,
@@ -260,6 +260,46 @@ def blockscaled_gemm(a_q: torch.Tensor, b_q: torch.Tensor, a_scale_inv: torch.Te
                                          a_scale_inv.data_ptr(), b_scale_inv.data_ptr(), out.data_ptr(),
                                          _out_dtype(out.dtype), ldc, _stream(a_q.device))
     _lib.check(st, "fp8_blockscaled_gemm")
+    return out
+
+
+# ------------------------------------------------------------ grouped GEMM --
+def grouped_gemm(a_q: torch.Tensor, b_q: torch.Tensor, group_offsets: torch.Tensor, a_scale_inv: torch.Tensor,
+                 b_scale_inv: torch.Tensor, fa="e4m3", fb="e4m3", out_dtype=torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MoE grouped GEMM: rows [offs[g], offs[g+1]) of a_q [M, K] times expert
+    g's b_q[g] ([G, N, K] uint8 codes): C[m] = (A_q[m] . B_q[g]^T) * sa * sb_g.
+    group_offsets: int32 device tensor [G+1]; a_scale_inv: 1 or M values;
+    b_scale_inv: G (one per expert) or G*N values.  Rows in no group are not
+    written (out is allocated uninitialized when not given)."""
+    M, K, lda = _matrix(a_q, "a_q")
+    if b_q.dim() != 3 or not b_q.is_cuda or b_q.stride(2) != 1:
+        raise ValueError("b_q must be a [G, N, K] device tensor with contiguous rows")
+    G, N, K2 = b_q.shape
+    if K != K2:
+        raise ValueError("K mismatch: %d vs %d" % (K, K2))
+    if (group_offsets.dtype != torch.int32 or not group_offsets.is_cuda or group_offsets.numel() != G + 1
+            or not group_offsets.is_contiguous()):
+        raise ValueError("group_offsets must be a contiguous int32 device tensor of G+1=%d entries" % (G + 1))
+    ldb = b_q.stride(1) if N > 1 else K
+    gstride = b_q.stride(0) if G > 1 else N * ldb
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    ldc = max(out.stride(0), 1) if out.shape[0] > 1 else max(N, 1)
+    a_row = 0 if a_scale_inv.numel() == 1 else 1
+    if a_row and a_scale_inv.numel() != M:
+        raise ValueError("a_scale_inv must hold 1 or M=%d values" % M)
+    if b_scale_inv.numel() == G:
+        b_row = 0
+    elif b_scale_inv.numel() == G * N:
+        b_row = 1
+    else:
+        raise ValueError("b_scale_inv must hold G=%d or G*N=%d values" % (G, G * N))
+    st = _lib.lib().fp8_grouped_gemm(a_q.data_ptr(), _fmt(fa), lda, b_q.data_ptr(), _fmt(fb), ldb, gstride, M, N, K,
+                                     G, group_offsets.data_ptr(), a_scale_inv.data_ptr(), a_row,
+                                     b_scale_inv.data_ptr(), b_row, out.data_ptr(), _out_dtype(out.dtype), ldc,
+                                     _stream(a_q.device))
+    _lib.check(st, "fp8_grouped_gemm")
     return out
 
 

@@ -30,6 +30,7 @@ FP8_TRANSPOSE_OUT = 2
 FP8_SPIKE_GUARD = 4
 FP8_KV_E4M3, FP8_KV_E5M2, FP8_KV_BF16 = 0, 1, 2
 FP8_KV_PER_TOKEN_HEAD, FP8_KV_PER_HEAD = 0, 1
+FP8_GROUPED_MAX_TILES = 1983
 HISTORY_BYTES = 128
 DIAG_BYTES = 16
 
@@ -52,6 +53,8 @@ SIGNATURES = {
     "fp8_scaled_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,
                                _P, _INT, _I64, _P]),
     "fp8_blockscaled_gemm": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _INT, _I64, _P]),
+    "fp8_grouped_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I32, _P, _P, _INT,
+                                _P, _INT, _P, _INT, _I64, _P]),
     "fp8_kv_store": (_INT, [_P, _INT, _I64, _I64, _I32, _I32, _P, _INT, _INT, _U32, _P, _P, _I64, _P, _P]),
     "fp8_kv_load": (_INT, [_P, _INT, _INT, _P, _I64, _I32, _I32, _P, _I64, _INT, _P, _I64, _P]),
 }

@@ -359,6 +359,47 @@ fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B,
     return launch_result(fp8mi::launch_blockscaled_gemm(g), "fp8_blockscaled_gemm");
 }
 
+static_assert(FP8_GROUPED_MAX_TILES == fp8mi::kGroupTableTiles, "grouped GEMM table size");
+
+fp8_status fp8_grouped_gemm(const uint8_t* A, fp8_format fa, int64_t lda, const uint8_t* B, fp8_format fb,
+                            int64_t ldb, int64_t b_group_stride, int64_t M, int64_t N, int64_t K, int32_t groups,
+                            const int32_t* group_offsets, const float* a_scale_inv, int a_per_row,
+                            const float* b_scale_inv, int b_per_row, void* C, fp8_out_dtype out_dtype, int64_t ldc,
+                            void* stream) {
+    if ((fa != FP8_E4M3 && fa != FP8_E5M2) || (fb != FP8_E4M3 && fb != FP8_E5M2))
+        return fail(FP8_ERR_INVALID_ARG, "formats fa=%d fb=%d must be FP8_E4M3 or FP8_E5M2", (int)fa, (int)fb);
+    if ((a_per_row != 0 && a_per_row != 1) || (b_per_row != 0 && b_per_row != 1))
+        return fail(FP8_ERR_INVALID_ARG, "a_per_row and b_per_row must be 0 or 1");
+    fp8_status st = check_gemm_common(A, lda, B, ldb, M, N, K, a_scale_inv, b_scale_inv, C, out_dtype, ldc);
+    if (st != FP8_OK) return st;
+    if (groups < 1) return fail(FP8_ERR_INVALID_ARG, "groups=%d must be >= 1", (int)groups);
+    if (group_offsets == nullptr) return fail(FP8_ERR_INVALID_ARG, "group_offsets is NULL");
+    if (!is_aligned(group_offsets, 4)) return fail(FP8_ERR_MISALIGNED, "group_offsets must be 4-byte aligned");
+    if (K > 0 && N > 0) {
+        if (b_group_stride < (N - 1) * ldb + K)
+            return fail(FP8_ERR_INVALID_ARG, "b_group_stride=%lld must be >= (N-1)*ldb + K = %lld",
+                        (long long)b_group_stride, (long long)((N - 1) * ldb + K));
+        if (b_group_stride % 16 != 0)
+            return fail(FP8_ERR_MISALIGNED, "b_group_stride=%lld must be a multiple of 16", (long long)b_group_stride);
+    }
+    if ((M + 255) / 256 + groups > FP8_GROUPED_MAX_TILES)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "ceil(M/256) + groups = %lld exceeds FP8_GROUPED_MAX_TILES (%d)",
+                    (long long)((M + 255) / 256 + groups), FP8_GROUPED_MAX_TILES);
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    uint32_t* scratch = nullptr;
+    if ((st = get_scratch((hipStream_t)stream, &scratch)) != FP8_OK) return st;
+    fp8mi::GemmArgs g;
+    g.A = A; g.B = B; g.fa = fa; g.fb = fb; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N; g.K = K;
+    g.sa = a_scale_inv; g.sb = b_scale_inv; g.sa_per_row = a_per_row; g.sb_per_row = b_per_row;
+    g.C = C; g.out_bf16 = out_dtype == FP8_OUT_BF16; g.ldc = ldc; g.stream = (hipStream_t)stream;
+    g.num_cus = cus; g.groups = groups; g.group_offsets = group_offsets; g.b_group_stride = b_group_stride;
+    g.scratch = scratch;
+    return launch_result(fp8mi::launch_grouped_gemm(g), "fp8_grouped_gemm");
+}
+
 // Shape and alignment rules shared by fp8_kv_store and fp8_kv_load.
 static fp8_status check_kv_common(const void* cache, int storage, int scaling, const void* scale_inv,
                                   int64_t capacity, int32_t heads, int32_t head_dim, int64_t n_tokens) {

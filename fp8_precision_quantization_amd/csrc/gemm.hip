@@ -47,6 +47,7 @@
 //     concurrently running tiles share A and B panels in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "device_common.hpp"
@@ -79,6 +80,10 @@ struct GemmParams {
     int tiles_m, tiles_n;
     int group_m;
     int vec_out;          // C rows allow 16-byte vector stores
+    // grouped GEMM: tile table (header, then one entry per 256-row tile of a
+    // group: expert, first row, end row of the group) and expert stride of B
+    const int4* gtab;
+    int64_t b_gstride;
 };
 
 template <int FX, int FY>
@@ -558,21 +563,52 @@ __device__ __forceinline__ void epilogue_slot(const GemmParams& p, const v16f (&
 // Linear tile of block b in round r (persistent grid of G blocks): the
 // blocks of one round take G consecutive tiles, each XCD a contiguous range
 // of them; the linear index is then grouped along M as in tile_coords.
-__device__ __forceinline__ bool tile_of_round(const GemmParams& p, int r, int& tm, int& tn) {
+__device__ __forceinline__ bool tile_of_round(const GemmParams& p, int tiles_m, int group_m, int r, int& tm,
+                                              int& tn) {
     const int G = gridDim.x;
     int b = blockIdx.x;
     if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
     const int t = r * G + b;
-    if (t >= p.tiles_m * p.tiles_n) return false;
-    const int per_group = p.group_m * p.tiles_n;
+    if (t >= tiles_m * p.tiles_n) return false;
+    const int per_group = group_m * p.tiles_n;
     const int group = t / per_group;
-    const int first_m = group * p.group_m;
-    const int gsize = min(p.tiles_m - first_m, p.group_m);
+    const int first_m = group * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
     const int in_group = t - group * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
     return true;
 }
+
+// Where the rows, the B operand and the B scales of M-tile tm come from.
+// Plain: rows [256 tm, M) of A, B and sb as given.  Grouped: the table entry
+// of tm names its expert g and its rows [m0, m_end) (at most 256 of them,
+// m_end the end of the group), B is expert g's matrix and sb its scale (one
+// per expert, or the expert's N row scales).
+template <bool GROUPED>
+struct TileRef {                  // plain: nothing to carry
+    __device__ __forceinline__ void load(const GemmParams&, int) {}
+    __device__ __forceinline__ int m0(const GemmParams&, int tm) const { return tm * 256; }
+    __device__ __forceinline__ int m_end(const GemmParams& p) const { return p.M; }
+    __device__ __forceinline__ const uint8_t* B(const GemmParams& p) const { return p.B; }
+};
+
+template <>
+struct TileRef<true> {
+    int row0, end;
+    const uint8_t* b;
+    const float* sb;
+    __device__ __forceinline__ void load(const GemmParams& p, int tm) {
+        const int4 e = p.gtab[1 + tm];
+        row0 = e.y;
+        end = e.z;
+        b = p.B + (int64_t)e.x * p.b_gstride;
+        sb = p.sb + (p.sb_row ? (int64_t)e.x * p.N : (int64_t)e.x);
+    }
+    __device__ __forceinline__ int m0(const GemmParams&, int) const { return row0; }
+    __device__ __forceinline__ int m_end(const GemmParams&) const { return end; }
+    __device__ __forceinline__ const uint8_t* B(const GemmParams&) const { return b; }
+};
 
 // Persistent scaled GEMM over 256 x 256 tiles with 128-byte K stages.
 // Stages are numbered globally over this block's tiles; the ring schedule
@@ -583,8 +619,15 @@ __device__ __forceinline__ bool tile_of_round(const GemmParams& p, int r, int& t
 // tile's first stage: the first odd-step wait of a tile counts them as in
 // flight (vector-memory operations complete in issue order).
 // Needs K > 256 (three stages) when a block runs more than one tile.
-template <int FA, int FB, bool OUT_BF16, bool RAGGED>
+// GROUPED: the M-tiles are those of the grouped GEMM's table, whose size
+// only the device knows.
+template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
+    int tiles_m = p.tiles_m, group_m = p.group_m;
+    if constexpr (GROUPED) {     // the table's size, within the host's bound (p.tiles_m)
+        tiles_m = min(p.gtab[0].x, p.tiles_m);
+        group_m = tiles_m < 4 ? tiles_m : 4;
+    }
     using E = Epi2<OUT_BF16>;
     constexpr int kVm2 = 8 + E::kStores < 63 ? 8 + E::kStores : 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -598,13 +641,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
     auto ptr = [&](int slot) { return g_ring + slot * kSlot2; };
 
     int tm, tn;
-    if (!tile_of_round(p, 0, tm, tn)) return;
+    if (!tile_of_round(p, tiles_m, group_m, 0, tm, tn)) return;
     int tm_n = 0, tn_n = 0;
-    bool has_next = tile_of_round(p, 1, tm_n, tn_n);
+    bool has_next = tile_of_round(p, tiles_m, group_m, 1, tm_n, tn_n);
+    TileRef<GROUPED> cur, nxt;
+    cur.load(p, tm);
+    if (has_next) nxt.load(p, tm_n);
 
     Dma2 da, db;
-    da.init(p.A, p.lda, tm * 256, p.M, wave);
-    db.init(p.B, p.ldb, tn * 256, p.N, wave);
+    da.init(p.A, p.lda, cur.m0(p, tm), cur.m_end(p), wave);
+    db.init(cur.B(p), p.ldb, tn * 256, p.N, wave);
 
     v16f acc[4][4];
 #pragma unroll
@@ -635,7 +681,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
                        // A(g+1) in sl+2, B(g+1) in sl+3, A(g+2) in sl+4, B(g+2) in sl
     int first_vm = 1;  // the first odd-step wait of a tile: 8, or 8 + the previous epilogue's stores
     for (int r = 0;; ++r) {
-        const int m0 = tm * 256, n0 = tn * 256;
+        const int m0 = cur.m0(p, tm), n0 = tn * 256;
         int s = 0;
         // stages whose DMA target (s + 2) is in this tile
         for (; s + 2 < nks; ++s) {
@@ -658,8 +704,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
         // every DMA of this tile is issued: point the descriptors at the next
         // tile, whose stages 0 and 1 are issued by this tile's last two stages
         if (has_next) {
-            da.init(p.A, p.lda, tm_n * 256, p.M, wave);
-            db.init(p.B, p.ldb, tn_n * 256, p.N, wave);
+            da.init(p.A, p.lda, nxt.m0(p, tm_n), nxt.m_end(p), wave);
+            db.init(nxt.B(p), p.ldb, tn_n * 256, p.N, wave);
         }
         for (; s < nks; ++s) {
             const int s1 = wrap(sl + 1), s2 = wrap(sl + 2), s3 = wrap(sl + 3), s4 = wrap(sl + 4);
@@ -673,12 +719,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
             sl = s2;
         }
         // B(last)'s slot is free until the next tile's first even step
-        const bool interior = p.vec_out && m0 + 256 <= p.M && n0 + 256 <= p.N;
-        epilogue_slot<OUT_BF16>(p, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+        const bool interior = p.vec_out && m0 + 256 <= cur.m_end(p) && n0 + 256 <= p.N;
+        if constexpr (GROUPED) {
+            GemmParams pt = p;           // the tile's rows end at its group's end
+            pt.M = cur.end;
+            pt.sb = cur.sb;
+            epilogue_slot<OUT_BF16>(pt, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+        } else {
+            epilogue_slot<OUT_BF16>(p, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+        }
         if (!has_next) break;
         first_vm = interior ? 2 : 1;
         tm = tm_n; tn = tn_n;
-        has_next = tile_of_round(p, r + 2, tm_n, tn_n);
+        if constexpr (GROUPED) cur = nxt;
+        has_next = tile_of_round(p, tiles_m, group_m, r + 2, tm_n, tn_n);
+        if (has_next) nxt.load(p, tm_n);
         __syncthreads();   // every wave is done with the staging slot
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -929,6 +984,8 @@ GemmParams make_params(const GemmArgs& a, int bm, int bn) {
     p.group_m = p.tiles_m < 4 ? p.tiles_m : 4;
     const int esz = a.out_bf16 ? 2 : 4;
     p.vec_out = ((a.ldc * esz) % 16 == 0) && ((uintptr_t)a.C % 16 == 0);   // 16-byte row chunks
+    p.gtab = nullptr;
+    p.b_gstride = 0;
     return p;
 }
 
@@ -942,8 +999,9 @@ hipError_t launch_scaled_typed(const GemmArgs& a) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
-        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false>, lds_scaled<OUT_BF16>());
-        if (attr_err == hipSuccess) attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true>, lds_scaled<OUT_BF16>());
+        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false>, lds_scaled<OUT_BF16>());
+        if (attr_err == hipSuccess)
+            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, false>, lds_scaled<OUT_BF16>());
     });
     if (attr_err != hipSuccess) return attr_err;
     const GemmParams p = make_params(a, 256, 256);
@@ -951,11 +1009,90 @@ hipError_t launch_scaled_typed(const GemmArgs& a) {
     if (grid > (unsigned)a.num_cus && a.K > 2 * kBK2) grid = (unsigned)a.num_cus;
     if (grid == 0) return hipSuccess;
     if (a.K % kBK2 != 0)
-        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true>), dim3(grid), dim3(kGemmThreads), lds_scaled<OUT_BF16>(),
-                           a.stream, p);
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, false>), dim3(grid), dim3(kGemmThreads),
+                           lds_scaled<OUT_BF16>(), a.stream, p);
     else
-        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false>), dim3(grid), dim3(kGemmThreads), lds_scaled<OUT_BF16>(),
-                           a.stream, p);
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false, false>), dim3(grid), dim3(kGemmThreads),
+                           lds_scaled<OUT_BF16>(), a.stream, p);
+    return hipGetLastError();
+}
+
+// Grouped GEMM ([DeepL bets on FP8] 3.2, MoE): one block builds the table of
+// 256-row tiles of every group from the device offsets (clamped to [0, M];
+// an end below its start makes the group empty; tiles past the table's
+// capacity are dropped, which only offsets that are not non-decreasing can
+// cause); the persistent GEMM then walks the table.
+__global__ __launch_bounds__(256) void k_group_table(const int32_t* __restrict__ offsets, int groups, int M,
+                                                     int* __restrict__ tab) {
+    __shared__ int part[256];
+    const int t = threadIdx.x;
+    const int per = (groups + 255) / 256;
+    const int g0 = min(groups, t * per), g1 = min(groups, g0 + per);
+    auto bounds = [&](int g, int& lo, int& hi) {
+        lo = min(max(offsets[g], 0), M);
+        hi = max(min(max(offsets[g + 1], 0), M), lo);
+    };
+    int cnt = 0;
+    for (int g = g0; g < g1; ++g) {
+        int lo, hi;
+        bounds(g, lo, hi);
+        cnt += (hi - lo + 255) / 256;
+    }
+    part[t] = cnt;
+    __syncthreads();
+    if (t == 0) {                     // exclusive prefix over 256 partial counts
+        int run = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int c = part[i];
+            part[i] = run;
+            run += c;
+        }
+        tab[0] = min(run, kGroupTableTiles);
+        tab[1] = tab[2] = tab[3] = 0;
+    }
+    __syncthreads();
+    int e = part[t];
+    for (int g = g0; g < g1; ++g) {
+        int lo, hi;
+        bounds(g, lo, hi);
+        for (int m = lo; m < hi; m += 256, ++e) {
+            if (e < kGroupTableTiles) {
+                int* w = tab + 4 + 4 * e;
+                w[0] = g; w[1] = m; w[2] = hi; w[3] = 0;
+            }
+        }
+    }
+}
+
+template <int FA, int FB, bool OUT_BF16>
+hipError_t launch_grouped_typed(const GemmArgs& a) {
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [&] {
+        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, true>, lds_scaled<OUT_BF16>());
+        if (attr_err == hipSuccess)
+            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, true>, lds_scaled<OUT_BF16>());
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    int* tab = reinterpret_cast<int*>(a.scratch + kScratchGroupTable);
+    hipLaunchKernelGGL(k_group_table, dim3(1), dim3(256), 0, a.stream, a.group_offsets, a.groups, (int)a.M, tab);
+    GemmParams p = make_params(a, 256, 256);
+    p.gtab = reinterpret_cast<const int4*>(tab);
+    p.b_gstride = a.b_group_stride;
+    // at most ceil(M / 256) + groups M-tiles (non-decreasing offsets), never
+    // more than the table holds; the kernel takes no more than this many, so
+    // that with K <= 256 (no persistent loop) every block runs one tile
+    const int64_t mt = std::min<int64_t>((a.M + 255) / 256 + a.groups, kGroupTableTiles);
+    p.tiles_m = (int)mt;
+    int64_t grid = mt * p.tiles_n;
+    if (grid > a.num_cus && a.K > 2 * kBK2) grid = a.num_cus;
+    if (grid == 0) return hipGetLastError();
+    if (a.K % kBK2 != 0)
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, true>), dim3((unsigned)grid), dim3(kGemmThreads),
+                           lds_scaled<OUT_BF16>(), a.stream, p);
+    else
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false, true>), dim3((unsigned)grid), dim3(kGemmThreads),
+                           lds_scaled<OUT_BF16>(), a.stream, p);
     return hipGetLastError();
 }
 
@@ -980,6 +1117,18 @@ hipError_t launch_scaled_gemm(const GemmArgs& a) {
 #define FP8MI_FMT_CASE(FA, FB)                                                              \
     if (a.fa == FA && a.fb == FB)                                                           \
         return a.out_bf16 ? launch_scaled_typed<FA, FB, true>(a) : launch_scaled_typed<FA, FB, false>(a);
+    FP8MI_FMT_CASE(0, 0)
+    FP8MI_FMT_CASE(1, 0)
+    FP8MI_FMT_CASE(0, 1)
+    FP8MI_FMT_CASE(1, 1)
+#undef FP8MI_FMT_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& a) {
+#define FP8MI_FMT_CASE(FA, FB)                                                              \
+    if (a.fa == FA && a.fb == FB)                                                           \
+        return a.out_bf16 ? launch_grouped_typed<FA, FB, true>(a) : launch_grouped_typed<FA, FB, false>(a);
     FP8MI_FMT_CASE(0, 0)
     FP8MI_FMT_CASE(1, 0)
     FP8MI_FMT_CASE(0, 1)

@@ -46,6 +46,12 @@ struct GemmArgs {
     int64_t ldc = 0;
     hipStream_t stream = nullptr;
     int num_cus = 256;
+    // grouped GEMM: B holds `groups` expert matrices, b_group_stride elements
+    // apart; group g is rows [group_offsets[g], group_offsets[g+1]) of A and C
+    int groups = 0;
+    const int32_t* group_offsets = nullptr;
+    int64_t b_group_stride = 0;
+    uint32_t* scratch = nullptr;
 };
 
 struct KvStoreArgs {
@@ -87,9 +93,15 @@ hipError_t launch_history_set_guard(fp8_amax_history* h, float threshold, hipStr
 hipError_t launch_zero_words(uint32_t* w, int n, hipStream_t stream);
 hipError_t launch_scaled_gemm(const GemmArgs& a);
 hipError_t launch_blockscaled_gemm(const GemmArgs& a);
+hipError_t launch_grouped_gemm(const GemmArgs& a);
 
 // Per-(device, stream) scratch the library allocates once (uint32 words).
 constexpr int kScratchWords = 16384;
+// Words [kScratchGroupTable, kScratchWords) hold the grouped GEMM's table of
+// 256-row tiles (a 4-word header, then 4 words per tile); the quantize
+// kernels use the words below it.
+constexpr int kScratchGroupTable = 8448;
+constexpr int kGroupTableTiles = (kScratchWords - kScratchGroupTable - 4) / 4;
 
 // Unit count of the element-wise tensor kernels must fit in 31 bits.
 constexpr int64_t kMaxUnits = (int64_t(1) << 31) - 1;

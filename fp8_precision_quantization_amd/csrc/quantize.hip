@@ -568,7 +568,7 @@ constexpr int kScratchDiag = 8192;           // fp8_diag of a guarded delayed ca
 constexpr int64_t kMaxCastBlocks = 4096;
 constexpr int64_t kMaxAmaxBlocks = 1024;   // a stream needs about 4 workgroups per CU (measured)
 static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchDiag, "scratch layout");
-static_assert(kScratchDiag + 4 <= kScratchWords, "scratch too small");
+static_assert(kScratchDiag + 4 <= kScratchGroupTable, "scratch layout: the grouped GEMM's table follows");
 
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
     int64_t b = (work_items + per_block - 1) / per_block;

@@ -20,16 +20,17 @@
  *   [Swift] "FP8 quantization support in ms-swift" (maplevalley.com.cn/news/
  *           598486): E4M3 / E5M2 and the dynamic per-tensor method.
  *   [DeepL] 3.1 also: the FP8 KV cache (half of BF16's memory) and the one
- *           layer whose K cache stayed in BF16.
+ *           layer whose K cache stayed in BF16; 3.2: MoE's grouped GEMM.
  *
  * Conventions for every entry point:
  *   - All pointers except the ones documented as host pointers are DEVICE
  *     pointers on the current HIP device.  The caller owns every input and
  *     output buffer.  The library never synchronizes the stream; its only
  *     allocation is a 64 KiB scratch buffer per (device, stream) pair, made
- *     with hipMalloc by the first per-tensor fp8_quantize / fp8_amax call on
- *     that pair and kept until the process ends (calls on one stream are
- *     ordered and share it; different streams never share one).
+ *     with hipMalloc by the first per-tensor fp8_quantize / fp8_amax call or
+ *     fp8_grouped_gemm call on that pair and kept until the process ends
+ *     (calls on one stream are ordered and share it; different streams never
+ *     share one).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call is asynchronous: it returns after host-side validation and
  *     the kernel launches.  A fault inside a kernel surfaces at the caller's
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FP8MI_ABI_VERSION 3
+#define FP8MI_ABI_VERSION 4
 
 typedef enum {
     FP8_OK = 0,
@@ -228,6 +229,35 @@ fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B,
                                 int64_t M, int64_t N, int64_t K,
                                 const float* a_scale_inv, const float* b_scale_inv,
                                 void* C, fp8_out_dtype out_dtype, int64_t ldc, void* stream);
+
+/* Grouped scaled FP8 GEMM for mixture-of-experts layers ([DeepL] 3.2: each
+ * token activates a few experts, so the batch's tokens are grouped by their
+ * routing and every group is multiplied with its own expert's weight; FP8
+ * halves the expert weights).  For every row m of group g, i.e.
+ * group_offsets[g] <= m < group_offsets[g+1]:
+ *   C[m,n] = (sum_k decode(A[m,k]) * decode(B_g[n,k])) * fl32(sa(m) * sb_g(n))
+ * with the arithmetic of fp8_scaled_gemm.  A: uint8 [M x K] codes of format
+ * fa (lda), the tokens sorted by group.  B: `groups` expert matrices, each
+ * uint8 [N x K] of format fb with row stride ldb, expert g at
+ * B + g * b_group_stride (b_group_stride >= (N-1)*ldb + K, a multiple of 16).
+ * group_offsets: DEVICE int32 [groups + 1], non-decreasing, within [0, M]
+ * (read on the device: out-of-range offsets are clamped, and decreasing ones
+ * leave the overlapping rows' values unspecified, never an out-of-range
+ * access).  Rows in no group are not written.  sa = a_scale_inv[0]
+ * (a_per_row == 0) or a_scale_inv[m] ([M]); sb_g(n) = b_scale_inv[g]
+ * (b_per_row == 0, one scale per expert, [groups]) or b_scale_inv[g*N + n]
+ * ([groups x N]).  C: [M x N] fp32 or bf16, leading dimension ldc.
+ * Requirements as fp8_scaled_gemm, plus groups >= 1 and
+ * ceil(M / 256) + groups <= FP8_GROUPED_MAX_TILES (the size of the table of
+ * 256-row tiles kept in the per-stream scratch), else
+ * FP8_ERR_UNSUPPORTED_SHAPE. */
+#define FP8_GROUPED_MAX_TILES 1983
+fp8_status fp8_grouped_gemm(const uint8_t* A, fp8_format fa, int64_t lda,
+                            const uint8_t* B, fp8_format fb, int64_t ldb, int64_t b_group_stride,
+                            int64_t M, int64_t N, int64_t K, int32_t groups, const int32_t* group_offsets,
+                            const float* a_scale_inv, int a_per_row,
+                            const float* b_scale_inv, int b_per_row,
+                            void* C, fp8_out_dtype out_dtype, int64_t ldc, void* stream);
 
 /* FP8 KV cache ([DeepL] 3.1: K and V caches held in FP8 take half of BF16's
  * memory; K's precision drives the attention scores, V's the mixed output;

@@ -26,6 +26,13 @@ Recipe (distribution parameters are standard deviations):
             (a page table) mapping logical row i to a cache row; the new
             tokens are the last 8192 logical rows (a context filled to
             32768).  Seed 11 (K), 12 (V), 13 (pages).  bf16.
+  * moe:    a Mixtral-style expert up-projection: 8 experts, hidden 4096,
+            ffn 14336, 4096 tokens each routed to its top-2 experts of
+            seeded logits N(0,1) + log(p_e), p ~ Dirichlet(2) (uneven
+            expert loads).  X [4096 x 4096] like mlp8b's X; the routed rows
+            (each token once per chosen expert) are sorted by expert, group
+            offsets [9]; W_e [14336 x 4096] ~ N(0, 0.02) from seed 100+e.
+            Seed 8.  bf16.
 Values are drawn in float32 (Student-t in float64, then float32) and rounded
 to bf16 with round-to-nearest-even by torch's CPU cast.
 """
@@ -36,7 +43,7 @@ import numpy as np
 __all__ = [
     "to_bf16_bits", "bf16_bits_to_f32", "normal", "activation_with_outliers",
     "student_t", "tiny", "mlp8b", "qkv", "mlp70b", "wgrad_step", "dgrad", "kv_keys", "kv_values",
-    "kv_pages", "CONFIGS",
+    "kv_pages", "moe_routing", "moe_weight", "CONFIGS",
 ]
 
 CONFIGS = {
@@ -46,6 +53,7 @@ CONFIGS = {
     "mlp70b": dict(M=2048, N=28672, K=8192),
     "wgrad": dict(tokens=8192, hidden=4096, steps=20, spike_step=12, spike=100.0),
     "kv": dict(heads=8, head_dim=128, capacity=32768, new_tokens=8192, page=16),
+    "moe": dict(tokens=4096, top_k=2, experts=8, N=14336, K=4096),
 }
 
 
@@ -161,3 +169,26 @@ def kv_pages(capacity: int = 32768, page: int = 16, seed: int = 13):
     perm = rng.permutation(capacity // page).astype(np.int64)
     i = np.arange(capacity, dtype=np.int64)
     return perm[i // page] * page + i % page
+
+
+def moe_routing(tokens: int = 4096, top_k: int = 2, experts: int = 8, K: int = 4096, seed: int = 8):
+    """(X_routed bf16 bits [tokens*top_k x K], offsets int64 [experts+1],
+    token index of each routed row): every token's top_k experts by seeded
+    logits N(0,1) + log(p_e), p ~ Dirichlet(2); routed rows sorted by
+    expert (stable in token order)."""
+    rng = np.random.default_rng(seed)
+    x = activation_with_outliers(rng, tokens, K)
+    p = rng.dirichlet(np.full(experts, 2.0))
+    logits = rng.standard_normal((tokens, experts)) + np.log(p)[None, :]
+    choice = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]        # [tokens, top_k]
+    expert = choice.reshape(-1)
+    token = np.repeat(np.arange(tokens), top_k)
+    order = np.argsort(expert, kind="stable")
+    counts = np.bincount(expert, minlength=experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return to_bf16_bits(x[token[order]]), offsets, token[order]
+
+
+def moe_weight(e: int, N: int = 14336, K: int = 4096):
+    """Expert e's weight [N x K], bf16 bits, N(0, 0.02) from seed 100+e."""
+    return to_bf16_bits(normal(np.random.default_rng(100 + e), N, K, 0.02))

@@ -36,7 +36,7 @@ def test_library_is_gfx950_only_code_object():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.fp8_abi_version() == 3
+    assert lib.fp8_abi_version() == 4
     for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARG"), (2, "FP8_ERR_UNSUPPORTED_SHAPE"),
                        (3, "FP8_ERR_MISALIGNED"), (4, "FP8_ERR_UNSUPPORTED_DEVICE"), (5, "FP8_ERR_HIP")]:
         assert L.status_name(code) == name
@@ -107,6 +107,36 @@ def qd(**kw):
 ])
 def test_quantize_dual_validation(kw, status, needle):
     st, msg = qd(**kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def gg(**kw):
+    a = dict(A=FAKE, fa=0, lda=256, B=FAKE, fb=0, ldb=256, gstride=512 * 256, M=1000, N=512, K=256, G=8,
+             offs=FAKE, sa=FAKE, sa_row=1, sb=FAKE, sb_row=0, C=FAKE, out_dt=L.FP8_OUT_BF16, ldc=512)
+    a.update(kw)
+    st = L.lib().fp8_grouped_gemm(a["A"], a["fa"], a["lda"], a["B"], a["fb"], a["ldb"], a["gstride"], a["M"], a["N"],
+                                  a["K"], a["G"], a["offs"], a["sa"], a["sa_row"], a["sb"], a["sb_row"], a["C"],
+                                  a["out_dt"], a["ldc"], None)
+    return st, L.lib().fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(fa=2), 1, "formats"),
+    (dict(sb_row=2), 1, "per_row"),
+    (dict(K=100, lda=112, ldb=112, gstride=512 * 112), 2, "multiple of 16"),
+    (dict(G=0), 1, "groups="),
+    (dict(offs=None), 1, "group_offsets is NULL"),
+    (dict(offs=FAKE + 2), 3, "group_offsets"),
+    (dict(gstride=511 * 256), 1, "b_group_stride"),
+    (dict(gstride=511 * 256 + 256 + 8), 3, "b_group_stride"),
+    (dict(M=256 * 1980, G=4), 2, "FP8_GROUPED_MAX_TILES"),
+    (dict(G=1984, M=0), 2, "FP8_GROUPED_MAX_TILES"),
+    (dict(C=None), 1, "C is NULL"),
+    (dict(lda=128), 1, "lda"),
+])
+def test_grouped_gemm_validation(kw, status, needle):
+    st, msg = gg(**kw)
     assert st == status, (st, msg)
     assert needle in msg
 
