@@ -467,26 +467,43 @@ struct Epi2 {
     static constexpr int kStores = kPasses * 8;         // 8 KiB per pass, 1 KiB per store
 };
 
-template <bool OUT_BF16>
-__device__ __forceinline__ void epilogue_slot(const GemmParams& p, const v16f (&acc)[4][4], int m0, int n0, int wm,
-                                              int wn, int wave, int lane_in, uint8_t* slot, bool interior) {
+// Scale of an epilogue: SMODE bit 0 = one A scale per row (else sa0), bit 1
+// = one B scale per column (else sb0); every mode multiplies the fp32 sum by
+// fl32(sa * sb).  The per-row and per-column scales a lane needs (4 rows, 64
+// columns) are loaded once at the start of the epilogue, so the only wait
+// for them is the one before the first pass; the scalar scales come in
+// through scalar loads, which never wait for the vector-memory DMA.
+template <bool OUT_BF16, int SMODE>
+__device__ __forceinline__ void epilogue_body(const GemmParams& p, const float* __restrict__ sbp, float sa0,
+                                              float sb0, const v16f (&acc)[4][4], int m0, int n0, int wm, int wn,
+                                              int wave, int lane, uint8_t* slot, bool interior) {
     using E = Epi2<OUT_BF16>;
-    // an opaque copy of the lane id: the per-lane address arithmetic below
-    // stays here instead of being hoisted out of the tile loop (where it
-    // would hold registers across the whole K loop)
-    int lane = lane_in;
-    asm volatile("" : "+v"(lane));
     constexpr int kEsz = E::kEsz, kJ = E::kJ;
     uint8_t* stage = slot + wave * 8192;
-    const float st_scale = (!p.sa_row && !p.sb_row) ? p.sa[0] * p.sb[0] : 1.0f;
     const int mw = m0 + wm * 128, nw = n0 + wn * 128;      // wave tile origin
     const int r_w = lane & 31;                              // row of this lane in a 32-row block
+    float sar[4];
+    float sbc[4][4][4];
+    if constexpr (SMODE & 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sar[i] = p.sa[min(mw + i * 32 + r_w, p.M - 1)];
+    }
+    if constexpr (SMODE & 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sbc[j][g][e] = sbp[min(nw + j * 32 + g * 8 + (lane >> 5) * 4 + e, p.N - 1)];
+    }
+    const float s00 = sa0 * sb0;
 #pragma unroll
     for (int pass = 0; pass < E::kPasses; ++pass) {
         const int i = pass / (4 / kJ);                      // 32-row block
         const int jb = (pass % (4 / kJ)) * kJ;              // first MFMA column block
-        float sam = 1.0f;
-        if (p.sa_row) sam = p.sa[min(mw + i * 32 + r_w, p.M - 1)];
+        float srow = s00;
+        if constexpr (SMODE == 1) srow = sar[i] * sb0;
         // 1. registers -> LDS: lane holds columns j*32 + g*8 + (lane/32)*4 + 0..3
 #pragma unroll
         for (int jj = 0; jj < kJ; ++jj) {
@@ -498,8 +515,9 @@ __device__ __forceinline__ void epilogue_slot(const GemmParams& p, const v16f (&
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float sc;
-                    if (!p.sa_row && !p.sb_row) sc = st_scale;
-                    else sc = sam * (p.sb_row ? p.sb[min(nw + j * 32 + g * 8 + (lane >> 5) * 4 + e, p.N - 1)] : p.sb[0]);
+                    if constexpr (SMODE == 3) sc = sar[i] * sbc[j][g][e];
+                    else if constexpr (SMODE == 2) sc = sa0 * sbc[j][g][e];
+                    else sc = srow;
                     v[e] = acc[j][i][4 * g + e] * sc;
                 }
                 const int byte = col * kEsz;                           // logical byte in the 256-byte row
@@ -560,6 +578,34 @@ __device__ __forceinline__ void epilogue_slot(const GemmParams& p, const v16f (&
     }
 }
 
+// Epilogue of one 256 x 256 tile: the scale mode is uniform, so one of the
+// four bodies runs.  p.sb (per-column mode) and sb0 are the tile's B scales.
+template <bool OUT_BF16>
+__device__ __forceinline__ void epilogue_slot(const GemmParams& p, float sa0, float sb0, const v16f (&acc)[4][4],
+                                              int m0, int n0, int wm, int wn, int wave, int lane_in, uint8_t* slot,
+                                              bool interior) {
+    // an opaque copy of the lane id: the per-lane address arithmetic stays
+    // here instead of being hoisted out of the tile loop (where it would
+    // hold registers across the whole K loop)
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    const int mode = (p.sa_row ? 1 : 0) | (p.sb_row ? 2 : 0);
+    if (mode == 0)
+        epilogue_body<OUT_BF16, 0>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+    else if (mode == 1)
+        epilogue_body<OUT_BF16, 1>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+    else if (mode == 2)
+        epilogue_body<OUT_BF16, 2>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+    else
+        epilogue_body<OUT_BF16, 3>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+}
+
+// A uniform fp32 load through the scalar cache (the address is wave-uniform
+// and the kernel never writes the data).
+__device__ __forceinline__ float load_uniform(const float* ptr) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) float*>(reinterpret_cast<uintptr_t>(ptr));
+}
+
 // Linear tile of block b in round r (persistent grid of G blocks): the
 // blocks of one round take G consecutive tiles, each XCD a contiguous range
 // of them; the linear index is then grouped along M as in tile_coords.
@@ -598,12 +644,14 @@ struct TileRef<true> {
     int row0, end;
     const uint8_t* b;
     const float* sb;
+    float sb0;
     __device__ __forceinline__ void load(const GemmParams& p, int tm) {
         const int4 e = p.gtab[1 + tm];
         row0 = e.y;
         end = e.z;
         b = p.B + (int64_t)e.x * p.b_gstride;
         sb = p.sb + (p.sb_row ? (int64_t)e.x * p.N : (int64_t)e.x);
+        sb0 = load_uniform(sb);
     }
     __device__ __forceinline__ int m0(const GemmParams&, int) const { return row0; }
     __device__ __forceinline__ int m_end(const GemmParams&) const { return end; }
@@ -624,6 +672,9 @@ struct TileRef<true> {
 template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
     int tiles_m = p.tiles_m, group_m = p.group_m;
+    // scalar scales (per-tensor modes; the grouped B scale is the tile's)
+    const float sa0 = load_uniform(p.sa);
+    const float sb0 = GROUPED ? 0.0f : load_uniform(p.sb);
     if constexpr (GROUPED) {     // the table's size, within the host's bound (p.tiles_m)
         tiles_m = min(p.gtab[0].x, p.tiles_m);
         group_m = tiles_m < 4 ? tiles_m : 4;
@@ -724,9 +775,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
             GemmParams pt = p;           // the tile's rows end at its group's end
             pt.M = cur.end;
             pt.sb = cur.sb;
-            epilogue_slot<OUT_BF16>(pt, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+            epilogue_slot<OUT_BF16>(pt, sa0, cur.sb0, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
         } else {
-            epilogue_slot<OUT_BF16>(p, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+            epilogue_slot<OUT_BF16>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
         }
         if (!has_next) break;
         first_vm = interior ? 2 : 1;

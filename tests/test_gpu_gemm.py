@@ -58,6 +58,26 @@ def test_scaled_gemm_parity(fa, fb, out, per_row):
         print(M, N, K, rep)
 
 
+@pytest.mark.parametrize("modes", [(False, True), (True, False)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_scaled_gemm_mixed_scale_modes(modes, out):
+    """One scale for A and one per column of B, and the converse: every
+    scale of both operands reaches every output (scales far from 1, so a
+    dropped factor fails), interior and edge tiles, persistent grid."""
+    a_row, b_row = modes
+    rng = np.random.default_rng(77 + 2 * a_row + b_row)
+    for M, N, K in [(700, 900, 384), (1300, 4100, 640)]:
+        A, B, sa, sb = _realistic_operands(rng, M, N, K, 0, 0, True)
+        sa = sa * np.float32(2.0 ** 9) if a_row else np.float32([sa[0] * 2.0 ** 9])
+        sb = sb * np.float32(2.0 ** -7) if b_row else np.float32([sb[0] * 2.0 ** -7])
+        sa, sb = sa.astype(np.float32), sb.astype(np.float32)
+        say("gemm mixed scales", modes, out, M, N, K)
+        y = _run_gemm(A, 0, B, 0, sa, sb, torch.float32 if out == "f32" else torch.bfloat16)
+        y32, p = oracle.gemm(A, 0, B, 0, sa, sb)
+        print(assert_gemm(host(y), y32, p, K, out, what=f"mixed {modes} {M}x{N}x{K}",
+                          exact=exact_checker(A, 0, B, 0, sa, sb)))
+
+
 def hw_group_bound(A, fa, B, fb, sa, sb):
     """Error bound of the FP8 matrix-core sum for arbitrary codes, derived from
     its measured behaviour: the products of each aligned group of 8

@@ -86,6 +86,7 @@ CASES = [  # sizes, N, K, lead
     ([700], 200, 384, 0),
     ([33, 66, 99, 132, 165, 198, 231, 264, 297], 256, 512, 2),
     ([400, 600], 640, 272, 0),            # K not a multiple of 128: the ragged-K kernel
+    ([260, 0, 513], 640, 768, 1),         # one A scale, per-row expert scales (mixed modes)
 ]
 
 
@@ -95,10 +96,12 @@ CASES = [  # sizes, N, K, lead
 def test_grouped_parity(case, fmts, out_dtype):
     sizes, N, K, lead = CASES[case]
     fa, fb = fmts
-    A, B, a_inv, b_inv, offsets = _problem(sizes, N, K, fa, fb, 10 + case, lead=lead, b_rows=case % 2 == 1)
+    A, B, a_inv, b_inv, offsets = _problem(sizes, N, K, fa, fb, 10 + case, lead=lead,
+                                           b_rows=case % 2 == 1 or case == 5)
+    scalar_a = case in (2, 5)
     say("grouped", sizes, N, K, fmts, out_dtype)
-    y = _run(A, B, a_inv, b_inv, offsets, fa, fb, out_dtype, a_rows=case != 2)
-    if case == 2:
+    y = _run(A, B, a_inv, b_inv, offsets, fa, fb, out_dtype, a_rows=not scalar_a)
+    if scalar_a:
         a_inv = a_inv[:1]
     _check(y, A, B, a_inv, b_inv, offsets, fa, fb, out_dtype, np.random.default_rng(case), what=str(sizes))
 
