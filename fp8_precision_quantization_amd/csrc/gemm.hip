@@ -172,10 +172,11 @@ struct Epi {
     static constexpr int kBytes = 4 * WM * kPitch;                        // all four waves
 };
 
-// Epilogue: scale, convert, and stage the wave's (BM/2) x (BN/2) tile in
-// LDS (the ring is free once every wave is past its last MFMA), then store
-// full row segments: 16 bytes per lane, 16 lanes per 256-byte row.
-template <int BM, int BN, bool OUT_BF16, bool BLOCK>
+// Epilogue of the block-scaled GEMM (its scales are applied by the
+// promotion): convert and stage the wave's (BM/2) x (BN/2) tile in LDS (the
+// ring is free once every wave is past its last MFMA), then store full row
+// segments: 16 bytes per lane, 16 lanes per 256-byte row.
+template <int BM, int BN, bool OUT_BF16>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const v16f (&acc)[BN / 64][BM / 64], int m0,
                                               int n0, int wm, int wn, int wave, int lane) {
     constexpr int TM = BM / 64;
@@ -184,10 +185,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const v16f (&
     constexpr int kEsz = E::kEsz, kCols = E::kCols, kPasses = E::kPasses, kPitch = E::kPitch;
     __syncthreads();
     uint8_t* stage = g_ring + wave * (WM * kPitch);
-    float st_scale = 1.0f;
-    if constexpr (!BLOCK) {
-        if (!p.sa_row && !p.sb_row) st_scale = p.sa[0] * p.sb[0];
-    }
     const int mw = m0 + wm * WM, nw = n0 + wn * WN;   // wave tile origin
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass) {
@@ -196,10 +193,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const v16f (&
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = i * 32 + (lane & 31);
-            float sam = 1.0f;
-            if constexpr (!BLOCK) {
-                if (p.sa_row) sam = p.sa[min(mw + row, p.M - 1)];
-            }
 #pragma unroll
             for (int jj = 0; jj < kCols / 32; ++jj) {
                 const int j = pass * (kCols / 32) + jj;
@@ -208,15 +201,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const v16f (&
                     const int col = jj * 32 + g * 8 + (lane >> 5) * 4;   // within the pass
                     float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float sc = 1.0f;
-                        if constexpr (!BLOCK) {
-                            if (!p.sa_row && !p.sb_row) sc = st_scale;
-                            else sc = sam * (p.sb_row ? p.sb[min(nw + j * 32 + g * 8 + (lane >> 5) * 4 + e, p.N - 1)]
-                                                      : p.sb[0]);
-                        }
-                        v[e] = acc[j][i][4 * g + e] * sc;
-                    }
+                    for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * g + e];
                     uint8_t* dst = stage + row * kPitch + col * kEsz;
                     if constexpr (OUT_BF16) {
                         typedef float f2 __attribute__((ext_vector_type(2)));
@@ -1004,7 +989,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bp(GemmParams p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], sc[i], acc[j][i][r]);
-    gemm_epilogue<256, 128, OUT_BF16, true>(p, acc, m0, n0, wm, wn, wave, lane);
+    gemm_epilogue<256, 128, OUT_BF16>(p, acc, m0, n0, wm, wn, wave, lane);
 }
 
 // ---------------------------------------------------------------- host side --
