@@ -864,12 +864,17 @@ __device__ __forceinline__ void mma_step_b(v16f (&part)[2][4], v16f (&acc)[2][4]
             set_half(nxt.a[i], e, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, e));
         }
     };
+    // acc[b] += part[b] * sc for elements [r0, r0 + n) of MFMA block b = (j = b % 2, i = b / 2)
+    auto promote = [&](int b, int r0, int n) {
+        const int pj = b % 2, pi = b / 2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (r >= r0 && r < r0 + n) acc[pj][pi][r] = __builtin_fmaf(part[pj][pi][r], sc[pi], acc[pj][pi][r]);
+    };
 #pragma unroll
     for (int q = 0; q < kMfma; ++q) {
         const int i = q / 2, j = q % 2;
         if constexpr (FRESH) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], sc[i], acc[j][i][r]);
             const v16f z = {};
             part[j][i] = mfma32<FB, FA>(cur.b[j], cur.a[i], z);
         } else {
@@ -894,6 +899,28 @@ __device__ __forceinline__ void mma_step_b(v16f (&part)[2][4], v16f (&acc)[2][4]
 #pragma unroll
             for (int d = 0; d < DMA::kCount; ++d)
                 if (d >= d0 && d < d1) dma(d);
+        }
+        // The promotion, spread over both steps so that its vector work runs
+        // beside the matrix instructions.  A block's part is final after the
+        // block's second-step MFMA: blocks 0-2 are promoted in the second
+        // step's later slots, blocks 3-7 in the next block's first step, each
+        // before the fresh MFMA that overwrites it (sc still holds the scales
+        // of the block being promoted in both places).
+        if constexpr (FRESH) {
+            if (q == 0) promote(3, 0, 8);
+            if (q == 1) promote(3, 8, 8);
+            if (q == 2) promote(4, 0, 8);
+            if (q == 3) promote(4, 8, 8);
+            if (q == 4) promote(5, 0, 16);
+            if (q == 5) promote(6, 0, 16);
+            if (q == 6) promote(7, 0, 16);
+        } else {
+            if (q == 2) promote(0, 0, 8);
+            if (q == 3) promote(0, 8, 8);
+            if (q == 4) promote(1, 0, 8);
+            if (q == 5) promote(1, 8, 8);
+            if (q == 6) promote(2, 0, 8);
+            if (q == 7) promote(2, 8, 8);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -982,13 +1009,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_bp(GemmParams p) {
                                         s + 2 < nks ? 1 : 0);
         sl = s1;
     }
-    // the last block's promotion
+    // the rest of the last block's promotion (blocks 0-2 were promoted in
+    // its second step)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int b = 3; b < 8; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[j][i][r] = __builtin_fmaf(part[j][i][r], sc[i], acc[j][i][r]);
+        for (int r = 0; r < 16; ++r)
+            acc[b % 2][b / 2][r] = __builtin_fmaf(part[b % 2][b / 2][r], sc[b / 2], acc[b % 2][b / 2][r]);
     gemm_epilogue<256, 128, OUT_BF16>(p, acc, m0, n0, wm, wn, wave, lane);
 }
 
