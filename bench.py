@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 # 2.0 + WRITE_SIZE x 1.0 per dispatch (factors from a plain 512 MiB copy, see
 # profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None whenever k_gemm changes
 # until the counters are taken again.
-GEMM_TRAFFIC_BYTES = 476156704
+GEMM_TRAFFIC_BYTES = 483130129
 # The same counters for one fp8_kv_load launch of the kv workload (see
 # profiles/kv_store_gather_8x128_paged_kernel_stats.md); None once k_kv_load
 # changes until they are taken again.
