@@ -297,6 +297,32 @@ def test_delayed_save_restore():
         assert np.array_equal(host(r.q), ref[t][0]) and host(r.scale_inv)[0] == ref[t][1]
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("with_diag", [False, True])
+def test_quantize_tensor_large_sizes_repeated(with_diag):
+    """Per-tensor just-in-time casts at the workloads' sizes and beyond
+    (ragged columns, fp32 inputs, 128 Mi elements), each twice in a row on
+    one stream so the second call reuses the scratch the first left: codes,
+    amax, scale and the saturation counters bit-exact with the oracle."""
+    for rows, cols, in_dtype in [(4096, 4096, "bf16"), (4096, 4104, "bf16"), (14336, 4096, "bf16"),
+                                 (16384, 8192, "bf16"), (2048, 4096, "f32"), (6000, 4096, "f32")]:
+        x = _inputs(rows, cols, in_dtype, rows + cols)
+        want = oracle.quantize(x, oracle.E4M3, "tensor")
+        xt = dev_input(x)
+        for rep in range(2):
+            say("quantize tensor size", rows, cols, in_dtype, "diag" if with_diag else "", rep)
+            diag = fp8.Diag() if with_diag else None
+            r = fp8.quantize(xt, "e4m3", "tensor", diag=diag)
+            assert np.array_equal(host(r.q), want["q"]), (rows, cols, rep)
+            assert host(r.amax).reshape(-1)[0] == want["amax"].reshape(-1)[0]
+            assert host(r.scale_inv).reshape(-1)[0] == want["scale_inv"].reshape(-1)[0]
+            if with_diag:
+                d = diag.read()
+                assert (d["sat"], d["nonfinite"], d["underflow"]) == (want["sat"], want["nonfinite"],
+                                                                       want["underflow"])
+        del xt
+
+
 def test_quantize_deterministic_and_stream_ordered():
     x = _inputs(1000, 2000, "bf16", 9)
     xt = dev_input(x)
