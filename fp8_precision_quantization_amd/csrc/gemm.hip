@@ -331,19 +331,21 @@ struct DmaL {
 };
 using Dma2 = DmaL<256>;
 
-// The 8 DMA instructions of one operand of one full stage, as a functor.
+// The DMA instructions of one operand of one full stage, as a functor.
+template <typename D>
 struct FullDma {
-    static constexpr int kCount = Dma2::kInst;
-    const Dma2* d;
+    static constexpr int kCount = D::kInst;
+    const D* d;
     uint32_t slot;
     int k0;
     __device__ __forceinline__ void operator()(int i) const { d->issue_full(slot, k0, i); }
 };
 
 // The same for the last stages: `on` and `full` are wave-uniform.
+template <typename D>
 struct TailDma {
-    static constexpr int kCount = Dma2::kInst;
-    const Dma2* d;
+    static constexpr int kCount = D::kInst;
+    const D* d;
     uint32_t slot;
     int k0, K;
     bool on, full;
@@ -362,47 +364,52 @@ __device__ __forceinline__ uint4 read_half2(const uint8_t* slot, int row, int h,
     return *reinterpret_cast<const uint4*>(slot + row * kBK2 + ((c ^ swz2(row)) << 4));
 }
 
-// All fragments of step h of a stage, in the order mma_step reads them.
-__device__ __forceinline__ void load_frags2(Frags<256, 256>& f, const uint8_t* As, const uint8_t* Bs, int h,
+// All fragments of step h of a stage, in the order mma_step reads them
+// (BM-row tile: a wave covers BM/2 rows, BM/64 blocks of 32).
+template <int BM>
+__device__ __forceinline__ void load_frags2(Frags<BM, 256>& f, const uint8_t* As, const uint8_t* Bs, int h,
                                             int wm, int wn) {
+    constexpr int TI = BM / 64;
     const int lane = threadIdx.x & 63;
-    set_half(f.a[0], 0, read_half2(As, wm * 128 + (lane & 31), h, 0));
-    set_half(f.a[0], 1, read_half2(As, wm * 128 + (lane & 31), h, 1));
+    set_half(f.a[0], 0, read_half2(As, wm * (BM / 2) + (lane & 31), h, 0));
+    set_half(f.a[0], 1, read_half2(As, wm * (BM / 2) + (lane & 31), h, 1));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         set_half(f.b[j], 0, read_half2(Bs, wn * 128 + j * 32 + (lane & 31), h, 0));
         set_half(f.b[j], 1, read_half2(Bs, wn * 128 + j * 32 + (lane & 31), h, 1));
     }
 #pragma unroll
-    for (int i = 1; i < 4; ++i) {
-        set_half(f.a[i], 0, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, 0));
-        set_half(f.a[i], 1, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, 1));
+    for (int i = 1; i < TI; ++i) {
+        set_half(f.a[i], 0, read_half2(As, wm * (BM / 2) + i * 32 + (lane & 31), h, 0));
+        set_half(f.a[i], 1, read_half2(As, wm * (BM / 2) + i * 32 + (lane & 31), h, 1));
     }
 }
 
-// The 16 MFMAs of one K = 64 step from `cur`, as an explicit program.
-// BAR: after the first MFMA, s_waitcnt vmcnt(N) lgkmcnt(0) and s_barrier,
-// with N = 0, 8 or VM2 for vmsel = 0, 1, 2.  The 16 LDS reads of the next
-// step's fragments (step h of the stage in As/Bs) are spread over the MFMAs
-// after the barrier, and so are the DMA functor's kCount instructions.
-template <int FA, int FB, bool BAR, int VM2, typename DMA>
-__device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const Frags<256, 256>& cur, Frags<256, 256>& nxt,
+// The 4 * BM/64 MFMAs of one K = 64 step from `cur`, as an explicit
+// program.  BAR: after the first MFMA, s_waitcnt vmcnt(N) lgkmcnt(0) and
+// s_barrier, with N = 0, VM1 or VM2 for vmsel = 0, 1, 2.  The LDS reads of
+// the next step's fragments (step h of the stage in As/Bs) are spread over
+// the MFMAs after the barrier, and so are the DMA functor's kCount
+// instructions.
+template <int FA, int FB, bool BAR, int VM1, int VM2, typename DMA, int BM>
+__device__ __forceinline__ void mma_step(v16f (&acc)[4][BM / 64], const Frags<BM, 256>& cur, Frags<BM, 256>& nxt,
                                          const uint8_t* As, const uint8_t* Bs, int h, int wm, int wn,
                                          const DMA& dma, int vmsel) {
-    constexpr int kReads = 16, kMfma = 16;
+    constexpr int TI = BM / 64;
+    constexpr int kReads = 2 * (TI + 4), kMfma = 4 * TI;
     constexpr int q0 = BAR ? 1 : 0;             // first MFMA followed by reads / DMA
     constexpr int kSlots = kMfma - q0;
     const int lane = threadIdx.x & 63;
     auto one_read = [&](int r) {
         const int f = r >> 1, e = r & 1;
         if (f == 0) {
-            set_half(nxt.a[0], e, read_half2(As, wm * 128 + (lane & 31), h, e));
+            set_half(nxt.a[0], e, read_half2(As, wm * (BM / 2) + (lane & 31), h, e));
         } else if (f <= 4) {
             const int j = f - 1;
             set_half(nxt.b[j], e, read_half2(Bs, wn * 128 + j * 32 + (lane & 31), h, e));
         } else {
             const int i = f - 4;
-            set_half(nxt.a[i], e, read_half2(As, wm * 128 + i * 32 + (lane & 31), h, e));
+            set_half(nxt.a[i], e, read_half2(As, wm * (BM / 2) + i * 32 + (lane & 31), h, e));
         }
     };
 #pragma unroll
@@ -412,7 +419,7 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const Frags<256, 256
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (BAR) {
             if (q == 0) {
-                if (vmsel == 1) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (vmsel == 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM1) : "memory");
                 else if (vmsel == 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM2) : "memory");
                 else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             }
@@ -434,21 +441,21 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const Frags<256, 256
     }
 }
 
-// Epilogue of one 256 x 256 tile staged through one 32 KiB ring slot: each
-// wave owns 8 KiB = 32 rows x 256 bytes of it, so it writes its 128 x 128
-// tile in passes of one 32-row MFMA block (bf16: all 128 columns, 4 passes;
-// fp32: 64 columns, 8 passes).  A pass writes the scaled, converted values
+// Epilogue of one BM x 256 tile staged through one 32 KiB ring slot: each
+// wave owns 8 KiB = 32 rows x 256 bytes of it, so it writes its (BM/2) x 128
+// tile in passes of one 32-row MFMA block (BM = 256, bf16: all 128 columns,
+// 4 passes; fp32: 64 columns, 8 passes; BM = 128: half as many).  A pass writes the scaled, converted values
 // (row r's 16-byte chunk c at physical chunk c ^ (r & 15)), reads them back
 // as 16-byte row chunks (16 lanes per 256-byte row segment) and stores them.
 // An interior tile with 16-byte aligned rows issues exactly kStores vector
 // stores per wave, unconditionally (the persistent loop's vmcnt accounting
 // relies on it).
-template <bool OUT_BF16>
+template <bool OUT_BF16, int BM>
 struct Epi2 {
     static constexpr int kEsz = OUT_BF16 ? 2 : 4;
     static constexpr int kCols = 256 / kEsz;            // columns per pass
     static constexpr int kJ = kCols / 32;               // MFMA column blocks per pass
-    static constexpr int kPasses = 4 * (4 / kJ);
+    static constexpr int kPasses = (BM / 64) * (4 / kJ);
     static constexpr int kStores = kPasses * 8;         // 8 KiB per pass, 1 KiB per store
 };
 
@@ -458,20 +465,21 @@ struct Epi2 {
 // columns) are loaded once at the start of the epilogue, so the only wait
 // for them is the one before the first pass; the scalar scales come in
 // through scalar loads, which never wait for the vector-memory DMA.
-template <bool OUT_BF16, int SMODE>
+template <bool OUT_BF16, int SMODE, int BM>
 __device__ __forceinline__ void epilogue_body(const GemmParams& p, const float* __restrict__ sbp, float sa0,
-                                              float sb0, const v16f (&acc)[4][4], int m0, int n0, int wm, int wn,
-                                              int wave, int lane, uint8_t* slot, bool interior) {
-    using E = Epi2<OUT_BF16>;
+                                              float sb0, const v16f (&acc)[4][BM / 64], int m0, int n0, int wm,
+                                              int wn, int wave, int lane, uint8_t* slot, bool interior) {
+    using E = Epi2<OUT_BF16, BM>;
+    constexpr int TI = BM / 64;
     constexpr int kEsz = E::kEsz, kJ = E::kJ;
     uint8_t* stage = slot + wave * 8192;
-    const int mw = m0 + wm * 128, nw = n0 + wn * 128;      // wave tile origin
+    const int mw = m0 + wm * (BM / 2), nw = n0 + wn * 128; // wave tile origin
     const int r_w = lane & 31;                              // row of this lane in a 32-row block
-    float sar[4];
+    float sar[TI];
     float sbc[4][4][4];
     if constexpr (SMODE & 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sar[i] = p.sa[min(mw + i * 32 + r_w, p.M - 1)];
+        for (int i = 0; i < TI; ++i) sar[i] = p.sa[min(mw + i * 32 + r_w, p.M - 1)];
     }
     if constexpr (SMODE & 2) {
 #pragma unroll
@@ -563,12 +571,12 @@ __device__ __forceinline__ void epilogue_body(const GemmParams& p, const float* 
     }
 }
 
-// Epilogue of one 256 x 256 tile: the scale mode is uniform, so one of the
+// Epilogue of one BM x 256 tile: the scale mode is uniform, so one of the
 // four bodies runs.  p.sb (per-column mode) and sb0 are the tile's B scales.
-template <bool OUT_BF16>
-__device__ __forceinline__ void epilogue_slot(const GemmParams& p, float sa0, float sb0, const v16f (&acc)[4][4],
-                                              int m0, int n0, int wm, int wn, int wave, int lane_in, uint8_t* slot,
-                                              bool interior) {
+template <bool OUT_BF16, int BM>
+__device__ __forceinline__ void epilogue_slot(const GemmParams& p, float sa0, float sb0,
+                                              const v16f (&acc)[4][BM / 64], int m0, int n0, int wm, int wn, int wave,
+                                              int lane_in, uint8_t* slot, bool interior) {
     // an opaque copy of the lane id: the per-lane address arithmetic stays
     // here instead of being hoisted out of the tile loop (where it would
     // hold registers across the whole K loop)
@@ -576,13 +584,13 @@ __device__ __forceinline__ void epilogue_slot(const GemmParams& p, float sa0, fl
     asm volatile("" : "+v"(lane));
     const int mode = (p.sa_row ? 1 : 0) | (p.sb_row ? 2 : 0);
     if (mode == 0)
-        epilogue_body<OUT_BF16, 0>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+        epilogue_body<OUT_BF16, 0, BM>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
     else if (mode == 1)
-        epilogue_body<OUT_BF16, 1>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+        epilogue_body<OUT_BF16, 1, BM>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
     else if (mode == 2)
-        epilogue_body<OUT_BF16, 2>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+        epilogue_body<OUT_BF16, 2, BM>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
     else
-        epilogue_body<OUT_BF16, 3>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
+        epilogue_body<OUT_BF16, 3, BM>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
 }
 
 // A uniform fp32 load through the scalar cache (the address is wave-uniform
@@ -616,16 +624,16 @@ __device__ __forceinline__ bool tile_of_round(const GemmParams& p, int tiles_m, 
 // of tm names its expert g and its rows [m0, m_end) (at most 256 of them,
 // m_end the end of the group), B is expert g's matrix and sb its scale (one
 // per expert, or the expert's N row scales).
-template <bool GROUPED>
+template <bool GROUPED, int BM>
 struct TileRef {                  // plain: nothing to carry
     __device__ __forceinline__ void load(const GemmParams&, int) {}
-    __device__ __forceinline__ int m0(const GemmParams&, int tm) const { return tm * 256; }
+    __device__ __forceinline__ int m0(const GemmParams&, int tm) const { return tm * BM; }
     __device__ __forceinline__ int m_end(const GemmParams& p) const { return p.M; }
     __device__ __forceinline__ const uint8_t* B(const GemmParams& p) const { return p.B; }
 };
 
 template <>
-struct TileRef<true> {
+struct TileRef<true, 256> {
     int row0, end;
     const uint8_t* b;
     const float* sb;
@@ -643,7 +651,9 @@ struct TileRef<true> {
     __device__ __forceinline__ const uint8_t* B(const GemmParams&) const { return b; }
 };
 
-// Persistent scaled GEMM over 256 x 256 tiles with 128-byte K stages.
+// Persistent scaled GEMM over BM x 256 tiles (BM = 256, or 128 for the
+// tiles of a last round that would leave half the CUs idle) with 128-byte K
+// stages.  Every output's K sum is the same chain of MFMAs whatever BM is.
 // Stages are numbered globally over this block's tiles; the ring schedule
 // of each stage is the one described above, so the first two stages of the
 // next tile stream in during the last two stages of the current one.  The
@@ -653,9 +663,11 @@ struct TileRef<true> {
 // flight (vector-memory operations complete in issue order).
 // Needs K > 256 (three stages) when a block runs more than one tile.
 // GROUPED: the M-tiles are those of the grouped GEMM's table, whose size
-// only the device knows.
-template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED>
+// only the device knows (BM = 256 only).
+template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED, int BM = 256>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
+    static_assert(BM == 256 || (BM == 128 && !GROUPED), "tile rows");
+    constexpr int TI = BM / 64;                  // 32-row MFMA blocks per wave
     int tiles_m = p.tiles_m, group_m = p.group_m;
     // scalar scales (per-tensor modes; the grouped B scale is the tile's)
     const float sa0 = load_uniform(p.sa);
@@ -664,8 +676,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
         tiles_m = min(p.gtab[0].x, p.tiles_m);
         group_m = tiles_m < 4 ? tiles_m : 4;
     }
-    using E = Epi2<OUT_BF16>;
-    constexpr int kVm2 = 8 + E::kStores < 63 ? 8 + E::kStores : 63;
+    using E = Epi2<OUT_BF16, BM>;
+    using DA = DmaL<BM>;
+    constexpr int kVm1 = DA::kInst;              // the A DMA of the even step may still fly
+    constexpr int kVm2 = kVm1 + E::kStores < 63 ? kVm1 + E::kStores : 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = p.K;
@@ -680,30 +694,31 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
     if (!tile_of_round(p, tiles_m, group_m, 0, tm, tn)) return;
     int tm_n = 0, tn_n = 0;
     bool has_next = tile_of_round(p, tiles_m, group_m, 1, tm_n, tn_n);
-    TileRef<GROUPED> cur, nxt;
+    TileRef<GROUPED, BM> cur, nxt;
     cur.load(p, tm);
     if (has_next) nxt.load(p, tm_n);
 
-    Dma2 da, db;
+    DA da;
+    Dma2 db;
     da.init(p.A, p.lda, cur.m0(p, tm), cur.m_end(p), wave);
     db.init(cur.B(p), p.ldb, tn * 256, p.N, wave);
 
-    v16f acc[4][4];
+    v16f acc[4][TI];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-    Frags<256, 256> f0, f1;
+    Frags<BM, 256> f0, f1;
     if (nks > 0) {
         da.issue(addr(0), 0, K);
         db.issue(addr(1), 0, K);
         if (nks > 1) {
             da.issue(addr(2), kBK2, K);
             db.issue(addr(3), kBK2, K);
-            wait_and_barrier<2 * Dma2::kInst>();
+            wait_and_barrier<DA::kInst + Dma2::kInst>();
         } else {
             wait_and_barrier<0>();
         }
@@ -725,15 +740,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
             const int vmsel = s == 0 ? first_vm : 1;
             if constexpr (RAGGED) {
                 const bool full = (s + 3) * kBK2 <= K;
-                const TailDma dA{&da, addr(s4), (s + 2) * kBK2, K, true, full};
-                mma_step<FA, FB, false, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
-                const TailDma dB{&db, addr(sl), (s + 2) * kBK2, K, true, full};
-                mma_step<FA, FB, true, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
+                const TailDma<DA> dA{&da, addr(s4), (s + 2) * kBK2, K, true, full};
+                mma_step<FA, FB, false, kVm1, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
+                const TailDma<Dma2> dB{&db, addr(sl), (s + 2) * kBK2, K, true, full};
+                mma_step<FA, FB, true, kVm1, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
             } else {
-                const FullDma dA{&da, addr(s4), (s + 2) * kBK2};
-                mma_step<FA, FB, false, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
-                const FullDma dB{&db, addr(sl), (s + 2) * kBK2};
-                mma_step<FA, FB, true, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
+                const FullDma<DA> dA{&da, addr(s4), (s + 2) * kBK2};
+                mma_step<FA, FB, false, kVm1, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
+                const FullDma<Dma2> dB{&db, addr(sl), (s + 2) * kBK2};
+                mma_step<FA, FB, true, kVm1, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
             }
             sl = s2;
         }
@@ -748,21 +763,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
             // odd-step wait: stage s+1 (this tile's, or the next tile's stage 0)
             // must be in; only the A issued in this even step may still fly
             const int vmsel = has_next ? 1 : 0;
-            const TailDma dA{&da, addr(s4), (s + 2 - nks) * kBK2, K, has_next, true};
-            mma_step<FA, FB, false, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
-            const TailDma dB{&db, addr(sl), (s + 2 - nks) * kBK2, K, has_next, true};
-            mma_step<FA, FB, true, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
+            const TailDma<DA> dA{&da, addr(s4), (s + 2 - nks) * kBK2, K, has_next, true};
+            mma_step<FA, FB, false, kVm1, kVm2>(acc, f0, f1, ptr(sl), ptr(s1), 1, wm, wn, dA, 0);
+            const TailDma<Dma2> dB{&db, addr(sl), (s + 2 - nks) * kBK2, K, has_next, true};
+            mma_step<FA, FB, true, kVm1, kVm2>(acc, f1, f0, ptr(s2), ptr(s3), 0, wm, wn, dB, vmsel);
             sl = s2;
         }
         // B(last)'s slot is free until the next tile's first even step
-        const bool interior = p.vec_out && m0 + 256 <= cur.m_end(p) && n0 + 256 <= p.N;
+        const bool interior = p.vec_out && m0 + BM <= cur.m_end(p) && n0 + 256 <= p.N;
         if constexpr (GROUPED) {
             GemmParams pt = p;           // the tile's rows end at its group's end
             pt.M = cur.end;
             pt.sb = cur.sb;
-            epilogue_slot<OUT_BF16>(pt, sa0, cur.sb0, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+            epilogue_slot<OUT_BF16, BM>(pt, sa0, cur.sb0, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
         } else {
-            epilogue_slot<OUT_BF16>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
+            epilogue_slot<OUT_BF16, BM>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, ptr(wrap(sl + 4)), interior);
         }
         if (!has_next) break;
         first_vm = interior ? 2 : 1;
@@ -774,7 +789,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
     }
@@ -1052,32 +1067,78 @@ GemmParams make_params(const GemmArgs& a, int bm, int bn) {
     return p;
 }
 
-// Scaled GEMM: 256 x 256 tiles, on a persistent grid of one block per CU
-// when there are more tiles than CUs and K has at least three stages.
-// (Measured: a last round left half full costs about half a round, since
-// the busy CUs then run faster; splitting it into half-width tiles does not
-// pay.)
-template <int FA, int FB, bool OUT_BF16>
-hipError_t launch_scaled_typed(const GemmArgs& a) {
+// One launch of the scaled GEMM kernel with BM-row tiles over p: a
+// persistent grid of one block per CU when there are more tiles than CUs
+// and K has at least three stages, else one block per tile.
+template <int FA, int FB, bool OUT_BF16, int BM>
+hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
-        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false>, lds_scaled<OUT_BF16>());
+        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false, BM>, lds_scaled<OUT_BF16>());
         if (attr_err == hipSuccess)
-            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, false>, lds_scaled<OUT_BF16>());
+            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, false, BM>, lds_scaled<OUT_BF16>());
     });
     if (attr_err != hipSuccess) return attr_err;
-    const GemmParams p = make_params(a, 256, 256);
     unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    if (grid > (unsigned)a.num_cus && a.K > 2 * kBK2) grid = (unsigned)a.num_cus;
+    if (grid > (unsigned)num_cus && p.K > 2 * kBK2) grid = (unsigned)num_cus;
     if (grid == 0) return hipSuccess;
-    if (a.K % kBK2 != 0)
-        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, false>), dim3(grid), dim3(kGemmThreads),
-                           lds_scaled<OUT_BF16>(), a.stream, p);
+    if (p.K % kBK2 != 0)
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, false, BM>), dim3(grid), dim3(kGemmThreads),
+                           lds_scaled<OUT_BF16>(), stream, p);
     else
-        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false, false>), dim3(grid), dim3(kGemmThreads),
-                           lds_scaled<OUT_BF16>(), a.stream, p);
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false, false, BM>), dim3(grid), dim3(kGemmThreads),
+                           lds_scaled<OUT_BF16>(), stream, p);
     return hipGetLastError();
+}
+
+// Columns [n0, N) of the GEMM as a problem of its own: B's rows, C's
+// columns and the per-column B scales from n0 on.
+GemmParams column_range(const GemmParams& p, int n0, int esz, int bm) {
+    GemmParams q = p;
+    q.B = p.B + (int64_t)n0 * p.ldb;
+    q.C = reinterpret_cast<uint8_t*>(p.C) + (int64_t)n0 * esz;
+    if (p.sb_row) q.sb = p.sb + n0;
+    q.N = p.N - n0;
+    q.tiles_m = (p.M + bm - 1) / bm;
+    q.tiles_n = (q.N + 255) / 256;
+    q.group_m = q.tiles_m < 4 ? q.tiles_m : 4;
+    return q;
+}
+
+// Scaled GEMM.  A single tile takes about the same time whether one CU or
+// all of them are busy (its K loop), so a round of tiles that fills at most
+// half the CUs costs nearly a full round.  Such a round runs as 128 x 256
+// tiles instead, which halves each CU's share of it: a problem with at most
+// half as many 256 x 256 tiles as CUs runs entirely as 128-row tiles; a
+// persistent one whose last round is at most half full runs its last
+// columns (enough 256-wide column tiles to hold that round's tiles) as a
+// second launch of 128-row tiles, one round of them, after the other
+// columns' whole rounds.  (With at most 128 rows, 128-row tiles always.)  Every output's K sum is the same chain of MFMAs
+// in both kernels, so the result is bit-identical to the 256-row tiling.
+template <int FA, int FB, bool OUT_BF16>
+hipError_t launch_scaled_typed(const GemmArgs& a) {
+    const GemmParams p = make_params(a, 256, 256);
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n, cus = a.num_cus;
+    if (tiles == 0) return hipSuccess;
+    if (2 * tiles <= cus || a.M <= 128)
+        return launch_tiles<FA, FB, OUT_BF16, 128>(make_params(a, 128, 256), a.num_cus, a.stream);
+    const int64_t last = tiles % cus;
+    if (tiles > cus && a.K > 2 * kBK2 && last != 0 && 2 * last <= cus) {
+        const int tail_n = (int)((last + p.tiles_m - 1) / p.tiles_m);            // column tiles of the tail
+        const int64_t half_tiles = (int64_t)((p.M + 127) / 128) * tail_n;
+        if (tail_n < p.tiles_n && half_tiles <= cus) {
+            const int n0 = (p.tiles_n - tail_n) * 256;
+            GemmParams head = p;
+            head.N = n0;
+            head.tiles_n = p.tiles_n - tail_n;
+            hipError_t e = launch_tiles<FA, FB, OUT_BF16, 256>(head, a.num_cus, a.stream);
+            if (e != hipSuccess) return e;
+            return launch_tiles<FA, FB, OUT_BF16, 128>(column_range(p, n0, a.out_bf16 ? 2 : 4, 128), a.num_cus,
+                                                       a.stream);
+        }
+    }
+    return launch_tiles<FA, FB, OUT_BF16, 256>(p, a.num_cus, a.stream);
 }
 
 // Grouped GEMM ([DeepL bets on FP8] 3.2, MoE): one block builds the table of

@@ -200,6 +200,71 @@ def test_gemm_column_ranges_bitwise():
     assert torch.equal(y[:, 12288:], y_tail)
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_split_last_round_parity_and_bitwise(out):
+    """A persistent problem whose last round is at most half full: its last
+    column tiles run as 128-row tiles in a second launch.  M, N and K
+    ragged, one scale per row of A and per column of B (the tail's scales
+    start at its first column).  Sampled outputs against the oracle (the
+    tail columns and the last rows included); then every output against the
+    same product computed with 256-row tiles only (A padded with zero rows
+    until the problem has more than half as many tiles as CUs), bit for bit."""
+    rng = np.random.default_rng(31)
+    M, N, K = 2000, 17000, 1040          # 8 x 67 tiles: two rounds + 24 tiles on 256 CUs
+    A, B, sa, sb = _realistic_operands(rng, M, N, K, 0, 0, True)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    say("gemm split last round", M, N, K, out)
+    y = _run_gemm(A, 0, B, 0, sa, sb, odt)
+    yh = host(y)
+    n_tail = 64 * 256
+    ms = np.concatenate([[0, M - 1, M - 1, 0], rng.integers(0, M, 2000), rng.integers(1792, M, 400)])
+    ns = np.concatenate([[0, N - 1, n_tail, n_tail - 1], rng.integers(0, N, 2000), rng.integers(n_tail, N, 400)])
+    y32, pp = oracle.gemm_sampled(A, 0, B, 0, sa, sb, ms, ns)
+    print(assert_gemm(yh[ms, ns], y32, pp, K, out, what="split last round",
+                      exact=exact_checker(A, 0, B, 0, sa, sb, ms, ns)))
+    Mp = 43 * 256                        # 43 x 67 tiles: one tile per block, 256 rows each
+    a_pad = torch.zeros((Mp, K), dtype=torch.uint8, device="cuda")
+    a_pad[:M] = dev_u8(A)
+    sa_pad = torch.ones(Mp, dtype=torch.float32, device="cuda")
+    sa_pad[:M] = dev_f32(sa)
+    b = dev_u8(B)
+    say("gemm split last round: 256-row reference, tail columns")
+    ref_tail = fp8.scaled_gemm(a_pad, b[n_tail:], sa_pad, dev_f32(sb[n_tail:]), out_dtype=odt)
+    say("gemm split last round: 256-row reference, head columns")
+    ref_head = fp8.scaled_gemm(a_pad[:M], b[:n_tail], dev_f32(sa), dev_f32(sb[:n_tail]), out_dtype=odt)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, n_tail:], ref_tail[:M])
+    assert torch.equal(y[:, :n_tail], ref_head)
+
+
+def test_gemm_128_row_tiles_bitwise_and_small_m_persistent():
+    """Problems with at most half as many 256-row tiles as CUs, and any with
+    at most 128 rows, run as 128-row tiles: their outputs equal the 256-row
+    tiling's bit for bit; a 100-row problem wide enough for the persistent
+    grid (274 column tiles) against the oracle."""
+    rng = np.random.default_rng(32)
+    M, N, K = 700, 3000, 768                  # 3 x 12 tiles
+    A = random_codes(rng, (M, K), 1)
+    B = random_codes(rng, (N, K), 0)
+    s = dev_f32(np.float32([0.125]))
+    say("gemm 128-row tiles bitwise", M, N, K)
+    y = fp8.scaled_gemm(dev_u8(A), dev_u8(B), s, s, "e5m2", "e4m3", torch.float32)
+    a_pad = torch.zeros((11 * 256, K), dtype=torch.uint8, device="cuda")   # 11 x 12 tiles > 128
+    a_pad[:M] = dev_u8(A)
+    ref = fp8.scaled_gemm(a_pad, dev_u8(B), s, s, "e5m2", "e4m3", torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref[:M])
+    M, N, K = 100, 70000, 512
+    A, B, sa, sb = _realistic_operands(rng, M, N, K, 0, 0, True)
+    say("gemm small M persistent", M, N, K)
+    yh = host(_run_gemm(A, 0, B, 0, sa, sb, torch.bfloat16))
+    ms = np.concatenate([[0, M - 1], rng.integers(0, M, 3000)])
+    ns = np.concatenate([[N - 1, 0], rng.integers(0, N, 3000)])
+    y32, pp = oracle.gemm_sampled(A, 0, B, 0, sa, sb, ms, ns)
+    print(assert_gemm(yh[ms, ns], y32, pp, K, "bf16", what="small M persistent",
+                      exact=exact_checker(A, 0, B, 0, sa, sb, ms, ns)))
+
+
 def test_gemm_strided_operands_and_output():
     rng = np.random.default_rng(6)
     M, N, K = 100, 130, 160
