@@ -35,11 +35,12 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 # rocprofv3 HBM traffic of one scaled-GEMM call on the mlp8b workload (its two
-# launches: 768 tiles of 256 x 256, then the last columns as 256 tiles of
-# 128 x 256): FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 per dispatch (factors from a
-# plain 512 MiB copy, see profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None
-# whenever k_gemm changes until the counters are taken again.
-GEMM_TRAFFIC_BYTES = 515710879
+# launches: k_gemm_p over 768 tiles of 256 x 256, then k_gemm_h over the last
+# columns as 256 tiles of 128 x 256): FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 per
+# dispatch (factors from a plain 512 MiB copy, see
+# profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None whenever either kernel
+# changes until the counters are taken again.
+GEMM_TRAFFIC_BYTES = 515656085
 # The same counters for one fp8_kv_load launch of the kv workload (see
 # profiles/kv_store_gather_8x128_paged_kernel_stats.md); None once k_kv_load
 # changes until they are taken again.

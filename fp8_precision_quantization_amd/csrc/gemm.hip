@@ -651,9 +651,7 @@ struct TileRef<true, 256> {
     __device__ __forceinline__ const uint8_t* B(const GemmParams&) const { return b; }
 };
 
-// Persistent scaled GEMM over BM x 256 tiles (BM = 256, or 128 for the
-// tiles of a last round that would leave half the CUs idle) with 128-byte K
-// stages.  Every output's K sum is the same chain of MFMAs whatever BM is.
+// Persistent scaled GEMM over 256 x 256 tiles with 128-byte K stages.
 // Stages are numbered globally over this block's tiles; the ring schedule
 // of each stage is the one described above, so the first two stages of the
 // next tile stream in during the last two stages of the current one.  The
@@ -663,11 +661,10 @@ struct TileRef<true, 256> {
 // flight (vector-memory operations complete in issue order).
 // Needs K > 256 (three stages) when a block runs more than one tile.
 // GROUPED: the M-tiles are those of the grouped GEMM's table, whose size
-// only the device knows (BM = 256 only).
-template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED, int BM = 256>
+// only the device knows.
+template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
-    static_assert(BM == 256 || (BM == 128 && !GROUPED), "tile rows");
-    constexpr int TI = BM / 64;                  // 32-row MFMA blocks per wave
+    constexpr int BM = 256, TI = BM / 64;        // tile rows; 32-row MFMA blocks per wave
     int tiles_m = p.tiles_m, group_m = p.group_m;
     // scalar scales (per-tensor modes; the grouped B scale is the tile's)
     const float sa0 = load_uniform(p.sa);
@@ -793,6 +790,102 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.0f;
     }
+}
+
+// ------------------------------------------------------------------------
+// Scaled GEMM over 128 x 256 tiles, one tile per block, for the launches
+// whose tiles would otherwise leave half the CUs idle.  A whole stage (A
+// 128 x 128 B, B 256 x 128 B: 48 KiB) fits three times in LDS: stage s
+// lives in slot s mod 3.  The odd step of stage s waits for stage s+1 (only
+// A(s+2) and B(s+2) may still fly), meets the other waves (every wave is
+// done reading stage s), then issues B(s+3) into stage s's slot; the next
+// even step issues A(s+3) there.  So B streams three stages ahead (less
+// the odd step) and A two, against one and two in k_gemm_p.  The MFMA
+// program, its fragment reads and the epilogue are those of k_gemm_p with
+// 128-row tiles, so every output's K sum is the same chain of MFMAs.
+// ------------------------------------------------------------------------
+constexpr int kHStage = 128 * kBK2 + 256 * kBK2;      // 48 KiB: A, then B
+constexpr int kHRing = 3 * kHStage;
+
+template <int FA, int FB, bool OUT_BF16>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
+    using DA = DmaL<128>;
+    constexpr int kVm1 = DA::kInst + Dma2::kInst;  // A(s+2) and B(s+2) may still fly
+    const float sa0 = load_uniform(p.sa);
+    const float sb0 = load_uniform(p.sb);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int K = p.K;
+    const int nks = (K + kBK2 - 1) / kBK2;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * 128, n0 = tn * 256;
+    const uint32_t ring = lds_addr(g_ring);
+    auto addr = [&](int slot) { return ring + (uint32_t)(slot * kHStage); };
+    auto aptr = [&](int slot) { return g_ring + slot * kHStage; };
+    auto bptr = [&](int slot) { return g_ring + slot * kHStage + 128 * kBK2; };
+
+    DA da;
+    Dma2 db;
+    da.init(p.A, p.lda, m0, p.M, wave);
+    db.init(p.B, p.ldb, n0, p.N, wave);
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+    Frags<128, 256> f0, f1;
+    if (nks > 0) {
+        // A(0), B(0), A(1), B(1), B(2); A(2) comes with the first even step
+        for (int i = 0; i < 2 && i < nks; ++i) {
+            da.issue(addr(i), i * kBK2, K);
+            db.issue(addr(i) + (uint32_t)(128 * kBK2), i * kBK2, K);
+        }
+        if (nks > 2) db.issue(addr(2) + (uint32_t)(128 * kBK2), 2 * kBK2, K);
+        if (nks > 2) wait_and_barrier<DA::kInst + 2 * Dma2::kInst>();
+        else if (nks == 2) wait_and_barrier<kVm1>();
+        else wait_and_barrier<0>();
+        load_frags2(f0, aptr(0), bptr(0), 0, wm, wn);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+
+    int cs = 0;                                    // slot of stage s
+    int s = 0;
+    // even step: the MFMAs of stage s's first half, the reads of its second;
+    // A(s+2) into stage s-1's slot (free since the last barrier).  Odd step:
+    // stage s+1 in (only A(s+2), B(s+2) may fly; nothing past the last
+    // stage), every wave done with stage s; reads of stage s+1's first half
+    // and B(s+3) into stage s's slot.  While both DMAs are whole stages the
+    // loop carries no branch around them.
+    for (; s + 3 < nks && (s + 4) * kBK2 <= K; ++s) {
+        const int ns = cs == 2 ? 0 : cs + 1;       // slot of stage s+1
+        const int ps = ns == 2 ? 0 : ns + 1;       // slot of stage s+2 (stage s-1's)
+        const FullDma<DA> dA{&da, addr(ps), (s + 2) * kBK2};
+        mma_step<FA, FB, false, kVm1, kVm1>(acc, f0, f1, aptr(cs), bptr(cs), 1, wm, wn, dA, 0);
+        const FullDma<Dma2> dB{&db, addr(cs) + (uint32_t)(128 * kBK2), (s + 3) * kBK2};
+        mma_step<FA, FB, true, kVm1, kVm1>(acc, f1, f0, aptr(ns), bptr(ns), 0, wm, wn, dB, 1);
+        cs = ns;
+    }
+    for (; s < nks; ++s) {
+        const int ns = cs == 2 ? 0 : cs + 1;
+        const int ps = ns == 2 ? 0 : ns + 1;
+        const TailDma<DA> dA{&da, addr(ps), (s + 2) * kBK2, K, s + 2 < nks, (s + 3) * kBK2 <= K};
+        mma_step<FA, FB, false, kVm1, kVm1>(acc, f0, f1, aptr(cs), bptr(cs), 1, wm, wn, dA, 0);
+        const TailDma<Dma2> dB{&db, addr(cs) + (uint32_t)(128 * kBK2), (s + 3) * kBK2, K, s + 3 < nks,
+                               (s + 4) * kBK2 <= K};
+        mma_step<FA, FB, true, kVm1, kVm1>(acc, f1, f0, aptr(ns), bptr(ns), 0, wm, wn, dB, s + 2 < nks ? 1 : 0);
+        cs = ns;
+    }
+    // the last odd step's fragment reads (of no stage) are done before the
+    // epilogue stages its values through the ring
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __syncthreads();
+    const bool interior = p.vec_out && m0 + 128 <= p.M && n0 + 256 <= p.N;
+    epilogue_slot<OUT_BF16, 128>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
 }
 
 // ------------------------------------------------------------------------
@@ -1043,7 +1136,8 @@ constexpr size_t lds_256x128() {
     return (size_t)kBRing > (size_t)Epi<256, 128, OUT_BF16>::kBytes ? (size_t)kBRing
                                                                     : (size_t)Epi<256, 128, OUT_BF16>::kBytes;
 }
-static_assert(lds_scaled<true>() <= 160 * 1024 && lds_256x128<false>() <= 160 * 1024, "LDS budget of one CU");
+static_assert(lds_scaled<true>() <= 160 * 1024 && lds_256x128<false>() <= 160 * 1024 && kHRing <= 160 * 1024,
+              "LDS budget of one CU");
 
 template <typename KERN>
 hipError_t set_lds(KERN kern, size_t bytes) {
@@ -1067,28 +1161,41 @@ GemmParams make_params(const GemmArgs& a, int bm, int bn) {
     return p;
 }
 
-// One launch of the scaled GEMM kernel with BM-row tiles over p: a
-// persistent grid of one block per CU when there are more tiles than CUs
-// and K has at least three stages, else one block per tile.
-template <int FA, int FB, bool OUT_BF16, int BM>
+// One launch of k_gemm_p over p: a persistent grid of one block per CU when
+// there are more tiles than CUs and K has at least three stages, else one
+// block per tile.
+template <int FA, int FB, bool OUT_BF16>
 hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
-        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false, BM>, lds_scaled<OUT_BF16>());
+        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false>, lds_scaled<OUT_BF16>());
         if (attr_err == hipSuccess)
-            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, false, BM>, lds_scaled<OUT_BF16>());
+            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, false>, lds_scaled<OUT_BF16>());
     });
     if (attr_err != hipSuccess) return attr_err;
     unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
     if (grid > (unsigned)num_cus && p.K > 2 * kBK2) grid = (unsigned)num_cus;
     if (grid == 0) return hipSuccess;
     if (p.K % kBK2 != 0)
-        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, false, BM>), dim3(grid), dim3(kGemmThreads),
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, false>), dim3(grid), dim3(kGemmThreads),
                            lds_scaled<OUT_BF16>(), stream, p);
     else
-        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false, false, BM>), dim3(grid), dim3(kGemmThreads),
+        hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false, false>), dim3(grid), dim3(kGemmThreads),
                            lds_scaled<OUT_BF16>(), stream, p);
+    return hipGetLastError();
+}
+
+// One launch of k_gemm_h over p (128-row tiles, one block each).
+template <int FA, int FB, bool OUT_BF16>
+hipError_t launch_half(const GemmParams& p, hipStream_t stream) {
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [&] { attr_err = set_lds(k_gemm_h<FA, FB, OUT_BF16>, (size_t)kHRing); });
+    if (attr_err != hipSuccess) return attr_err;
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_gemm_h<FA, FB, OUT_BF16>), dim3(grid), dim3(kGemmThreads), (size_t)kHRing, stream, p);
     return hipGetLastError();
 }
 
@@ -1109,20 +1216,20 @@ GemmParams column_range(const GemmParams& p, int n0, int esz, int bm) {
 // Scaled GEMM.  A single tile takes about the same time whether one CU or
 // all of them are busy (its K loop), so a round of tiles that fills at most
 // half the CUs costs nearly a full round.  Such a round runs as 128 x 256
-// tiles instead, which halves each CU's share of it: a problem with at most
-// half as many 256 x 256 tiles as CUs runs entirely as 128-row tiles; a
-// persistent one whose last round is at most half full runs its last
-// columns (enough 256-wide column tiles to hold that round's tiles) as a
-// second launch of 128-row tiles, one round of them, after the other
-// columns' whole rounds.  (With at most 128 rows, 128-row tiles always.)  Every output's K sum is the same chain of MFMAs
-// in both kernels, so the result is bit-identical to the 256-row tiling.
+// tiles of k_gemm_h instead, which halves each CU's share of it: a problem
+// with at most half as many 256 x 256 tiles as CUs, or with at most 128
+// rows, runs entirely on them; a persistent problem whose last round is at
+// most half full runs its last columns (enough 256-wide column tiles to hold
+// that round's tiles) as a second launch of 128-row tiles, one round of
+// them, after the other columns' whole rounds.  Every output's K sum is the
+// same chain of MFMAs in both kernels, so the result is bit-identical to
+// the 256-row tiling.
 template <int FA, int FB, bool OUT_BF16>
 hipError_t launch_scaled_typed(const GemmArgs& a) {
     const GemmParams p = make_params(a, 256, 256);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n, cus = a.num_cus;
     if (tiles == 0) return hipSuccess;
-    if (2 * tiles <= cus || a.M <= 128)
-        return launch_tiles<FA, FB, OUT_BF16, 128>(make_params(a, 128, 256), a.num_cus, a.stream);
+    if (2 * tiles <= cus || a.M <= 128) return launch_half<FA, FB, OUT_BF16>(make_params(a, 128, 256), a.stream);
     const int64_t last = tiles % cus;
     if (tiles > cus && a.K > 2 * kBK2 && last != 0 && 2 * last <= cus) {
         const int tail_n = (int)((last + p.tiles_m - 1) / p.tiles_m);            // column tiles of the tail
@@ -1132,13 +1239,12 @@ hipError_t launch_scaled_typed(const GemmArgs& a) {
             GemmParams head = p;
             head.N = n0;
             head.tiles_n = p.tiles_n - tail_n;
-            hipError_t e = launch_tiles<FA, FB, OUT_BF16, 256>(head, a.num_cus, a.stream);
+            hipError_t e = launch_tiles<FA, FB, OUT_BF16>(head, a.num_cus, a.stream);
             if (e != hipSuccess) return e;
-            return launch_tiles<FA, FB, OUT_BF16, 128>(column_range(p, n0, a.out_bf16 ? 2 : 4, 128), a.num_cus,
-                                                       a.stream);
+            return launch_half<FA, FB, OUT_BF16>(column_range(p, n0, a.out_bf16 ? 2 : 4, 128), a.stream);
         }
     }
-    return launch_tiles<FA, FB, OUT_BF16, 256>(p, a.num_cus, a.stream);
+    return launch_tiles<FA, FB, OUT_BF16>(p, a.num_cus, a.stream);
 }
 
 // Grouped GEMM ([DeepL bets on FP8] 3.2, MoE): one block builds the table of
