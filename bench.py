@@ -9,8 +9,14 @@ epilogue.  Default workload: the 8B-style MLP up-projection
 N(0, 0.02), per-tensor dynamic E4M3 scaling, Y bf16).
 
 Prints ONE JSON line.  `value` = whole-step throughput in TFLOP/s
-(2MNK / step time); the GEMM kernel's own TFLOP/s and % of the FP8 MFMA peak,
-and the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.
+(2MNK / step time); the GEMM's own TFLOP/s and % of the FP8 MFMA peak, and
+the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.  After
+the timed steps, `kernels` also gets the graphics clock sampled (amd-smi)
+while the GEMM repeats for 1.5 s, the GEMM's % of the FP8 peak at that
+clock, and a plain 512 MiB device copy's bandwidth as the practical
+streaming ceiling of the quantize; per-step times come as mean and as
+median / p10 / p90.  `cpu_baseline` is the oracle on a bounded sample of
+the same step (quantize on all threads and on one, GEMM on all threads).
 
     python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|dgrad|moe|kv|tiny]
 
@@ -79,7 +85,91 @@ def parse():
     ap.add_argument("--cpu-cols", type=int, default=4096, help="W rows in the CPU-baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for the HBM byte counters)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 1.5 s GEMM loop that samples the graphics clock")
     return ap.parse_args()
+
+
+def spread(ms):
+    """Median, p10 and p90 of per-step times (ms)."""
+    return {"median": round(float(np.median(ms)), 4), "p10": round(float(np.percentile(ms, 10)), 4),
+            "p90": round(float(np.percentile(ms, 90)), 4)}
+
+
+def copy_ceiling_gbs(torch, mib: int = 512, reps: int = 10) -> float:
+    """Bytes read + written per second of a plain device copy of `mib` MiB
+    (two buffers alternating, so no copy's source is still cached): the
+    practical ceiling a streaming kernel is measured against, beside the
+    published HBM peak."""
+    n = mib * 2 ** 20
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1)
+    for i in range(2):
+        bufs[2 + i].copy_(bufs[i])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        bufs[2 + (i & 1)].copy_(bufs[i & 1])
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def gemm_clock_mhz(torch, run, seconds: float = 1.5):
+    """Mean graphics clock (MHz) over the GPU's XCDs while `run` (one GEMM
+    call) repeats back to back for about `seconds`, from amd-smi's metrics
+    table.  The table refreshes with a lag of about half a second, so only
+    samples from the second half of the loop, with the GPU fully busy, count.
+    None where amd-smi is not available or no sample qualifies."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        bus = torch.cuda.get_device_properties(0).pci_bus_id
+        match = [h for h in handles if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus]
+        h = match[0] if len(match) == 1 else (handles[0] if len(handles) == 1 else None)
+        if h is None:
+            return None
+        amdsmi.amdsmi_get_gpu_metrics_info(h)
+    except Exception:
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    calls = max(10, int(seconds / (e0.elapsed_time(e1) * 1e-3 / 5)))
+    samples, done = [], threading.Event()
+
+    def sample():
+        while not done.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clks = m.get("current_gfxclks")
+                clks = [c for c in clks if isinstance(c, int)] if isinstance(clks, list) else []
+                if not clks and isinstance(m.get("current_gfxclk"), int):
+                    clks = [m["current_gfxclk"]]
+                samples.append((time.perf_counter(), clks, m.get("average_gfx_activity")))
+            except Exception:
+                pass
+            time.sleep(0.02)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    for _ in range(calls):
+        run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    done.set()
+    th.join()
+    mid = t0 + 0.5 * (t1 - t0)
+    good = [c for t, clks, act in samples if t >= mid and isinstance(act, int) and act >= 90 for c in clks]
+    return round(float(np.mean(good)), 1) if good else None
 
 
 def calibrate_copy(mib: int):
@@ -373,10 +463,23 @@ def kv_main(args, torch, fp8, synth):
     print(json.dumps(out), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, workload, synth):
     """The oracle, untuned, on a bounded sample of the same step: quantize the
     first `cpu_rows` rows of X and `cpu_cols` rows of W, then the GEMM block
-    Y[:cpu_rows, :cpu_cols] with the full K."""
+    Y[:cpu_rows, :cpu_cols] with the full K, on all the threads it gets;
+    the quantize again on one thread.  `value` is the sample's whole-step
+    rate; the quantize (algorithmic bytes of the two passes, as on the GPU)
+    and the GEMM are also reported on their own."""
     import oracle
     if workload not in ("mlp8b", "tiny"):
         return None
@@ -388,15 +491,31 @@ def cpu_baseline(args, workload, synth):
         X, W = synth.mlp8b()
         X, W = np.ascontiguousarray(X[:r]), np.ascontiguousarray(W[:c])
     K = X.shape[1]
+    in_bytes = X.dtype.itemsize          # bf16 bits (uint16) or fp32
+    qbytes = (X.size + W.size) * (2 * in_bytes + 1)
     t0 = time.perf_counter()
     qx = oracle.quantize(X, oracle.E4M3, "tensor")
     qw = oracle.quantize(W, oracle.E4M3, "tensor")
+    t1 = time.perf_counter()
     y, _ = oracle.gemm(qx["q"], 0, qw["q"], 0, qx["scale_inv"], qw["scale_inv"], with_p=True)
-    dt = time.perf_counter() - t0
+    t2 = time.perf_counter()
     threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t3 = time.perf_counter()
+        oracle.quantize(X, oracle.E4M3, "tensor")
+        oracle.quantize(W, oracle.E4M3, "tensor")
+        t4 = time.perf_counter()
+    finally:
+        oracle.set_num_threads(threads)
+    dt = t2 - t0
     return {"value": 2.0 * r * c * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "quantize X[:%d], W[:%d] (per-tensor E4M3) + GEMM Y[:%d, :%d] with K=%d: %.1f s"
-                      % (r, c, r, c, K, dt)}
+                      % (r, c, r, c, K, dt),
+            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "quantize_gbs": round(qbytes / (t1 - t0) / 1e9, 3),
+            "quantize_gbs_1_thread": round(qbytes / (t4 - t3) / 1e9, 3),
+            "gemm_gflops": round(2.0 * r * c * K / (t2 - t1) / 1e9, 2)}
 
 
 def main():
@@ -443,6 +562,10 @@ def main():
     gemm_tflops = flops / (g_ms.mean() * 1e-3) / 1e12
     qbytes = st.quant_bytes()
     q_gbs = qbytes / (q_ms.mean() * 1e-3) / 1e9
+    # after the timed region: the graphics clock under the GEMM, and a plain
+    # copy's bandwidth as the practical streaming ceiling
+    clock = None if args.no_clock else gemm_clock_mhz(torch, st.gemm)
+    copy_gbs = copy_ceiling_gbs(torch)
     roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
             "traffic": GEMM_TRAFFIC_BYTES if args.workload == "mlp8b" else None}
@@ -465,10 +588,17 @@ def main():
             "gemm_ms": round(float(g_ms.mean()), 4),
             "gemm_tflops": round(gemm_tflops, 2),
             "gemm_pct_fp8_peak": round(100 * gemm_tflops / PEAK_FP8_TFLOPS, 2),
+            "gemm_ms_spread": spread(g_ms),
+            "gemm_clock_mhz": clock,
+            "gemm_pct_fp8_peak_at_clock": (round(100 * gemm_tflops / (PEAK_FP8_TFLOPS * clock / 2400.0), 2)
+                                           if clock else None),
             "quantize_ms": round(float(q_ms.mean()), 4),
+            "quantize_ms_spread": spread(q_ms),
             "quantize_gbs": round(q_gbs, 1),
             "quantize_pct_hbm_peak": round(100 * q_gbs / PEAK_HBM_GBS, 2),
             "quantize_bytes": int(qbytes),
+            "copy_ceiling_gbs": round(copy_gbs, 1),
+            "quantize_pct_copy_ceiling": round(100 * q_gbs / copy_gbs, 2),
         },
         "roofline": roof,
         "cpu_baseline": cpu,

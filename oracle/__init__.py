@@ -90,12 +90,20 @@ def lib():
         L.or_kv_load.argtypes = [P, i32, i32, P, i64, i64, i64, P, i64, i32, P, i64]
         L.or_num_threads.restype = i32
         L.or_num_threads.argtypes = []
+        L.or_set_num_threads.restype = None
+        L.or_set_num_threads.argtypes = [i32]
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return int(lib().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (for timing it; results do not
+    depend on the thread count)."""
+    lib().or_set_num_threads(int(n))
 
 
 def _p(a: np.ndarray):

@@ -546,3 +546,6 @@ void or_kv_load(const void* cache, int storage, int scaling, const float* scale_
 
 /* Threads the OpenMP loops above use (reported with CPU timings). */
 int or_num_threads(void) { return omp_get_max_threads(); }
+
+/* Threads of the parallel loops above (timing only; results do not depend on it). */
+void or_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
