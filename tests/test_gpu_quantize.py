@@ -76,6 +76,26 @@ def test_codec_fp32_random_and_midpoints(fmt, k):
     assert mism.size == 0, (mism[:8].tolist(), v[tuple(mism[0])], got[tuple(mism[0])], want[tuple(mism[0])])
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_codec_exhaustive_over_active_binades(fmt):
+    """Every fp32 of both signs in the binades where an FP8 code varies
+    (from two binades below the smallest subnormal to the one past the
+    largest value: E4M3 21, E5M2 35 binades of 2^23 values) through the
+    GPU cast at scale 1.0, against the oracle, one binade per call."""
+    from tests.test_oracle_pins import active_binades, binade_bits
+    for e in active_binades(fmt):
+        for sg in (0, 1):
+            v = binade_bits(e, sg).view(np.float32).reshape(-1, 4096)
+            say("codec binade", FMT_NAME[fmt], e, sg)
+            r, _ = _quantize_fixed_scale(v, fmt, 0)
+            got = host(r.q)
+            want, _ = oracle.quantize_with_scales(v, fmt, "tensor", np.float32([1.0]))
+            mism = np.argwhere(got != want)
+            assert mism.size == 0, (e, sg, mism[:4].tolist(), v[tuple(mism[0])], got[tuple(mism[0])],
+                                    want[tuple(mism[0])])
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_codec_nan_inputs(fmt):
     payloads = np.array([0x7FC00000, 0x7F800001, 0x7FFFFFFF, 0xFFC00000, 0xFF800001, 0xFFFFFFFF],

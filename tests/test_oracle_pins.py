@@ -147,6 +147,41 @@ def test_encode_random_and_strided_fp32(fmt):
     assert np.array_equal(oracle.encode(fmt, v), torch_sat_encode(fmt, v))
 
 
+def active_binades(fmt):
+    """Unbiased exponents e whose binade [2^e, 2^(e+1)) holds fp32 values
+    with more than one FP8 code: from two binades below the smallest
+    subnormal to the binade past the largest finite value.  Every fp32
+    below encodes to +-0 and every one above saturates."""
+    t = oracle.decode_table(fmt)
+    pos = t[:128][np.isfinite(t[:128])]
+    lo = int(np.floor(np.log2(pos[pos > 0].min()))) - 2
+    hi = int(np.ceil(np.log2(pos.max()))) + 1
+    return range(lo, hi)
+
+
+def binade_bits(e: int, sign: int) -> np.ndarray:
+    return (np.uint32(sign << 31) | np.uint32((e + 127) << 23) |
+            np.arange(1 << 23, dtype=np.uint32)).astype(np.uint32)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encode_exhaustive_over_active_binades(fmt):
+    """Every fp32 of both signs in the binades where the code varies (E4M3:
+    21 binades, E5M2: 35; 2^23 values each) against torch's clamped cast;
+    the binades outside are covered by the strided sweep above."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(e, sg) for e in active_binades(fmt) for sg in (0, 1)]
+
+    def check(job):
+        v = binade_bits(*job).view(np.float32)
+        return job, np.array_equal(oracle.encode(fmt, v), torch_sat_encode(fmt, v))
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        bad = [job for job, ok in ex.map(check, jobs) if not ok]
+    assert not bad, bad
+    assert len(jobs) == 2 * (21 if fmt == oracle.E4M3 else 35)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_encode_specials(fmt):
     top = 0x7E if fmt == oracle.E4M3 else 0x7B
