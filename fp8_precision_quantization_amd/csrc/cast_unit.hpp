@@ -80,6 +80,28 @@ __device__ __forceinline__ Pack<InT> load_unit(const InT* __restrict__ x, int64_
     return p;
 }
 
+// Whole unit u of a contiguous, 16-byte aligned tensor: elements
+// [8u, 8u + 8) with plain 16-byte loads (the flat fast path).
+template <typename InT>
+__device__ __forceinline__ Pack<InT> load_flat(const InT* __restrict__ x, uint32_t u) {
+    Pack<InT> p;
+    const uint4* src = reinterpret_cast<const uint4*>(x);
+    if constexpr (sizeof(InT) == 2) {
+        const uint4 r = src[u];
+        p.w[0] = r.x; p.w[1] = r.y; p.w[2] = r.z; p.w[3] = r.w;
+    } else {
+        const uint4 r0 = src[2 * (uint64_t)u], r1 = src[2 * (uint64_t)u + 1];
+        p.w[0] = r0.x; p.w[1] = r0.y; p.w[2] = r0.z; p.w[3] = r0.w;
+        p.w[4] = r1.x; p.w[5] = r1.y; p.w[6] = r1.z; p.w[7] = r1.w;
+    }
+    return p;
+}
+
+// The 8 codes of whole unit u of a contiguous, 8-byte aligned code array.
+__device__ __forceinline__ void store_flat(uint8_t* __restrict__ q, uint32_t u, uint2 codes) {
+    reinterpret_cast<uint2*>(q)[u] = codes;
+}
+
 struct Counters {
     uint32_t sat = 0, nonfinite = 0, under = 0;
 };

@@ -116,7 +116,10 @@ constexpr int kUnroll = 4;
 
 // Per-tensor amax, pass 1: grid-stride over units, one partial per block.
 // `gate` non-null: run only while the history is empty (delayed bootstrap).
-template <typename InT>
+// FLAT: the tensor is one contiguous, 16-byte aligned run of g.cols
+// elements (g.rows == 1, vec_in), so every unit but a ragged last one is
+// whole and loads with plain indexing; block 0's thread 0 takes the last.
+template <typename InT, bool FLAT>
 __global__ __launch_bounds__(kThreads) void k_amax_partials(const InT* __restrict__ x, UnitGeom g,
                                                             bool vec_in, uint32_t* __restrict__ partials,
                                                             const fp8_amax_history* gate) {
@@ -124,7 +127,25 @@ __global__ __launch_bounds__(kThreads) void k_amax_partials(const InT* __restric
     if (gate != nullptr && gate->count != 0) return;
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t m = 0;
-    for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < g.units; u0 += stride * kUnroll) {
+    if constexpr (FLAT) {
+        const uint32_t whole = (uint32_t)(g.cols / 8);
+        for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < whole; u0 += stride * kUnroll) {
+            Pack<InT> p[kUnroll];
+#pragma unroll
+            for (int i = 0; i < kUnroll; ++i) {
+                const uint32_t u = u0 + i * stride;
+                p[i] = u < whole ? load_flat<InT>(x, u) : Pack<InT>{};
+            }
+#pragma unroll
+            for (int i = 0; i < kUnroll; ++i) m = max(m, p[i].abs_max());
+        }
+        if (whole < g.units && blockIdx.x == 0 && threadIdx.x == 0) {
+            int64_t off, qoff;
+            int nv;
+            g.locate(whole, off, qoff, nv);
+            m = max(m, load_unit<InT>(x, off, nv, false).abs_max());
+        }
+    } else for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < g.units; u0 += stride * kUnroll) {
         Pack<InT> p[kUnroll];
 #pragma unroll
         for (int i = 0; i < kUnroll; ++i) {
@@ -221,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h
 // writes amax_out).  DELAYED: s from the history (or the bootstrap partials
 // while it is empty); each block stores its own amax partial for the finish
 // kernel.  RECAST: s recorded by a guarded finish kernel, or nothing to do.
-template <typename InT, int FMT, int MODE, bool DIAG>
+template <typename InT, int FMT, int MODE, bool DIAG, bool FLAT>
 __global__ __launch_bounds__(kThreads) void k_cast_tensor(
     const InT* __restrict__ x, UnitGeom g, bool vec_in, uint8_t* __restrict__ q, bool vec_out,
     const uint32_t* __restrict__ partials_in, int n_in, const fp8_amax_history* hist, bool pow2,
@@ -245,7 +266,33 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t m = 0;
     Counters cnt;
-    for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < g.units; u0 += stride * kUnroll) {
+    if constexpr (FLAT) {     // contiguous input and codes: whole units, then the ragged last one
+        const uint32_t whole = (uint32_t)(g.cols / 8);
+        for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < whole; u0 += stride * kUnroll) {
+            Pack<InT> p[kUnroll];
+#pragma unroll
+            for (int i = 0; i < kUnroll; ++i) {
+                const uint32_t u = u0 + i * stride;
+                p[i] = u < whole ? load_flat<InT>(x, u) : Pack<InT>{};
+            }
+#pragma unroll
+            for (int i = 0; i < kUnroll; ++i) {
+                const uint32_t u = u0 + i * stride;
+                if (u < whole) {
+                    if constexpr (DELAYED) m = max(m, p[i].abs_max());
+                    store_flat(q, u, encode_unit<FMT, DIAG>(p[i], s, cnt));
+                }
+            }
+        }
+        if (whole < g.units && blockIdx.x == 0 && threadIdx.x == 0) {
+            int64_t off, qoff;
+            int nv;
+            g.locate(whole, off, qoff, nv);
+            const Pack<InT> p = load_unit<InT>(x, off, nv, false);
+            if constexpr (DELAYED) m = max(m, p.abs_max());
+            store_unit(q, qoff, nv, false, encode_unit<FMT, DIAG>(p, s, cnt));
+        }
+    } else for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < g.units; u0 += stride * kUnroll) {
         Pack<InT> p[kUnroll];
         int64_t qo[kUnroll];
         int nv[kUnroll];
@@ -619,9 +666,16 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
         const unsigned tgrid = grid_for(tiles, 1, kMaxCastBlocks);
         const bool v16 = a.q != nullptr && aligned(a.q, 16) && a.ldq % 16 == 0;
         const bool v2 = a.q2 != nullptr && aligned(a.q2, 8) && a.ldq2 % 8 == 0;
+        // contiguous, aligned input (and codes): the kernels' plain-indexed fast path
+        const bool flat_in = g.rows == 1 && vec_in;
+        const bool flat = flat_in && vec_out;
         // pass 1: amax partials (JIT), or the bootstrap partials of an empty history
-        hipLaunchKernelGGL(k_amax_partials<InT>, dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in, amax_partials,
-                           (const fp8_amax_history*)a.hist);
+        if (flat_in)
+            hipLaunchKernelGGL((k_amax_partials<InT, true>), dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in,
+                               amax_partials, (const fp8_amax_history*)a.hist);
+        else
+            hipLaunchKernelGGL((k_amax_partials<InT, false>), dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in,
+                               amax_partials, (const fp8_amax_history*)a.hist);
         if (!a.write_q) {
             hipLaunchKernelGGL(k_reduce_amax, dim3(1), dim3(kThreads), 0, st, (const uint32_t*)amax_partials,
                                (int)agrid, a.amax);
@@ -635,9 +689,14 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
                                (const uint32_t*)amax_partials, (int)agrid,                                \
                                (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
                                cast_partials, a.q2, a.ldq2, v2);                                          \
+        else if (flat)                                                                                    \
+            hipLaunchKernelGGL((k_cast_tensor<InT, FMT, MODE, DG, true>), dim3(cgrid), dim3(kThreads), 0, st, x,\
+                               g, vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,       \
+                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
+                               cast_partials);                                                            \
         else                                                                                              \
-            hipLaunchKernelGGL((k_cast_tensor<InT, FMT, MODE, DG>), dim3(cgrid), dim3(kThreads), 0, st, x, g,   \
-                               vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,          \
+            hipLaunchKernelGGL((k_cast_tensor<InT, FMT, MODE, DG, false>), dim3(cgrid), dim3(kThreads), 0, st,  \
+                               x, g, vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,    \
                                (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
                                cast_partials);                                                            \
     } while (0)
