@@ -206,8 +206,11 @@ fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows,
  * C: [M x N] fp32 or bf16 (round-to-nearest-even), leading dimension ldc.
  * Requirements: K % 16 == 0; A, B 16-byte aligned; lda, ldb multiples of 16
  * and <= 2^23; C aligned to its element size.  Results are bit-reproducible run to run
- * (no split-K, no atomics); they may differ from another tiling in the last
- * bits of the fp32 sum ([DeepL] 5.3). */
+ * (no split-K, no atomics).  Every output's K sum is the same sequence of
+ * matrix-core operations whatever M and N are and however the call splits
+ * into launches (256- or 128-row tiles), so an output's bits do not depend
+ * on the rest of the problem; they may differ from another library's
+ * tiling in the last bits of the fp32 sum ([DeepL] 5.3). */
 fp8_status fp8_scaled_gemm(const uint8_t* A, fp8_format fa, int64_t lda,
                            const uint8_t* B, fp8_format fb, int64_t ldb,
                            int64_t M, int64_t N, int64_t K,
