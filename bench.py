@@ -10,7 +10,14 @@ N(0, 0.02), per-tensor dynamic E4M3 scaling, Y bf16).
 
 Prints ONE JSON line.  `value` = whole-step throughput in TFLOP/s
 (2MNK / step time); the GEMM's own TFLOP/s and % of the FP8 MFMA peak, and
-the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.  After
+the quantize GB/s and % of HBM peak, are in `kernels` and `roofline`.  The
+K steps are timed as a whole by two HIP events around the loop (an event
+recorded between kernels costs the GPU several microseconds of idle time,
+so none is); the GEMM's and the quantize's own times come from K calls of
+each back to back, and their per-step spreads from a further K steps with
+events around each operation.  In a step the quantize also pays for the
+write-back of the previous GEMM's output from the cache, so its share of a
+step (step minus GEMM) is reported beside its own time.  After
 the timed steps, `kernels` also gets the graphics clock sampled (amd-smi)
 while the GEMM repeats for 1.5 s, the GEMM's % of the FP8 peak at that
 clock, and a plain 512 MiB device copy's bandwidth as the practical
@@ -88,6 +95,21 @@ def parse():
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the 1.5 s GEMM loop that samples the graphics clock")
     return ap.parse_args()
+
+
+def loop_ms(torch, fn, n: int) -> float:
+    """Mean ms per call of fn over n calls back to back, timed by two HIP
+    events around the whole loop (nothing else on the stream between the
+    calls: a HIP event recorded between kernels costs the GPU several
+    microseconds of idle time here)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
 
 
 def spread(ms):
@@ -414,21 +436,19 @@ def kv_main(args, torch, fp8, synth):
         st.store()
         st.load()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for s in range(K):
-        ev[s][0].record()
+
+    def step():
         st.store()
-        ev[s][1].record()
         st.load()
-        ev[s][2].record()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / K
-    s_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    l_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+
+    def store_only():                 # advances the layer as a step does
+        st.store()
+        st.i += 1
+
+    # the K steps timed as a whole, then each operation back to back
+    ms = loop_ms(torch, step, K)
+    s_ms = loop_ms(torch, store_only, K)
+    l_ms = loop_ms(torch, st.load, K)
     sb, lb = st.store_bytes(), st.load_bytes()
     s_gbs, l_gbs = sb / (s_ms * 1e-3) / 1e9, lb / (l_ms * 1e-3) / 1e9
     # the gather kernel dominates; its launches are the two loads of a step
@@ -539,29 +559,39 @@ def main():
     for _ in range(args.warmup):
         st.quantize()
         st.gemm()
-    torch.cuda.synchronize()
     K = args.steps
+
+    def step():
+        st.quantize()
+        st.gemm()
+
+    def quantize_only():              # advances the input rotation as a step does
+        st.quantize()
+        st.i += 1
+
+    # the K steps, timed as a whole: only the work between the two events
+    ms = loop_ms(torch, step, K)
+    # each operation on its own, back to back: its launches' own time
+    g_mean = loop_ms(torch, st.gemm, K)
+    q_mean = loop_ms(torch, quantize_only, K)
+    # per-step spread of each operation, from events around each call (these
+    # times include the events' own idle gaps)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
     for s in range(K):
         ev[s][0].record()
         st.quantize()
         ev[s][1].record()
         st.gemm()
         ev[s][2].record()
-    stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
     q_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
     g_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
-    ms = total_ms / K
     flops = 2.0 * st.M * st.N * st.K
-    gemm_tflops = flops / (g_ms.mean() * 1e-3) / 1e12
+    gemm_tflops = flops / (g_mean * 1e-3) / 1e12
     qbytes = st.quant_bytes()
-    q_gbs = qbytes / (q_ms.mean() * 1e-3) / 1e9
+    q_gbs = qbytes / (q_mean * 1e-3) / 1e9
     # after the timed region: the graphics clock under the GEMM, and a plain
     # copy's bandwidth as the practical streaming ceiling
     clock = None if args.no_clock else gemm_clock_mhz(torch, st.gemm)
@@ -585,15 +615,19 @@ def main():
         "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": WORKLOADS[args.workload], "M": st.M, "N": st.N, "K": st.K},
         "kernels": {
-            "gemm_ms": round(float(g_ms.mean()), 4),
+            "gemm_ms": round(g_mean, 4),
             "gemm_tflops": round(gemm_tflops, 2),
             "gemm_pct_fp8_peak": round(100 * gemm_tflops / PEAK_FP8_TFLOPS, 2),
             "gemm_ms_spread": spread(g_ms),
             "gemm_clock_mhz": clock,
             "gemm_pct_fp8_peak_at_clock": (round(100 * gemm_tflops / (PEAK_FP8_TFLOPS * clock / 2400.0), 2)
                                            if clock else None),
-            "quantize_ms": round(float(q_ms.mean()), 4),
+            "quantize_ms": round(q_mean, 4),
             "quantize_ms_spread": spread(q_ms),
+            # the quantize's share of a step (step minus the GEMM): it also
+            # pays for writing back the previous GEMM's cached output
+            "quantize_ms_in_step": round(ms - g_mean, 4),
+            "quantize_gbs_in_step": round(qbytes / ((ms - g_mean) * 1e-3) / 1e9, 1) if ms > g_mean else None,
             "quantize_gbs": round(q_gbs, 1),
             "quantize_pct_hbm_peak": round(100 * q_gbs / PEAK_HBM_GBS, 2),
             "quantize_bytes": int(qbytes),
