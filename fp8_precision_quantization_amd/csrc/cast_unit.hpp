@@ -48,15 +48,31 @@ template <> struct Pack<float> {             // 8 fp32 values
     }
 };
 
+// One 16-byte load; NT: non-temporal (streaming), so a tensor read once
+// does not displace the cache's lines (a line already cached still hits).
+// Measured per kernel: the flat per-tensor passes, the block casts and the
+// transposed cast gain from it; the row cast and the KV store lose, and
+// keep ordinary loads.
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const void* p) {
+    if constexpr (NT) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(t.x, t.y, t.z, t.w);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
+
 // Load `nvalid` (0..8) elements starting at x + off; missing ones are 0.
 // `vec`: x + off is 16-byte aligned and the unit is whole.
-template <typename InT>
+template <typename InT, bool NT = false>
 __device__ __forceinline__ Pack<InT> load_unit(const InT* __restrict__ x, int64_t off, int nvalid,
                                                bool vec) {
     Pack<InT> p;
     if constexpr (sizeof(InT) == 2) {
         if (vec && nvalid == 8) {
-            const uint4 r = *reinterpret_cast<const uint4*>(x + off);
+            const uint4 r = load16<NT>(x + off);
             p.w[0] = r.x; p.w[1] = r.y; p.w[2] = r.z; p.w[3] = r.w;
         } else {
 #pragma unroll
@@ -68,8 +84,8 @@ __device__ __forceinline__ Pack<InT> load_unit(const InT* __restrict__ x, int64_
         }
     } else {
         if (vec && nvalid == 8) {
-            const uint4 r0 = *reinterpret_cast<const uint4*>(x + off);
-            const uint4 r1 = *reinterpret_cast<const uint4*>(x + off + 4);
+            const uint4 r0 = load16<NT>(x + off);
+            const uint4 r1 = load16<NT>(x + off + 4);
             p.w[0] = r0.x; p.w[1] = r0.y; p.w[2] = r0.z; p.w[3] = r0.w;
             p.w[4] = r1.x; p.w[5] = r1.y; p.w[6] = r1.z; p.w[7] = r1.w;
         } else {
@@ -81,16 +97,16 @@ __device__ __forceinline__ Pack<InT> load_unit(const InT* __restrict__ x, int64_
 }
 
 // Whole unit u of a contiguous, 16-byte aligned tensor: elements
-// [8u, 8u + 8) with plain 16-byte loads (the flat fast path).
+// [8u, 8u + 8) with plain non-temporal 16-byte loads (the flat fast path).
 template <typename InT>
 __device__ __forceinline__ Pack<InT> load_flat(const InT* __restrict__ x, uint32_t u) {
     Pack<InT> p;
     const uint4* src = reinterpret_cast<const uint4*>(x);
     if constexpr (sizeof(InT) == 2) {
-        const uint4 r = src[u];
+        const uint4 r = load16<true>(src + u);
         p.w[0] = r.x; p.w[1] = r.y; p.w[2] = r.z; p.w[3] = r.w;
     } else {
-        const uint4 r0 = src[2 * (uint64_t)u], r1 = src[2 * (uint64_t)u + 1];
+        const uint4 r0 = load16<true>(src + 2 * (uint64_t)u), r1 = load16<true>(src + 2 * (uint64_t)u + 1);
         p.w[0] = r0.x; p.w[1] = r0.y; p.w[2] = r0.z; p.w[3] = r0.w;
         p.w[4] = r1.x; p.w[5] = r1.y; p.w[6] = r1.z; p.w[7] = r1.w;
     }

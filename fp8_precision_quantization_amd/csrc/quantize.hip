@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
             const int64_t r = r0 + rr + 16 * i;
             const int nv = (r < rows) ? nvc : 0;
             if (nv > 0) {
-                p[i] = load_unit<InT>(x, r * ld + c, nv, vec_in);
+                p[i] = load_unit<InT, true>(x, r * ld + c, nv, vec_in);
             } else {
 #pragma unroll
                 for (int k = 0; k < (int)(sizeof(p[i].w) / 4); ++k) p[i].w[k] = 0u;
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_1x128(
                 xo[i] = r * ld + c;
                 qo[i] = r * ldq + c;
                 if (nv[i] > 0) {
-                    p[i] = load_unit<InT>(x, xo[i], nv[i], vec_in);
+                    p[i] = load_unit<InT, true>(x, xo[i], nv[i], vec_in);
                     m[i] = p[i].abs_max();
                 }
             }
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_128x128(
     for (int i = 0; i < 8; ++i) {
         const int64_t r = r0 + rr + 16 * i;
         if (r < rows && nvc > 0) {
-            p[i] = load_unit<InT>(x, r * ld + c, nvc, vec_in);
+            p[i] = load_unit<InT, true>(x, r * ld + c, nvc, vec_in);
             m = max(m, p[i].abs_max());
         }
     }
