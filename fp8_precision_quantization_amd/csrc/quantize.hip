@@ -435,9 +435,12 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
     }
 }
 
-// Row-wise: one wave per row, the row held in registers when it has at most
-// 64*NU units (a second read otherwise).  [DeepL] 2.3 (per-row scaling of
-// activations); [Soup] rowwise recipe (power-of-two scales).
+// Row-wise: a persistent grid of waves, wave w taking rows w, w + W, w + 2W
+// ... (W waves in all).  A row of at most 64*NU units is held in registers,
+// and the next row's loads are in flight while this one is reduced and
+// encoded (two register sets, alternating); longer rows are read twice.
+// [DeepL] 2.3 (per-row scaling of activations); [Soup] rowwise recipe
+// (power-of-two scales).
 template <typename InT, int FMT, bool DIAG, bool WRITE_Q, int NU = 8>
 __global__ __launch_bounds__(kThreads) void k_cast_rows(
     const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
@@ -445,61 +448,66 @@ __global__ __launch_bounds__(kThreads) void k_cast_rows(
     float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag) {
     __shared__ uint32_t lds[16];
     const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const bool active = r < rows;
+    const int64_t W = (int64_t)gridDim.x * 4;
+    const int64_t r0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t upr = (cols + 7) / 8;
-    const InT* xr = x + (active ? r : 0) * ld;
-    uint8_t* qr = q + (active ? r : 0) * ldq;
     Counters cnt;
-    if (upr <= 64 * NU) {
-        Pack<InT> p[NU];
+    auto nvalid = [&](int64_t c) { return cols - c >= 8 ? 8 : (int)(cols - c); };
+    // the row's amax, its scale, and (WRITE_Q) its codes from units held in p
+    auto finish = [&](const Pack<InT>* p, int64_t r) {
         uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const int64_t u = lane + 64 * i;
-            if (active && u < upr) {
-                const int64_t c = u * 8;
-                const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
-                p[i] = load_unit<InT>(xr, c, nv, vec_in);
-                m = max(m, p[i].abs_max());
-            }
-        }
+        for (int i = 0; i < NU; ++i)
+            if (lane + 64 * i < upr) m = max(m, p[i].abs_max());
         m = wave_max_u32(m);
         const float s = scale_from_amax_bits<FMT>(m, pow2);
-        if (active && lane == 0) {
+        if (lane == 0) {
             amax_out[r] = __uint_as_float(m);
             if (WRITE_Q) scale_inv_out[r] = recip_rn(s);
         }
         if constexpr (WRITE_Q) {
+            uint8_t* qr = q + r * ldq;
 #pragma unroll
             for (int i = 0; i < NU; ++i) {
                 const int64_t u = lane + 64 * i;
-                if (active && u < upr) {
-                    const int64_t c = u * 8;
-                    const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
-                    store_unit(qr, c, nv, vec_out, encode_unit<FMT, DIAG>(p[i], s, cnt));
-                }
+                if (u < upr) store_unit(qr, u * 8, nvalid(u * 8), vec_out, encode_unit<FMT, DIAG>(p[i], s, cnt));
             }
         }
+    };
+    auto load = [&](Pack<InT>* p, int64_t r) {
+        const InT* xr = x + r * ld;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int64_t u = lane + 64 * i;
+            if (u < upr) p[i] = load_unit<InT>(xr, u * 8, nvalid(u * 8), vec_in);
+        }
+    };
+    if (upr <= 64 * NU) {
+        Pack<InT> pa[NU], pb[NU];
+        if (r0 < rows) load(pa, r0);
+        for (int64_t r = r0; r < rows; r += 2 * W) {
+            const int64_t r1 = r + W, r2 = r + 2 * W;
+            if (r1 < rows) load(pb, r1);
+            finish(pa, r);
+            if (r2 < rows) load(pa, r2);
+            if (r1 < rows) finish(pb, r1);
+        }
     } else {
-        uint32_t m = 0;
-        for (int64_t u = lane; active && u < upr; u += 64) {
-            const int64_t c = u * 8;
-            const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
-            m = max(m, load_unit<InT>(xr, c, nv, vec_in).abs_max());
-        }
-        m = wave_max_u32(m);
-        const float s = scale_from_amax_bits<FMT>(m, pow2);
-        if (active && lane == 0) {
-            amax_out[r] = __uint_as_float(m);
-            if (WRITE_Q) scale_inv_out[r] = recip_rn(s);
-        }
-        if constexpr (WRITE_Q) {
-            for (int64_t u = lane; active && u < upr; u += 64) {
-                const int64_t c = u * 8;
-                const int nv = cols - c >= 8 ? 8 : (int)(cols - c);
-                store_unit(qr, c, nv, vec_out,
-                           encode_unit<FMT, DIAG>(load_unit<InT>(xr, c, nv, vec_in), s, cnt));
+        for (int64_t r = r0; r < rows; r += W) {
+            const InT* xr = x + r * ld;
+            uint32_t m = 0;
+            for (int64_t u = lane; u < upr; u += 64) m = max(m, load_unit<InT>(xr, u * 8, nvalid(u * 8), vec_in).abs_max());
+            m = wave_max_u32(m);
+            const float s = scale_from_amax_bits<FMT>(m, pow2);
+            if (lane == 0) {
+                amax_out[r] = __uint_as_float(m);
+                if (WRITE_Q) scale_inv_out[r] = recip_rn(s);
+            }
+            if constexpr (WRITE_Q) {
+                uint8_t* qr = q + r * ldq;
+                for (int64_t u = lane; u < upr; u += 64)
+                    store_unit(qr, u * 8, nvalid(u * 8), vec_out,
+                               encode_unit<FMT, DIAG>(load_unit<InT>(xr, u * 8, nvalid(u * 8), vec_in), s, cnt));
             }
         }
     }
@@ -616,6 +624,8 @@ constexpr int64_t kMaxCastBlocks = 4096;
 constexpr int64_t kMaxAmaxBlocks = 1024;   // a stream needs about 4 workgroups per CU (measured)
 static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchDiag, "scratch layout");
 static_assert(kScratchDiag + 4 <= kScratchGroupTable, "scratch layout: the grouped GEMM's table follows");
+
+constexpr int64_t kRowBlocksPerCU = 3;   // measured: 2 and 3 per CU, 3 faster
 
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
     int64_t b = (work_items + per_block - 1) / per_block;
@@ -746,8 +756,8 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
     } while (0)
 
     if (a.gran == FP8_GRAN_ROW) {
-        const dim3 grid((unsigned)((a.rows + 3) / 4));
-        // rows up to 4096 elements are held in registers
+        // a persistent grid of kRowBlocksPerCU blocks (4 waves each) per CU
+        const dim3 grid(grid_for(a.rows, 4, (int64_t)a.num_cus * kRowBlocksPerCU));
         FP8MI_GROUP_LAUNCH(k_cast_rows, grid);
     } else if (a.gran == FP8_GRAN_BLOCK_1x128) {
         const int64_t G = a.rows * ((a.cols + 127) / 128);
