@@ -84,6 +84,7 @@ struct GemmParams {
     // group: expert, first row, end row of the group) and expert stride of B
     const int4* gtab;
     int64_t b_gstride;
+    int main_grid;        // grouped: the persistent grid, when k_gemm_h takes a last round split off (else 0)
 };
 
 template <int FX, int FY>
@@ -602,13 +603,32 @@ __device__ __forceinline__ float load_uniform(const float* ptr) {
 // Linear tile of block b in round r (persistent grid of G blocks): the
 // blocks of one round take G consecutive tiles, each XCD a contiguous range
 // of them; the linear index is then grouped along M as in tile_coords.
-__device__ __forceinline__ bool tile_of_round(const GemmParams& p, int tiles_m, int group_m, int r, int& tm,
-                                              int& tn) {
+__device__ __forceinline__ void tile_of_linear(const GemmParams& p, int tiles_m, int group_m, int t, int& tm,
+                                               int& tn) {
+    const int per_group = group_m * p.tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int in_group = t - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+// Grouped: the linear tiles [0, T) of a persistent grid of G blocks whose
+// last round is at most half full end at the last whole round; k_gemm_h
+// takes the rest as 128-row halves.
+__device__ __forceinline__ int grouped_main_tiles(int T, int G) {
+    const int rem = T % G;
+    return (T > G && rem != 0 && 2 * rem <= G) ? T - rem : T;
+}
+
+__device__ __forceinline__ bool tile_of_round(const GemmParams& p, int tiles_m, int group_m, int limit, int r,
+                                              int& tm, int& tn) {
     const int G = gridDim.x;
     int b = blockIdx.x;
     if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
     const int t = r * G + b;
-    if (t >= tiles_m * p.tiles_n) return false;
+    if (t >= limit) return false;
     const int per_group = group_m * p.tiles_n;
     const int group = t / per_group;
     const int first_m = group * group_m;
@@ -688,9 +708,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
     auto ptr = [&](int slot) { return g_ring + slot * kSlot2; };
 
     int tm, tn;
-    if (!tile_of_round(p, tiles_m, group_m, 0, tm, tn)) return;
+    int limit = tiles_m * p.tiles_n;
+    if constexpr (GROUPED) {
+        if (p.main_grid) limit = grouped_main_tiles(limit, (int)gridDim.x);
+    }
+    if (!tile_of_round(p, tiles_m, group_m, limit, 0, tm, tn)) return;
     int tm_n = 0, tn_n = 0;
-    bool has_next = tile_of_round(p, tiles_m, group_m, 1, tm_n, tn_n);
+    bool has_next = tile_of_round(p, tiles_m, group_m, limit, 1, tm_n, tn_n);
     TileRef<GROUPED, BM> cur, nxt;
     cur.load(p, tm);
     if (has_next) nxt.load(p, tm_n);
@@ -780,7 +804,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
         first_vm = interior ? 2 : 1;
         tm = tm_n; tn = tn_n;
         if constexpr (GROUPED) cur = nxt;
-        has_next = tile_of_round(p, tiles_m, group_m, r + 2, tm_n, tn_n);
+        has_next = tile_of_round(p, tiles_m, group_m, limit, r + 2, tm_n, tn_n);
         if (has_next) nxt.load(p, tm_n);
         __syncthreads();   // every wave is done with the staging slot
 #pragma unroll
@@ -807,19 +831,43 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
 constexpr int kHStage = 128 * kBK2 + 256 * kBK2;      // 48 KiB: A, then B
 constexpr int kHRing = 3 * kHStage;
 
-template <int FA, int FB, bool OUT_BF16>
+// GROUPED: the blocks take the grouped GEMM's tiles that the persistent
+// kernel left (its last round, when at most half full: grouped_main_tiles
+// with the grid p.main_grid), block b the half b % 2 of the b/2-th of them;
+// a tile's half past its group's end, and blocks past the tiles, exit.
+template <int FA, int FB, bool OUT_BF16, bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
     using DA = DmaL<128>;
     constexpr int kVm1 = DA::kInst + Dma2::kInst;  // A(s+2) and B(s+2) may still fly
     const float sa0 = load_uniform(p.sa);
-    const float sb0 = load_uniform(p.sb);
+    float sb0;
+    int tm, tn, m0, m_end;
+    const uint8_t* Bp = p.B;
+    const float* sbp = p.sb;
+    if constexpr (GROUPED) {
+        const int tiles_m = min(p.gtab[0].x, p.tiles_m);
+        const int T = tiles_m * p.tiles_n;
+        const int t = grouped_main_tiles(T, p.main_grid) + (int)(blockIdx.x >> 1);
+        if (t >= T) return;
+        tile_of_linear(p, tiles_m, tiles_m < 4 ? tiles_m : 4, t, tm, tn);
+        const int4 e = p.gtab[1 + tm];
+        m0 = e.y + 128 * (int)(blockIdx.x & 1);
+        m_end = e.z;
+        if (m0 >= m_end) return;
+        Bp = p.B + (int64_t)e.x * p.b_gstride;
+        sbp = p.sb + (p.sb_row ? (int64_t)e.x * p.N : (int64_t)e.x);
+        sb0 = load_uniform(sbp);
+    } else {
+        sb0 = load_uniform(p.sb);
+        tile_coords(p, tm, tn);
+        m0 = tm * 128;
+        m_end = p.M;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = p.K;
     const int nks = (K + kBK2 - 1) / kBK2;
-    int tm, tn;
-    tile_coords(p, tm, tn);
-    const int m0 = tm * 128, n0 = tn * 256;
+    const int n0 = tn * 256;
     const uint32_t ring = lds_addr(g_ring);
     auto addr = [&](int slot) { return ring + (uint32_t)(slot * kHStage); };
     auto aptr = [&](int slot) { return g_ring + slot * kHStage; };
@@ -827,8 +875,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
 
     DA da;
     Dma2 db;
-    da.init(p.A, p.lda, m0, p.M, wave);
-    db.init(p.B, p.ldb, n0, p.N, wave);
+    da.init(p.A, p.lda, m0, m_end, wave);
+    db.init(Bp, p.ldb, n0, p.N, wave);
 
     v16f acc[4][2];
 #pragma unroll
@@ -884,8 +932,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
     // epilogue stages its values through the ring
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __syncthreads();
-    const bool interior = p.vec_out && m0 + 128 <= p.M && n0 + 256 <= p.N;
-    epilogue_slot<OUT_BF16, 128>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
+    const bool interior = p.vec_out && m0 + 128 <= m_end && n0 + 256 <= p.N;
+    if constexpr (GROUPED) {
+        GemmParams pt = p;           // the tile's rows end at its group's end
+        pt.M = m_end;
+        pt.sb = sbp;
+        epilogue_slot<OUT_BF16, 128>(pt, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
+    } else {
+        epilogue_slot<OUT_BF16, 128>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -1158,6 +1213,7 @@ GemmParams make_params(const GemmArgs& a, int bm, int bn) {
     p.vec_out = ((a.ldc * esz) % 16 == 0) && ((uintptr_t)a.C % 16 == 0);   // 16-byte row chunks
     p.gtab = nullptr;
     p.b_gstride = 0;
+    p.main_grid = 0;
     return p;
 }
 
@@ -1186,16 +1242,18 @@ hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// One launch of k_gemm_h over p (128-row tiles, one block each).
-template <int FA, int FB, bool OUT_BF16>
-hipError_t launch_half(const GemmParams& p, hipStream_t stream) {
+// One launch of k_gemm_h: over p's tiles (128-row tiles, one block each),
+// or GROUPED over the grouped GEMM's split-off last round (`grid` blocks).
+template <int FA, int FB, bool OUT_BF16, bool GROUPED = false>
+hipError_t launch_half(const GemmParams& p, hipStream_t stream, unsigned grid_grouped = 0) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [&] { attr_err = set_lds(k_gemm_h<FA, FB, OUT_BF16>, (size_t)kHRing); });
+    std::call_once(once, [&] { attr_err = set_lds(k_gemm_h<FA, FB, OUT_BF16, GROUPED>, (size_t)kHRing); });
     if (attr_err != hipSuccess) return attr_err;
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    const unsigned grid = GROUPED ? grid_grouped : (unsigned)(p.tiles_m * p.tiles_n);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm_h<FA, FB, OUT_BF16>), dim3(grid), dim3(kGemmThreads), (size_t)kHRing, stream, p);
+    hipLaunchKernelGGL((k_gemm_h<FA, FB, OUT_BF16, GROUPED>), dim3(grid), dim3(kGemmThreads), (size_t)kHRing,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -1315,15 +1373,21 @@ hipError_t launch_grouped_typed(const GemmArgs& a) {
     const int64_t mt = std::min<int64_t>((a.M + 255) / 256 + a.groups, kGroupTableTiles);
     p.tiles_m = (int)mt;
     int64_t grid = mt * p.tiles_n;
-    if (grid > a.num_cus && a.K > 2 * kBK2) grid = a.num_cus;
+    // persistent: a last round of tiles at most half full (the count is
+    // known on the device only) is split off to k_gemm_h as 128-row halves
+    const bool split = grid > a.num_cus && a.K > 2 * kBK2;
+    if (split) grid = a.num_cus;
     if (grid == 0) return hipGetLastError();
+    p.main_grid = split ? (int)grid : 0;
     if (a.K % kBK2 != 0)
         hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, true>), dim3((unsigned)grid), dim3(kGemmThreads),
                            lds_scaled<OUT_BF16>(), a.stream, p);
     else
         hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, false, true>), dim3((unsigned)grid), dim3(kGemmThreads),
                            lds_scaled<OUT_BF16>(), a.stream, p);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !split) return e;
+    return launch_half<FA, FB, OUT_BF16, true>(p, a.stream, (unsigned)grid);
 }
 
 // Block-scaled GEMM (E4M3 x E4M3): 256 x 128 tiles, one block each.

@@ -123,6 +123,34 @@ def test_grouped_groups_equal_plain_gemm_bitwise():
         assert np.array_equal(y[lo:hi].view(np.uint32), host(ref).view(np.uint32)), g
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_grouped_split_last_round(out_dtype):
+    """A persistent grouped GEMM whose last round is at most half full
+    (13 M-tiles x 20 N-tiles = 260 tiles on 256 CUs): the last 4 tiles, all
+    of the last group's single tile of 129 rows, run as 128-row halves (the
+    second half one row).  K ragged, one scale per A row and per expert
+    row.  Every group against the oracle, and bit for bit against the plain
+    scaled GEMM of its rows with its expert."""
+    sizes, N, K = [300, 0, 513, 700, 1000, 129], 5120, 528
+    A, B, a_inv, b_inv, offsets = _problem(sizes, N, K, 0, 0, 41, lead=3, b_rows=True)
+    say("grouped split last round", out_dtype)
+    y = _run(A, B, a_inv, b_inv, offsets, 0, 0, out_dtype)
+    _check(y, A, B, a_inv, b_inv, offsets, 0, 0, out_dtype, np.random.default_rng(7), per_group=300,
+           what="split last round")
+    for g in range(len(sizes)):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi == lo:
+            continue
+        say("grouped split last round: plain GEMM of group", g)
+        ref = fp8.scaled_gemm(dev_u8(A[lo:hi]), dev_u8(B[g]), torch.from_numpy(a_inv[lo:hi]).cuda(),
+                              torch.from_numpy(b_inv[g]).cuda(), out_dtype=out_dtype)
+        got, want = y[lo:hi], host(ref)
+        if out_dtype == torch.bfloat16:
+            assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), g
+        else:
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), g
+
+
 def test_grouped_one_group_is_plain_gemm_and_repeatable():
     M, N, K = 1000, 1280, 768
     A, B, a_inv, b_inv, offsets = _problem([M], N, K, 0, 0, 22, tail=0)
