@@ -442,12 +442,13 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[4][BM / 64], const Frags<BM
     }
 }
 
-// Epilogue of one BM x 256 tile staged through one 32 KiB ring slot: each
-// wave owns 8 KiB = 32 rows x 256 bytes of it, so it writes its (BM/2) x 128
+// Epilogue of one BM x 256 tile staged through 32 KiB of LDS: each wave
+// owns 8 KiB = 32 rows x 256 bytes of it, so it writes its (BM/2) x 128
 // tile in passes of one 32-row MFMA block (BM = 256, bf16: all 128 columns,
-// 4 passes; fp32: 64 columns, 8 passes; BM = 128: half as many).  A pass writes the scaled, converted values
-// (row r's 16-byte chunk c at physical chunk c ^ (r & 15)), reads them back
-// as 16-byte row chunks (16 lanes per 256-byte row segment) and stores them.
+// 4 passes; fp32: 64 columns, 8 passes; BM = 128: half as many).  A pass
+// writes the scaled, converted values (row r's 16-byte chunk c at physical
+// chunk c ^ (r & 15)), reads them back as 16-byte row chunks (16 lanes per
+// 256-byte row segment) and stores them.
 // An interior tile with 16-byte aligned rows issues exactly kStores vector
 // stores per wave, unconditionally (the persistent loop's vmcnt accounting
 // relies on it).

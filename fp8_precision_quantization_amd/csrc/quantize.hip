@@ -496,7 +496,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_rows(
         for (int64_t r = r0; r < rows; r += W) {
             const InT* xr = x + r * ld;
             uint32_t m = 0;
-            for (int64_t u = lane; u < upr; u += 64) m = max(m, load_unit<InT>(xr, u * 8, nvalid(u * 8), vec_in).abs_max());
+            for (int64_t u = lane; u < upr; u += 64)
+                m = max(m, load_unit<InT>(xr, u * 8, nvalid(u * 8), vec_in).abs_max());
             m = wave_max_u32(m);
             const float s = scale_from_amax_bits<FMT>(m, pow2);
             if (lane == 0) {
