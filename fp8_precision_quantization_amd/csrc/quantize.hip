@@ -15,6 +15,8 @@
 // convert.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "cast_unit.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -358,11 +360,11 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
     const int64_t tiles = ((rows + 127) / 128) * tiles_c;
     uint32_t m = 0;
     Counters cnt;
-    for (int64_t tl = blockIdx.x; tl < tiles; tl += gridDim.x) {
-        const int64_t r0 = (tl / tiles_c) * 128, c0 = (tl % tiles_c) * 128;
-        const int64_t c = c0 + cu * 8;
+    // this thread's 8 units of tile tl (zeros past the matrix)
+    Pack<InT> p[8];
+    auto load_tile = [&](int64_t tl) {
+        const int64_t r0 = (tl / tiles_c) * 128, c = (tl % tiles_c) * 128 + cu * 8;
         const int nvc = (int)(cols - c >= 8 ? 8 : (cols - c > 0 ? cols - c : 0));
-        Pack<InT> p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t r = r0 + rr + 16 * i;
@@ -374,6 +376,14 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
                 for (int k = 0; k < (int)(sizeof(p[i].w) / 4); ++k) p[i].w[k] = 0u;
             }
         }
+    };
+    // grid-stride over tiles; the next tile's loads are issued as soon as
+    // this tile's codes are in LDS, so they overlap its transposed stores
+    if ((int64_t)blockIdx.x < tiles) load_tile(blockIdx.x);
+    for (int64_t tl = blockIdx.x; tl < tiles; tl += gridDim.x) {
+        const int64_t r0 = (tl / tiles_c) * 128, c0 = (tl % tiles_c) * 128;
+        const int64_t c = c0 + cu * 8;
+        const int nvc = (int)(cols - c >= 8 ? 8 : (cols - c > 0 ? cols - c : 0));
         __syncthreads();   // the previous tile's gathers are done with `tile`
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -385,6 +395,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
             if (q2 != nullptr && r0 + r < rows && nvc > 0) store_unit(q2, (r0 + r) * ldq2 + c, nvc, vec_out2, codes);
         }
         __syncthreads();
+        if (tl + gridDim.x < tiles) load_tile(tl + gridDim.x);
         // gather: thread (rs = t % 8, cl4 = t / 8) takes input rows rs*16 ..
         // rs*16+15 of input columns 4*cl4 .. 4*cl4+3 as 16 words (one row
         // each), transposes the four 4x4 byte blocks with byte permutes and
@@ -626,6 +637,7 @@ constexpr int64_t kMaxAmaxBlocks = 1024;   // a stream needs about 4 workgroups 
 static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchDiag, "scratch layout");
 static_assert(kScratchDiag + 4 <= kScratchGroupTable, "scratch layout: the grouped GEMM's table follows");
 
+constexpr int64_t kTBlocksPerCU = 4;     // transposed cast: tiles per block = tiles / (CUs * this)
 constexpr int64_t kRowBlocksPerCU = 3;   // measured: 2 and 3 per CU, 3 faster
 
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
@@ -674,7 +686,7 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
         const unsigned agrid = grid_for(g.units, (int64_t)kThreads * kUnroll, kMaxAmaxBlocks);
         const unsigned cgrid = grid_for(g.units, (int64_t)kThreads * kUnroll, cap);
         const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 127) / 128);
-        const unsigned tgrid = grid_for(tiles, 1, kMaxCastBlocks);
+        const unsigned tgrid = grid_for(tiles, 1, std::min<int64_t>(kMaxCastBlocks, (int64_t)a.num_cus * kTBlocksPerCU));
         const bool v16 = a.q != nullptr && aligned(a.q, 16) && a.ldq % 16 == 0;
         const bool v2 = a.q2 != nullptr && aligned(a.q2, 8) && a.ldq2 % 8 == 0;
         // contiguous, aligned input (and codes): the kernels' plain-indexed fast path
