@@ -231,6 +231,45 @@ def test_quantize_transposed(shape, fmt):
     assert (d["sat"], d["underflow"]) == (want["sat"], want["underflow"])
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_transposed_and_dual_many_tiles(fmt):
+    """More 128x128 tiles (33 x 40 = 1320) than the transposed cast's grid
+    (4 blocks per CU), so blocks walk several tiles, ragged ones included,
+    with the next tile's loads in flight: the transposed codes, and both
+    layouts of the dual cast, against the oracle."""
+    rows, cols = 4100, 5000
+    x = _inputs(rows, cols, "bf16", 78)
+    want = oracle.quantize(x, fmt, "tensor")
+    xt = dev_input(x)
+    say("quantize transposed many tiles", FMT_NAME[fmt])
+    r = fp8.quantize(xt, FMT_NAME[fmt], "tensor", transpose=True)
+    assert np.array_equal(host(r.q), want["q"].T)
+    assert host(r.scale_inv)[0] == want["scale_inv"][0, 0]
+    say("quantize dual many tiles", FMT_NAME[fmt])
+    rd, qt = fp8.quantize_dual(xt, FMT_NAME[fmt])
+    assert np.array_equal(host(rd.q), want["q"]) and np.array_equal(host(qt), want["q"].T)
+    assert host(rd.scale_inv)[0] == want["scale_inv"][0, 0]
+
+
+@pytest.mark.parametrize("shape", [(7000, 3000), (5000, 4104)])
+def test_quantize_rows_persistent_loop(shape):
+    """More rows than the row cast's persistent grid has waves (3 blocks of 4
+    waves per CU), so every wave loops over rows with the next row's loads in
+    flight: ragged rows held in registers (3000) and rows past 4096 elements
+    (the two-read path); codes, per-row scales and amaxes, counters."""
+    rows, cols = shape
+    x = _inputs(rows, cols, "bf16", 79)
+    say("quantize rows persistent", shape)
+    diag = fp8.Diag()
+    r = fp8.quantize(dev_input(x), "e4m3", "row", pow2=True, diag=diag)
+    want = oracle.quantize(x, oracle.E4M3, "row", True)
+    assert np.array_equal(host(r.q), want["q"])
+    assert np.array_equal(host(r.scale_inv).reshape(-1), want["scale_inv"].reshape(-1))
+    assert np.array_equal(host(r.amax).reshape(-1), want["amax"].reshape(-1))
+    d = diag.read()
+    assert (d["sat"], d["nonfinite"], d["underflow"]) == (want["sat"], want["nonfinite"], want["underflow"])
+
+
 # ---------------------------------------------------------------- delayed --
 @pytest.mark.parametrize("transpose", [False, True])
 def test_delayed_ring_20_steps(transpose):
