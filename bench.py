@@ -22,7 +22,8 @@ the timed steps, `kernels` also gets the graphics clock sampled (amd-smi)
 while the GEMM repeats for 1.5 s, the GEMM's % of the FP8 peak at that
 clock, and a plain 512 MiB device copy's bandwidth as the practical
 streaming ceiling of the quantize; per-step times come as mean and as
-median / p10 / p90.  `cpu_baseline` is the oracle on a bounded sample of
+median / p10 / p90; `quantize_rel_err` is each operand's ||dequant(q) - x|| /
+||x|| with its granularity and format.  `cpu_baseline` is the oracle on a bounded sample of
 the same step (quantize on all threads and on one, GEMM on all threads).
 
     python bench.py [--steps K] [--warmup W] [--workload mlp8b|qkv|mlp70b|wgrad|dgrad|moe|kv|tiny]
@@ -110,6 +111,28 @@ def loop_ms(torch, fn, n: int) -> float:
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n
+
+
+def quant_rel_err(torch, x, q, s_inv, fmt: str, gran: str, transposed: bool = False) -> float:
+    """Relative error ||dequant(q) - x|| / ||x|| (Frobenius) of one cast,
+    on the GPU with torch: codes decoded through torch's own float8 view of
+    all 256 codes, times each element's group scale_inv."""
+    dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    table = torch.arange(256, dtype=torch.uint8).view(dt).to(torch.float32).to(q.device)
+    xf = x.to(torch.float32)
+    if transposed:
+        xf = xf.t()
+    R, C = xf.shape
+    if gran == "tensor":
+        s = s_inv.reshape(1, 1)
+    elif gran == "row":
+        s = s_inv.reshape(R, 1)
+    elif gran == "1x128":
+        s = s_inv.reshape(R, -1).repeat_interleave(128, dim=1)[:, :C]
+    else:
+        s = s_inv.reshape(-(-R // 128), -1).repeat_interleave(128, dim=0)[:R].repeat_interleave(128, dim=1)[:, :C]
+    err = (table[q.long()] * s - xf).norm() / xf.norm()
+    return float(err)
 
 
 def spread(ms):
@@ -309,6 +332,7 @@ class Step:
     def quantize(self):
         fp8, i = self.fp8, self.i
         x, w = self.xs[i % len(self.xs)], self.ws[i % len(self.ws)]
+        self.last_inputs = (x, w)
         if self.workload == "dgrad":
             fp8.quantize_dual(x, "e5m2", history=self.h_dy, out=self.xq, out_t=self.xqt,
                               scale_inv_out=self.sx, amax_out=self.ax)
@@ -337,6 +361,23 @@ class Step:
         else:
             fp8.scaled_gemm(self.xq, self.wq, self.sx.reshape(-1), self.sw.reshape(-1), out=self.y)
         self.i += 1
+
+    def quant_errors(self) -> dict:
+        """Relative error of each operand's cast (the last quantize's inputs,
+        codes and scales)."""
+        t, (x, w) = self.torch, self.last_inputs
+        if self.workload == "wgrad":      # dY^T in E5M2, X^T in E4M3, per tensor
+            ops = [("dY", x, self.xq, self.sx, "e5m2", "tensor", True),
+                   ("X", w, self.wq, self.sw, "e4m3", "tensor", True)]
+        elif self.workload == "dgrad":    # dY in E5M2 (delayed), W^T in E4M3
+            ops = [("dY", x, self.xq, self.sx, "e5m2", "tensor", False),
+                   ("W", w, self.wq, self.sw, "e4m3", "tensor", True)]
+        else:
+            ops = [("X", x, self.xq, self.sx, "e4m3", self.gx, False)]
+            if self.workload != "moe":    # the experts' weights are cast once, outside the steps
+                ops.append(("W", w, self.wq, self.sw, "e4m3", self.gw, False))
+        return {name: {"rel_err": round(quant_rel_err(t, a, q, s, f, g, tr), 6), "granularity": g, "format": f}
+                for name, a, q, s, f, g, tr in ops}
 
     def quant_bytes(self) -> float:
         """Algorithmic HBM bytes of the two casts of one step."""
@@ -596,6 +637,8 @@ def main():
     # copy's bandwidth as the practical streaming ceiling
     clock = None if args.no_clock else gemm_clock_mhz(torch, st.gemm)
     copy_gbs = copy_ceiling_gbs(torch)
+    st.quantize()
+    q_err = st.quant_errors()
     roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
             "traffic": GEMM_TRAFFIC_BYTES if args.workload == "mlp8b" else None}
@@ -631,6 +674,7 @@ def main():
             "quantize_gbs": round(q_gbs, 1),
             "quantize_pct_hbm_peak": round(100 * q_gbs / PEAK_HBM_GBS, 2),
             "quantize_bytes": int(qbytes),
+            "quantize_rel_err": q_err,
             "copy_ceiling_gbs": round(copy_gbs, 1),
             "quantize_pct_copy_ceiling": round(100 * q_gbs / copy_gbs, 2),
         },
