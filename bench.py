@@ -98,6 +98,17 @@ def parse():
     return ap.parse_args()
 
 
+def phase(torch, name: str):
+    """A named range (roctx on ROCm, through torch's nvtx module) around a
+    phase of the run, visible in rocprofv3's marker trace; a no-op where the
+    module is unavailable."""
+    import contextlib
+    try:
+        return torch.cuda.nvtx.range(name)
+    except Exception:
+        return contextlib.nullcontext()
+
+
 def loop_ms(torch, fn, n: int) -> float:
     """Mean ms per call of fn over n calls back to back, timed by two HIP
     events around the whole loop (nothing else on the stream between the
@@ -611,10 +622,13 @@ def main():
         st.i += 1
 
     # the K steps, timed as a whole: only the work between the two events
-    ms = loop_ms(torch, step, K)
+    with phase(torch, "timed steps"):
+        ms = loop_ms(torch, step, K)
     # each operation on its own, back to back: its launches' own time
-    g_mean = loop_ms(torch, st.gemm, K)
-    q_mean = loop_ms(torch, quantize_only, K)
+    with phase(torch, "gemm back to back"):
+        g_mean = loop_ms(torch, st.gemm, K)
+    with phase(torch, "quantize back to back"):
+        q_mean = loop_ms(torch, quantize_only, K)
     # per-step spread of each operation, from events around each call (these
     # times include the events' own idle gaps)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -635,8 +649,10 @@ def main():
     q_gbs = qbytes / (q_mean * 1e-3) / 1e9
     # after the timed region: the graphics clock under the GEMM, and a plain
     # copy's bandwidth as the practical streaming ceiling
-    clock = None if args.no_clock else gemm_clock_mhz(torch, st.gemm)
-    copy_gbs = copy_ceiling_gbs(torch)
+    with phase(torch, "clock under the gemm"):
+        clock = None if args.no_clock else gemm_clock_mhz(torch, st.gemm)
+    with phase(torch, "copy ceiling"):
+        copy_gbs = copy_ceiling_gbs(torch)
     st.quantize()
     q_err = st.quant_errors()
     roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
