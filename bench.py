@@ -340,26 +340,30 @@ class Step:
         self.y = T.empty((M, N), dtype=out_dt, device=dev)
         self.elems = xs[0].numel() + (0 if workload == "moe" else ws[0].numel())
 
-    def quantize(self):
+    def quantize(self, dx=None, dw=None):
+        """Cast this step's operands; dx, dw: optional fp8.Diag counters of
+        the first and the second operand's cast."""
         fp8, i = self.fp8, self.i
         x, w = self.xs[i % len(self.xs)], self.ws[i % len(self.ws)]
         self.last_inputs = (x, w)
         if self.workload == "dgrad":
-            fp8.quantize_dual(x, "e5m2", history=self.h_dy, out=self.xq, out_t=self.xqt,
+            fp8.quantize_dual(x, "e5m2", history=self.h_dy, diag=dx, out=self.xq, out_t=self.xqt,
                               scale_inv_out=self.sx, amax_out=self.ax)
-            fp8.quantize(w, "e4m3", "tensor", transpose=True, out=self.wq, scale_inv_out=self.sw,
+            fp8.quantize(w, "e4m3", "tensor", transpose=True, diag=dw, out=self.wq, scale_inv_out=self.sw,
                          amax_out=self.aw)
         elif self.workload == "wgrad":
-            fp8.quantize(x, "e5m2", "tensor", history=self.h_dy, transpose=True, out=self.xq,
+            fp8.quantize(x, "e5m2", "tensor", history=self.h_dy, transpose=True, diag=dx, out=self.xq,
                          scale_inv_out=self.sx, amax_out=self.ax)
-            fp8.quantize(w, "e4m3", "tensor", history=self.h_x, transpose=True, out=self.wq,
+            fp8.quantize(w, "e4m3", "tensor", history=self.h_x, transpose=True, diag=dw, out=self.wq,
                          scale_inv_out=self.sw, amax_out=self.aw)
         elif self.workload == "moe":
-            fp8.quantize(x, "e4m3", "row", out=self.xq, scale_inv_out=self.sx, amax_out=self.ax)
+            fp8.quantize(x, "e4m3", "row", diag=dx, out=self.xq, scale_inv_out=self.sx, amax_out=self.ax)
         else:
             pow2 = self.workload == "qkv"
-            fp8.quantize(x, "e4m3", self.gx, pow2=pow2, out=self.xq, scale_inv_out=self.sx, amax_out=self.ax)
-            fp8.quantize(w, "e4m3", self.gw, pow2=pow2, out=self.wq, scale_inv_out=self.sw, amax_out=self.aw)
+            fp8.quantize(x, "e4m3", self.gx, pow2=pow2, diag=dx, out=self.xq, scale_inv_out=self.sx,
+                         amax_out=self.ax)
+            fp8.quantize(w, "e4m3", self.gw, pow2=pow2, diag=dw, out=self.wq, scale_inv_out=self.sw,
+                         amax_out=self.aw)
 
     def gemm(self):
         fp8 = self.fp8
@@ -373,9 +377,10 @@ class Step:
             fp8.scaled_gemm(self.xq, self.wq, self.sx.reshape(-1), self.sw.reshape(-1), out=self.y)
         self.i += 1
 
-    def quant_errors(self) -> dict:
+    def quant_errors(self, counts=None) -> dict:
         """Relative error of each operand's cast (the last quantize's inputs,
-        codes and scales)."""
+        codes and scales), with its saturation / non-finite / underflow
+        counts when `counts` (the two fp8.Diag of that quantize) is given."""
         t, (x, w) = self.torch, self.last_inputs
         if self.workload == "wgrad":      # dY^T in E5M2, X^T in E4M3, per tensor
             ops = [("dY", x, self.xq, self.sx, "e5m2", "tensor", True),
@@ -387,8 +392,12 @@ class Step:
             ops = [("X", x, self.xq, self.sx, "e4m3", self.gx, False)]
             if self.workload != "moe":    # the experts' weights are cast once, outside the steps
                 ops.append(("W", w, self.wq, self.sw, "e4m3", self.gw, False))
-        return {name: {"rel_err": round(quant_rel_err(t, a, q, s, f, g, tr), 6), "granularity": g, "format": f}
-                for name, a, q, s, f, g, tr in ops}
+        out = {}
+        for k, (name, a, q, s, f, g, tr) in enumerate(ops):
+            out[name] = {"rel_err": round(quant_rel_err(t, a, q, s, f, g, tr), 6), "granularity": g, "format": f}
+            if counts is not None:
+                out[name].update(counts[k].read())
+        return out
 
     def quant_bytes(self) -> float:
         """Algorithmic HBM bytes of the two casts of one step."""
@@ -653,8 +662,9 @@ def main():
         clock = None if args.no_clock else gemm_clock_mhz(torch, st.gemm)
     with phase(torch, "copy ceiling"):
         copy_gbs = copy_ceiling_gbs(torch)
-    st.quantize()
-    q_err = st.quant_errors()
+    diags = (fp8.Diag(), fp8.Diag())
+    st.quantize(*diags)
+    q_err = st.quant_errors(diags)
     roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
             "traffic": GEMM_TRAFFIC_BYTES if args.workload == "mlp8b" else None}
