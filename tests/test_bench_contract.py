@@ -1,0 +1,52 @@
+"""bench.py's host-side contract: more than one GPU is refused before any
+GPU work, and the quantization-error diagnostic it reports equals a direct
+computation from the oracle's codes and scales (run here on CPU tensors)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr and r.stdout.strip() == ""
+
+
+@pytest.mark.parametrize("gran", ["tensor", "row", "1x128", "128x128"])
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_quant_rel_err_matches_direct_computation(gran, fmt):
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((300, 260)) * np.exp(rng.uniform(-3, 3, (300, 1)))).astype(np.float32)
+    r = oracle.quantize(x, fmt, gran)
+    t = oracle.decode_table(fmt)
+    R, C = x.shape
+    s = r["scale_inv"].astype(np.float64)
+    if gran == "tensor":
+        se = np.full((R, C), s.ravel()[0])
+    elif gran == "row":
+        se = np.repeat(s.reshape(R, 1), C, axis=1)
+    elif gran == "1x128":
+        se = np.repeat(s.reshape(R, -1), 128, axis=1)[:, :C]
+    else:
+        se = np.repeat(np.repeat(s.reshape(-(-R // 128), -1), 128, axis=0)[:R], 128, axis=1)[:, :C]
+    xh = t[r["q"]].astype(np.float64) * se
+    want = np.linalg.norm(xh - x) / np.linalg.norm(x.astype(np.float64))
+    got = bench.quant_rel_err(torch, torch.from_numpy(x), torch.from_numpy(r["q"]),
+                              torch.from_numpy(r["scale_inv"].astype(np.float32)),
+                              "e4m3" if fmt == oracle.E4M3 else "e5m2", gran)
+    assert abs(got - want) <= 1e-5 * want
+    gt = bench.quant_rel_err(torch, torch.from_numpy(np.ascontiguousarray(x.T)), torch.from_numpy(r["q"]),
+                             torch.from_numpy(r["scale_inv"].astype(np.float32)),
+                             "e4m3" if fmt == oracle.E4M3 else "e5m2", gran, transposed=True)
+    assert abs(gt - want) <= 1e-5 * want

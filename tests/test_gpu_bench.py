@@ -1,0 +1,61 @@
+"""bench.py on the GPU, in a process of its own: its one JSON line carries
+every field the benchmark contract names, with the roofline and the
+kernels' figures consistent with each other (a short run of the small
+workload and of the KV workload)."""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+        "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu):
+    yield
+
+
+def _run(*args):
+    say("bench", *args)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                       timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return json.loads(lines[0])
+
+
+@pytest.mark.timeout(300)
+def test_bench_line_contract_tiny():
+    d = _run("--workload", "tiny", "--steps", "5", "--warmup", "2", "--no-cpu-baseline", "--no-clock")
+    assert KEYS <= set(d) and d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
+    assert d["higher_is_better"] is True and d["vs_baseline"] is None and "workload" in d["config"]
+    roof = d["roofline"]
+    assert {"bound", "achieved", "peak", "unit", "frac", "traffic"} <= set(roof)
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 5000.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    k = d["kernels"]
+    flops = 2.0 * 256 ** 3
+    assert abs(roof["achieved"] - flops / (k["gemm_ms"] * 1e-3) / 1e12) <= 0.01 * roof["achieved"] + 0.01
+    assert abs(d["value"] - flops / (d["ms_per_step"] * 1e-3) / 1e12) <= 0.01 * d["value"] + 0.01
+    assert set(k["quantize_rel_err"]) == {"X", "W"} and 0 < k["quantize_rel_err"]["X"]["rel_err"] < 0.05
+    assert k["copy_ceiling_gbs"] > 0 and d["cpu_baseline"] is None
+
+
+@pytest.mark.timeout(300)
+def test_bench_line_contract_kv():
+    d = _run("--workload", "kv", "--steps", "5", "--warmup", "2", "--no-cpu-baseline")
+    assert KEYS <= set(d) and d["unit"] == "GB/s" and d["n_gpus"] == 1
+    roof = d["roofline"]
+    assert roof["bound"] == "hbm" and roof["peak"] == 8000.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
