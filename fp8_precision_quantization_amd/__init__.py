@@ -50,6 +50,11 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _same_device(t: torch.Tensor, device: torch.device, name: str) -> None:
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+
+
 def _matrix(x: torch.Tensor, name: str):
     if x.dim() != 2:
         raise ValueError("%s must be 2-D, got shape %s" % (name, tuple(x.shape)))
@@ -58,6 +63,40 @@ def _matrix(x: torch.Tensor, name: str):
     if x.stride(1) != 1 and x.shape[1] > 1:
         raise ValueError("%s must have a contiguous last dimension" % name)
     return x.shape[0], x.shape[1], max(x.stride(0), 1) if x.shape[0] > 1 else max(x.shape[1], 1)
+
+
+def _buf(t: torch.Tensor, n: int, dtype, device: torch.device, name: str) -> int:
+    """Pointer of a buffer the library reads or writes as n packed elements
+    of dtype on device; raises before any launch if t is not one."""
+    if not isinstance(t, torch.Tensor) or t.device != device:
+        raise ValueError("%s must be a tensor on %s" % (name, device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.numel() != n or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous tensor of %d elements, got shape %s"
+                         % (name, n, tuple(t.shape)))
+    return t.data_ptr()
+
+
+def _out_matrix(out: torch.Tensor, rows: int, cols: int, dtype, device: torch.device, name: str) -> int:
+    """Leading dimension of an output matrix [rows, cols] of dtype on device
+    with a contiguous last dimension; raises before any launch if out is not one."""
+    if not isinstance(out, torch.Tensor) or out.device != device:
+        raise ValueError("%s must be a tensor on %s" % (name, device))
+    if out.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, out.dtype))
+    if tuple(out.shape) != (rows, cols):
+        raise ValueError("%s must have shape %s, got %s" % (name, (rows, cols), tuple(out.shape)))
+    if cols > 1 and out.stride(1) != 1:
+        raise ValueError("%s must have a contiguous last dimension" % name)
+    return max(out.stride(0), 1) if rows > 1 else max(cols, 1)
+
+
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= d
+    return n
 
 
 def group_grid(granularity, rows: int, cols: int):
@@ -146,13 +185,16 @@ def quantize(x: torch.Tensor, fmt="e4m3", granularity="tensor", pow2: bool = Fal
     fmt_name = fmt if isinstance(fmt, str) else ("e4m3" if fmt == 0 else "e5m2")
     grid = group_grid(granularity, rows, cols)
     dev = x.device
+    oshape = (cols, rows) if transpose else (rows, cols)
     if out is None:
-        out = torch.empty((cols, rows) if transpose else (rows, cols), dtype=torch.uint8, device=dev)
-    ldq = max(out.stride(0), 1) if out.shape[0] > 1 else max(out.shape[1], 1)
+        out = torch.empty(oshape, dtype=torch.uint8, device=dev)
+    ldq = _out_matrix(out, oshape[0], oshape[1], torch.uint8, dev, "out")
     if scale_inv_out is None:
         scale_inv_out = torch.empty(grid, dtype=torch.float32, device=dev)
     if amax_out is None:
         amax_out = torch.empty(grid, dtype=torch.float32, device=dev)
+    _buf(scale_inv_out, _numel(grid), torch.float32, dev, "scale_inv_out")
+    _buf(amax_out, _numel(grid), torch.float32, dev, "amax_out")
     flags = ((_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_TRANSPOSE_OUT if transpose else 0)
              | (_lib.FP8_SPIKE_GUARD if spike_guard else 0))
     st = _lib.lib().fp8_quantize(
@@ -184,12 +226,14 @@ def quantize_dual(x: torch.Tensor, fmt="e5m2", pow2: bool = False, history: Opti
         out = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if out_t is None:
         out_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
-    ldq = max(out.stride(0), 1) if out.shape[0] > 1 else max(out.shape[1], 1)
-    ldqt = max(out_t.stride(0), 1) if out_t.shape[0] > 1 else max(out_t.shape[1], 1)
+    ldq = _out_matrix(out, rows, cols, torch.uint8, dev, "out")
+    ldqt = _out_matrix(out_t, cols, rows, torch.uint8, dev, "out_t")
     if scale_inv_out is None:
         scale_inv_out = torch.empty((1, 1), dtype=torch.float32, device=dev)
     if amax_out is None:
         amax_out = torch.empty((1, 1), dtype=torch.float32, device=dev)
+    _buf(scale_inv_out, 1, torch.float32, dev, "scale_inv_out")
+    _buf(amax_out, 1, torch.float32, dev, "amax_out")
     flags = (_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_SPIKE_GUARD if spike_guard else 0)
     st = _lib.lib().fp8_quantize_dual(
         x.data_ptr(), in_dt, rows, cols, ld, _fmt(fmt), flags,
@@ -205,8 +249,10 @@ def amax(x: torch.Tensor, granularity="tensor", out: Optional[torch.Tensor] = No
     in_dt = _lib.FP8_IN_BF16 if x.dtype == torch.bfloat16 else _lib.FP8_IN_F32
     if x.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("x must be bfloat16 or float32")
+    grid = group_grid(granularity, rows, cols)
     if out is None:
-        out = torch.empty(group_grid(granularity, rows, cols), dtype=torch.float32, device=x.device)
+        out = torch.empty(grid, dtype=torch.float32, device=x.device)
+    _buf(out, _numel(grid), torch.float32, x.device, "out")
     st = _lib.lib().fp8_amax(x.data_ptr(), in_dt, rows, cols, ld, _gran(granularity), out.data_ptr(),
                              _stream(x.device))
     _lib.check(st, "fp8_amax")
@@ -229,15 +275,19 @@ def scaled_gemm(a_q: torch.Tensor, b_q: torch.Tensor, a_scale_inv: torch.Tensor,
     N, K2, ldb = _matrix(b_q, "b_q")
     if K != K2:
         raise ValueError("K mismatch: %d vs %d" % (K, K2))
+    dev = a_q.device
+    _same_device(b_q, dev, "b_q")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
-    ldc = max(out.stride(0), 1) if out.shape[0] > 1 else max(N, 1)
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    ldc = _out_matrix(out, M, N, out.dtype, dev, "out")
     a_row = 0 if a_scale_inv.numel() == 1 else 1
     b_row = 0 if b_scale_inv.numel() == 1 else 1
     if a_row and a_scale_inv.numel() != M:
         raise ValueError("a_scale_inv must hold 1 or M=%d values" % M)
     if b_row and b_scale_inv.numel() != N:
         raise ValueError("b_scale_inv must hold 1 or N=%d values" % N)
+    _buf(a_scale_inv, M if a_row else 1, torch.float32, dev, "a_scale_inv")
+    _buf(b_scale_inv, N if b_row else 1, torch.float32, dev, "b_scale_inv")
     st = _lib.lib().fp8_scaled_gemm(a_q.data_ptr(), _fmt(fa), lda, b_q.data_ptr(), _fmt(fb), ldb, M, N, K,
                                     a_scale_inv.data_ptr(), a_row, b_scale_inv.data_ptr(), b_row,
                                     out.data_ptr(), _out_dtype(out.dtype), ldc, _stream(a_q.device))
@@ -253,9 +303,14 @@ def blockscaled_gemm(a_q: torch.Tensor, b_q: torch.Tensor, a_scale_inv: torch.Te
     N, K2, ldb = _matrix(b_q, "b_q")
     if K != K2:
         raise ValueError("K mismatch: %d vs %d" % (K, K2))
+    dev = a_q.device
+    _same_device(b_q, dev, "b_q")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
-    ldc = max(out.stride(0), 1) if out.shape[0] > 1 else max(N, 1)
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    ldc = _out_matrix(out, M, N, out.dtype, dev, "out")
+    if K % 128 == 0 and N % 128 == 0:     # else the library reports the unsupported shape
+        _buf(a_scale_inv, M * (K // 128), torch.float32, dev, "a_scale_inv")
+        _buf(b_scale_inv, (N // 128) * (K // 128), torch.float32, dev, "b_scale_inv")
     st = _lib.lib().fp8_blockscaled_gemm(a_q.data_ptr(), lda, b_q.data_ptr(), ldb, M, N, K,
                                          a_scale_inv.data_ptr(), b_scale_inv.data_ptr(), out.data_ptr(),
                                          _out_dtype(out.dtype), ldc, _stream(a_q.device))
@@ -283,9 +338,12 @@ def grouped_gemm(a_q: torch.Tensor, b_q: torch.Tensor, group_offsets: torch.Tens
         raise ValueError("group_offsets must be a contiguous int32 device tensor of G+1=%d entries" % (G + 1))
     ldb = b_q.stride(1) if N > 1 else K
     gstride = b_q.stride(0) if G > 1 else N * ldb
+    dev = a_q.device
+    _same_device(b_q, dev, "b_q")
+    _same_device(group_offsets, dev, "group_offsets")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
-    ldc = max(out.stride(0), 1) if out.shape[0] > 1 else max(N, 1)
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    ldc = _out_matrix(out, M, N, out.dtype, dev, "out")
     a_row = 0 if a_scale_inv.numel() == 1 else 1
     if a_row and a_scale_inv.numel() != M:
         raise ValueError("a_scale_inv must hold 1 or M=%d values" % M)
@@ -295,6 +353,8 @@ def grouped_gemm(a_q: torch.Tensor, b_q: torch.Tensor, group_offsets: torch.Tens
         b_row = 1
     else:
         raise ValueError("b_scale_inv must hold G=%d or G*N=%d values" % (G, G * N))
+    _buf(a_scale_inv, M if a_row else 1, torch.float32, dev, "a_scale_inv")
+    _buf(b_scale_inv, G * N if b_row else G, torch.float32, dev, "b_scale_inv")
     st = _lib.lib().fp8_grouped_gemm(a_q.data_ptr(), _fmt(fa), lda, b_q.data_ptr(), _fmt(fb), ldb, gstride, M, N, K,
                                      G, group_offsets.data_ptr(), a_scale_inv.data_ptr(), a_row,
                                      b_scale_inv.data_ptr(), b_row, out.data_ptr(), _out_dtype(out.dtype), ldc,
@@ -325,6 +385,16 @@ def _kv_rows(x: torch.Tensor, heads: int, head_dim: int, name: str):
     return n, (x.stride(0) if n > 1 else heads * head_dim)
 
 
+def _kv_scales(scale_inv: Optional[torch.Tensor], storage: str, scaling: str, capacity: int, heads: int,
+               device: torch.device):
+    """Pointer of a cache's scales: [capacity, heads] per (token, head), [heads]
+    fixed per head; none for bf16 storage (the library reports a missing one)."""
+    if scale_inv is None or storage == "bf16":
+        return _ptr(scale_inv)
+    n = capacity * heads if scaling == "token_head" else heads
+    return _buf(scale_inv, n, torch.float32, device, "scale_inv")
+
+
 def _slots(slots: Optional[torch.Tensor], n: int):
     if slots is None:
         return None
@@ -350,9 +420,13 @@ def kv_store(x: torch.Tensor, cache: torch.Tensor, scale_inv: Optional[torch.Ten
     want = torch.bfloat16 if storage == "bf16" else torch.uint8
     if cache.dtype != want or not cache.is_contiguous():
         raise ValueError("cache must be a contiguous %s tensor" % want)
+    _same_device(x, cache.device, "x")
+    if slots is not None:
+        _same_device(slots, cache.device, "slots")
     st = _lib.lib().fp8_kv_store(
         x.data_ptr(), in_dt, n, ld, heads, head_dim, _slots(slots, n), KV_STORAGE[storage],
-        KV_SCALING[scaling], _lib.FP8_SCALE_POW2 if pow2 else 0, cache.data_ptr(), _ptr(scale_inv), capacity,
+        KV_SCALING[scaling], _lib.FP8_SCALE_POW2 if pow2 else 0, cache.data_ptr(),
+        _kv_scales(scale_inv, storage, scaling, capacity, heads, cache.device), capacity,
         _ptr(diag.buf) if diag is not None else None, _stream(cache.device))
     _lib.check(st, "fp8_kv_store")
 
@@ -370,8 +444,12 @@ def kv_load(cache: torch.Tensor, scale_inv: Optional[torch.Tensor], n: Optional[
     n2, ld_out = _kv_rows(out, heads, head_dim, "out")
     if n2 != n:
         raise ValueError("out has %d rows, expected %d" % (n2, n))
+    _same_device(out, cache.device, "out")
+    if slots is not None:
+        _same_device(slots, cache.device, "slots")
     st = _lib.lib().fp8_kv_load(
-        cache.data_ptr(), KV_STORAGE[storage], KV_SCALING[scaling], _ptr(scale_inv), capacity, heads, head_dim,
+        cache.data_ptr(), KV_STORAGE[storage], KV_SCALING[scaling],
+        _kv_scales(scale_inv, storage, scaling, capacity, heads, cache.device), capacity, heads, head_dim,
         _slots(slots, n), n, _out_dtype(out.dtype), out.data_ptr(), ld_out, _stream(cache.device))
     _lib.check(st, "fp8_kv_load")
     return out

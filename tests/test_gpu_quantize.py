@@ -401,3 +401,53 @@ def test_invalid_args_on_gpu_raise():
     assert "TRANSPOSE" in str(e.value)
     with pytest.raises(fp8.Fp8Error):
         fp8.quantize(x, 7, "tensor")
+
+
+def test_binding_rejects_wrong_buffers():
+    """Output and scale buffers of the wrong dtype, size, layout or device
+    raise in the binding before any launch (the library itself only sees
+    pointers)."""
+    dev = "cuda"
+    x = torch.zeros((64, 256), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="out must have shape"):
+        fp8.quantize(x, "e4m3", "tensor", out=torch.empty((64, 255), dtype=torch.uint8, device=dev))
+    with pytest.raises(TypeError, match="out must be"):
+        fp8.quantize(x, "e4m3", "tensor", out=torch.empty((64, 256), dtype=torch.int8, device=dev))
+    with pytest.raises(ValueError, match="out must have shape"):
+        fp8.quantize(x, "e4m3", "tensor", transpose=True, out=torch.empty((64, 256), dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError, match="scale_inv_out must be a contiguous tensor of 64"):
+        fp8.quantize(x, "e4m3", "row", scale_inv_out=torch.empty(63, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError, match="amax_out must be a contiguous tensor of 128"):
+        fp8.quantize(x, "e4m3", "1x128", amax_out=torch.empty((64, 4), dtype=torch.float32, device=dev)[:, ::2])
+    with pytest.raises(ValueError, match="scale_inv_out must be a tensor on"):
+        fp8.quantize(x, "e4m3", "tensor", scale_inv_out=torch.empty(1, dtype=torch.float32))
+    with pytest.raises(ValueError, match="out_t must have shape"):
+        fp8.quantize_dual(x, out_t=torch.empty((64, 256), dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError, match="out must be a contiguous tensor of 128"):
+        fp8.amax(x, "1x128", out=torch.empty(3, dtype=torch.float32, device=dev))
+    a = torch.zeros((64, 256), dtype=torch.uint8, device=dev)
+    b = torch.zeros((128, 256), dtype=torch.uint8, device=dev)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    with pytest.raises(TypeError, match="a_scale_inv must be"):
+        fp8.scaled_gemm(a, b, one.double(), one)
+    with pytest.raises(ValueError, match="out must have shape"):
+        fp8.scaled_gemm(a, b, one, one, out=torch.empty((64, 127), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError, match="b_q must be"):
+        fp8.scaled_gemm(a, b.cpu(), one, one)
+    with pytest.raises(ValueError, match="a_scale_inv must be a contiguous tensor of 128"):
+        fp8.blockscaled_gemm(a, b, torch.ones(64, dtype=torch.float32, device=dev),
+                             torch.ones(2, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError, match="b_scale_inv must be a contiguous tensor of 2"):
+        fp8.blockscaled_gemm(a, b, torch.ones((64, 2), dtype=torch.float32, device=dev),
+                             torch.ones(1, dtype=torch.float32, device=dev))
+    offs = torch.tensor([0, 32, 64], dtype=torch.int32, device=dev)
+    bg = torch.zeros((2, 128, 256), dtype=torch.uint8, device=dev)
+    with pytest.raises(TypeError, match="b_scale_inv must be"):
+        fp8.grouped_gemm(a, bg, offs, one, torch.ones(2, dtype=torch.float16, device=dev))
+    cache = fp8.KVTensorCache(16, 2, 128)
+    with pytest.raises(ValueError, match="scale_inv must be a contiguous tensor of 32"):
+        fp8.kv_store(torch.zeros((4, 256), dtype=torch.bfloat16, device=dev), cache.data,
+                     torch.zeros(31, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError, match="scale_inv must be a contiguous tensor of 32"):
+        fp8.kv_load(cache.data, torch.zeros((16, 2), dtype=torch.float32, device=dev).t(), n=4)
+    torch.cuda.synchronize()
