@@ -1201,6 +1201,24 @@ hipError_t set_lds(KERN kern, size_t bytes) {
                                (int)bytes);
 }
 
+// One-time set-up of a launch site (its kernels' LDS attribute) on each
+// device a call runs on: the attribute is set with the device current, so a
+// process that drives several GPUs sets it on every one of them.
+struct PerDeviceOnce {
+    static constexpr int kDevices = 64;
+    std::once_flag flag[kDevices];
+    hipError_t err[kDevices] = {};
+    template <typename F>
+    hipError_t run(F&& f) {
+        int dev = 0;
+        const hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+        std::call_once(flag[dev], [&] { err[dev] = f(); });
+        return err[dev];
+    }
+};
+
 GemmParams make_params(const GemmArgs& a, int bm, int bn) {
     GemmParams p;
     p.A = a.A; p.B = a.B; p.lda = a.lda; p.ldb = a.ldb;
@@ -1223,12 +1241,10 @@ GemmParams make_params(const GemmArgs& a, int bm, int bn) {
 // block per tile.
 template <int FA, int FB, bool OUT_BF16>
 hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [&] {
-        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false>, lds_scaled<OUT_BF16>());
-        if (attr_err == hipSuccess)
-            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, false>, lds_scaled<OUT_BF16>());
+    static PerDeviceOnce once;
+    const hipError_t attr_err = once.run([] {
+        const hipError_t e = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false>, lds_scaled<OUT_BF16>());
+        return e != hipSuccess ? e : set_lds(k_gemm_p<FA, FB, OUT_BF16, true, false>, lds_scaled<OUT_BF16>());
     });
     if (attr_err != hipSuccess) return attr_err;
     unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
@@ -1247,9 +1263,8 @@ hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream) {
 // or GROUPED over the grouped GEMM's split-off last round (`grid` blocks).
 template <int FA, int FB, bool OUT_BF16, bool GROUPED = false>
 hipError_t launch_half(const GemmParams& p, hipStream_t stream, unsigned grid_grouped = 0) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [&] { attr_err = set_lds(k_gemm_h<FA, FB, OUT_BF16, GROUPED>, (size_t)kHRing); });
+    static PerDeviceOnce once;
+    const hipError_t attr_err = once.run([] { return set_lds(k_gemm_h<FA, FB, OUT_BF16, GROUPED>, (size_t)kHRing); });
     if (attr_err != hipSuccess) return attr_err;
     const unsigned grid = GROUPED ? grid_grouped : (unsigned)(p.tiles_m * p.tiles_n);
     if (grid == 0) return hipSuccess;
@@ -1355,12 +1370,10 @@ __global__ __launch_bounds__(256) void k_group_table(const int32_t* __restrict__
 
 template <int FA, int FB, bool OUT_BF16>
 hipError_t launch_grouped_typed(const GemmArgs& a) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [&] {
-        attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, true>, lds_scaled<OUT_BF16>());
-        if (attr_err == hipSuccess)
-            attr_err = set_lds(k_gemm_p<FA, FB, OUT_BF16, true, true>, lds_scaled<OUT_BF16>());
+    static PerDeviceOnce once;
+    const hipError_t attr_err = once.run([] {
+        const hipError_t e = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, true>, lds_scaled<OUT_BF16>());
+        return e != hipSuccess ? e : set_lds(k_gemm_p<FA, FB, OUT_BF16, true, true>, lds_scaled<OUT_BF16>());
     });
     if (attr_err != hipSuccess) return attr_err;
     int* tab = reinterpret_cast<int*>(a.scratch + kScratchGroupTable);
@@ -1394,9 +1407,8 @@ hipError_t launch_grouped_typed(const GemmArgs& a) {
 // Block-scaled GEMM (E4M3 x E4M3): 256 x 128 tiles, one block each.
 template <bool OUT_BF16>
 hipError_t launch_block_typed(const GemmArgs& a) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [&] { attr_err = set_lds(k_gemm_bp<0, 0, OUT_BF16>, lds_256x128<OUT_BF16>()); });
+    static PerDeviceOnce once;
+    const hipError_t attr_err = once.run([] { return set_lds(k_gemm_bp<0, 0, OUT_BF16>, lds_256x128<OUT_BF16>()); });
     if (attr_err != hipSuccess) return attr_err;
     const GemmParams p = make_params(a, 256, 128);
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
