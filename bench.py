@@ -605,7 +605,7 @@ def cpu_baseline(args, workload, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus %d)"
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
