@@ -191,6 +191,7 @@ def gemm_clock_mhz(torch, run, seconds: float = 1.5):
         match = [h for h in handles if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus]
         h = match[0] if len(match) == 1 else (handles[0] if len(handles) == 1 else None)
         if h is None:
+            amdsmi.amdsmi_shut_down()
             return None
         amdsmi.amdsmi_get_gpu_metrics_info(h)
     except Exception:
@@ -226,6 +227,10 @@ def gemm_clock_mhz(torch, run, seconds: float = 1.5):
     t1 = time.perf_counter()
     done.set()
     th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
     mid = t0 + 0.5 * (t1 - t0)
     good = [c for t, clks, act in samples if t >= mid and isinstance(act, int) and act >= 90 for c in clks]
     return round(float(np.mean(good)), 1) if good else None
