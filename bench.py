@@ -564,43 +564,62 @@ def cpu_model() -> str:
 
 def cpu_baseline(args, workload, synth):
     """The oracle, untuned, on a bounded sample of the same step: quantize the
-    first `cpu_rows` rows of X and `cpu_cols` rows of W, then the GEMM block
-    Y[:cpu_rows, :cpu_cols] with the full K, on all the threads it gets;
-    the quantize again on one thread.  `value` is the sample's whole-step
-    rate; the quantize (algorithmic bytes of the two passes, as on the GPU)
-    and the GEMM are also reported on their own."""
+    first `cpu_rows` rows of X and `cpu_cols` rows of W (half as many of
+    each for the block-scaled workload, whose K is twice as long), then the
+    GEMM block Y[:cpu_rows, :cpu_cols] with the full K, on all the threads
+    it gets; the quantize again on one thread.  `value` is the sample's
+    whole-step rate; the quantize (algorithmic bytes, as on the GPU) and the
+    GEMM are also reported on their own.  None for the workloads without a
+    sampled leg (the backward and grouped GEMMs)."""
     import oracle
-    if workload not in ("mlp8b", "tiny"):
+    if workload not in ("mlp8b", "tiny", "qkv", "mlp70b"):
         return None
+    gx = gw = "tensor"
+    pow2 = block = False
     if workload == "tiny":
         X, W = synth.tiny()
         r, c = 256, 256
     else:
         r, c = args.cpu_rows, args.cpu_cols
-        X, W = synth.mlp8b()
+        if workload == "qkv":
+            gx = gw = "row"
+            pow2 = True
+        elif workload == "mlp70b":      # K = 8192: half the rows and columns keep the sample's time alike
+            gx, gw, block = "1x128", "128x128", True
+            r, c = r // 2, c // 2
+        X, W = getattr(synth, workload)()
         X, W = np.ascontiguousarray(X[:r]), np.ascontiguousarray(W[:c])
     K = X.shape[1]
     in_bytes = X.dtype.itemsize          # bf16 bits (uint16) or fp32
-    qbytes = (X.size + W.size) * (2 * in_bytes + 1)
+    # the GPU's algorithmic bytes: a per-tensor cast reads its input twice
+    qbytes = (X.size + W.size) * ((2 if gx == "tensor" else 1) * in_bytes + 1)
+
+    def quantize_both():
+        return (oracle.quantize(X, oracle.E4M3, gx, pow2=pow2), oracle.quantize(W, oracle.E4M3, gw, pow2=pow2))
+
     t0 = time.perf_counter()
-    qx = oracle.quantize(X, oracle.E4M3, "tensor")
-    qw = oracle.quantize(W, oracle.E4M3, "tensor")
+    qx, qw = quantize_both()
     t1 = time.perf_counter()
-    y, _ = oracle.gemm(qx["q"], 0, qw["q"], 0, qx["scale_inv"], qw["scale_inv"], with_p=True)
+    if block:
+        ms, ns = np.repeat(np.arange(r), c), np.tile(np.arange(c), r)
+        oracle.blockgemm_sampled(qx["q"], qw["q"], qx["scale_inv"], qw["scale_inv"], ms, ns)
+    else:
+        oracle.gemm(qx["q"], 0, qw["q"], 0, qx["scale_inv"].reshape(-1), qw["scale_inv"].reshape(-1), with_p=True)
     t2 = time.perf_counter()
     threads = oracle.num_threads()
     oracle.set_num_threads(1)
     try:
         t3 = time.perf_counter()
-        oracle.quantize(X, oracle.E4M3, "tensor")
-        oracle.quantize(W, oracle.E4M3, "tensor")
+        quantize_both()
         t4 = time.perf_counter()
     finally:
         oracle.set_num_threads(threads)
     dt = t2 - t0
+    what = {"tensor": "per-tensor E4M3", "row": "per-row power-of-two E4M3",
+            "1x128": "E4M3, X in 1x128 and W in 128x128 blocks"}[gx]
     return {"value": 2.0 * r * c * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "quantize X[:%d], W[:%d] (per-tensor E4M3) + GEMM Y[:%d, :%d] with K=%d: %.1f s"
-                      % (r, c, r, c, K, dt),
+            "sample": "quantize X[:%d], W[:%d] (%s) + GEMM Y[:%d, :%d] with K=%d: %.1f s"
+                      % (r, c, what, r, c, K, dt),
             "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
             "quantize_gbs": round(qbytes / (t1 - t0) / 1e9, 3),
             "quantize_gbs_1_thread": round(qbytes / (t4 - t3) / 1e9, 3),
