@@ -569,16 +569,30 @@ def cpu_baseline(args, workload, synth):
     GEMM block Y[:cpu_rows, :cpu_cols] with the full K, on all the threads
     it gets; the quantize again on one thread.  `value` is the sample's
     whole-step rate; the quantize (algorithmic bytes, as on the GPU) and the
-    GEMM are also reported on their own.  None for the workloads without a
-    sampled leg (the backward and grouped GEMMs)."""
+    GEMM are also reported on their own.  The backward workloads take the
+    GEMM operands as the GPU casts them (transposed slices, E5M2 gradients);
+    the grouped workload has no sampled leg (None)."""
     import oracle
-    if workload not in ("mlp8b", "tiny", "qkv", "mlp70b"):
+    if workload not in ("mlp8b", "tiny", "qkv", "mlp70b", "wgrad", "dgrad"):
         return None
     gx = gw = "tensor"
+    fx, fw = oracle.E4M3, oracle.E4M3
     pow2 = block = False
     if workload == "tiny":
         X, W = synth.tiny()
         r, c = 256, 256
+    elif workload in ("wgrad", "dgrad"):
+        # the GEMM operands as the GPU casts them: dW = (dY^T)(X^T)^T over the
+        # tokens, dX = dY (W^T)^T over the layer's outputs; E5M2 gradients
+        fx = oracle.E5M2
+        if workload == "wgrad":
+            dy, x = synth.wgrad_step(0)
+            r, c = args.cpu_rows // 2, args.cpu_cols // 2
+            X, W = np.ascontiguousarray(dy[:, :r].T), np.ascontiguousarray(x[:, :c].T)
+        else:
+            dy, w = synth.dgrad()
+            r, c = args.cpu_rows // 4, args.cpu_cols // 2
+            X, W = np.ascontiguousarray(dy[:r]), np.ascontiguousarray(w[:, :c].T)
     else:
         r, c = args.cpu_rows, args.cpu_cols
         if workload == "qkv":
@@ -591,11 +605,13 @@ def cpu_baseline(args, workload, synth):
         X, W = np.ascontiguousarray(X[:r]), np.ascontiguousarray(W[:c])
     K = X.shape[1]
     in_bytes = X.dtype.itemsize          # bf16 bits (uint16) or fp32
-    # the GPU's algorithmic bytes: a per-tensor cast reads its input twice
-    qbytes = (X.size + W.size) * ((2 if gx == "tensor" else 1) * in_bytes + 1)
+    # the GPU's algorithmic bytes: a just-in-time per-tensor cast reads its
+    # input twice (the delayed casts of the backward workloads once)
+    passes = 2 if gx == "tensor" and workload not in ("wgrad", "dgrad") else 1
+    qbytes = (X.size + W.size) * (passes * in_bytes + 1)
 
     def quantize_both():
-        return (oracle.quantize(X, oracle.E4M3, gx, pow2=pow2), oracle.quantize(W, oracle.E4M3, gw, pow2=pow2))
+        return (oracle.quantize(X, fx, gx, pow2=pow2), oracle.quantize(W, fw, gw, pow2=pow2))
 
     t0 = time.perf_counter()
     qx, qw = quantize_both()
@@ -604,7 +620,7 @@ def cpu_baseline(args, workload, synth):
         ms, ns = np.repeat(np.arange(r), c), np.tile(np.arange(c), r)
         oracle.blockgemm_sampled(qx["q"], qw["q"], qx["scale_inv"], qw["scale_inv"], ms, ns)
     else:
-        oracle.gemm(qx["q"], 0, qw["q"], 0, qx["scale_inv"].reshape(-1), qw["scale_inv"].reshape(-1), with_p=True)
+        oracle.gemm(qx["q"], fx, qw["q"], fw, qx["scale_inv"].reshape(-1), qw["scale_inv"].reshape(-1), with_p=True)
     t2 = time.perf_counter()
     threads = oracle.num_threads()
     oracle.set_num_threads(1)
@@ -617,9 +633,16 @@ def cpu_baseline(args, workload, synth):
     dt = t2 - t0
     what = {"tensor": "per-tensor E4M3", "row": "per-row power-of-two E4M3",
             "1x128": "E4M3, X in 1x128 and W in 128x128 blocks"}[gx]
+    if workload == "wgrad":
+        sample = ("quantize dY[:, :%d]^T (E5M2), X[:, :%d]^T (E4M3), per tensor + GEMM dW[:%d, :%d] with K=%d "
+                  "tokens: %.1f s" % (r, c, r, c, K, dt))
+    elif workload == "dgrad":
+        sample = ("quantize dY[:%d] (E5M2), W[:, :%d]^T (E4M3), per tensor + GEMM dX[:%d, :%d] with K=%d: %.1f s"
+                  % (r, c, r, c, K, dt))
+    else:
+        sample = "quantize X[:%d], W[:%d] (%s) + GEMM Y[:%d, :%d] with K=%d: %.1f s" % (r, c, what, r, c, K, dt)
     return {"value": 2.0 * r * c * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "quantize X[:%d], W[:%d] (%s) + GEMM Y[:%d, :%d] with K=%d: %.1f s"
-                      % (r, c, what, r, c, K, dt),
+            "sample": sample,
             "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
             "quantize_gbs": round(qbytes / (t1 - t0) / 1e9, 3),
             "quantize_gbs_1_thread": round(qbytes / (t4 - t3) / 1e9, 3),
