@@ -571,13 +571,15 @@ def cpu_baseline(args, workload, synth):
     whole-step rate; the quantize (algorithmic bytes, as on the GPU) and the
     GEMM are also reported on their own.  The backward workloads take the
     GEMM operands as the GPU casts them (transposed slices, E5M2 gradients);
-    the grouped workload has no sampled leg (None)."""
+    the grouped one takes routed rows of one expert with that expert's
+    weight, cast outside the step as on the GPU."""
     import oracle
-    if workload not in ("mlp8b", "tiny", "qkv", "mlp70b", "wgrad", "dgrad"):
+    if workload not in ("mlp8b", "tiny", "qkv", "mlp70b", "wgrad", "dgrad", "moe"):
         return None
     gx = gw = "tensor"
     fx, fw = oracle.E4M3, oracle.E4M3
     pow2 = block = False
+    w_in_step = True                     # the weight's cast is part of the step
     if workload == "tiny":
         X, W = synth.tiny()
         r, c = 256, 256
@@ -593,6 +595,15 @@ def cpu_baseline(args, workload, synth):
             dy, w = synth.dgrad()
             r, c = args.cpu_rows // 4, args.cpu_cols // 2
             X, W = np.ascontiguousarray(dy[:r]), np.ascontiguousarray(w[:, :c].T)
+    elif workload == "moe":
+        # the first routed rows, all in expert 0's group, times that expert's
+        # weight (served in FP8: cast once, outside the step, as on the GPU)
+        cfg = synth.CONFIGS["moe"]
+        Xr, offsets, _ = synth.moe_routing(cfg["tokens"], cfg["top_k"], cfg["experts"], cfg["K"])
+        r, c = min(args.cpu_rows, int(offsets[1] - offsets[0])), args.cpu_cols
+        X = np.ascontiguousarray(Xr[int(offsets[0]):int(offsets[0]) + r])
+        W = np.ascontiguousarray(synth.moe_weight(0, cfg["N"], cfg["K"])[:c])
+        gx, w_in_step = "row", False
     else:
         r, c = args.cpu_rows, args.cpu_cols
         if workload == "qkv":
@@ -608,10 +619,12 @@ def cpu_baseline(args, workload, synth):
     # the GPU's algorithmic bytes: a just-in-time per-tensor cast reads its
     # input twice (the delayed casts of the backward workloads once)
     passes = 2 if gx == "tensor" and workload not in ("wgrad", "dgrad") else 1
-    qbytes = (X.size + W.size) * (passes * in_bytes + 1)
+    qbytes = (X.size + (W.size if w_in_step else 0)) * (passes * in_bytes + 1)
+    qw_fixed = None if w_in_step else oracle.quantize(W, fw, gw, pow2=pow2)
 
     def quantize_both():
-        return (oracle.quantize(X, fx, gx, pow2=pow2), oracle.quantize(W, fw, gw, pow2=pow2))
+        qx = oracle.quantize(X, fx, gx, pow2=pow2)
+        return qx, (oracle.quantize(W, fw, gw, pow2=pow2) if w_in_step else qw_fixed)
 
     t0 = time.perf_counter()
     qx, qw = quantize_both()
@@ -639,6 +652,9 @@ def cpu_baseline(args, workload, synth):
     elif workload == "dgrad":
         sample = ("quantize dY[:%d] (E5M2), W[:, :%d]^T (E4M3), per tensor + GEMM dX[:%d, :%d] with K=%d: %.1f s"
                   % (r, c, r, c, K, dt))
+    elif workload == "moe":
+        sample = ("quantize %d routed rows of expert 0 (per-row E4M3) + GEMM with its FP8 weight W_0[:%d] "
+                  "(cast outside the step) with K=%d: %.1f s" % (r, c, K, dt))
     else:
         sample = "quantize X[:%d], W[:%d] (%s) + GEMM Y[:%d, :%d] with K=%d: %.1f s" % (r, c, what, r, c, K, dt)
     return {"value": 2.0 * r * c * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
