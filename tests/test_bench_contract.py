@@ -50,3 +50,17 @@ def test_quant_rel_err_matches_direct_computation(gran, fmt):
                              torch.from_numpy(r["scale_inv"].astype(np.float32)),
                              "e4m3" if fmt == oracle.E4M3 else "e5m2", gran, transposed=True)
     assert abs(gt - want) <= 1e-5 * want
+
+
+@pytest.mark.parametrize("workload", ["tiny", "mlp8b", "qkv", "mlp70b", "wgrad", "dgrad", "moe"])
+def test_cpu_baseline_leg_of_every_workload(workload):
+    """The CPU-oracle leg runs for every GEMM workload (small samples here)
+    and reports what the bench line promises: a positive rate, the cores,
+    what the sample was, and the quantize and GEMM rates on their own."""
+    import types
+    import synth
+    args = types.SimpleNamespace(cpu_rows=32, cpu_cols=256)
+    d = bench.cpu_baseline(args, workload, synth)
+    assert d["kind"] == "oracle" and d["unit"] == "TFLOP/s" and d["value"] > 0 and d["cores"] >= 1
+    assert d["quantize_gbs"] > 0 and d["quantize_gbs_1_thread"] > 0 and d["gemm_gflops"] > 0
+    assert "GEMM" in d["sample"] and d["sample"].endswith(" s")
