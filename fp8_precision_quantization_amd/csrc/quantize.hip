@@ -638,7 +638,7 @@ static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchDiag, "scratch la
 static_assert(kScratchDiag + 4 <= kScratchGroupTable, "scratch layout: the grouped GEMM's table follows");
 
 constexpr int64_t kTBlocksPerCU = 4;     // transposed cast: tiles per block = tiles / (CUs * this)
-constexpr int64_t kRowBlocksPerCU = 3;   // measured: 2 and 3 per CU, 3 faster
+constexpr int64_t kRowBlocksPerCU = 3;   // measured: 2, 3 and 4 per CU, 3 fastest
 
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
     int64_t b = (work_items + per_block - 1) / per_block;
