@@ -81,6 +81,7 @@ def lib():
         L.or_gemm_sampled.argtypes = [P, i32, i64, P, i32, i64, i64, P, i32, P, i32, P, P, i64, P, P]
         L.or_gemm.argtypes = [P, i32, i64, P, i32, i64, i64, i64, i64, P, i32, P, i32, P, i64, P, i64]
         L.or_blockgemm_sampled.argtypes = [P, i64, P, i64, i64, P, P, P, P, i64, P, P]
+        L.or_blockgemm.argtypes = [P, i64, P, i64, i64, i64, i64, P, P, P, i64, P, i64]
         L.or_gemm_exact_sampled.argtypes = [P, i32, i64, P, i32, i64, i64, P, i32, P, i32, i32,
                                             P, P, i64, P]
         L.or_f32_to_bf16.restype = ctypes.c_uint16
@@ -302,6 +303,24 @@ def blockgemm_sampled(A, B, a_inv, b_inv, ms, ns):
     lib().or_blockgemm_sampled(_p(A), K, _p(B), K, K, _p(a_inv), _p(b_inv), _p(ms), _p(ns),
                                ms.size, _p(y), _p(p))
     return y, p
+
+
+def blockgemm(A, B, a_inv, b_inv, with_p: bool = True):
+    """Full block-scaled GEMM (A: [M,K] with a_inv [M, K/128]; B: [N,K] with
+    b_inv [N/128, K/128]; K % 128 == 0)."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2 and K % 128 == 0
+    a_inv = np.ascontiguousarray(a_inv, dtype=np.float32)
+    b_inv = np.ascontiguousarray(b_inv, dtype=np.float32)
+    assert a_inv.size == M * (K // 128) and b_inv.size == ((N + 127) // 128) * (K // 128)
+    Y = np.empty((M, N), dtype=np.float32)
+    P = np.empty((M, N), dtype=np.float64) if with_p else None
+    lib().or_blockgemm(_p(A), K, _p(B), K, M, N, K, _p(a_inv), _p(b_inv), _p(Y), N,
+                       _p(P) if with_p else None, N)
+    return (Y, P) if with_p else Y
 
 
 def gemm_exact_sampled(A, fa, B, fb, a_inv, b_inv, ms, ns, block_mode=False):

@@ -28,6 +28,7 @@
 #include <math.h>
 #include <float.h>
 #include <omp.h>
+#include <stdlib.h>
 
 enum { OR_E4M3 = 0, OR_E5M2 = 1 };
 enum { OR_GRAN_TENSOR = 0, OR_GRAN_ROW = 1, OR_GRAN_1x128 = 2, OR_GRAN_128x128 = 3 };
@@ -305,85 +306,147 @@ void or_delayed_step(or_ring* r, const void* x, int in_dtype, int64_t rows, int6
 
 /* ------------------------------------------------------------------------ */
 /* O7. Scaled GEMM, Y = X . W^T with both operands K-contiguous.             */
-/* Dequantize each operand (A_hat = fl32(decode(q) * s_inv)), then an fp32    */
-/* triple loop accumulating in k order; P = sum_k |A_hat*B_hat| in fp64 is    */
-/* returned for the error floor.  a_per_row / b_per_row select a scalar or   */
-/* one scale per row of A (per output row) / of B (per output column).       */
+/* Step 1, dequantize every operand element: A_hat = fl32(decode(q) * s_inv) */
+/* with the s_inv of the element's group; decode(q) is read from the table   */
+/* of all 256 codes that or_decode (the closed form above) fills.            */
+/* Step 2, an fp32 triple loop: Y32[m,n] = sum over k, in k order, of        */
+/* fl32(A_hat[m,k] * B_hat[n,k]), one rounding per product and per add; and  */
+/* P = sum_k |A_hat * B_hat| in fp64 for the error floor.                    */
+/* Scale layouts: a_per_row / b_per_row select a scalar or one scale per row */
+/* of A (per output row) / of B (per output column).  The block-scaled form  */
+/* ([DeepL] 2.3, per-block scaling) has one scale per (row of A, 128-wide K  */
+/* block), a_inv[m*(K/128)+kb], and one per (128 rows of B, 128-wide K       */
+/* block), b_inv[(n/128)*(K/128)+kb]; it needs K % 128 == 0.                 */
+/* OpenMP splits the outputs across threads; each output is one thread's     */
+/* k-ordered chain, so the results do not depend on the thread count.        */
 /* ------------------------------------------------------------------------ */
-static inline float deq(int fmt, uint8_t code, float s_inv) {
-    return (float)or_decode(fmt, code) * s_inv;
+typedef struct {
+    float a[256], b[256];   /* decode tables of the two formats */
+} or_tables;
+
+static void fill_tables(int fa, int fb, or_tables* t) {
+    for (int c = 0; c < 256; ++c) {
+        t->a[c] = (float)or_decode(fa, (uint8_t)c);   /* every FP8 value is a binary32 value */
+        t->b[c] = (float)or_decode(fb, (uint8_t)c);
+    }
 }
 
-/* Generic sampled form: computes n outputs at (ms[i], ns[i]). */
+/* Scale of element (r, k) of an operand: mode 0 = one scalar, 1 = one per
+ * row, 2 = A's 1x128 blocks, 3 = B's 128x128 blocks (K % 128 == 0). */
+enum { SC_SCALAR = 0, SC_ROW = 1, SC_A_BLOCK = 2, SC_B_BLOCK = 3 };
+
+static inline float scale_at(const float* s, int mode, int64_t r, int64_t k, int64_t kb_n) {
+    switch (mode) {
+    case SC_SCALAR:  return s[0];
+    case SC_ROW:     return s[r];
+    case SC_A_BLOCK: return s[r * kb_n + k / 128];
+    default:         return s[(r / 128) * kb_n + k / 128];
+    }
+}
+
+/* Step 1 for rows [0, rows) of one operand into out[rows x K]. */
+static void dequantize_rows(const uint8_t* q, int64_t ldq, int64_t rows, int64_t K, const float* tab,
+                            const float* s, int mode, float* out) {
+    int64_t kb_n = K / 128;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = tab[q[r * ldq + k]] * scale_at(s, mode, r, k, kb_n);
+}
+
+/* Step 2 for one output: the k-ordered fp32 sum and the fp64 sum of |products|. */
+static inline void dot_f32(const float* a, const float* b, int64_t K, float* y, double* p) {
+    float acc = 0.0f;
+    double pabs = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        float prod = a[k] * b[k];
+        acc = acc + prod;
+        pabs += fabs((double)a[k] * (double)b[k]);
+    }
+    *y = acc;
+    *p = pabs;
+}
+
+/* Every output of an M x N problem.  B_hat is formed once; each thread
+ * forms the row of A_hat it works on. */
+static void gemm_full(const uint8_t* A, int fa, int64_t lda, const float* a_inv, int amode,
+                      const uint8_t* B, int fb, int64_t ldb, const float* b_inv, int bmode,
+                      int64_t M, int64_t N, int64_t K, float* Y32, int64_t ldy, double* P, int64_t ldp) {
+    or_tables t;
+    fill_tables(fa, fb, &t);
+    int64_t kb_n = K / 128;
+    float* Bh = (float*)malloc(sizeof(float) * (size_t)(N > 0 ? N : 1) * (size_t)(K > 0 ? K : 1));
+    dequantize_rows(B, ldb, N, K, t.b, b_inv, bmode, Bh);
+    #pragma omp parallel
+    {
+        float* Ah = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t k = 0; k < K; ++k) Ah[k] = t.a[A[m * lda + k]] * scale_at(a_inv, amode, m, k, kb_n);
+            for (int64_t nn = 0; nn < N; ++nn) {
+                float y;
+                double p;
+                dot_f32(Ah, Bh + nn * K, K, &y, &p);
+                Y32[m * ldy + nn] = y;
+                if (P) P[m * ldp + nn] = p;
+            }
+        }
+        free(Ah);
+    }
+    free(Bh);
+}
+
+/* The outputs (ms[i], ns[i]), each dequantizing its own row pair. */
+static void gemm_sampled(const uint8_t* A, int fa, int64_t lda, const float* a_inv, int amode,
+                         const uint8_t* B, int fb, int64_t ldb, const float* b_inv, int bmode, int64_t K,
+                         const int64_t* ms, const int64_t* ns, int64_t n, float* y32, double* p64) {
+    or_tables t;
+    fill_tables(fa, fb, &t);
+    int64_t kb_n = K / 128;
+    #pragma omp parallel
+    {
+        float* ab = (float*)malloc(sizeof(float) * 2 * (size_t)(K > 0 ? K : 1));
+        #pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t m = ms[i], nn = ns[i];
+            for (int64_t k = 0; k < K; ++k) {
+                ab[k] = t.a[A[m * lda + k]] * scale_at(a_inv, amode, m, k, kb_n);
+                ab[K + k] = t.b[B[nn * ldb + k]] * scale_at(b_inv, bmode, nn, k, kb_n);
+            }
+            double p;
+            dot_f32(ab, ab + K, K, &y32[i], &p);
+            if (p64) p64[i] = p;
+        }
+        free(ab);
+    }
+}
+
 void or_gemm_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb, int64_t ldb,
                      int64_t K, const float* a_inv, int a_per_row, const float* b_inv, int b_per_row,
                      const int64_t* ms, const int64_t* ns, int64_t n, float* y32, double* p64) {
-    #pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t i = 0; i < n; ++i) {
-        int64_t m = ms[i], nn = ns[i];
-        float sa = a_per_row ? a_inv[m] : a_inv[0];
-        float sb = b_per_row ? b_inv[nn] : b_inv[0];
-        float acc = 0.0f;
-        double pabs = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            float av = deq(fa, A[m * lda + k], sa);
-            float bv = deq(fb, B[nn * ldb + k], sb);
-            float prod = av * bv;
-            acc = acc + prod;
-            pabs += fabs((double)av * (double)bv);
-        }
-        y32[i] = acc;
-        if (p64) p64[i] = pabs;
-    }
+    gemm_sampled(A, fa, lda, a_inv, a_per_row ? SC_ROW : SC_SCALAR, B, fb, ldb, b_inv,
+                 b_per_row ? SC_ROW : SC_SCALAR, K, ms, ns, n, y32, p64);
 }
 
 void or_gemm(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb, int64_t ldb,
              int64_t M, int64_t N, int64_t K, const float* a_inv, int a_per_row,
              const float* b_inv, int b_per_row, float* Y32, int64_t ldy, double* P, int64_t ldp) {
-    #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t m = 0; m < M; ++m) {
-        float sa = a_per_row ? a_inv[m] : a_inv[0];
-        for (int64_t nn = 0; nn < N; ++nn) {
-            float sb = b_per_row ? b_inv[nn] : b_inv[0];
-            float acc = 0.0f;
-            double pabs = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
-                float av = deq(fa, A[m * lda + k], sa);
-                float bv = deq(fb, B[nn * ldb + k], sb);
-                float prod = av * bv;
-                acc = acc + prod;
-                pabs += fabs((double)av * (double)bv);
-            }
-            Y32[m * ldy + nn] = acc;
-            if (P) P[m * ldp + nn] = pabs;
-        }
-    }
+    gemm_full(A, fa, lda, a_inv, a_per_row ? SC_ROW : SC_SCALAR, B, fb, ldb, b_inv,
+              b_per_row ? SC_ROW : SC_SCALAR, M, N, K, Y32, ldy, P, ldp);
 }
 
-/* Block-scaled GEMM ([DeepL] 2.3, per-block scaling): A has one scale per
- * (row, 128-wide K block), a_inv[m*(K/128)+kb]; B one per (128-row block,
- * 128-wide K block), b_inv[(n/128)*(K/128)+kb].  Same fp32 k-order loop with
- * each element dequantized by its own block scale.  Requires K % 128 == 0. */
 void or_blockgemm_sampled(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t K,
                           const float* a_inv, const float* b_inv,
                           const int64_t* ms, const int64_t* ns, int64_t n, float* y32, double* p64) {
-    int64_t kb_n = K / 128;
-    #pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t i = 0; i < n; ++i) {
-        int64_t m = ms[i], nn = ns[i];
-        float acc = 0.0f;
-        double pabs = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            int64_t kb = k / 128;
-            float av = deq(OR_E4M3, A[m * lda + k], a_inv[m * kb_n + kb]);
-            float bv = deq(OR_E4M3, B[nn * ldb + k], b_inv[(nn / 128) * kb_n + kb]);
-            float prod = av * bv;
-            acc = acc + prod;
-            pabs += fabs((double)av * (double)bv);
-        }
-        y32[i] = acc;
-        if (p64) p64[i] = pabs;
-    }
+    gemm_sampled(A, OR_E4M3, lda, a_inv, SC_A_BLOCK, B, OR_E4M3, ldb, b_inv, SC_B_BLOCK, K, ms, ns, n,
+                 y32, p64);
+}
+
+void or_blockgemm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M, int64_t N,
+                  int64_t K, const float* a_inv, const float* b_inv, float* Y32, int64_t ldy, double* P,
+                  int64_t ldp) {
+    gemm_full(A, OR_E4M3, lda, a_inv, SC_A_BLOCK, B, OR_E4M3, ldb, b_inv, SC_B_BLOCK, M, N, K, Y32, ldy,
+              P, ldp);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -394,10 +457,12 @@ void or_blockgemm_sampled(const uint8_t* A, int64_t lda, const uint8_t* B, int64
 /* for the final scaling).  Block mode sums per K block with its own scales.  */
 /* Non-finite codes are not allowed here (the caller filters them).           */
 /* ------------------------------------------------------------------------ */
-static inline int64_t code_to_int(int fmt, uint8_t code) {
-    /* decode(code) * 2^9 (E4M3) or * 2^16 (E5M2); exact integer */
-    double v = or_decode(fmt, code) * (fmt == OR_E4M3 ? 512.0 : 65536.0);
-    return (int64_t)v;
+static void int_table(int fmt, int64_t* t) {
+    /* decode(code) * 2^9 (E4M3) or * 2^16 (E5M2): an exact integer */
+    for (int c = 0; c < 256; ++c) {
+        double v = or_decode(fmt, (uint8_t)c) * (fmt == OR_E4M3 ? 512.0 : 65536.0);
+        t[c] = isfinite(v) ? (int64_t)v : 0;
+    }
 }
 
 void or_gemm_exact_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb,
@@ -406,6 +471,9 @@ void or_gemm_exact_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t*
                            const int64_t* ms, const int64_t* ns, int64_t n, double* y_exact) {
     int64_t kb_n = K / 128;
     int shift = (fa == OR_E4M3 ? 9 : 16) + (fb == OR_E4M3 ? 9 : 16);
+    int64_t ta[256], tb[256];
+    int_table(fa, ta);
+    int_table(fb, tb);
     #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t i = 0; i < n; ++i) {
         int64_t m = ms[i], nn = ns[i];
@@ -413,7 +481,7 @@ void or_gemm_exact_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t*
         if (!block_mode) {
             __int128 d = 0;
             for (int64_t k = 0; k < K; ++k)
-                d += (__int128)code_to_int(fa, A[m * lda + k]) * (__int128)code_to_int(fb, B[nn * ldb + k]);
+                d += (__int128)ta[A[m * lda + k]] * (__int128)tb[B[nn * ldb + k]];
             float sa = a_per_row ? a_inv[m] : a_inv[0];
             float sb = b_per_row ? b_inv[nn] : b_inv[0];
             total = (long double)d * (long double)sa * (long double)sb;
@@ -421,7 +489,7 @@ void or_gemm_exact_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t*
             for (int64_t kb = 0; kb < kb_n; ++kb) {
                 __int128 d = 0;
                 for (int64_t k = kb * 128; k < kb * 128 + 128; ++k)
-                    d += (__int128)code_to_int(fa, A[m * lda + k]) * (__int128)code_to_int(fb, B[nn * ldb + k]);
+                    d += (__int128)ta[A[m * lda + k]] * (__int128)tb[B[nn * ldb + k]];
                 total += (long double)d * (long double)a_inv[m * kb_n + kb]
                          * (long double)b_inv[(nn / 128) * kb_n + kb];
             }

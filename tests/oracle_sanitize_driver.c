@@ -43,6 +43,8 @@ void or_gemm(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb, in
 void or_blockgemm_sampled(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t K,
                           const float* a_inv, const float* b_inv, const int64_t* ms, const int64_t* ns, int64_t n,
                           float* y32, double* p64);
+void or_blockgemm(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                  const float* a_inv, const float* b_inv, float* Y32, int64_t ldy, double* P, int64_t ldp);
 void or_gemm_exact_sampled(const uint8_t* A, int fa, int64_t lda, const uint8_t* B, int fb, int64_t ldb,
                            int64_t K, const float* a_inv, int a_per_row, const float* b_inv, int b_per_row,
                            int block_mode, const int64_t* ms, const int64_t* ns, int64_t n, double* y_exact);
@@ -157,6 +159,7 @@ static void gemm_cases(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
                 for (int64_t i = 0; i < M * kb; ++i) ba[i] = ldexpf(1.0f, (int)(next_u64() % 5) - 2);
                 for (int64_t i = 0; i < nblk * kb; ++i) bb[i] = ldexpf(1.0f, (int)(next_u64() % 5) - 2);
                 or_blockgemm_sampled(A, lda, B, ldb, K, ba, bb, ms, nsv, ns_, y, p);
+                or_blockgemm(A, lda, B, ldb, M, N, K, ba, bb, Y, ldy, P, ldy);
                 or_gemm_exact_sampled(A, 0, lda, B, 0, ldb, K, ba, 1, bb, 1, 1, ms, nsv, ns_, ye);
                 free(ba); free(bb);
             }

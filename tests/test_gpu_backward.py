@@ -13,7 +13,8 @@ import torch
 import oracle
 import synth
 from tests.gpu_util import dev_input, host, say
-from tests.parity import assert_gemm, exact_checker
+from tests.mfma_model import gemm_model_at
+from tests.parity import assert_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +97,7 @@ def test_backward_gemms_parity_and_accuracy():
     ns = np.concatenate([[K - 1, 0], rng.integers(0, K, 1500)])
     y32, p = oracle.gemm_sampled(ody["q"], oracle.E5M2, wt_q, oracle.E4M3, sdy, sw, ms, ns)
     print(assert_gemm(dx[ms, ns], y32, p, N, "f32", what="dgrad",
-                      exact=exact_checker(ody["q"], oracle.E5M2, wt_q, oracle.E4M3, sdy, sw, ms, ns)))
+                      model=gemm_model_at(ody["q"], oracle.E5M2, wt_q, oracle.E4M3, sdy, sw, ms, ns)))
 
     say("wgrad gemm", N, K, M)
     dw = host(fp8.scaled_gemm(dyt, rxt.q, rdy.scale_inv.reshape(-1), rxt.scale_inv.reshape(-1),
@@ -107,7 +108,7 @@ def test_backward_gemms_parity_and_accuracy():
     ns = np.concatenate([[K - 1, 0], rng.integers(0, K, 1500)])
     y32, p = oracle.gemm_sampled(dyt_q, oracle.E5M2, xt_q, oracle.E4M3, sdy, sx, ms, ns)
     print(assert_gemm(dw[ms, ns], y32, p, M, "f32", what="wgrad",
-                      exact=exact_checker(dyt_q, oracle.E5M2, xt_q, oracle.E4M3, sdy, sx, ms, ns)))
+                      model=gemm_model_at(dyt_q, oracle.E5M2, xt_q, oracle.E4M3, sdy, sx, ms, ns)))
 
     # accuracy against the high-precision products of the same bf16 inputs
     dy64 = synth.bf16_bits_to_f32(dy).astype(np.float64)

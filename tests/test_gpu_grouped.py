@@ -15,7 +15,8 @@ import torch
 import oracle
 import synth
 from tests.gpu_util import dev_u8, host, random_codes, say
-from tests.parity import assert_gemm, exact_checker
+from tests.mfma_model import gemm_model_at
+from tests.parity import assert_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -70,7 +71,7 @@ def _check(y, A, B, a_inv, b_inv, offsets, fa, fb, out_dtype, rng, per_group=400
         ns = np.concatenate([[0, N - 1], rng.integers(0, N, per_group)])
         y32, p = oracle.gemm_sampled(A, fa, B[g], fb, a_inv, b2[g], ms, ns)
         assert_gemm(y[ms, ns], y32, p, K, odt, what="%s group %d" % (what, g),
-                    exact=exact_checker(A, fa, B[g], fb, a_inv, b2[g], ms, ns))
+                    model=gemm_model_at(A, fa, B[g], fb, a_inv, b2[g], ms, ns))
     outside = np.ones(M, bool)
     for g in range(G):
         outside[offsets[g]:offsets[g + 1]] = False

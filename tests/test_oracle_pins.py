@@ -527,3 +527,43 @@ def test_bf16_rne_matches_torch():
     ours = oracle.f32_to_bf16(v)
     ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)
+
+
+@pytest.mark.parametrize("block", [False, True])
+def test_gemm_table_decode_equals_closed_form_k_loop(block):
+    """The GEMM loops decode through the 256-entry table; the same sums
+    written as a numpy k-ordered fp32 loop over operands decoded one element
+    at a time by the closed form (or_decode), with one rounding per product
+    and per add, agree bit for bit (full and sampled forms, scalar, per-row
+    and block scales)."""
+    rng = np.random.default_rng(31 + block)
+    M, N, K = 37, 130, 384
+    fa, fb = (0, 0) if block else (1, 0)
+    A = _rand_codes(rng, (M, K), fa)
+    B = _rand_codes(rng, (N, K), fb)
+    dec = np.vectorize(lambda f, c: oracle.lib().or_decode(f, int(c)))
+    Ad = dec(fa, A).astype(np.float32)
+    Bd = dec(fb, B).astype(np.float32)
+    if block:
+        sa = (rng.random((M, K // 128)) + 0.25).astype(np.float32)
+        sb = (rng.random(((N + 127) // 128, K // 128)) * 0.01 + 1e-3).astype(np.float32)
+        Ah = (Ad * np.repeat(sa, 128, axis=1)).astype(np.float32)
+        Bh = (Bd * np.repeat(np.repeat(sb, 128, axis=0)[:N], 128, axis=1)).astype(np.float32)
+        Y, P = oracle.blockgemm(A, B, sa, sb)
+    else:
+        sa = (rng.random(M) + 0.5).astype(np.float32)
+        sb = np.float32(0.0625)
+        Ah = (Ad * sa[:, None]).astype(np.float32)
+        Bh = (Bd * sb).astype(np.float32)
+        Y, P = oracle.gemm(A, fa, B, fb, sa, sb)
+    ref = np.zeros((M, N), np.float32)
+    for k in range(K):
+        ref = (ref + (Ah[:, k:k + 1] * Bh[None, :, k]).astype(np.float32)).astype(np.float32)
+    assert np.array_equal(Y.view(np.uint32), ref.view(np.uint32))
+    assert np.allclose(P, np.abs(Ah.astype(np.float64)) @ np.abs(Bh.astype(np.float64)).T, rtol=1e-12)
+    ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    if block:
+        y2, p2 = oracle.blockgemm_sampled(A, B, sa, sb, ms.ravel(), ns.ravel())
+    else:
+        y2, p2 = oracle.gemm_sampled(A, fa, B, fb, sa, sb, ms.ravel(), ns.ravel())
+    assert np.array_equal(y2, Y.ravel()) and np.array_equal(p2, P.ravel())
