@@ -20,8 +20,9 @@ write-back of the previous GEMM's output from the cache, so its share of a
 step (step minus GEMM) is reported beside its own time.  After
 the timed steps, `kernels` also gets the graphics clock sampled (amd-smi)
 while the GEMM repeats for 1.5 s, the GEMM's % of the FP8 peak at that
-clock, and a plain 512 MiB device copy's bandwidth as the practical
-streaming ceiling of the quantize; per-step times come as mean and as
+clock, and hand-written streaming probes (read-only, copy, and 16 bytes read
+per 8 written, the cast's own pattern) as the practical HBM ceilings of the
+quantize; per-step times come as mean and as
 median / p10 / p90; `quantize_rel_err` is each operand's ||dequant(q) - x|| /
 ||x|| with its granularity and format.  `cpu_baseline` is the oracle on a bounded sample of
 the same step (quantize on all threads and on one, GEMM on all threads).
@@ -48,17 +49,31 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
-# rocprofv3 HBM traffic of one scaled-GEMM call on the mlp8b workload (its two
-# launches: k_gemm_p over 768 tiles of 256 x 256, then k_gemm_h over the last
-# columns as 256 tiles of 128 x 256): FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 per
-# dispatch (factors from a plain 512 MiB copy, see
-# profiles/k_gemm_mlp8b_hbm_traffic.md).  Reset to None whenever either kernel
-# changes until the counters are taken again.
-GEMM_TRAFFIC_BYTES = 515462247
-# The same counters for one fp8_kv_load launch of the kv workload (see
-# profiles/kv_store_gather_8x128_paged_kernel_stats.md); None once k_kv_load
-# changes until they are taken again.
-KV_LOAD_TRAFFIC_BYTES = 104882176
+# rocprofv3 HBM traffic of one call of the roofline kernel: FETCH_SIZE x 2.0 +
+# WRITE_SIZE x 1.0 per dispatch (factors from a plain 512 MiB copy), with the
+# first 16 hex digits of the sha256 of the kernel source the counters were
+# taken with.  A run whose source differs reports no traffic (null) and says
+# the figure is stale, until the counters are taken again.
+#   mlp8b: one scaled-GEMM call (profiles/k_gemm_mlp8b_hbm_traffic.md)
+#   kv: one fp8_kv_load launch (profiles/kv_store_gather_8x128_paged_kernel_stats.md)
+TRAFFIC = {
+    "mlp8b": {"bytes": 515462247, "source": "csrc/gemm.hip", "sha16": "0acc0d89b17d8d8f"},
+    "kv": {"bytes": 104882176, "source": "csrc/kvcache.hip", "sha16": "119ccf3371e008a4"},
+}
+
+
+def traffic(workload: str):
+    """(bytes, note): the recorded HBM bytes of the roofline kernel when its
+    source is the one the counters were taken with, else (None, why)."""
+    import hashlib
+    t = TRAFFIC.get(workload)
+    if t is None:
+        return None, "no counters taken for this workload"
+    path = os.path.join(ROOT, "fp8_precision_quantization_amd", t["source"])
+    sha = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    if sha != t["sha16"]:
+        return None, "stale: %s changed since the counters were taken (%s, now %s)" % (t["source"], t["sha16"], sha)
+    return t["bytes"], "rocprofv3 FETCH_SIZE/WRITE_SIZE with %s at %s" % (t["source"], sha)
 
 WORKLOADS = {
     "tiny": "tiny: X, W [256 x 256] fp32 N(0,1); per-tensor E4M3; Y fp32",
@@ -95,6 +110,10 @@ def parse():
                     help="only run a plain device copy of MIB MiB (reference for the HBM byte counters)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the 1.5 s GEMM loop that samples the graphics clock")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload block (the other GEMM workloads timed in the same run)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="back-to-back calls per operation in the per-workload block")
     return ap.parse_args()
 
 
@@ -152,28 +171,54 @@ def spread(ms):
             "p90": round(float(np.percentile(ms, 90)), 4)}
 
 
-def copy_ceiling_gbs(torch, mib: int = 512, reps: int = 5, rounds: int = 4) -> float:
-    """Bytes read + written per second of a plain device copy of `mib` MiB
-    (two buffers alternating, so no copy's source is still cached), the best
-    of `rounds` rounds of `reps` copies: the practical ceiling a streaming
-    kernel is measured against, beside the published HBM peak."""
+def stream_ceilings(torch, mib: int = 1024, reps: int = 5, rounds: int = 3) -> dict:
+    """HBM ceilings from the hand-written streaming probes (libfp8probe.so):
+    a read-only stream, a copy, and 16 bytes read per 8 written (a bf16 ->
+    FP8 cast's pattern without its arithmetic), each over `mib` MiB of
+    source alternating between two buffers (so nothing is left in the
+    256 MB Infinity Cache), the best of `rounds` rounds of `reps` launches;
+    GB/s of bytes read + written.  For each, the best of 4 and 8 workgroups
+    per CU."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_precision_quantization_amd", "libfp8probe.so")
+    if not os.path.exists(path):
+        raise ImportError("libfp8probe.so is not built at %s" % path)
+    L = ctypes.CDLL(path)
+    P, I64, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.fp8probe_read.argtypes = [P, I64, P, I64, INT, P]
+    L.fp8probe_copy.argtypes = [P, P, I64, INT, P]
+    L.fp8probe_read2_write1.argtypes = [P, P, I64, INT, P]
     n = mib * 2 ** 20
-    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
-    for b in bufs:
-        b.fill_(1)
-    for i in range(2):
-        bufs[2 + i].copy_(bufs[i])
-    torch.cuda.synchronize()
+    src = [torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(i + 1) for i in range(2)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    launches = {
+        "read": (lambda i, b: L.fp8probe_read(src[i].data_ptr(), n, sink.data_ptr(), sink.numel(), b, stream), n),
+        "copy": (lambda i, b: L.fp8probe_copy(src[i].data_ptr(), dst[i].data_ptr(), n, b, stream), 2 * n),
+        "read2_write1": (lambda i, b: L.fp8probe_read2_write1(src[i].data_ptr(), dst[i].data_ptr(), n, b, stream),
+                         n + n // 2),
+    }
+    out = {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = 0.0
-    for _ in range(rounds):
-        e0.record()
-        for i in range(reps):
-            bufs[2 + (i & 1)].copy_(bufs[i & 1])
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    return best
+    for name, (run, nbytes) in launches.items():
+        best = 0.0
+        for bpc in (4, 8):
+            for i in range(2):
+                if run(i, bpc) != 0:
+                    raise RuntimeError("fp8probe %s failed" % name)
+            torch.cuda.synchronize()
+            for _ in range(rounds):
+                e0.record()
+                for r in range(reps):
+                    run(r & 1, bpc)
+                e1.record()
+                torch.cuda.synchronize()
+                best = max(best, nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        out[name + "_gbs"] = round(best, 1)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 def gemm_clock_mhz(torch, run, seconds: float = 1.5):
@@ -522,9 +567,11 @@ def kv_main(args, torch, fp8, synth):
     s_gbs, l_gbs = sb / (s_ms * 1e-3) / 1e9, lb / (l_ms * 1e-3) / 1e9
     # the gather kernel dominates; its launches are the two loads of a step
     per_launch = lb / 2
+    tb, tnote = traffic("kv")
     roof = {"bound": "hbm", "achieved": round(l_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(l_gbs / PEAK_HBM_GBS, 4), "traffic": KV_LOAD_TRAFFIC_BYTES,
-            "algorithmic_bytes_per_launch": int(per_launch)}
+            "frac": round(l_gbs / PEAK_HBM_GBS, 4), "traffic": tb, "traffic_note": tnote,
+            "algorithmic_bytes_per_launch": int(per_launch),
+            "time": "load_ms: mean of K back-to-back gathers between two events, per launch"}
     cpu = None if args.no_cpu_baseline else kv_cpu_baseline(synth)
     out = {
         "metric": "FP8 KV-cache store + paged gather-dequantize GB/s (% HBM peak)",
@@ -550,6 +597,46 @@ def kv_main(args, torch, fp8, synth):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+CONFIG_WORKLOADS = ("qkv", "mlp70b", "wgrad", "dgrad", "moe")
+
+
+def workload_block(torch, fp8, synth, workload: str, steps: int) -> dict:
+    """One other GEMM workload timed in the same run, so that one default
+    bench line records every configuration: its GEMM (`steps` calls back to
+    back between two events), its quantize likewise, and whole steps, with
+    the GEMM's TFLOP/s and fraction of the FP8 MFMA peak."""
+    st = Step(workload, torch, fp8, synth)
+    for _ in range(3):
+        st.quantize()
+        st.gemm()
+
+    def step():
+        st.quantize()
+        st.gemm()
+
+    def quantize_only():
+        st.quantize()
+        st.i += 1
+
+    with phase(torch, "workload %s" % workload):
+        ms = loop_ms(torch, step, steps)
+        g_ms = loop_ms(torch, st.gemm, steps)
+        q_ms = loop_ms(torch, quantize_only, steps)
+    flops = 2.0 * st.M * st.N * st.K
+    tflops = flops / (g_ms * 1e-3) / 1e12
+    qbytes = st.quant_bytes()
+    out = {"M": st.M, "N": st.N, "K": st.K, "steps": steps,
+           "gemm_ms": round(g_ms, 4), "gemm_tflops": round(tflops, 2),
+           "gemm_frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+           "quantize_ms": round(q_ms, 4), "quantize_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+           "quantize_frac_hbm_peak": round(qbytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "step_ms": round(ms, 4), "step_tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_model() -> str:
@@ -722,19 +809,26 @@ def main():
     gemm_tflops = flops / (g_mean * 1e-3) / 1e12
     qbytes = st.quant_bytes()
     q_gbs = qbytes / (q_mean * 1e-3) / 1e9
-    # after the timed region: a plain copy's bandwidth as the practical
-    # streaming ceiling (before the clock probe's 1.5 s of GEMMs heat the
-    # chip), and the graphics clock under the GEMM
-    with phase(torch, "copy ceiling"):
-        copy_gbs = copy_ceiling_gbs(torch)
+    # after the timed region: the streaming probes' ceilings (before the
+    # clock probe's 1.5 s of GEMMs heat the chip), and the graphics clock
+    # under the GEMM
+    with phase(torch, "stream ceilings"):
+        ceil = stream_ceilings(torch)
     with phase(torch, "clock under the gemm"):
         clock = None if args.no_clock else gemm_clock_mhz(torch, st.gemm)
     diags = (fp8.Diag(), fp8.Diag())
     st.quantize(*diags)
     q_err = st.quant_errors(diags)
+    others = None
+    if not args.no_configs:
+        others = {}
+        for w in CONFIG_WORKLOADS:
+            if w != args.workload:
+                others[w] = workload_block(torch, fp8, synth, w, args.config_steps)
+    tb, tnote = traffic(args.workload)
     roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-            "traffic": GEMM_TRAFFIC_BYTES if args.workload == "mlp8b" else None}
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": tb, "traffic_note": tnote,
+            "time": "kernels.gemm_ms: mean of K back-to-back GEMM calls between two events"}
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, args.workload, synth)
     out = {
         "metric": "FP8 scaled-GEMM TFLOPS (% of FP8 MFMA peak); quantize GB/s (% HBM peak)",
@@ -768,8 +862,12 @@ def main():
             "quantize_pct_hbm_peak": round(100 * q_gbs / PEAK_HBM_GBS, 2),
             "quantize_bytes": int(qbytes),
             "quantize_rel_err": q_err,
-            "copy_ceiling_gbs": round(copy_gbs, 1),
-            "quantize_pct_copy_ceiling": round(100 * q_gbs / copy_gbs, 2),
+            "stream_ceilings": ceil,
+            # against the probe with the cast's own 2:1 read:write pattern
+            "quantize_pct_read2_write1_ceiling": round(100 * q_gbs / ceil["read2_write1_gbs"], 2),
+            # the other GEMM workloads, each timed in this run (GEMM, quantize
+            # and whole steps; TFLOP/s and fraction of the FP8 peak)
+            "workloads": others,
         },
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -22,7 +22,7 @@ from ._lib import Fp8Error  # noqa: F401
 
 __all__ = ["quantize", "quantize_dual", "amax", "scaled_gemm", "blockscaled_gemm", "AmaxHistory", "Diag",
            "QuantResult", "Fp8Error", "FORMATS", "GRANULARITIES", "group_grid", "kv_store", "kv_load",
-           "KVTensorCache", "KVCache", "grouped_gemm"]
+           "KVTensorCache", "KVCache", "grouped_gemm", "workspace"]
 
 FORMATS = {"e4m3": _lib.FP8_E4M3, "e5m2": _lib.FP8_E5M2}
 GRANULARITIES = {"tensor": _lib.FP8_GRAN_TENSOR, "row": _lib.FP8_GRAN_ROW,
@@ -90,6 +90,29 @@ def _out_matrix(out: torch.Tensor, rows: int, cols: int, dtype, device: torch.de
     if cols > 1 and out.stride(1) != 1:
         raise ValueError("%s must have a contiguous last dimension" % name)
     return max(out.stride(0), 1) if rows > 1 else max(cols, 1)
+
+
+def workspace(device="cuda") -> torch.Tensor:
+    """A workspace for the calls that need one (fp8_workspace_size() bytes).
+    Calls ordered on one stream may share it; calls running concurrently on
+    different streams need one each."""
+    return torch.empty(_lib.WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+
+
+def _workspace(ws: Optional[torch.Tensor], needed: bool, device: torch.device):
+    """(tensor kept alive for the call, pointer, bytes).  Without one given, a
+    needed workspace comes from torch's allocator, whose blocks are reused in
+    the order of the current stream."""
+    if not needed and ws is None:
+        return None, None, 0
+    if ws is None:
+        ws = workspace(device)
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < _lib.WORKSPACE_BYTES:
+        raise ValueError("workspace must hold %d bytes, got %d" % (_lib.WORKSPACE_BYTES, nbytes))
+    return ws, ws.data_ptr(), nbytes
 
 
 def _numel(shape) -> int:
@@ -174,7 +197,8 @@ def quantize(x: torch.Tensor, fmt="e4m3", granularity="tensor", pow2: bool = Fal
              diag: Optional[Diag] = None, out: Optional[torch.Tensor] = None,
              spike_guard: bool = False,
              scale_inv_out: Optional[torch.Tensor] = None,
-             amax_out: Optional[torch.Tensor] = None) -> QuantResult:
+             amax_out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> QuantResult:
     rows, cols, ld = _matrix(x, "x")
     if x.dtype == torch.bfloat16:
         in_dt = _lib.FP8_IN_BF16
@@ -197,11 +221,12 @@ def quantize(x: torch.Tensor, fmt="e4m3", granularity="tensor", pow2: bool = Fal
     _buf(amax_out, _numel(grid), torch.float32, dev, "amax_out")
     flags = ((_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_TRANSPOSE_OUT if transpose else 0)
              | (_lib.FP8_SPIKE_GUARD if spike_guard else 0))
+    ws, ws_ptr, ws_bytes = _workspace(workspace, _gran(granularity) == _lib.FP8_GRAN_TENSOR, dev)
     st = _lib.lib().fp8_quantize(
         x.data_ptr(), in_dt, rows, cols, ld, _fmt(fmt), _gran(granularity), flags,
         _ptr(history.buf) if history is not None else None, out.data_ptr(), ldq,
         scale_inv_out.data_ptr(), amax_out.data_ptr(), _ptr(diag.buf) if diag is not None else None,
-        _stream(dev))
+        ws_ptr, ws_bytes, _stream(dev))
     _lib.check(st, "fp8_quantize")
     return QuantResult(out, scale_inv_out, amax_out, fmt_name)
 
@@ -210,7 +235,8 @@ def quantize_dual(x: torch.Tensor, fmt="e5m2", pow2: bool = False, history: Opti
                   diag: Optional[Diag] = None, spike_guard: bool = False,
                   out: Optional[torch.Tensor] = None, out_t: Optional[torch.Tensor] = None,
                   scale_inv_out: Optional[torch.Tensor] = None,
-                  amax_out: Optional[torch.Tensor] = None):
+                  amax_out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
     """Per-tensor quantization into both layouts from one pass over x
     (fp8_quantize_dual).  Returns (QuantResult with q [rows x cols], qt [cols x rows])."""
     rows, cols, ld = _matrix(x, "x")
@@ -235,16 +261,18 @@ def quantize_dual(x: torch.Tensor, fmt="e5m2", pow2: bool = False, history: Opti
     _buf(scale_inv_out, 1, torch.float32, dev, "scale_inv_out")
     _buf(amax_out, 1, torch.float32, dev, "amax_out")
     flags = (_lib.FP8_SCALE_POW2 if pow2 else 0) | (_lib.FP8_SPIKE_GUARD if spike_guard else 0)
+    ws, ws_ptr, ws_bytes = _workspace(workspace, True, dev)
     st = _lib.lib().fp8_quantize_dual(
         x.data_ptr(), in_dt, rows, cols, ld, _fmt(fmt), flags,
         _ptr(history.buf) if history is not None else None, out.data_ptr(), ldq, out_t.data_ptr(), ldqt,
         scale_inv_out.data_ptr(), amax_out.data_ptr(), _ptr(diag.buf) if diag is not None else None,
-        _stream(dev))
+        ws_ptr, ws_bytes, _stream(dev))
     _lib.check(st, "fp8_quantize_dual")
     return QuantResult(out, scale_inv_out, amax_out, fmt_name), out_t
 
 
-def amax(x: torch.Tensor, granularity="tensor", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def amax(x: torch.Tensor, granularity="tensor", out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     rows, cols, ld = _matrix(x, "x")
     in_dt = _lib.FP8_IN_BF16 if x.dtype == torch.bfloat16 else _lib.FP8_IN_F32
     if x.dtype not in (torch.bfloat16, torch.float32):
@@ -253,8 +281,9 @@ def amax(x: torch.Tensor, granularity="tensor", out: Optional[torch.Tensor] = No
     if out is None:
         out = torch.empty(grid, dtype=torch.float32, device=x.device)
     _buf(out, _numel(grid), torch.float32, x.device, "out")
+    ws, ws_ptr, ws_bytes = _workspace(workspace, _gran(granularity) == _lib.FP8_GRAN_TENSOR, x.device)
     st = _lib.lib().fp8_amax(x.data_ptr(), in_dt, rows, cols, ld, _gran(granularity), out.data_ptr(),
-                             _stream(x.device))
+                             ws_ptr, ws_bytes, _stream(x.device))
     _lib.check(st, "fp8_amax")
     return out
 
@@ -321,7 +350,7 @@ def blockscaled_gemm(a_q: torch.Tensor, b_q: torch.Tensor, a_scale_inv: torch.Te
 # ------------------------------------------------------------ grouped GEMM --
 def grouped_gemm(a_q: torch.Tensor, b_q: torch.Tensor, group_offsets: torch.Tensor, a_scale_inv: torch.Tensor,
                  b_scale_inv: torch.Tensor, fa="e4m3", fb="e4m3", out_dtype=torch.bfloat16,
-                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """MoE grouped GEMM: rows [offs[g], offs[g+1]) of a_q [M, K] times expert
     g's b_q[g] ([G, N, K] uint8 codes): C[m] = (A_q[m] . B_q[g]^T) * sa * sb_g.
     group_offsets: int32 device tensor [G+1]; a_scale_inv: 1 or M values;
@@ -355,10 +384,11 @@ def grouped_gemm(a_q: torch.Tensor, b_q: torch.Tensor, group_offsets: torch.Tens
         raise ValueError("b_scale_inv must hold G=%d or G*N=%d values" % (G, G * N))
     _buf(a_scale_inv, M if a_row else 1, torch.float32, dev, "a_scale_inv")
     _buf(b_scale_inv, G * N if b_row else G, torch.float32, dev, "b_scale_inv")
+    ws, ws_ptr, ws_bytes = _workspace(workspace, True, dev)
     st = _lib.lib().fp8_grouped_gemm(a_q.data_ptr(), _fmt(fa), lda, b_q.data_ptr(), _fmt(fb), ldb, gstride, M, N, K,
                                      G, group_offsets.data_ptr(), a_scale_inv.data_ptr(), a_row,
                                      b_scale_inv.data_ptr(), b_row, out.data_ptr(), _out_dtype(out.dtype), ldc,
-                                     _stream(a_q.device))
+                                     ws_ptr, ws_bytes, _stream(a_q.device))
     _lib.check(st, "fp8_grouped_gemm")
     return out
 

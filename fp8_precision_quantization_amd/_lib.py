@@ -33,6 +33,7 @@ FP8_KV_PER_TOKEN_HEAD, FP8_KV_PER_HEAD = 0, 1
 FP8_GROUPED_MAX_TILES = 1983
 HISTORY_BYTES = 128
 DIAG_BYTES = 16
+WORKSPACE_BYTES = 65536
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -45,16 +46,19 @@ SIGNATURES = {
     "fp8_abi_version": (_INT, []),
     "fp8_status_string": (ctypes.c_char_p, [_INT]),
     "fp8_last_error": (ctypes.c_char_p, []),
+    "fp8_workspace_size": (_I64, []),
     "fp8_history_init": (_INT, [_P, _I32, _P]),
     "fp8_history_set_guard": (_INT, [_P, ctypes.c_float, _P]),
-    "fp8_amax": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P]),
-    "fp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U32, _P, _P, _I64, _P, _P, _P, _P]),
-    "fp8_quantize_dual": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _U32, _P, _P, _I64, _P, _I64, _P, _P, _P, _P]),
+    "fp8_amax": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P, _I64, _P]),
+    "fp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U32, _P, _P, _I64, _P, _P, _P, _P, _I64,
+                            _P]),
+    "fp8_quantize_dual": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _U32, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                                 _I64, _P]),
     "fp8_scaled_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,
                                _P, _INT, _I64, _P]),
     "fp8_blockscaled_gemm": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _INT, _I64, _P]),
     "fp8_grouped_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I32, _P, _P, _INT,
-                                _P, _INT, _P, _INT, _I64, _P]),
+                                _P, _INT, _P, _INT, _I64, _P, _I64, _P]),
     "fp8_kv_store": (_INT, [_P, _INT, _I64, _I64, _I32, _I32, _P, _INT, _INT, _U32, _P, _P, _I64, _P, _P]),
     "fp8_kv_load": (_INT, [_P, _INT, _INT, _P, _I64, _I32, _I32, _P, _I64, _INT, _P, _I64, _P]),
 }

@@ -1,9 +1,11 @@
-"""Build libfp8mi.so (gfx950 only) in-tree with hipcc.
+"""Build libfp8mi.so (gfx950 only) in-tree with hipcc, and libfp8probe.so,
+the HBM streaming probes the benchmark measures its ceilings with.
 
     python -m fp8_precision_quantization_amd.build
 
 Every HIP source is compiled for gfx950 with packed-fp32 instructions
-disabled, then linked into fp8_precision_quantization_amd/libfp8mi.so.
+disabled, then linked into fp8_precision_quantization_amd/libfp8mi.so (and
+the probe into libfp8probe.so).
 """
 from __future__ import annotations
 
@@ -17,7 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8mi.so")
+PROBE_LIB = os.path.join(PKG, "libfp8probe.so")
 SOURCES = ["quantize.hip", "gemm.hip", "kvcache.hip", "api.cpp"]
+PROBE_SOURCES = ["stream_probe.hip"]
 HEADERS = ["device_common.hpp", "cast_unit.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -37,18 +41,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -9,10 +9,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <map>
 #include <mutex>
 #include <string>
-#include <utility>
 
 #include "fp8mi.h"
 #include "launch.hpp"
@@ -74,36 +72,16 @@ fp8_status check_device(int* cus) {
     return FP8_OK;
 }
 
-// Scratch for the per-tensor reductions: one buffer per (device, stream),
-// allocated on the first quantize/amax call that uses the pair and kept for
-// the life of the process.  Calls on one stream are ordered, so they can
-// share it; calls on different streams never do.
-std::mutex g_scratch_mutex;
-std::map<std::pair<int, uintptr_t>, uint32_t*> g_scratch;
-
-fp8_status get_scratch(hipStream_t stream, uint32_t** out) {
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(FP8_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-    std::lock_guard<std::mutex> lock(g_scratch_mutex);
-    auto key = std::make_pair(dev, (uintptr_t)stream);
-    auto it = g_scratch.find(key);
-    if (it != g_scratch.end()) {
-        *out = it->second;
-        return FP8_OK;
-    }
-    void* p = nullptr;
-    e = hipMalloc(&p, sizeof(uint32_t) * fp8mi::kScratchWords);
-    if (e != hipSuccess) return fail(FP8_ERR_HIP, "scratch allocation failed: %s", hipGetErrorString(e));
-    // zeroed once, in stream order (a kernel, not a memset node): the
-    // guarded delayed cast relies on its diagnostic words starting at zero
-    e = fp8mi::launch_zero_words(static_cast<uint32_t*>(p), fp8mi::kScratchWords, stream);
-    if (e != hipSuccess) {
-        hipFree(p);
-        return fail(FP8_ERR_HIP, "scratch initialization failed: %s", hipGetErrorString(e));
-    }
-    g_scratch[key] = static_cast<uint32_t*>(p);
-    *out = static_cast<uint32_t*>(p);
+// The caller's workspace: needed by the per-tensor reductions and the grouped
+// GEMM's tile table, optional elsewhere.
+fp8_status check_workspace(bool needed, void* ws, int64_t bytes, uint32_t** out) {
+    *out = static_cast<uint32_t*>(ws);
+    if (!needed) return FP8_OK;
+    if (ws == nullptr) return fail(FP8_ERR_INVALID_ARG, "workspace is NULL (this call needs fp8_workspace_size() bytes)");
+    if (bytes < FP8_WORKSPACE_BYTES)
+        return fail(FP8_ERR_INVALID_ARG, "workspace_bytes=%lld is below fp8_workspace_size()=%d", (long long)bytes,
+                    FP8_WORKSPACE_BYTES);
+    if ((uintptr_t)ws % 16 != 0) return fail(FP8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
     return FP8_OK;
 }
 
@@ -165,6 +143,8 @@ const char* fp8_status_string(fp8_status s) {
 
 const char* fp8_last_error(void) { return g_last_error.c_str(); }
 
+int64_t fp8_workspace_size(void) { return FP8_WORKSPACE_BYTES; }
+
 fp8_status fp8_history_init(fp8_amax_history* hist, int32_t len, void* stream) {
     if (hist == nullptr) return fail(FP8_ERR_INVALID_ARG, "hist is NULL");
     if (len < 1 || len > 16) return fail(FP8_ERR_INVALID_ARG, "history length %d not in 1..16", len);
@@ -186,19 +166,21 @@ fp8_status fp8_history_set_guard(fp8_amax_history* hist, float threshold, void* 
 }
 
 fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
-                    fp8_granularity gran, float* amax_out, void* stream) {
+                    fp8_granularity gran, float* amax_out, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
     fp8_status st = check_matrix_in(x, in_dtype, rows, cols, ld);
     if (st != FP8_OK) return st;
     if (!valid_gran(gran)) return fail(FP8_ERR_INVALID_ARG, "granularity %d is not a fp8_granularity", (int)gran);
     if (amax_out == nullptr && num_groups(gran, rows, cols) > 0)
         return fail(FP8_ERR_INVALID_ARG, "amax_out is NULL");
     if (!is_aligned(amax_out, 4)) return fail(FP8_ERR_MISALIGNED, "amax_out is not 4-byte aligned");
+    uint32_t* scratch = nullptr;
+    st = check_workspace(gran == FP8_GRAN_TENSOR, workspace, workspace_bytes, &scratch);
+    if (st != FP8_OK) return st;
     int cus = 0;
     st = check_device(&cus);
     if (st != FP8_OK) return st;
     if (num_groups(gran, rows, cols) == 0) return ok();
-    uint32_t* scratch = nullptr;
-    if (gran == FP8_GRAN_TENSOR && (st = get_scratch((hipStream_t)stream, &scratch)) != FP8_OK) return st;
     fp8mi::QuantArgs a;
     a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
     a.gran = gran; a.write_q = false; a.amax = amax_out; a.ldq = cols; a.scratch = scratch;
@@ -211,7 +193,8 @@ fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t 
 static fp8_status quantize_impl(const char* what, const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols,
                                 int64_t ld, fp8_format fmt, fp8_granularity gran, uint32_t flags,
                                 fp8_amax_history* hist, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
-                                bool dual, float* scale_inv_out, float* amax_out, fp8_diag* diag, void* stream) {
+                                bool dual, float* scale_inv_out, float* amax_out, fp8_diag* diag,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
     fp8_status st = check_matrix_in(x, in_dtype, rows, cols, ld);
     if (st != FP8_OK) return st;
     if (fmt != FP8_E4M3 && fmt != FP8_E5M2)
@@ -246,12 +229,13 @@ static fp8_status quantize_impl(const char* what, const void* x, fp8_in_dtype in
     if (!is_aligned(scale_inv_out, 4) || !is_aligned(amax_out, 4))
         return fail(FP8_ERR_MISALIGNED, "scale_inv_out and amax_out must be 4-byte aligned");
     if (diag != nullptr && !is_aligned(diag, 4)) return fail(FP8_ERR_MISALIGNED, "diag must be 4-byte aligned");
+    uint32_t* scratch = nullptr;
+    st = check_workspace(gran == FP8_GRAN_TENSOR, workspace, workspace_bytes, &scratch);
+    if (st != FP8_OK) return st;
     int cus = 0;
     st = check_device(&cus);
     if (st != FP8_OK) return st;
     if (num_groups(gran, rows, cols) == 0) return ok();
-    uint32_t* scratch = nullptr;
-    if (gran == FP8_GRAN_TENSOR && (st = get_scratch((hipStream_t)stream, &scratch)) != FP8_OK) return st;
     fp8mi::QuantArgs a;
     a.scratch = scratch;
     a.x = x; a.in_bf16 = in_dtype == FP8_IN_BF16; a.rows = rows; a.cols = cols; a.ld = ld;
@@ -270,17 +254,17 @@ static fp8_status quantize_impl(const char* what, const void* x, fp8_in_dtype in
 fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
                         fp8_format fmt, fp8_granularity gran, uint32_t flags, fp8_amax_history* hist,
                         uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out, fp8_diag* diag,
-                        void* stream) {
+                        void* workspace, int64_t workspace_bytes, void* stream) {
     return quantize_impl("fp8_quantize", x, in_dtype, rows, cols, ld, fmt, gran, flags, hist, q, ldq, nullptr, 0,
-                         false, scale_inv_out, amax_out, diag, stream);
+                         false, scale_inv_out, amax_out, diag, workspace, workspace_bytes, stream);
 }
 
 fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
                              fp8_format fmt, uint32_t flags, fp8_amax_history* hist, uint8_t* q, int64_t ldq,
                              uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* amax_out, fp8_diag* diag,
-                             void* stream) {
+                             void* workspace, int64_t workspace_bytes, void* stream) {
     return quantize_impl("fp8_quantize_dual", x, in_dtype, rows, cols, ld, fmt, FP8_GRAN_TENSOR, flags, hist, q,
-                         ldq, qt, ldqt, true, scale_inv_out, amax_out, diag, stream);
+                         ldq, qt, ldqt, true, scale_inv_out, amax_out, diag, workspace, workspace_bytes, stream);
 }
 
 static fp8_status check_gemm_common(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M,
@@ -360,12 +344,13 @@ fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B,
 }
 
 static_assert(FP8_GROUPED_MAX_TILES == fp8mi::kGroupTableTiles, "grouped GEMM table size");
+static_assert(FP8_WORKSPACE_BYTES == 4 * fp8mi::kScratchWords, "workspace size");
 
 fp8_status fp8_grouped_gemm(const uint8_t* A, fp8_format fa, int64_t lda, const uint8_t* B, fp8_format fb,
                             int64_t ldb, int64_t b_group_stride, int64_t M, int64_t N, int64_t K, int32_t groups,
                             const int32_t* group_offsets, const float* a_scale_inv, int a_per_row,
                             const float* b_scale_inv, int b_per_row, void* C, fp8_out_dtype out_dtype, int64_t ldc,
-                            void* stream) {
+                            void* workspace, int64_t workspace_bytes, void* stream) {
     if ((fa != FP8_E4M3 && fa != FP8_E5M2) || (fb != FP8_E4M3 && fb != FP8_E5M2))
         return fail(FP8_ERR_INVALID_ARG, "formats fa=%d fb=%d must be FP8_E4M3 or FP8_E5M2", (int)fa, (int)fb);
     if ((a_per_row != 0 && a_per_row != 1) || (b_per_row != 0 && b_per_row != 1))
@@ -385,12 +370,13 @@ fp8_status fp8_grouped_gemm(const uint8_t* A, fp8_format fa, int64_t lda, const 
     if ((M + 255) / 256 + groups > FP8_GROUPED_MAX_TILES)
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "ceil(M/256) + groups = %lld exceeds FP8_GROUPED_MAX_TILES (%d)",
                     (long long)((M + 255) / 256 + groups), FP8_GROUPED_MAX_TILES);
+    uint32_t* scratch = nullptr;
+    st = check_workspace(true, workspace, workspace_bytes, &scratch);
+    if (st != FP8_OK) return st;
     int cus = 0;
     st = check_device(&cus);
     if (st != FP8_OK) return st;
     if (M == 0 || N == 0) return ok();
-    uint32_t* scratch = nullptr;
-    if ((st = get_scratch((hipStream_t)stream, &scratch)) != FP8_OK) return st;
     fp8mi::GemmArgs g;
     g.A = A; g.B = B; g.fa = fa; g.fb = fb; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N; g.K = K;
     g.sa = a_scale_inv; g.sb = b_scale_inv; g.sa_per_row = a_per_row; g.sb_per_row = b_per_row;

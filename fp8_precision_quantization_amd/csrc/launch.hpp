@@ -27,7 +27,7 @@ struct QuantArgs {
     float* scale_inv = nullptr;
     float* amax = nullptr;
     fp8_diag* diag = nullptr;
-    uint32_t* scratch = nullptr;  // library scratch of kScratchWords words, owned per (device, stream)
+    uint32_t* scratch = nullptr;  // the caller's workspace, kScratchWords words (per-tensor granularity)
     hipStream_t stream = nullptr;
     int num_cus = 256;
 };
@@ -90,12 +90,11 @@ hipError_t launch_kv_store(const KvStoreArgs& a);
 hipError_t launch_kv_load(const KvLoadArgs& a);
 hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream);
 hipError_t launch_history_set_guard(fp8_amax_history* h, float threshold, hipStream_t stream);
-hipError_t launch_zero_words(uint32_t* w, int n, hipStream_t stream);
 hipError_t launch_scaled_gemm(const GemmArgs& a);
 hipError_t launch_blockscaled_gemm(const GemmArgs& a);
 hipError_t launch_grouped_gemm(const GemmArgs& a);
 
-// Per-(device, stream) scratch the library allocates once (uint32 words).
+// Words of the caller's workspace (FP8_WORKSPACE_BYTES / 4).
 constexpr int kScratchWords = 16384;
 // Words [kScratchGroupTable, kScratchWords) hold the grouped GEMM's table of
 // 256-row tiles (a 4-word header, then 4 words per tile); the quantize

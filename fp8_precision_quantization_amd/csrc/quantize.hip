@@ -217,15 +217,10 @@ __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h
             scale_inv_out[0] = recip_rn(sj);
             h->spikes = h->spikes + 1u;
         }
-        if (diag_tmp != nullptr) {
-            if (!spiked && diag != nullptr) {
-                diag->sat_count += diag_tmp->sat_count;
-                diag->nonfinite_count += diag_tmp->nonfinite_count;
-                diag->underflow_count += diag_tmp->underflow_count;
-            }
-            diag_tmp->sat_count = 0u;
-            diag_tmp->nonfinite_count = 0u;
-            diag_tmp->underflow_count = 0u;
+        if (diag_tmp != nullptr && !spiked && diag != nullptr) {
+            diag->sat_count += diag_tmp->sat_count;
+            diag->nonfinite_count += diag_tmp->nonfinite_count;
+            diag->underflow_count += diag_tmp->underflow_count;
         }
     }
     h->amax[pos] = amax_now;
@@ -628,10 +623,10 @@ __global__ __launch_bounds__(kThreads) void k_cast_128x128(
 // ---------------------------------------------------------------- host side --
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Scratch layout (uint32 words of the per-stream scratch, kScratchWords).
+// Workspace layout (uint32 words of the caller's workspace, kScratchWords).
 constexpr int kScratchCastPartials = 0;      // <= kMaxCastBlocks partials of a delayed cast
 constexpr int kScratchAmaxPartials = 4096;   // <= kMaxAmaxBlocks partials of pass 1
-constexpr int kScratchDiag = 8192;           // fp8_diag of a guarded delayed cast (zero between calls)
+constexpr int kScratchDiag = 8192;           // fp8_diag of a guarded delayed cast's first pass
 constexpr int64_t kMaxCastBlocks = 4096;
 constexpr int64_t kMaxAmaxBlocks = 1024;   // a stream needs about 4 workgroups per CU (measured)
 static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchDiag, "scratch layout");
@@ -724,9 +719,12 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
                                cast_partials);                                                            \
     } while (0)
         if (delayed) {
-            // with the guard, the first cast's diagnostics wait in scratch
+            // with the guard, the first cast's diagnostics wait in the
+            // workspace (cleared first: its contents are arbitrary)
             fp8_diag* diag_tmp = a.guard ? reinterpret_cast<fp8_diag*>(a.scratch + kScratchDiag) : nullptr;
             fp8_diag* d1 = a.guard ? diag_tmp : a.diag;
+            if (a.guard && diag)
+                hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, st, a.scratch + kScratchDiag, 4);
             if (diag) FP8MI_TENSOR_CAST(kModeDelayed, true, d1);
             else FP8MI_TENSOR_CAST(kModeDelayed, false, d1);
             const int nparts = (int)(a.transpose ? tgrid : cgrid);
@@ -800,11 +798,6 @@ hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t str
 
 hipError_t launch_history_set_guard(fp8_amax_history* h, float threshold, hipStream_t stream) {
     hipLaunchKernelGGL(k_history_set_guard, dim3(1), dim3(64), 0, stream, h, threshold);
-    return hipGetLastError();
-}
-
-hipError_t launch_zero_words(uint32_t* w, int n, hipStream_t stream) {
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, stream, w, n);
     return hipGetLastError();
 }
 

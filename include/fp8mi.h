@@ -24,13 +24,19 @@
  *
  * Conventions for every entry point:
  *   - All pointers except the ones documented as host pointers are DEVICE
- *     pointers on the current HIP device.  The caller owns every input and
- *     output buffer.  The library never synchronizes the stream; its only
- *     allocation is a 64 KiB scratch buffer per (device, stream) pair, made
- *     with hipMalloc by the first per-tensor fp8_quantize / fp8_amax call or
- *     fp8_grouped_gemm call on that pair and kept until the process ends
- *     (calls on one stream are ordered and share it; different streams never
- *     share one).
+ *     pointers on the current HIP device.  The caller owns every buffer:
+ *     inputs, outputs, scale arrays, histories, counters and the workspace
+ *     of the calls that need one.  The library never allocates, frees or
+ *     synchronizes.
+ *   - Workspace: the per-tensor reductions of fp8_amax / fp8_quantize /
+ *     fp8_quantize_dual (FP8_GRAN_TENSOR) and the grouped GEMM's tile table
+ *     need `workspace`, device memory of at least fp8_workspace_size() bytes,
+ *     16-byte aligned (else FP8_ERR_INVALID_ARG / FP8_ERR_MISALIGNED).  It
+ *     needs no initialization and holds nothing the caller reads; a call
+ *     owns it from launch until its kernels finish, so calls in flight at
+ *     the same time (different streams) need different workspaces, while
+ *     calls ordered on one stream can share one.  Calls that do not need it
+ *     accept NULL.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call is asynchronous: it returns after host-side validation and
  *     the kernel launches.  A fault inside a kernel surfaces at the caller's
@@ -43,8 +49,8 @@
  *   - Matrices are row-major with an explicit leading dimension (elements
  *     between consecutive rows, >= the number of columns).
  *   - Scale convention: dequantized value = decode(q) * scale_inv.
- *   - Reentrant; the global state is a per-device architecture cache and the
- *     per-(device, stream) scratch buffers.
+ *   - Reentrant; the only global state is a per-device architecture cache
+ *     and the kernels' per-device launch attributes.
  */
 #ifndef FP8MI_H
 #define FP8MI_H
@@ -55,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FP8MI_ABI_VERSION 4
+#define FP8MI_ABI_VERSION 5
 
 typedef enum {
     FP8_OK = 0,
@@ -149,6 +155,14 @@ const char* fp8_status_string(fp8_status status);
  * a successful call). */
 const char* fp8_last_error(void);
 
+/* Bytes of the workspace the per-tensor quantize / amax calls and the
+ * grouped GEMM take (FP8_WORKSPACE_BYTES: 64 KiB).  Words of it carry one
+ * partial maximum per workgroup of a reduction pass (combined by the next
+ * kernel instead of by same-address atomics), the first pass's counters of
+ * a guarded delayed cast, and the grouped GEMM's table of row tiles. */
+#define FP8_WORKSPACE_BYTES 65536
+int64_t fp8_workspace_size(void);
+
 /* Zero a history and set its window length (1..16) on `stream`. */
 fp8_status fp8_history_init(fp8_amax_history* hist, int32_t len, void* stream);
 
@@ -162,7 +176,8 @@ fp8_status fp8_history_set_guard(fp8_amax_history* hist, float threshold, void* 
  * fp8_granularity).  A NaN anywhere in a group gives NaN, else an Inf gives
  * Inf.  Any pointer alignment is accepted; 16-byte-aligned rows are fastest. */
 fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
-                    fp8_granularity gran, float* amax_out, void* stream);
+                    fp8_granularity gran, float* amax_out, void* workspace, int64_t workspace_bytes,
+                    void* stream);
 
 /* Scaled quantization ([DeepL] 2.1, 2.3; [Soup] recipes; [Swift] dynamic
  * per-tensor):
@@ -177,22 +192,24 @@ fp8_status fp8_amax(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t 
  * hist: NULL = just in time; non-NULL = delayed scaling (FP8_GRAN_TENSOR
  * only); amax_out then receives the current step's amax and scale_inv_out
  * the inverse of the scale actually used.
- * diag: optional counters (NULL to skip the counting). */
+ * diag: optional counters (NULL to skip the counting).
+ * workspace: needed with FP8_GRAN_TENSOR (see the conventions above). */
 fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols,
                         int64_t ld, fp8_format fmt, fp8_granularity gran, uint32_t flags,
                         fp8_amax_history* hist, uint8_t* q, int64_t ldq, float* scale_inv_out,
-                        float* amax_out, fp8_diag* diag, void* stream);
+                        float* amax_out, fp8_diag* diag, void* workspace, int64_t workspace_bytes,
+                        void* stream);
 
 /* Per-tensor quantization with both layouts from one pass over x: q
  * [rows x cols] (ldq >= cols) and qt [cols x rows] (ldqt >= rows), the same
  * codes.  A gradient feeds the data-gradient GEMM as dY and the weight-
  * gradient GEMM as dY^T, both in E5M2 ([DeepL] 2.1), so one read of dY gives
  * both operands.  Arguments and rules as fp8_quantize with FP8_GRAN_TENSOR;
- * flags: FP8_SCALE_POW2, FP8_SPIKE_GUARD. */
+ * flags: FP8_SCALE_POW2, FP8_SPIKE_GUARD.  workspace: required. */
 fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
                              fp8_format fmt, uint32_t flags, fp8_amax_history* hist, uint8_t* q, int64_t ldq,
                              uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* amax_out, fp8_diag* diag,
-                             void* stream);
+                             void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Scaled FP8 GEMM ([H100] FP8 matrix multiply-add in hardware; [Soup]
  * tensorwise and rowwise GEMMs; [DeepL] 2.2 results return to high
@@ -252,7 +269,7 @@ fp8_status fp8_blockscaled_gemm(const uint8_t* A, int64_t lda, const uint8_t* B,
  * ([groups x N]).  C: [M x N] fp32 or bf16, leading dimension ldc.
  * Requirements as fp8_scaled_gemm, plus groups >= 1 and
  * ceil(M / 256) + groups <= FP8_GROUPED_MAX_TILES (the size of the table of
- * 256-row tiles kept in the per-stream scratch), else
+ * 256-row tiles the call builds in the workspace, which is required), else
  * FP8_ERR_UNSUPPORTED_SHAPE. */
 #define FP8_GROUPED_MAX_TILES 1983
 fp8_status fp8_grouped_gemm(const uint8_t* A, fp8_format fa, int64_t lda,
@@ -260,7 +277,8 @@ fp8_status fp8_grouped_gemm(const uint8_t* A, fp8_format fa, int64_t lda,
                             int64_t M, int64_t N, int64_t K, int32_t groups, const int32_t* group_offsets,
                             const float* a_scale_inv, int a_per_row,
                             const float* b_scale_inv, int b_per_row,
-                            void* C, fp8_out_dtype out_dtype, int64_t ldc, void* stream);
+                            void* C, fp8_out_dtype out_dtype, int64_t ldc,
+                            void* workspace, int64_t workspace_bytes, void* stream);
 
 /* FP8 KV cache ([DeepL] 3.1: K and V caches held in FP8 take half of BF16's
  * memory; K's precision drives the attention scores, V's the mixed output;

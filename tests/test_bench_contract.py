@@ -64,3 +64,14 @@ def test_cpu_baseline_leg_of_every_workload(workload):
     assert d["kind"] == "oracle" and d["unit"] == "TFLOP/s" and d["value"] > 0 and d["cores"] >= 1
     assert d["quantize_gbs"] > 0 and d["quantize_gbs_1_thread"] > 0 and d["gemm_gflops"] > 0
     assert "GEMM" in d["sample"] and d["sample"].endswith(" s")
+
+
+def test_traffic_figure_goes_stale_with_its_kernel(monkeypatch):
+    """The recorded HBM bytes are reported only with the kernel source they
+    were measured on."""
+    b, note = bench.traffic("mlp8b")
+    assert b == bench.TRAFFIC["mlp8b"]["bytes"] and "rocprofv3" in note
+    monkeypatch.setitem(bench.TRAFFIC, "mlp8b", dict(bench.TRAFFIC["mlp8b"], sha16="0" * 16))
+    b, note = bench.traffic("mlp8b")
+    assert b is None and note.startswith("stale")
+    assert bench.traffic("tiny")[0] is None

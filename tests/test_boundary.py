@@ -27,6 +27,19 @@ def test_library_exports_every_header_function():
     assert set(declared) <= exported
 
 
+def test_library_never_allocates_or_synchronizes():
+    """The caller owns every buffer: the library imports no HIP allocation,
+    free, memset or synchronization routine."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    imported = {ln.split()[-1].split("@")[0] for ln in out.splitlines() if ln.strip()}
+    assert any(s.startswith("hipLaunchKernel") for s in imported), sorted(imported)
+    forbidden = [s for s in imported
+                 if s.startswith(("hipMalloc", "hipFree", "hipExtMalloc", "hipHostMalloc", "hipMemset",
+                                  "hipDeviceSynchronize", "hipStreamSynchronize", "hipEventSynchronize",
+                                  "hipMemcpy", "hipMallocAsync", "hipMemPool"))]
+    assert forbidden == [], forbidden
+
+
 def test_library_is_gfx950_only_code_object():
     out = subprocess.run(["strings", "-n", "8", L.LIB_PATH], capture_output=True, text=True).stdout
     assert "gfx950" in out
@@ -36,7 +49,8 @@ def test_library_is_gfx950_only_code_object():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.fp8_abi_version() == 4
+    assert lib.fp8_abi_version() == 5
+    assert lib.fp8_workspace_size() == L.WORKSPACE_BYTES
     for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARG"), (2, "FP8_ERR_UNSUPPORTED_SHAPE"),
                        (3, "FP8_ERR_MISALIGNED"), (4, "FP8_ERR_UNSUPPORTED_DEVICE"), (5, "FP8_ERR_HIP")]:
         assert L.status_name(code) == name
@@ -48,11 +62,11 @@ FAKE = 0x10000          # 64 KiB-aligned fake device address, never dereferenced
 def q(**kw):
     a = dict(x=FAKE, in_dt=L.FP8_IN_BF16, rows=64, cols=64, ld=64, fmt=L.FP8_E4M3,
              gran=L.FP8_GRAN_TENSOR, flags=0, hist=None, q=FAKE, ldq=64, sinv=FAKE, amax=FAKE,
-             diag=None)
+             diag=None, ws=FAKE, ws_bytes=L.WORKSPACE_BYTES)
     a.update(kw)
     st = L.lib().fp8_quantize(a["x"], a["in_dt"], a["rows"], a["cols"], a["ld"], a["fmt"], a["gran"],
                               a["flags"], a["hist"], a["q"], a["ldq"], a["sinv"], a["amax"], a["diag"],
-                              None)
+                              a["ws"], a["ws_bytes"], None)
     return st, L.lib().fp8_last_error().decode()
 
 
@@ -78,6 +92,9 @@ def q(**kw):
     (dict(rows=2 ** 32), 2, "2^31"),
     (dict(flags=4), 1, "FP8_SPIKE_GUARD"),
     (dict(flags=16), 1, "flag"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(ws_bytes=L.WORKSPACE_BYTES - 16), 1, "workspace_bytes"),
+    (dict(ws=FAKE + 8), 3, "workspace"),
 ])
 def test_quantize_validation(kw, status, needle):
     st, msg = q(**kw)
@@ -87,11 +104,12 @@ def test_quantize_validation(kw, status, needle):
 
 def qd(**kw):
     a = dict(x=FAKE, in_dt=L.FP8_IN_BF16, rows=64, cols=96, ld=96, fmt=L.FP8_E5M2, flags=0, hist=None,
-             q=FAKE, ldq=96, qt=FAKE, ldqt=64, sinv=FAKE, amax=FAKE, diag=None)
+             q=FAKE, ldq=96, qt=FAKE, ldqt=64, sinv=FAKE, amax=FAKE, diag=None, ws=FAKE,
+             ws_bytes=L.WORKSPACE_BYTES)
     a.update(kw)
     st = L.lib().fp8_quantize_dual(a["x"], a["in_dt"], a["rows"], a["cols"], a["ld"], a["fmt"], a["flags"],
                                    a["hist"], a["q"], a["ldq"], a["qt"], a["ldqt"], a["sinv"], a["amax"],
-                                   a["diag"], None)
+                                   a["diag"], a["ws"], a["ws_bytes"], None)
     return st, L.lib().fp8_last_error().decode()
 
 
@@ -104,6 +122,7 @@ def qd(**kw):
     (dict(flags=4), 1, "FP8_SPIKE_GUARD"),
     (dict(fmt=5), 1, "format"),
     (dict(x=FAKE + 1), 3, "aligned"),
+    (dict(ws=None), 1, "workspace is NULL"),
 ])
 def test_quantize_dual_validation(kw, status, needle):
     st, msg = qd(**kw)
@@ -113,11 +132,12 @@ def test_quantize_dual_validation(kw, status, needle):
 
 def gg(**kw):
     a = dict(A=FAKE, fa=0, lda=256, B=FAKE, fb=0, ldb=256, gstride=512 * 256, M=1000, N=512, K=256, G=8,
-             offs=FAKE, sa=FAKE, sa_row=1, sb=FAKE, sb_row=0, C=FAKE, out_dt=L.FP8_OUT_BF16, ldc=512)
+             offs=FAKE, sa=FAKE, sa_row=1, sb=FAKE, sb_row=0, C=FAKE, out_dt=L.FP8_OUT_BF16, ldc=512,
+             ws=FAKE, ws_bytes=L.WORKSPACE_BYTES)
     a.update(kw)
     st = L.lib().fp8_grouped_gemm(a["A"], a["fa"], a["lda"], a["B"], a["fb"], a["ldb"], a["gstride"], a["M"], a["N"],
                                   a["K"], a["G"], a["offs"], a["sa"], a["sa_row"], a["sb"], a["sb_row"], a["C"],
-                                  a["out_dt"], a["ldc"], None)
+                                  a["out_dt"], a["ldc"], a["ws"], a["ws_bytes"], None)
     return st, L.lib().fp8_last_error().decode()
 
 
@@ -134,6 +154,8 @@ def gg(**kw):
     (dict(G=1984, M=0), 2, "FP8_GROUPED_MAX_TILES"),
     (dict(C=None), 1, "C is NULL"),
     (dict(lda=128), 1, "lda"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(ws_bytes=100), 1, "workspace_bytes"),
 ])
 def test_grouped_gemm_validation(kw, status, needle):
     st, msg = gg(**kw)
@@ -261,9 +283,12 @@ def test_history_and_amax_validation():
     assert lib.fp8_history_init(FAKE, 0, None) == L.FP8_ERR_INVALID_ARG
     assert lib.fp8_history_init(FAKE, 17, None) == L.FP8_ERR_INVALID_ARG
     assert lib.fp8_history_init(FAKE + 8, 16, None) == L.FP8_ERR_MISALIGNED
-    assert lib.fp8_amax(FAKE, 1, 4, 4, 4, 5, FAKE, None) == L.FP8_ERR_INVALID_ARG
-    assert lib.fp8_amax(FAKE, 1, 4, 4, 4, 0, None, None) == L.FP8_ERR_INVALID_ARG
-    assert lib.fp8_amax(FAKE + 1, 1, 4, 4, 4, 0, FAKE, None) == L.FP8_ERR_MISALIGNED
+    W = L.WORKSPACE_BYTES
+    assert lib.fp8_amax(FAKE, 1, 4, 4, 4, 5, FAKE, FAKE, W, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_amax(FAKE, 1, 4, 4, 4, 0, None, FAKE, W, None) == L.FP8_ERR_INVALID_ARG
+    assert lib.fp8_amax(FAKE + 1, 1, 4, 4, 4, 0, FAKE, FAKE, W, None) == L.FP8_ERR_MISALIGNED
+    assert lib.fp8_amax(FAKE, 1, 4, 4, 4, 0, FAKE, None, W, None) == L.FP8_ERR_INVALID_ARG
+    assert "workspace" in lib.fp8_last_error().decode()
 
 
 def test_history_struct_is_128_bytes():
@@ -282,3 +307,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(ImportError):
         L.lib()
+
+
+def test_probe_library_exports_its_header():
+    """libfp8probe.so (the benchmark's HBM streaming probes) exports what
+    include/fp8probe.h declares and nothing of the FP8 method."""
+    import re
+    probe = os.path.join(os.path.dirname(L.LIB_PATH), "libfp8probe.so")
+    text = open(os.path.join(os.path.dirname(L.HEADER), "fp8probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = set(re.findall(r"\b(fp8probe_[a-z_0-9]+)\s*\(", text))
+    out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert declared == {"fp8probe_read", "fp8probe_copy", "fp8probe_read2_write1"}
+    assert declared <= exported and not any(s.startswith("fp8_") for s in exported)
+    lib = ctypes.CDLL(probe)
+    lib.fp8probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    assert lib.fp8probe_copy(FAKE, FAKE, 24, 4, None) == -1      # not a multiple of 16: nothing launched

@@ -37,7 +37,7 @@ def _run(*args):
 
 @pytest.mark.timeout(300)
 def test_bench_line_contract_tiny():
-    d = _run("--workload", "tiny", "--steps", "5", "--warmup", "2", "--no-cpu-baseline")
+    d = _run("--workload", "tiny", "--steps", "5", "--warmup", "2", "--no-cpu-baseline", "--config-steps", "2")
     assert KEYS <= set(d) and d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
     # the clock probe ran (amd-smi may find no fully busy sample for so small a GEMM)
     clk = d["kernels"]["gemm_clock_mhz"]
@@ -52,7 +52,19 @@ def test_bench_line_contract_tiny():
     assert abs(roof["achieved"] - flops / (k["gemm_ms"] * 1e-3) / 1e12) <= 0.01 * roof["achieved"] + 0.01
     assert abs(d["value"] - flops / (d["ms_per_step"] * 1e-3) / 1e12) <= 0.01 * d["value"] + 0.01
     assert set(k["quantize_rel_err"]) == {"X", "W"} and 0 < k["quantize_rel_err"]["X"]["rel_err"] < 0.05
-    assert k["copy_ceiling_gbs"] > 0 and d["cpu_baseline"] is None
+    c = k["stream_ceilings"]
+    assert 0 < c["copy_gbs"] <= c["read_gbs"] * 1.05 and c["read2_write1_gbs"] > 0 and d["cpu_baseline"] is None
+    assert abs(k["quantize_pct_read2_write1_ceiling"] - 100 * k["quantize_gbs"] / c["read2_write1_gbs"]) < 0.05
+    assert "time" in roof and roof["traffic"] is None     # no counters for the tiny workload
+    # every other GEMM workload timed in the same run, with consistent figures
+    w = k["workloads"]
+    assert set(w) == {"qkv", "mlp70b", "wgrad", "dgrad", "moe"}
+    for name, b in w.items():
+        fl = 2.0 * b["M"] * b["N"] * b["K"]
+        assert abs(b["gemm_tflops"] - fl / (b["gemm_ms"] * 1e-3) / 1e12) <= 0.01 * b["gemm_tflops"] + 0.01, name
+        assert abs(b["gemm_frac_fp8_peak"] - b["gemm_tflops"] / 5000.0) < 1e-3, name
+        assert b["step_ms"] > 0 and b["quantize_ms"] > 0, name
+    assert (w["mlp70b"]["M"], w["mlp70b"]["N"], w["mlp70b"]["K"]) == (2048, 28672, 8192)
 
 
 @pytest.mark.timeout(300)
