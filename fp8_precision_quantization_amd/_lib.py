@@ -52,6 +52,8 @@ SIGNATURES = {
     "fp8_amax": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _P, _P, _I64, _P]),
     "fp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U32, _P, _P, _I64, _P, _P, _P, _P, _I64,
                             _P]),
+    "fp8_quantize_noalloc": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _U32, _P, _P, _I64, _P, _P, _P,
+                                    _P]),
     "fp8_quantize_dual": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _U32, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
                                  _I64, _P]),
     "fp8_scaled_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,

@@ -259,6 +259,21 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
                          false, scale_inv_out, amax_out, diag, workspace, workspace_bytes, stream);
 }
 
+fp8_status fp8_quantize_noalloc(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                fp8_format fmt, fp8_granularity gran, uint32_t flags, fp8_amax_history* hist,
+                                uint8_t* q, int64_t ldq, float* scale_inv_out, float* amax_out, fp8_diag* diag,
+                                void* stream) {
+    int cus = 0;
+    fp8_status st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    uint32_t* ws = nullptr;
+    const hipError_t e = fp8mi::static_workspace(&ws);
+    if (e != hipSuccess)
+        return fail(FP8_ERR_HIP, "fp8_quantize_noalloc: the device workspace's address: %s", hipGetErrorString(e));
+    return quantize_impl("fp8_quantize_noalloc", x, in_dtype, rows, cols, ld, fmt, gran, flags, hist, q, ldq,
+                         nullptr, 0, false, scale_inv_out, amax_out, diag, ws, FP8_WORKSPACE_BYTES, stream);
+}
+
 fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols, int64_t ld,
                              fp8_format fmt, uint32_t flags, fp8_amax_history* hist, uint8_t* q, int64_t ldq,
                              uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* amax_out, fp8_diag* diag,

@@ -86,6 +86,9 @@ struct KvLoadArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a);
+// Address on the current device of the workspace fp8_quantize_noalloc uses
+// (a device array of kScratchWords words); taken once per device.
+hipError_t static_workspace(uint32_t** out);
 hipError_t launch_kv_store(const KvStoreArgs& a);
 hipError_t launch_kv_load(const KvLoadArgs& a);
 hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream);

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "cast_unit.hpp"
 #include "device_common.hpp"
@@ -671,7 +672,8 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
     g.units = (uint32_t)(g.rows * (int64_t)g.upr);
     const bool vec_in = aligned(x, 16) && (g.rows == 1 || (g.ld * esz) % 16 == 0);
     const bool vec_out = a.q != nullptr && aligned(a.q, 8) && (g.rows == 1 || g.ldq % 8 == 0);
-    const unsigned cap = (unsigned)(a.num_cus * 8);
+    // delayed casts keep one partial per block in the workspace: at most kMaxCastBlocks
+    const unsigned cap = (unsigned)std::min<int64_t>((int64_t)a.num_cus * 8, kMaxCastBlocks);
     hipStream_t st = a.stream;
 
     if (a.gran == FP8_GRAN_TENSOR) {
@@ -789,6 +791,32 @@ hipError_t launch_quantize(const QuantArgs& a) {
         return a.fmt == 0 ? quantize_typed<uint16_t, kE4M3>(a) : quantize_typed<uint16_t, kE5M2>(a);
     }
     return a.fmt == 0 ? quantize_typed<float, kE4M3>(a) : quantize_typed<float, kE5M2>(a);
+}
+
+// The workspace of fp8_quantize_noalloc: 64 KiB of device memory in the
+// library's own code object, one copy per device, held until the process
+// ends.  Every call on a device shares that device's copy.  In host code the
+// array's name is not a device address; its address on the current device
+// comes from hipGetSymbolAddress, taken once per device.
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+hipError_t static_workspace(uint32_t** out) {
+    constexpr int kDevices = 64;
+    static std::once_flag once[kDevices];
+    static uint32_t* ptr[kDevices] = {};
+    static hipError_t err[kDevices] = {};
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [&] {
+        void* p = nullptr;
+        err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err[dev] == hipSuccess && p == nullptr) err[dev] = hipErrorInvalidSymbol;
+        ptr[dev] = static_cast<uint32_t*>(p);
+    });
+    *out = ptr[dev];
+    return err[dev];
 }
 
 hipError_t launch_history_init(fp8_amax_history* h, int32_t len, hipStream_t stream) {

@@ -200,6 +200,25 @@ fp8_status fp8_quantize(const void* x, fp8_in_dtype in_dtype, int64_t rows, int6
                         float* amax_out, fp8_diag* diag, void* workspace, int64_t workspace_bytes,
                         void* stream);
 
+/* fp8_quantize for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments and results without the workspace, which is a 64 KiB array in
+ * device memory that the library holds, one per device, from the first call
+ * on that device until the process ends (that first call looks up its
+ * address).  The call itself allocates nothing.  Every call on a device
+ * shares that device's array, so calls that can overlap on one device (on
+ * different streams, or from different threads) race and must not be
+ * issued; calls ordered on one stream are fine.  The array's use does not
+ * grow with the tensor (per-workgroup partial maxima of at most 4096 + 1024
+ * workgroups and 4 counter words, all below word 8196 of its 16384), so
+ * every size fp8_quantize accepts is accepted here, every other is rejected
+ * by the same checks with the same messages, and nothing of it needs
+ * clearing by the caller. */
+fp8_status fp8_quantize_noalloc(const void* x, fp8_in_dtype in_dtype, int64_t rows, int64_t cols,
+                                int64_t ld, fp8_format fmt, fp8_granularity gran, uint32_t flags,
+                                fp8_amax_history* hist, uint8_t* q, int64_t ldq, float* scale_inv_out,
+                                float* amax_out, fp8_diag* diag, void* stream);
+
 /* Per-tensor quantization with both layouts from one pass over x: q
  * [rows x cols] (ldq >= cols) and qt [cols x rows] (ldqt >= rows), the same
  * codes.  A gradient feeds the data-gradient GEMM as dY and the weight-
