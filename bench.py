@@ -604,9 +604,10 @@ CONFIG_WORKLOADS = ("qkv", "mlp70b", "wgrad", "dgrad", "moe")
 
 def workload_block(torch, fp8, synth, workload: str, steps: int) -> dict:
     """One other GEMM workload timed in the same run, so that one default
-    bench line records every configuration: its GEMM (`steps` calls back to
-    back between two events), its quantize likewise, and whole steps, with
-    the GEMM's TFLOP/s and fraction of the FP8 MFMA peak."""
+    bench line records every configuration: whole steps, its GEMM (the mean
+    over `steps` steps of the call between two events around it), its
+    quantize (calls back to back between two events), with the GEMM's
+    TFLOP/s and fraction of the FP8 MFMA peak."""
     st = Step(workload, torch, fp8, synth)
     for _ in range(3):
         st.quantize()
@@ -622,7 +623,14 @@ def workload_block(torch, fp8, synth, workload: str, steps: int) -> dict:
 
     with phase(torch, "workload %s" % workload):
         ms = loop_ms(torch, step, steps)
-        g_ms = loop_ms(torch, st.gemm, steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e in ev:
+            st.quantize()
+            e[0].record()
+            st.gemm()
+            e[1].record()
+        torch.cuda.synchronize()
+        g_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         q_ms = loop_ms(torch, quantize_only, steps)
     flops = 2.0 * st.M * st.N * st.K
     tflops = flops / (g_ms * 1e-3) / 1e12
@@ -786,27 +794,30 @@ def main():
     # the K steps, timed as a whole: only the work between the two events
     with phase(torch, "timed steps"):
         ms = loop_ms(torch, step, K)
-    # each operation on its own, back to back: its launches' own time
-    with phase(torch, "gemm back to back"):
-        g_mean = loop_ms(torch, st.gemm, K)
-    with phase(torch, "quantize back to back"):
-        q_mean = loop_ms(torch, quantize_only, K)
-    # per-step spread of each operation, from events around each call (these
-    # times include the events' own idle gaps)
+    # K more steps with events around each operation: each launch's duration
+    # as it runs in a step (these include the events' own short gaps)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
-    for s in range(K):
-        ev[s][0].record()
-        st.quantize()
-        ev[s][1].record()
-        st.gemm()
-        ev[s][2].record()
-    torch.cuda.synchronize()
+    with phase(torch, "steps with events"):
+        for s in range(K):
+            ev[s][0].record()
+            st.quantize()
+            ev[s][1].record()
+            st.gemm()
+            ev[s][2].record()
+        torch.cuda.synchronize()
     q_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
     g_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    g_step = float(g_ms.mean())
+    # each operation on its own, back to back: a GEMM then also absorbs the
+    # write-back of the previous one's output, which in a step the quantize does
+    with phase(torch, "gemm back to back"):
+        g_b2b = loop_ms(torch, st.gemm, K)
+    with phase(torch, "quantize back to back"):
+        q_mean = loop_ms(torch, quantize_only, K)
     flops = 2.0 * st.M * st.N * st.K
-    gemm_tflops = flops / (g_mean * 1e-3) / 1e12
+    gemm_tflops = flops / (g_step * 1e-3) / 1e12
     qbytes = st.quant_bytes()
     q_gbs = qbytes / (q_mean * 1e-3) / 1e9
     # after the timed region: the streaming probes' ceilings (before the
@@ -828,7 +839,7 @@ def main():
     tb, tnote = traffic(args.workload)
     roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": tb, "traffic_note": tnote,
-            "time": "kernels.gemm_ms: mean of K back-to-back GEMM calls between two events"}
+            "time": "kernels.gemm_ms: mean over K steps of the GEMM call between two events around it"}
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, args.workload, synth)
     out = {
         "metric": "FP8 scaled-GEMM TFLOPS (% of FP8 MFMA peak); quantize GB/s (% HBM peak)",
@@ -845,10 +856,12 @@ def main():
         "data": "synthetic (seeded numpy PCG64)",
         "config": {"workload": WORKLOADS[args.workload], "M": st.M, "N": st.N, "K": st.K},
         "kernels": {
-            "gemm_ms": round(g_mean, 4),
+            "gemm_ms": round(g_step, 4),
             "gemm_tflops": round(gemm_tflops, 2),
             "gemm_pct_fp8_peak": round(100 * gemm_tflops / PEAK_FP8_TFLOPS, 2),
             "gemm_ms_spread": spread(g_ms),
+            "gemm_ms_back_to_back": round(g_b2b, 4),
+            "gemm_tflops_back_to_back": round(flops / (g_b2b * 1e-3) / 1e12, 2),
             "gemm_clock_mhz": clock,
             "gemm_pct_fp8_peak_at_clock": (round(100 * gemm_tflops / (PEAK_FP8_TFLOPS * clock / 2400.0), 2)
                                            if clock else None),
@@ -856,8 +869,8 @@ def main():
             "quantize_ms_spread": spread(q_ms),
             # the quantize's share of a step (step minus the GEMM): it also
             # pays for writing back the previous GEMM's cached output
-            "quantize_ms_in_step": round(ms - g_mean, 4),
-            "quantize_gbs_in_step": round(qbytes / ((ms - g_mean) * 1e-3) / 1e9, 1) if ms > g_mean else None,
+            "quantize_ms_in_step": round(ms - g_step, 4),
+            "quantize_gbs_in_step": round(qbytes / ((ms - g_step) * 1e-3) / 1e9, 1) if ms > g_step else None,
             "quantize_gbs": round(q_gbs, 1),
             "quantize_pct_hbm_peak": round(100 * q_gbs / PEAK_HBM_GBS, 2),
             "quantize_bytes": int(qbytes),

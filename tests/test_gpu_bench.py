@@ -50,6 +50,7 @@ def test_bench_line_contract_tiny():
     k = d["kernels"]
     flops = 2.0 * 256 ** 3
     assert abs(roof["achieved"] - flops / (k["gemm_ms"] * 1e-3) / 1e12) <= 0.01 * roof["achieved"] + 0.01
+    assert k["gemm_ms_back_to_back"] > 0 and "in step" not in roof["time"] and "two events" in roof["time"]
     assert abs(d["value"] - flops / (d["ms_per_step"] * 1e-3) / 1e12) <= 0.01 * d["value"] + 0.01
     assert set(k["quantize_rel_err"]) == {"X", "W"} and 0 < k["quantize_rel_err"]["X"]["rel_err"] < 0.05
     c = k["stream_ceilings"]
