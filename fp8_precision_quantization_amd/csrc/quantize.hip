@@ -26,6 +26,9 @@ namespace fp8mi {
 namespace {
 
 constexpr int kThreads = 256;
+// Transposed cast: workgroups per CU (a workgroup's 4 waves take one SIMD
+// each, so also the waves per SIMD its registers must allow).
+constexpr int kTBlocksPerCU = 4;
 using namespace cast;
 
 // Unit u of a [rows x cols] matrix: rows == 1 is the flat (contiguous) case.
@@ -81,19 +84,111 @@ __device__ __forceinline__ uint32_t reduce_partials(const uint32_t* __restrict__
     return m;
 }
 
-// Delayed scale ([DeepL] 2.3): max over the history window; with an empty
-// history, the just-in-time amax of the current step (bootstrap partials).
-template <int FMT>
-__device__ __forceinline__ float delayed_scale(const fp8_amax_history* h, const uint32_t* boot, int n_boot,
-                                               bool pow2, uint32_t* lds) {
+// Block-wide max, returned to every thread.
+__device__ __forceinline__ uint32_t block_max_all(uint32_t v, uint32_t* lds) {
+    v = wave_max_u32(v);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();
+    if (lane == 0) lds[w] = v;
+    __syncthreads();
+    v = max(max(lds[0], lds[1]), max(lds[2], lds[3]));
+    __syncthreads();
+    return v;
+}
+
+// One block's max |x| over a whole [rows x cols] (ld) tensor, to every
+// thread: the just-in-time amax that the first delayed call needs while its
+// history is still empty (once per history, so one block suffices).
+template <typename InT>
+__device__ __forceinline__ uint32_t whole_tensor_amax(const InT* __restrict__ x, int64_t rows, int64_t cols,
+                                                      int64_t ld, bool vec_in, uint32_t* lds) {
+    constexpr int U = 8;
+    const int64_t upr = (cols + 7) / 8, units = rows * upr;
+    uint32_t m = 0;
+    for (int64_t u0 = threadIdx.x; u0 < units; u0 += (int64_t)kThreads * U) {
+        Pack<InT> p[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int64_t u = u0 + (int64_t)i * kThreads;
+            if (u < units) {
+                const int64_t r = u / upr, c = (u - r * upr) * 8;
+                p[i] = load_unit<InT>(x, r * ld + c, cols - c >= 8 ? 8 : (int)(cols - c), vec_in);
+            } else {
+                p[i] = Pack<InT>{};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) m = max(m, p[i].abs_max());
+    }
+    return block_max_all(m, lds);
+}
+
+// Delayed scaling ([DeepL bets on FP8] 2.3: the factor comes from earlier
+// steps' statistics).  The history's sync words are zero between calls
+// (fp8_history_init zeroes them, and so does the finish kernel of every
+// call): sync[0] and sync[1] publish the bootstrap amax of an empty history
+// (a token, then its bits), sync[2] hands out bootstrap tickets.  Workgroups
+// exchange these words only through atomic read-modify-writes, each waited
+// for before the next: no fence, so no workgroup writes back or invalidates
+// its XCD's L2.
+__device__ __forceinline__ uint32_t sync_read(uint32_t* w) { return atomicOr(w, 0u); }
+
+// Wait until this thread's memory operations, atomics included, are done.
+__device__ __forceinline__ void wait_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Start of a call: the scale from the window's max; with an empty history,
+// from this step's just-in-time amax.  That bootstrap is computed by one
+// workgroup, the one that takes ticket 0 (it is running, so the others can
+// wait for it whatever else is resident).
+constexpr uint32_t kBootSpins = 1u << 20;
+
+template <int FMT, typename BootAmax>
+__device__ __forceinline__ float delayed_begin(fp8_amax_history* h, bool pow2, uint32_t* lds,
+                                               BootAmax boot_amax) {
     const int32_t count = h->count;
     uint32_t basis = 0;
-    if (count <= 0) {
-        basis = reduce_partials(boot, n_boot, lds);
-    } else {
+    if (count > 0) {
         const int n = count > 16 ? 16 : count;
         for (int i = 0; i < n; ++i) basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
+        return scale_from_amax_bits<FMT>(basis, pow2);
     }
+    const uint32_t token = h->steps + 1u;
+    __syncthreads();
+    if (threadIdx.x == 0) lds[8] = atomicAdd(&h->sync[2], 1u);
+    __syncthreads();
+    const uint32_t ticket = lds[8];
+    if (ticket == 0) {
+        basis = boot_amax();
+        if (threadIdx.x == 0) {
+            atomicExch(&h->sync[1], basis);
+            wait_memory();                       // the bits are in place before the token
+            atomicExch(&h->sync[0], token);
+        }
+    } else {
+        // The wait is bounded: should the ticket holder never publish (a
+        // history whose sync words were not zero), this workgroup reads the
+        // tensor itself after about a quarter of a second.
+        if (threadIdx.x == 0) {
+            uint32_t got = 0;
+            for (uint32_t i = 0; i < kBootSpins; ++i) {
+                if (sync_read(&h->sync[0]) == token) {
+                    got = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+            lds[9] = got ? sync_read(&h->sync[1]) : 0u;
+            lds[10] = got;
+        }
+        __syncthreads();
+        basis = lds[9];
+        if (lds[10] == 0u) basis = boot_amax();
+    }
+    __syncthreads();
     return scale_from_amax_bits<FMT>(basis, pow2);
 }
 
@@ -117,27 +212,41 @@ __global__ void k_history_init(fp8_amax_history* h, int32_t len) {
 
 constexpr int kUnroll = 4;
 
-// Per-tensor amax, pass 1: grid-stride over units, one partial per block.
-// `gate` non-null: run only while the history is empty (delayed bootstrap).
-// FLAT: the tensor is one contiguous, 16-byte aligned run of g.cols
-// elements (g.rows == 1, vec_in), so every unit but a ragged last one is
-// whole and loads with plain indexing; block 0's thread 0 takes the last.
+// The whole units [beg, end) of a flat tensor that block b streams: one
+// contiguous run per block, `chunk` units long (a multiple of the kThreads *
+// kUnroll units one iteration covers).  Per-block runs keep each block's
+// consecutive loads in the same DRAM pages; measured on 1 GiB, contiguous
+// runs read at about 7.0 TB/s for 2 to 16 blocks per CU, where a
+// grid-stride loop over the same units falls to 5.2-5.9 TB/s at 4 to 8.
+__device__ __forceinline__ void flat_run(uint32_t whole, uint32_t chunk, uint32_t& beg, uint32_t& end) {
+    const uint64_t b = (uint64_t)blockIdx.x * chunk, e = b + chunk;
+    beg = (uint32_t)(b < whole ? b : whole);
+    end = (uint32_t)(e < whole ? e : whole);
+}
+
+// Per-tensor amax, pass 1: one partial per block.  FLAT: the tensor is one
+// contiguous, 16-byte aligned run of g.cols elements (g.rows == 1, vec_in),
+// so every unit but a ragged last one is whole and loads with plain
+// indexing, each block streaming its own run of `chunk` units; block 0's
+// thread 0 takes the ragged last unit.  Otherwise a grid-stride loop over
+// the 2-D geometry.
 template <typename InT, bool FLAT>
 __global__ __launch_bounds__(kThreads) void k_amax_partials(const InT* __restrict__ x, UnitGeom g,
-                                                            bool vec_in, uint32_t* __restrict__ partials,
-                                                            const fp8_amax_history* gate) {
+                                                            uint32_t chunk, bool vec_in,
+                                                            uint32_t* __restrict__ partials) {
     __shared__ uint32_t lds[16];
-    if (gate != nullptr && gate->count != 0) return;
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t m = 0;
     if constexpr (FLAT) {
         const uint32_t whole = (uint32_t)(g.cols / 8);
-        for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < whole; u0 += stride * kUnroll) {
+        uint32_t beg, end;
+        flat_run(whole, chunk, beg, end);
+        for (uint32_t u0 = beg + threadIdx.x; u0 < end; u0 += kThreads * kUnroll) {
             Pack<InT> p[kUnroll];
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i) {
-                const uint32_t u = u0 + i * stride;
-                p[i] = u < whole ? load_flat<InT>(x, u) : Pack<InT>{};
+                const uint32_t u = u0 + i * kThreads;
+                p[i] = u < end ? load_flat<InT>(x, u) : Pack<InT>{};
             }
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i) m = max(m, p[i].abs_max());
@@ -234,16 +343,17 @@ __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h
     h->scale = s;
     h->scale_inv = 1.0f / s;
     h->steps = h->steps + 1;
+    for (int i = 0; i < 3; ++i) h->sync[i] = 0u;
 }
 
 // Per-tensor cast.  JIT: s from the amax partials of pass 1 (block 0 also
-// writes amax_out).  DELAYED: s from the history (or the bootstrap partials
-// while it is empty); each block stores its own amax partial for the finish
-// kernel.  RECAST: s recorded by a guarded finish kernel, or nothing to do.
+// writes amax_out).  DELAYED: s from the history (delayed_begin); each
+// block stores its own amax partial for the finish kernel.  RECAST: s
+// recorded by a guarded finish kernel, or nothing to do.
 template <typename InT, int FMT, int MODE, bool DIAG, bool FLAT>
 __global__ __launch_bounds__(kThreads) void k_cast_tensor(
-    const InT* __restrict__ x, UnitGeom g, bool vec_in, uint8_t* __restrict__ q, bool vec_out,
-    const uint32_t* __restrict__ partials_in, int n_in, const fp8_amax_history* hist, bool pow2,
+    const InT* __restrict__ x, UnitGeom g, uint32_t chunk, bool vec_in, uint8_t* __restrict__ q, bool vec_out,
+    const uint32_t* __restrict__ partials_in, int n_in, fp8_amax_history* hist, bool pow2,
     float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag,
     uint32_t* __restrict__ partials_out) {
     __shared__ uint32_t lds[16];
@@ -253,7 +363,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
         if (hist->internal[0] == 0u) return;
         s = __uint_as_float(hist->internal[1]);
     } else if constexpr (DELAYED) {
-        s = delayed_scale<FMT>(hist, partials_in, n_in, pow2, lds);
+        s = delayed_begin<FMT>(hist, pow2, lds,
+                               [&] { return whole_tensor_amax<InT>(x, g.rows, g.cols, g.ld, vec_in, lds); });
     } else {
         const uint32_t am = reduce_partials(partials_in, n_in, lds);
         s = scale_from_amax_bits<FMT>(am, pow2);
@@ -264,19 +375,21 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
     const uint32_t stride = gridDim.x * kThreads;
     uint32_t m = 0;
     Counters cnt;
-    if constexpr (FLAT) {     // contiguous input and codes: whole units, then the ragged last one
+    if constexpr (FLAT) {     // contiguous input and codes: this block's run of whole units, then the ragged last one
         const uint32_t whole = (uint32_t)(g.cols / 8);
-        for (uint32_t u0 = blockIdx.x * kThreads + threadIdx.x; u0 < whole; u0 += stride * kUnroll) {
+        uint32_t beg, end;
+        flat_run(whole, chunk, beg, end);
+        for (uint32_t u0 = beg + threadIdx.x; u0 < end; u0 += kThreads * kUnroll) {
             Pack<InT> p[kUnroll];
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i) {
-                const uint32_t u = u0 + i * stride;
-                p[i] = u < whole ? load_flat<InT>(x, u) : Pack<InT>{};
+                const uint32_t u = u0 + i * kThreads;
+                p[i] = u < end ? load_flat<InT>(x, u) : Pack<InT>{};
             }
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i) {
-                const uint32_t u = u0 + i * stride;
-                if (u < whole) {
+                const uint32_t u = u0 + i * kThreads;
+                if (u < end) {
                     if constexpr (DELAYED) m = max(m, p[i].abs_max());
                     store_flat(q, u, encode_unit<FMT, DIAG>(p[i], s, cnt));
                 }
@@ -328,10 +441,10 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
 // (q2[r][c], ld ldq2) from the same pass, for a gradient that feeds both
 // backward GEMMs.
 template <typename InT, int FMT, int MODE, bool DIAG>
-__global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
+__global__ __launch_bounds__(kThreads, kTBlocksPerCU) void k_cast_tensor_t(
     const InT* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, bool vec_in,
     uint8_t* __restrict__ q, int64_t ldq, bool vec_out16, const uint32_t* __restrict__ partials_in,
-    int n_in, const fp8_amax_history* hist, bool pow2, float* __restrict__ scale_inv_out,
+    int n_in, fp8_amax_history* hist, bool pow2, float* __restrict__ scale_inv_out,
     float* __restrict__ amax_out, fp8_diag* diag, uint32_t* __restrict__ partials_out,
     uint8_t* __restrict__ q2, int64_t ldq2, bool vec_out2) {
     __shared__ uint32_t lds[16];
@@ -342,7 +455,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
         if (hist->internal[0] == 0u) return;
         s = __uint_as_float(hist->internal[1]);
     } else if constexpr (DELAYED) {
-        s = delayed_scale<FMT>(hist, partials_in, n_in, pow2, lds);
+        s = delayed_begin<FMT>(hist, pow2, lds,
+                               [&] { return whole_tensor_amax<InT>(x, rows, cols, ld, vec_in, lds); });
     } else {
         const uint32_t am = reduce_partials(partials_in, n_in, lds);
         s = scale_from_amax_bits<FMT>(am, pow2);
@@ -384,8 +498,15 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor_t(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = rr + 16 * i;
-            if constexpr (DELAYED) m = max(m, p[i].abs_max());
+            if constexpr (DELAYED) {
+                m = max(m, p[i].abs_max());
+                // keep the running max (and counters) here: left free, the
+                // compiler sinks these reductions past the next tile's loads
+                // and holds two tiles of input (158 VGPRs instead of 94)
+                asm volatile("" : "+v"(m));
+            }
             const uint2 codes = encode_unit<FMT, DIAG>(p[i], s, cnt);
+            if constexpr (DIAG) asm volatile("" : "+v"(cnt.sat), "+v"(cnt.nonfinite), "+v"(cnt.under));
             const int pos = cu ^ ((r >> 4) & 15);
             *reinterpret_cast<uint2*>(&tile[r * 128 + pos * 8]) = codes;
             if (q2 != nullptr && r0 + r < rows && nvc > 0) store_unit(q2, (r0 + r) * ldq2 + c, nvc, vec_out2, codes);
@@ -633,7 +754,6 @@ constexpr int64_t kMaxAmaxBlocks = 1024;   // a stream needs about 4 workgroups 
 static_assert(kScratchAmaxPartials + kMaxAmaxBlocks <= kScratchDiag, "scratch layout");
 static_assert(kScratchDiag + 4 <= kScratchGroupTable, "scratch layout: the grouped GEMM's table follows");
 
-constexpr int64_t kTBlocksPerCU = 4;     // transposed cast: tiles per block = tiles / (CUs * this)
 constexpr int64_t kRowBlocksPerCU = 3;   // measured: 2, 3 and 4 per CU, 3 fastest
 
 inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
@@ -641,6 +761,17 @@ inline unsigned grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
     if (b < 1) b = 1;
     if (b > cap) b = cap;
     return (unsigned)b;
+}
+
+// Blocks for a flat pass over `whole` units with at most `cap` blocks: each
+// block's run (*chunk units) is a whole number of loop iterations, so the
+// runs start on 16 KiB boundaries (bf16) of a 16-byte aligned tensor.
+inline unsigned flat_grid(int64_t whole, int64_t cap, uint32_t* chunk) {
+    const int64_t step = (int64_t)kThreads * kUnroll;
+    int64_t per = (whole + cap - 1) / cap;
+    per = std::max<int64_t>(step, (per + step - 1) / step * step);
+    *chunk = (uint32_t)per;
+    return (unsigned)std::max<int64_t>(1, (whole + per - 1) / per);
 }
 
 template <typename InT, int FMT>
@@ -677,52 +808,46 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
     hipStream_t st = a.stream;
 
     if (a.gran == FP8_GRAN_TENSOR) {
-        uint32_t* cast_partials = a.scratch + kScratchCastPartials;
         uint32_t* amax_partials = a.scratch + kScratchAmaxPartials;
+        uint32_t* cast_partials = a.scratch + kScratchCastPartials;
         const bool delayed = a.hist != nullptr;
-        const unsigned agrid = grid_for(g.units, (int64_t)kThreads * kUnroll, kMaxAmaxBlocks);
-        const unsigned cgrid = grid_for(g.units, (int64_t)kThreads * kUnroll, cap);
-        const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 127) / 128);
-        const unsigned tgrid = grid_for(tiles, 1, std::min<int64_t>(kMaxCastBlocks, (int64_t)a.num_cus * kTBlocksPerCU));
-        const bool v16 = a.q != nullptr && aligned(a.q, 16) && a.ldq % 16 == 0;
-        const bool v2 = a.q2 != nullptr && aligned(a.q2, 8) && a.ldq2 % 8 == 0;
         // contiguous, aligned input (and codes): the kernels' plain-indexed fast path
         const bool flat_in = g.rows == 1 && vec_in;
         const bool flat = flat_in && vec_out;
-        // pass 1: amax partials (JIT), or the bootstrap partials of an empty history
-        if (flat_in)
-            hipLaunchKernelGGL((k_amax_partials<InT, true>), dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in,
-                               amax_partials, (const fp8_amax_history*)a.hist);
-        else
-            hipLaunchKernelGGL((k_amax_partials<InT, false>), dim3(agrid), dim3(kThreads), 0, st, x, g, vec_in,
-                               amax_partials, (const fp8_amax_history*)a.hist);
-        if (!a.write_q) {
-            hipLaunchKernelGGL(k_reduce_amax, dim3(1), dim3(kThreads), 0, st, (const uint32_t*)amax_partials,
-                               (int)agrid, a.amax);
-            return hipGetLastError();
-        }
+        // flat passes: each block streams one run of whole units
+        uint32_t achunk = 0, cchunk = 0;
+        const unsigned agrid = flat_in ? flat_grid(g.cols / 8, kMaxAmaxBlocks, &achunk)
+                                       : grid_for(g.units, (int64_t)kThreads * kUnroll, kMaxAmaxBlocks);
+        const unsigned cgrid = flat ? flat_grid(g.cols / 8, cap, &cchunk)
+                                    : grid_for(g.units, (int64_t)kThreads * kUnroll, cap);
+        const int64_t tiles = ((a.rows + 127) / 128) * ((a.cols + 127) / 128);
+        const unsigned tgrid =
+            grid_for(tiles, 1, std::min<int64_t>(kMaxCastBlocks, (int64_t)a.num_cus * kTBlocksPerCU));
+        const bool v16 = a.q != nullptr && aligned(a.q, 16) && a.ldq % 16 == 0;
+        const bool v2 = a.q2 != nullptr && aligned(a.q2, 8) && a.ldq2 % 8 == 0;
 #define FP8MI_TENSOR_CAST(MODE, DG, DIAGP)                                                                  \
     do {                                                                                                  \
         if (a.transpose)                                                                                  \
             hipLaunchKernelGGL((k_cast_tensor_t<InT, FMT, MODE, DG>), dim3(tgrid), dim3(kThreads), 0, st, x,    \
                                a.rows, a.cols, a.ld, vec_in, a.q, a.ldq, v16,                             \
-                               (const uint32_t*)amax_partials, (int)agrid,                                \
-                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
-                               cast_partials, a.q2, a.ldq2, v2);                                          \
+                               (const uint32_t*)amax_partials, (int)agrid, a.hist, a.pow2, a.scale_inv,   \
+                               a.amax, DIAGP, cast_partials, a.q2, a.ldq2, v2);                           \
         else if (flat)                                                                                    \
             hipLaunchKernelGGL((k_cast_tensor<InT, FMT, MODE, DG, true>), dim3(cgrid), dim3(kThreads), 0, st, x,\
-                               g, vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,       \
-                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
-                               cast_partials);                                                            \
+                               g, cchunk, vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,\
+                               a.hist, a.pow2, a.scale_inv, a.amax, DIAGP, cast_partials);               \
         else                                                                                              \
             hipLaunchKernelGGL((k_cast_tensor<InT, FMT, MODE, DG, false>), dim3(cgrid), dim3(kThreads), 0, st,  \
-                               x, g, vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,    \
-                               (const fp8_amax_history*)a.hist, a.pow2, a.scale_inv, a.amax, DIAGP,       \
-                               cast_partials);                                                            \
+                               x, g, 0u, vec_in, a.q, vec_out, (const uint32_t*)amax_partials, (int)agrid,\
+                               a.hist, a.pow2, a.scale_inv, a.amax, DIAGP, cast_partials);               \
     } while (0)
         if (delayed) {
-            // with the guard, the first cast's diagnostics wait in the
-            // workspace (cleared first: its contents are arbitrary)
+            // the cast (its scale from the history, or from its own
+            // bootstrap while the history is empty), then the one-block
+            // finish that pushes the ring.  With the guard, the cast's
+            // diagnostics wait in the workspace (cleared first: its contents
+            // are arbitrary), and a re-cast follows that does nothing unless
+            // the finish saw a spike.
             fp8_diag* diag_tmp = a.guard ? reinterpret_cast<fp8_diag*>(a.scratch + kScratchDiag) : nullptr;
             fp8_diag* d1 = a.guard ? diag_tmp : a.diag;
             if (a.guard && diag)
@@ -741,10 +866,22 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
                                    (const uint32_t*)cast_partials, nparts, a.pow2, a.amax, a.scale_inv, a.diag,
                                    (fp8_diag*)nullptr);
             }
-        } else {
-            if (diag) FP8MI_TENSOR_CAST(kModeJit, true, a.diag);
-            else FP8MI_TENSOR_CAST(kModeJit, false, a.diag);
+            return hipGetLastError();
         }
+        // just in time: pass 1, the amax partials
+        if (flat_in)
+            hipLaunchKernelGGL((k_amax_partials<InT, true>), dim3(agrid), dim3(kThreads), 0, st, x, g, achunk,
+                               vec_in, amax_partials);
+        else
+            hipLaunchKernelGGL((k_amax_partials<InT, false>), dim3(agrid), dim3(kThreads), 0, st, x, g, 0u,
+                               vec_in, amax_partials);
+        if (!a.write_q) {
+            hipLaunchKernelGGL(k_reduce_amax, dim3(1), dim3(kThreads), 0, st, (const uint32_t*)amax_partials,
+                               (int)agrid, a.amax);
+            return hipGetLastError();
+        }
+        if (diag) FP8MI_TENSOR_CAST(kModeJit, true, a.diag);
+        else FP8MI_TENSOR_CAST(kModeJit, false, a.diag);
 #undef FP8MI_TENSOR_CAST
         return hipGetLastError();
     }

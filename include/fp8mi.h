@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FP8MI_ABI_VERSION 5
+#define FP8MI_ABI_VERSION 6
 
 typedef enum {
     FP8_OK = 0,
@@ -130,7 +130,11 @@ typedef struct fp8_diag {
  * fp8_history_init().  Saving and restoring the 128 bytes (a device copy)
  * checkpoints the state.  `scale`/`scale_inv` hold the scale the NEXT call
  * will use (for inspection).  Calls sharing one history must be ordered on
- * one stream. */
+ * one stream.  A delayed call is the cast and a one-workgroup finish that
+ * pushes the ring; on an empty history the cast's workgroups share the
+ * just-in-time amax through `sync`, which the finish clears (a call cut
+ * short by a device fault can leave it non-zero: fp8_history_init, or
+ * restoring a checkpoint taken between calls, clears it). */
 typedef struct fp8_amax_history {
     float amax[16];         /* raw amax of past steps; slot `pos` is written next */
     int32_t len;            /* window length, 1..16 */
@@ -142,7 +146,8 @@ typedef struct fp8_amax_history {
     uint32_t steps;         /* calls completed */
     float spike_threshold;  /* FP8_SPIKE_GUARD threshold, 0 after fp8_history_init (off) */
     uint32_t spikes;        /* guarded calls that cast again */
-    uint32_t reserved[6];
+    uint32_t sync[3];       /* used by the kernels during a call; zero between calls */
+    uint32_t reserved[3];
 } fp8_amax_history;
 
 /* Library version of this header (FP8MI_ABI_VERSION). */

@@ -49,7 +49,7 @@ def test_library_is_gfx950_only_code_object():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.fp8_abi_version() == 5
+    assert lib.fp8_abi_version() == 6
     assert lib.fp8_workspace_size() == L.WORKSPACE_BYTES
     for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARG"), (2, "FP8_ERR_UNSUPPORTED_SHAPE"),
                        (3, "FP8_ERR_MISALIGNED"), (4, "FP8_ERR_UNSUPPORTED_DEVICE"), (5, "FP8_ERR_HIP")]:
@@ -295,9 +295,10 @@ def test_history_struct_is_128_bytes():
     text = open(L.HEADER).read()
     body = text[text.index("typedef struct fp8_amax_history"):]
     body = body[:body.index("} fp8_amax_history;")]
-    # amax, len/pos/count, internal, scale pair, steps, spike threshold, spikes, reserved
-    words = 16 + 3 + 2 + 2 + 1 + 1 + 1 + 6
-    assert "float amax[16]" in body and "uint32_t internal[2]" in body and "uint32_t reserved[6]" in body
+    # amax, len/pos/count, internal, scale pair, steps, spike threshold, spikes, sync, reserved
+    words = 16 + 3 + 2 + 2 + 1 + 1 + 1 + 3 + 3
+    assert "float amax[16]" in body and "uint32_t internal[2]" in body and "uint32_t sync[3]" in body
+    assert "uint32_t reserved[3]" in body
     assert "float spike_threshold" in body and "uint32_t spikes" in body
     assert words * 4 == L.HISTORY_BYTES
 

@@ -336,6 +336,51 @@ def test_delayed_spike_guard_20_steps(transpose, with_diag):
     assert h_dy.state()["spike_threshold"] == 10.0
 
 
+@pytest.mark.parametrize("case", ["flat_bf16", "strided_bf16", "flat_f32", "transposed_f32", "dual_bf16"])
+def test_delayed_bootstrap_in_cast_many_workgroups(case):
+    """Delayed casts on a tensor that takes about a thousand workgroups:
+    step 0 (an empty history: inside the cast, one workgroup reads the whole
+    tensor for the just-in-time bootstrap while the others wait for it) and
+    four more steps against the oracle ring; the history's sync words are
+    zero after every call; a reset history bootstraps again."""
+    rows, cols = 3000, 4104
+    rng = np.random.default_rng(77)
+    f32 = case.endswith("f32")
+    h = fp8.AmaxHistory(16)
+    o = oracle.DelayedScaler(oracle.E5M2)
+    for t in range(7):
+        if t == 5:                   # start over from an empty history
+            h.reset()
+            o = oracle.DelayedScaler(oracle.E5M2)
+        x = (rng.standard_t(3, size=(rows, cols)) * 1e-3 * (1.0 + t)).astype(np.float32)
+        data = x if f32 else synth.to_bf16_bits(x)
+        say("delayed bootstrap in cast", case, "step", t)
+        if case == "strided_bf16":
+            wide = np.zeros((rows, cols + 40), dtype=np.uint16)
+            wide[:, :cols] = data
+            xt = dev_input(wide)[:, :cols]
+        else:
+            xt = dev_input(data)
+        diag = fp8.Diag()
+        if case == "dual_bf16":
+            r, qt = fp8.quantize_dual(xt, "e5m2", history=h, diag=diag)
+        else:
+            r = fp8.quantize(xt, "e5m2", "tensor", history=h, transpose=case.startswith("transposed"), diag=diag)
+        w = o.step(data)
+        got = host(r.q)
+        assert np.array_equal(got, w["q"].T if case.startswith("transposed") else w["q"]), (case, t)
+        if case == "dual_bf16":
+            assert np.array_equal(host(qt), w["q"].T), (case, t)
+        assert host(r.scale_inv)[0] == w["scale_inv"] and host(r.amax)[0] == w["amax"], (case, t)
+        assert diag.read()["sat"] == w["sat"], (case, t)
+        st, os_ = h.state(), o.state()
+        assert (st["count"], st["pos"]) == (os_["count"], os_["pos"]), (case, t)
+        assert np.array_equal(st["amax"].numpy(), os_["amax"]), (case, t)
+        assert st["steps"] == (t + 1 if t < 5 else t - 4), (case, t)
+        words = host(h.buf)
+        assert np.all(words[26:32] == 0), (case, t, words[26:32])
+
+
 def test_delayed_save_restore():
     tokens, hidden = 256, 256
     h = fp8.AmaxHistory(16)
