@@ -177,8 +177,8 @@ def stream_ceilings(torch, mib: int = 1024, reps: int = 5, rounds: int = 3) -> d
     FP8 cast's pattern without its arithmetic), each over `mib` MiB of
     source alternating between two buffers (so nothing is left in the
     256 MB Infinity Cache), the best of `rounds` rounds of `reps` launches;
-    GB/s of bytes read + written.  For each, the best of 4 and 8 workgroups
-    per CU."""
+    GB/s of bytes read + written.  For each, the best of 2, 4 and 8
+    workgroups per CU (each workgroup streaming one contiguous run)."""
     import ctypes
     path = os.path.join(ROOT, "fp8_precision_quantization_amd", "libfp8probe.so")
     if not os.path.exists(path):
@@ -203,7 +203,7 @@ def stream_ceilings(torch, mib: int = 1024, reps: int = 5, rounds: int = 3) -> d
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for name, (run, nbytes) in launches.items():
         best = 0.0
-        for bpc in (4, 8):
+        for bpc in (2, 4, 8):
             for i in range(2):
                 if run(i, bpc) != 0:
                     raise RuntimeError("fp8probe %s failed" % name)

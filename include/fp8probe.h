@@ -8,9 +8,9 @@
  * caller.  Each call launches one kernel on `stream` (a hipStream_t as
  * void*, NULL = the null stream) and returns 0, a negative value for an
  * invalid argument (nothing launched), or the HIP error of the launch.
- * blocks_per_cu: workgroups of 256 threads per compute unit in the
- * grid-stride launch (the grid is also capped at one unit of four 16-byte
- * loads per thread).
+ * blocks_per_cu (>= 1): workgroups of 256 threads per compute unit; each
+ * workgroup streams one contiguous run of the data (fewer workgroups when
+ * the runs would be shorter than 16 KiB).
  */
 #ifndef FP8PROBE_H
 #define FP8PROBE_H
