@@ -25,15 +25,14 @@ template <> struct Pack<uint16_t> {          // 8 bf16 values packed in 4 words
         const uint32_t v = w[i >> 1];
         return __uint_as_float((i & 1) ? (v & 0xFFFF0000u) : (v << 16));
     }
+    // max |x| as binary32 bits: the 16-bit magnitudes compared two at a time
+    // (packed unsigned 16-bit max), then widened
     __device__ __forceinline__ uint32_t abs_max() const {
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t hi = w[i] & 0x7FFF0000u;
-            const uint32_t lo = (w[i] << 16) & 0x7FFF0000u;
-            m = max(m, max(hi, lo));
-        }
-        return m;
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        auto mag = [](uint32_t v) { return __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu); };
+        const u16x2 t = __builtin_elementwise_max(__builtin_elementwise_max(mag(w[0]), mag(w[1])),
+                                                  __builtin_elementwise_max(mag(w[2]), mag(w[3])));
+        return (uint32_t)max(t[0], t[1]) << 16;
     }
 };
 
@@ -122,7 +121,10 @@ struct Counters {
     uint32_t sat = 0, nonfinite = 0, under = 0;
 };
 
-// Encode a unit with scale s; optionally count the diagnostics.
+// Encode a unit with scale s; optionally count the diagnostics.  A NaN
+// input makes the unit's max |x| bits exceed Inf's; only then does the
+// rare fix-up run, writing the NaN code 0x7F with the input's sign (the
+// clamp and convert leave an unspecified byte for a NaN).
 template <int FMT, bool DIAG, typename InT>
 __device__ __forceinline__ uint2 encode_unit(const Pack<InT>& p, float s, Counters& cnt) {
     float v[8];
@@ -131,14 +133,7 @@ __device__ __forceinline__ uint2 encode_unit(const Pack<InT>& p, float s, Counte
     uint2 out;
     out.x = encode4<FMT>(v[0], v[1], v[2], v[3]);
     out.y = encode4<FMT>(v[4], v[5], v[6], v[7]);
-    // The convert instructions give every NaN one canonical code (E4M3 0xFF,
-    // E5M2 0xFE) whatever its sign, and after the clamp no other input can
-    // produce that byte.  A has-zero-byte test on code ^ canonical finds them
-    // (about one instruction per element); the rare fix-up writes the NaN
-    // code 0x7F with the input's sign.
-    constexpr uint32_t kHwNaN = FMT == kE4M3 ? 0xFFFFFFFFu : 0xFEFEFEFEu;
-    const uint32_t nx = out.x ^ kHwNaN, ny = out.y ^ kHwNaN;
-    if (__builtin_expect(((((nx - 0x01010101u) & ~nx) | ((ny - 0x01010101u) & ~ny)) & 0x80808080u) != 0u, 0)) {
+    if (__builtin_expect(p.abs_max() > kInfBits, 0)) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t bx = __float_as_uint(p.get(i));

@@ -224,6 +224,25 @@ __device__ __forceinline__ void flat_run(uint32_t whole, uint32_t chunk, uint32_
     end = (uint32_t)(e < whole ? e : whole);
 }
 
+// The units [it + t, it + t + kThreads, ...) of one loop iteration of a flat
+// run ending at `end` (t = threadIdx.x).  A whole iteration, the usual case,
+// issues all kUnroll loads with no per-unit test, so they are in flight
+// together; with a test per load the compiler waits for each load before
+// the next one's branch.  Units past `end` read as zeros.
+template <typename InT>
+__device__ __forceinline__ void load_iteration(const InT* __restrict__ x, uint32_t it, uint32_t end,
+                                               Pack<InT> (&p)[kUnroll]) {
+    const uint32_t u0 = it + threadIdx.x;
+    if (it + kThreads * kUnroll <= end) {
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) p[i] = load_flat<InT>(x, u0 + i * kThreads);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i)
+            p[i] = u0 + i * kThreads < end ? load_flat<InT>(x, u0 + i * kThreads) : Pack<InT>{};
+    }
+}
+
 // Per-tensor amax, pass 1: one partial per block.  FLAT: the tensor is one
 // contiguous, 16-byte aligned run of g.cols elements (g.rows == 1, vec_in),
 // so every unit but a ragged last one is whole and loads with plain
@@ -241,13 +260,9 @@ __global__ __launch_bounds__(kThreads) void k_amax_partials(const InT* __restric
         const uint32_t whole = (uint32_t)(g.cols / 8);
         uint32_t beg, end;
         flat_run(whole, chunk, beg, end);
-        for (uint32_t u0 = beg + threadIdx.x; u0 < end; u0 += kThreads * kUnroll) {
+        for (uint32_t it = beg; it < end; it += kThreads * kUnroll) {
             Pack<InT> p[kUnroll];
-#pragma unroll
-            for (int i = 0; i < kUnroll; ++i) {
-                const uint32_t u = u0 + i * kThreads;
-                p[i] = u < end ? load_flat<InT>(x, u) : Pack<InT>{};
-            }
+            load_iteration(x, it, end, p);
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i) m = max(m, p[i].abs_max());
         }
@@ -379,16 +394,12 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
         const uint32_t whole = (uint32_t)(g.cols / 8);
         uint32_t beg, end;
         flat_run(whole, chunk, beg, end);
-        for (uint32_t u0 = beg + threadIdx.x; u0 < end; u0 += kThreads * kUnroll) {
+        for (uint32_t it = beg; it < end; it += kThreads * kUnroll) {
             Pack<InT> p[kUnroll];
+            load_iteration(x, it, end, p);
 #pragma unroll
             for (int i = 0; i < kUnroll; ++i) {
-                const uint32_t u = u0 + i * kThreads;
-                p[i] = u < end ? load_flat<InT>(x, u) : Pack<InT>{};
-            }
-#pragma unroll
-            for (int i = 0; i < kUnroll; ++i) {
-                const uint32_t u = u0 + i * kThreads;
+                const uint32_t u = it + threadIdx.x + i * kThreads;
                 if (u < end) {
                     if constexpr (DELAYED) m = max(m, p[i].abs_max());
                     store_flat(q, u, encode_unit<FMT, DIAG>(p[i], s, cnt));
@@ -704,6 +715,44 @@ __global__ __launch_bounds__(kThreads) void k_cast_1x128(
     if constexpr (DIAG) block_add_diag(cnt, lds, diag);
 }
 
+// 1x128 blocks of a contiguous, aligned tensor whose rows are whole blocks
+// (cols % 128 == 0, codes contiguous too): unit u (8 elements) lies in block
+// u / 16, so the flat unit order is the block order and no row arithmetic
+// is needed.  Each workgroup streams one contiguous run of whole blocks
+// (kThreads * kUnroll units per iteration); 16 consecutive lanes hold one
+// block, whose max is a DPP reduction inside their 16-lane row.
+template <typename InT, int FMT, bool DIAG, bool WRITE_Q>
+__global__ __launch_bounds__(kThreads) void k_cast_1x128_flat(
+    const InT* __restrict__ x, uint32_t units, uint32_t chunk, uint8_t* __restrict__ q, bool pow2,
+    float* __restrict__ scale_inv_out, float* __restrict__ amax_out, fp8_diag* diag) {
+    __shared__ uint32_t lds[16];
+    uint32_t beg, end;
+    flat_run(units, chunk, beg, end);
+    Counters cnt;
+    // runs, ends and iterations are multiples of 16 units, so the 16 lanes of
+    // a block are active or idle together
+    for (uint32_t it = beg; it < end; it += kThreads * kUnroll) {
+        const uint32_t u0 = it + threadIdx.x;
+        Pack<InT> p[kUnroll];
+        load_iteration(x, it, end, p);
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const uint32_t u = u0 + i * kThreads;
+            const uint32_t gm = group_max_u32<16>(p[i].abs_max());
+            const float s = scale_from_amax_bits<FMT>(gm, pow2);
+            const float si = recip_rn(s);
+            if (u < end) {
+                if ((threadIdx.x & 15) == 0) {
+                    amax_out[u >> 4] = __uint_as_float(gm);
+                    if (WRITE_Q) scale_inv_out[u >> 4] = si;
+                }
+                if constexpr (WRITE_Q) store_flat(q, u, encode_unit<FMT, DIAG>(p[i], s, cnt));
+            }
+        }
+    }
+    if constexpr (DIAG) block_add_diag(cnt, lds, diag);
+}
+
 // 128x128 blocks: one workgroup per block, 8 units per thread held in
 // registers.  amax/scale arrays are [ceil(rows/128) x ceil(cols/128)].
 template <typename InT, int FMT, bool DIAG, bool WRITE_Q>
@@ -919,8 +968,23 @@ hipError_t quantize_geom(const QuantArgs& a, const InT* x, int esz) {
         FP8MI_GROUP_LAUNCH(k_cast_rows, grid);
     } else if (a.gran == FP8_GRAN_BLOCK_1x128) {
         const int64_t G = a.rows * ((a.cols + 127) / 128);
-        const dim3 grid(grid_for(G, 16 * kUnroll, (int64_t)a.num_cus * 8));
-        FP8MI_GROUP_LAUNCH(k_cast_1x128, grid);
+        const int64_t units = a.rows * a.cols / 8;
+        const bool flat = a.cols % 128 == 0 && a.ld == a.cols && (!a.write_q || a.ldq == a.cols) && gvec_in &&
+                          (!a.write_q || aligned(a.q, 8)) && units < ((int64_t)1 << 31);
+        if (flat) {
+            uint32_t chunk = 0;
+            const dim3 grid(flat_grid(units, (int64_t)a.num_cus * 8, &chunk));
+#define FP8MI_1x128_FLAT(DG, WQ)                                                                          \
+    hipLaunchKernelGGL((k_cast_1x128_flat<InT, FMT, DG, WQ>), grid, dim3(kThreads), 0, st, x, (uint32_t)units, \
+                       chunk, a.q, a.pow2, a.scale_inv, a.amax, a.diag)
+            if (!a.write_q) FP8MI_1x128_FLAT(false, false);
+            else if (diag) FP8MI_1x128_FLAT(true, true);
+            else FP8MI_1x128_FLAT(false, true);
+#undef FP8MI_1x128_FLAT
+        } else {
+            const dim3 grid(grid_for(G, 16 * kUnroll, (int64_t)a.num_cus * 8));
+            FP8MI_GROUP_LAUNCH(k_cast_1x128, grid);
+        }
     } else {
         const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
         FP8MI_GROUP_LAUNCH(k_cast_128x128, grid);
