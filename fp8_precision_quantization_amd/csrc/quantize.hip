@@ -481,10 +481,18 @@ __global__ __launch_bounds__(kThreads, kTBlocksPerCU) void k_cast_tensor_t(
     const int64_t tiles = ((rows + 127) / 128) * tiles_c;
     uint32_t m = 0;
     Counters cnt;
-    // this thread's 8 units of tile tl (zeros past the matrix)
+    // this thread's 8 units of tile tl (zeros past the matrix).  An interior
+    // tile of an aligned matrix issues its 8 loads with no per-unit test, so
+    // they are in flight together (the ragged path's 2-byte loads would
+    // otherwise make the compiler wait before each vector load).
     Pack<InT> p[8];
     auto load_tile = [&](int64_t tl) {
         const int64_t r0 = (tl / tiles_c) * 128, c = (tl % tiles_c) * 128 + cu * 8;
+        if (vec_in && r0 + 128 <= rows && (tl % tiles_c) * 128 + 128 <= cols) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p[i] = load_unit<InT, true>(x, (r0 + rr + 16 * i) * ld + c, 8, true);
+            return;
+        }
         const int nvc = (int)(cols - c >= 8 ? 8 : (cols - c > 0 ? cols - c : 0));
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
