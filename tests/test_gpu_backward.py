@@ -120,3 +120,57 @@ def test_backward_gemms_parity_and_accuracy():
     # E5M2 keeps 2 mantissa bits, E4M3 3: per product about 2^-4 relative
     # rounding error, uncorrelated over K terms; a few percent normwise
     assert e_dx < 0.1 and e_dw < 0.1
+
+
+@pytest.mark.timeout(600)
+def test_rowwise_with_gw_hp_backward():
+    """The Soup recipe table's rowwise_with_gw_hp backward: the data gradient
+    dX = dY W through FP8 with per-row power-of-two scales (dY's rows E5M2,
+    and W^T's rows, i.e. one scale per column of W, E4M3: the per-row x
+    per-column scaled GEMM), and the weight gradient dW = dY^T X kept in
+    high precision (bf16 inputs, fp32 accumulation; no FP8 GEMM).  The FP8
+    dgrad is checked against the oracle on every output; the accuracies of
+    both against fp64 products of the same bf16 inputs show what the recipe
+    buys: the FP8 gradients are a few percent off (normwise), the
+    high-precision dW agrees to fp32 rounding."""
+    M, N, K = 1024, 2048, 1024          # tokens, layer outputs, layer inputs
+    rng = np.random.default_rng(47)
+    dy = synth.to_bf16_bits((rng.standard_t(3, size=(M, N)) * 1e-3).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    wt = np.ascontiguousarray(w.T)                                     # W^T [K x N]
+    say("rowwise backward quantize")
+    rdy = fp8.quantize(dev_input(dy), "e5m2", "row", pow2=True)
+    rwt = fp8.quantize(dev_input(wt), "e4m3", "row", pow2=True)
+    ody = oracle.quantize(dy, oracle.E5M2, "row", pow2=True)
+    owt = oracle.quantize(wt, oracle.E4M3, "row", pow2=True)
+    assert np.array_equal(host(rdy.q), ody["q"]) and np.array_equal(host(rwt.q), owt["q"])
+    assert np.array_equal(host(rdy.scale_inv).ravel(), ody["scale_inv"].ravel())
+    assert np.array_equal(host(rwt.scale_inv).ravel(), owt["scale_inv"].ravel())
+    sdy, swt = ody["scale_inv"].ravel(), owt["scale_inv"].ravel()
+    assert np.all(np.frexp(sdy)[0] == 0.5) and np.all(np.frexp(swt)[0] == 0.5)   # powers of two
+
+    say("rowwise dgrad gemm", M, K, N)
+    dx = host(fp8.scaled_gemm(rdy.q, rwt.q, rdy.scale_inv.reshape(-1), rwt.scale_inv.reshape(-1),
+                              "e5m2", "e4m3", torch.float32))                 # [M x K]
+    y32, p = oracle.gemm(ody["q"], oracle.E5M2, owt["q"], oracle.E4M3, sdy, swt)
+    rep = assert_gemm(dx.reshape(-1), y32.reshape(-1), p.reshape(-1), N, "f32", what="rowwise dgrad",
+                      model=gemm_model_at(ody["q"], oracle.E5M2, owt["q"], oracle.E4M3, sdy, swt))
+    assert rep["n"] == M * K
+    print(rep)
+
+    say("high-precision wgrad (bf16 inputs, fp32 accumulation)")
+    dev = torch.device("cuda:0")
+    dyt_bf = torch.from_numpy(synth.bf16_bits_to_f32(dy)).to(dev).t().contiguous()     # [N x M]
+    x_f = torch.from_numpy(synth.bf16_bits_to_f32(x)).to(dev)                          # [M x K]
+    dw_hp = host(torch.matmul(dyt_bf, x_f))                                            # fp32 products of bf16 values
+
+    dy64 = synth.bf16_bits_to_f32(dy).astype(np.float64)
+    w64 = synth.bf16_bits_to_f32(w).astype(np.float64)
+    x64 = synth.bf16_bits_to_f32(x).astype(np.float64)
+    e_dx = _rel(dx, dy64 @ w64)
+    e_dw = _rel(dw_hp, dy64.T @ x64)
+    print("rowwise_with_gw_hp normwise error vs fp64: dgrad (FP8 rows) %.4f, wgrad (high precision) %.2e"
+          % (e_dx, e_dw))
+    assert e_dx < 0.1            # per-row E5M2 x E4M3: a few percent, as the tensorwise recipe
+    assert e_dw < 1e-4           # fp32 accumulation of exact bf16 products
