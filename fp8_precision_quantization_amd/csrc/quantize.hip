@@ -96,21 +96,22 @@ __device__ __forceinline__ uint32_t block_max_all(uint32_t v, uint32_t* lds) {
     return v;
 }
 
-// One block's max |x| over a whole [rows x cols] (ld) tensor, to every
-// thread: the just-in-time amax that the first delayed call needs while its
-// history is still empty (once per history, so one block suffices).
+// One block's max |x| over units [beg, end) of a [rows x cols] (ld) tensor
+// (units of 8 elements in row-major order), to every thread: a piece of the
+// just-in-time amax that the first delayed call needs while its history is
+// still empty.
 template <typename InT>
-__device__ __forceinline__ uint32_t whole_tensor_amax(const InT* __restrict__ x, int64_t rows, int64_t cols,
-                                                      int64_t ld, bool vec_in, uint32_t* lds) {
+__device__ __forceinline__ uint32_t units_amax(const InT* __restrict__ x, int64_t rows, int64_t cols,
+                                               int64_t ld, bool vec_in, int64_t beg, int64_t end, uint32_t* lds) {
     constexpr int U = 8;
-    const int64_t upr = (cols + 7) / 8, units = rows * upr;
+    const int64_t upr = (cols + 7) / 8;
     uint32_t m = 0;
-    for (int64_t u0 = threadIdx.x; u0 < units; u0 += (int64_t)kThreads * U) {
+    for (int64_t u0 = beg + threadIdx.x; u0 < end; u0 += (int64_t)kThreads * U) {
         Pack<InT> p[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int64_t u = u0 + (int64_t)i * kThreads;
-            if (u < units) {
+            if (u < end) {
                 const int64_t r = u / upr, c = (u - r * upr) * 8;
                 p[i] = load_unit<InT>(x, r * ld + c, cols - c >= 8 ? 8 : (int)(cols - c), vec_in);
             } else {
@@ -126,11 +127,16 @@ __device__ __forceinline__ uint32_t whole_tensor_amax(const InT* __restrict__ x,
 // Delayed scaling ([DeepL bets on FP8] 2.3: the factor comes from earlier
 // steps' statistics).  The history's sync words are zero between calls
 // (fp8_history_init zeroes them, and so does the finish kernel of every
-// call): sync[0] and sync[1] publish the bootstrap amax of an empty history
-// (a token, then its bits), sync[2] hands out bootstrap tickets.  Workgroups
-// exchange these words only through atomic read-modify-writes, each waited
-// for before the next: no fence, so no workgroup writes back or invalidates
-// its XCD's L2.
+// call).  While the history is empty the call needs this step's just-in-time
+// amax first: the tensor is cut into as many slices as the grid has
+// workgroups, each arriving workgroup claims slices from sync[2] until none
+// is left, folds each slice's max into sync[1] and counts it done in
+// sync[0].  A workgroup then waits until every slice is done.  It waits only
+// for slices already claimed, i.e. for running workgroups, so the scheme
+// assumes nothing about which workgroups are resident.  The words are
+// exchanged only through atomic read-modify-writes, each waited for before
+// the next: no fence, so no workgroup writes back or invalidates its XCD's
+// L2.
 __device__ __forceinline__ uint32_t sync_read(uint32_t* w) { return atomicOr(w, 0u); }
 
 // Wait until this thread's memory operations, atomics included, are done.
@@ -140,15 +146,17 @@ __device__ __forceinline__ void wait_memory() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Start of a call: the scale from the window's max; with an empty history,
-// from this step's just-in-time amax.  That bootstrap is computed by one
-// workgroup, the one that takes ticket 0 (it is running, so the others can
-// wait for it whatever else is resident).
+// The wait for the slices is bounded: should they never all be counted (a
+// history whose sync words were not zero), a workgroup reads the whole
+// tensor itself after about a quarter of a second.
 constexpr uint32_t kBootSpins = 1u << 20;
 
-template <int FMT, typename BootAmax>
-__device__ __forceinline__ float delayed_begin(fp8_amax_history* h, bool pow2, uint32_t* lds,
-                                               BootAmax boot_amax) {
+// Start of a call: the scale from the window's max; with an empty history,
+// from this step's just-in-time amax over the tensor's `units` units
+// (slice_amax(beg, end) gives one block's max over units [beg, end)).
+template <int FMT, typename SliceAmax>
+__device__ __forceinline__ float delayed_begin(fp8_amax_history* h, bool pow2, uint32_t* lds, int64_t units,
+                                               SliceAmax slice_amax) {
     const int32_t count = h->count;
     uint32_t basis = 0;
     if (count > 0) {
@@ -156,38 +164,38 @@ __device__ __forceinline__ float delayed_begin(fp8_amax_history* h, bool pow2, u
         for (int i = 0; i < n; ++i) basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
         return scale_from_amax_bits<FMT>(basis, pow2);
     }
-    const uint32_t token = h->steps + 1u;
-    __syncthreads();
-    if (threadIdx.x == 0) lds[8] = atomicAdd(&h->sync[2], 1u);
-    __syncthreads();
-    const uint32_t ticket = lds[8];
-    if (ticket == 0) {
-        basis = boot_amax();
-        if (threadIdx.x == 0) {
-            atomicExch(&h->sync[1], basis);
-            wait_memory();                       // the bits are in place before the token
-            atomicExch(&h->sync[0], token);
-        }
-    } else {
-        // The wait is bounded: should the ticket holder never publish (a
-        // history whose sync words were not zero), this workgroup reads the
-        // tensor itself after about a quarter of a second.
-        if (threadIdx.x == 0) {
-            uint32_t got = 0;
-            for (uint32_t i = 0; i < kBootSpins; ++i) {
-                if (sync_read(&h->sync[0]) == token) {
-                    got = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(8);
-            }
-            lds[9] = got ? sync_read(&h->sync[1]) : 0u;
-            lds[10] = got;
-        }
+    const uint32_t slices = gridDim.x;
+    const int64_t per = (units + slices - 1) / slices;
+    for (;;) {
         __syncthreads();
-        basis = lds[9];
-        if (lds[10] == 0u) basis = boot_amax();
+        if (threadIdx.x == 0) lds[8] = atomicAdd(&h->sync[2], 1u);
+        __syncthreads();
+        const uint32_t sl = lds[8];
+        if (sl >= slices) break;
+        const int64_t beg = (int64_t)sl * per;
+        const int64_t end = beg + per < units ? beg + per : units;
+        const uint32_t m = beg < end ? slice_amax(beg, end) : 0u;
+        if (threadIdx.x == 0) {
+            atomicMax(&h->sync[1], m);
+            wait_memory();                       // the max is in place before the slice counts as done
+            atomicAdd(&h->sync[0], 1u);
+        }
     }
+    if (threadIdx.x == 0) {
+        uint32_t got = 0;
+        for (uint32_t i = 0; i < kBootSpins; ++i) {
+            if (sync_read(&h->sync[0]) >= slices) {
+                got = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        lds[9] = got ? sync_read(&h->sync[1]) : 0u;
+        lds[10] = got;
+    }
+    __syncthreads();
+    basis = lds[9];
+    if (lds[10] == 0u) basis = slice_amax(0, units);
     __syncthreads();
     return scale_from_amax_bits<FMT>(basis, pow2);
 }
@@ -378,8 +386,9 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
         if (hist->internal[0] == 0u) return;
         s = __uint_as_float(hist->internal[1]);
     } else if constexpr (DELAYED) {
-        s = delayed_begin<FMT>(hist, pow2, lds,
-                               [&] { return whole_tensor_amax<InT>(x, g.rows, g.cols, g.ld, vec_in, lds); });
+        s = delayed_begin<FMT>(hist, pow2, lds, (int64_t)g.units, [&](int64_t b, int64_t e) {
+            return units_amax<InT>(x, g.rows, g.cols, g.ld, vec_in, b, e, lds);
+        });
     } else {
         const uint32_t am = reduce_partials(partials_in, n_in, lds);
         s = scale_from_amax_bits<FMT>(am, pow2);
@@ -466,8 +475,9 @@ __global__ __launch_bounds__(kThreads, kTBlocksPerCU) void k_cast_tensor_t(
         if (hist->internal[0] == 0u) return;
         s = __uint_as_float(hist->internal[1]);
     } else if constexpr (DELAYED) {
-        s = delayed_begin<FMT>(hist, pow2, lds,
-                               [&] { return whole_tensor_amax<InT>(x, rows, cols, ld, vec_in, lds); });
+        s = delayed_begin<FMT>(hist, pow2, lds, rows * ((cols + 7) / 8), [&](int64_t b, int64_t e) {
+            return units_amax<InT>(x, rows, cols, ld, vec_in, b, e, lds);
+        });
     } else {
         const uint32_t am = reduce_partials(partials_in, n_in, lds);
         s = scale_from_amax_bits<FMT>(am, pow2);
