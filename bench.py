@@ -412,6 +412,10 @@ class Step:
                          scale_inv_out=self.sw, amax_out=self.aw)
         elif self.workload == "moe":
             fp8.quantize(x, "e4m3", "row", diag=dx, out=self.xq, scale_inv_out=self.sx, amax_out=self.ax)
+        elif self.gx == "tensor" and self.gw == "tensor":
+            # both operands per tensor, just in time: one amax and one cast launch for the two
+            fp8.quantize_tensors([x, w], "e4m3", outs=[self.xq, self.wq], diags=[dx, dw],
+                                 scale_inv_outs=[self.sx, self.sw], amax_outs=[self.ax, self.aw])
         else:
             pow2 = self.workload == "qkv"
             fp8.quantize(x, "e4m3", self.gx, pow2=pow2, diag=dx, out=self.xq, scale_inv_out=self.sx,

@@ -12,6 +12,7 @@ call raises if the library is missing or the device is not gfx950.
 """
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
@@ -20,7 +21,7 @@ import torch
 from . import _lib
 from ._lib import Fp8Error  # noqa: F401
 
-__all__ = ["quantize", "quantize_dual", "amax", "scaled_gemm", "blockscaled_gemm", "AmaxHistory", "Diag",
+__all__ = ["quantize", "quantize_dual", "quantize_tensors", "amax", "scaled_gemm", "blockscaled_gemm", "AmaxHistory", "Diag",
            "QuantResult", "Fp8Error", "FORMATS", "GRANULARITIES", "group_grid", "kv_store", "kv_load",
            "KVTensorCache", "KVCache", "grouped_gemm", "workspace"]
 
@@ -269,6 +270,67 @@ def quantize_dual(x: torch.Tensor, fmt="e5m2", pow2: bool = False, history: Opti
         ws_ptr, ws_bytes, _stream(dev))
     _lib.check(st, "fp8_quantize_dual")
     return QuantResult(out, scale_inv_out, amax_out, fmt_name), out_t
+
+
+def quantize_tensors(xs, fmt="e4m3", pow2: bool = False, outs=None, diags=None, scale_inv_outs=None,
+                     amax_outs=None, workspace: Optional[torch.Tensor] = None) -> list:
+    """Just-in-time per-tensor quantization of up to 8 contiguous tensors in
+    one amax launch and one cast launch (fp8_quantize_tensors).  xs: 2-D
+    contiguous tensors of one dtype (bfloat16 or float32) on one device;
+    outs: optional uint8 tensors of the same shapes; diags: optional Diag per
+    tensor (None entries skip the counting); scale_inv_outs, amax_outs:
+    optional one-element fp32 tensors per tensor.  Returns one QuantResult
+    per tensor, each equal to quantize(x, fmt, "tensor", pow2)."""
+    xs = list(xs)
+    n = len(xs)
+    if not 1 <= n <= _lib.MAX_TENSORS:
+        raise ValueError("quantize_tensors takes 1..%d tensors, got %d" % (_lib.MAX_TENSORS, n))
+    dev = xs[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be device tensors, got %s" % dev)
+    dt = xs[0].dtype
+    if dt == torch.bfloat16:
+        in_dt = _lib.FP8_IN_BF16
+    elif dt == torch.float32:
+        in_dt = _lib.FP8_IN_F32
+    else:
+        raise TypeError("tensors must be bfloat16 or float32, got %s" % dt)
+    fmt_name = fmt if isinstance(fmt, str) else ("e4m3" if fmt == 0 else "e5m2")
+    outs = list(outs) if outs is not None else [None] * n
+    diags = list(diags) if diags is not None else [None] * n
+    sinvs = list(scale_inv_outs) if scale_inv_outs is not None else [None] * n
+    amaxs = list(amax_outs) if amax_outs is not None else [None] * n
+    if len(outs) != n or len(diags) != n or len(sinvs) != n or len(amaxs) != n:
+        raise ValueError("outs, diags, scale_inv_outs and amax_outs must have one entry per tensor")
+    descs = (_lib.Fp8Tensor * n)()
+    results = []
+    for i, x in enumerate(xs):
+        if x.dtype != dt:
+            raise TypeError("tensor %d is %s, tensor 0 is %s" % (i, x.dtype, dt))
+        _same_device(x, dev, "tensor %d" % i)
+        if x.dim() != 2:
+            raise ValueError("tensor %d must be 2-D, got shape %s" % (i, tuple(x.shape)))
+        rows, cols = x.shape
+        if x.numel() > 0 and not x.is_contiguous():
+            raise ValueError("tensor %d must be contiguous" % i)
+        out = outs[i]
+        if out is None:
+            out = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        _out_matrix(out, rows, cols, torch.uint8, dev, "outs[%d]" % i)
+        if not out.is_contiguous():
+            raise ValueError("outs[%d] must be contiguous" % i)
+        sinv = sinvs[i] if sinvs[i] is not None else torch.empty((1, 1), dtype=torch.float32, device=dev)
+        am = amaxs[i] if amaxs[i] is not None else torch.empty((1, 1), dtype=torch.float32, device=dev)
+        _buf(sinv, 1, torch.float32, dev, "scale_inv_outs[%d]" % i)
+        _buf(am, 1, torch.float32, dev, "amax_outs[%d]" % i)
+        descs[i] = _lib.Fp8Tensor(x.data_ptr(), rows, cols, out.data_ptr(), sinv.data_ptr(), am.data_ptr(),
+                                  _ptr(diags[i].buf) if diags[i] is not None else None)
+        results.append(QuantResult(out, sinv, am, fmt_name))
+    ws, ws_ptr, ws_bytes = _workspace(workspace, True, dev)
+    st = _lib.lib().fp8_quantize_tensors(ctypes.cast(descs, ctypes.c_void_p), n, in_dt, _fmt(fmt), _lib.FP8_SCALE_POW2 if pow2 else 0,
+                                         ws_ptr, ws_bytes, _stream(dev))
+    _lib.check(st, "fp8_quantize_tensors")
+    return results
 
 
 def amax(x: torch.Tensor, granularity="tensor", out: Optional[torch.Tensor] = None,

@@ -34,12 +34,20 @@ FP8_GROUPED_MAX_TILES = 1983
 HISTORY_BYTES = 128
 DIAG_BYTES = 16
 WORKSPACE_BYTES = 65536
+MAX_TENSORS = 8
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _INT = ctypes.c_int
 _U32 = ctypes.c_uint32
+
+
+class Fp8Tensor(ctypes.Structure):
+    """fp8_tensor, one descriptor of fp8_quantize_tensors (56 bytes)."""
+    _fields_ = [("x", _P), ("rows", _I64), ("cols", _I64), ("q", _P), ("scale_inv", _P), ("amax", _P),
+                ("diag", _P)]
+
 
 # name -> (restype, argtypes); must match include/fp8mi.h
 SIGNATURES = {
@@ -56,6 +64,7 @@ SIGNATURES = {
                                     _P]),
     "fp8_quantize_dual": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _U32, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
                                  _I64, _P]),
+    "fp8_quantize_tensors": (_INT, [_P, _I32, _INT, _INT, _U32, _P, _I64, _P]),
     "fp8_scaled_gemm": (_INT, [_P, _INT, _I64, _P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,
                                _P, _INT, _I64, _P]),
     "fp8_blockscaled_gemm": (_INT, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _INT, _I64, _P]),

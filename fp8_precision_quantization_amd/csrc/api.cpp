@@ -282,6 +282,53 @@ fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows,
                          ldq, qt, ldqt, true, scale_inv_out, amax_out, diag, workspace, workspace_bytes, stream);
 }
 
+fp8_status fp8_quantize_tensors(const fp8_tensor* tensors, int32_t count, fp8_in_dtype in_dtype, fp8_format fmt,
+                                uint32_t flags, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (tensors == nullptr) return fail(FP8_ERR_INVALID_ARG, "tensors is NULL");
+    if (count < 1 || count > FP8_MAX_TENSORS)
+        return fail(FP8_ERR_INVALID_ARG, "count=%d not in 1..%d", (int)count, FP8_MAX_TENSORS);
+    if (in_dtype != FP8_IN_F32 && in_dtype != FP8_IN_BF16)
+        return fail(FP8_ERR_INVALID_ARG, "in_dtype %d is not FP8_IN_F32 or FP8_IN_BF16", (int)in_dtype);
+    if (fmt != FP8_E4M3 && fmt != FP8_E5M2)
+        return fail(FP8_ERR_INVALID_ARG, "format %d is not FP8_E4M3 or FP8_E5M2", (int)fmt);
+    if (flags & ~FP8_SCALE_POW2)
+        return fail(FP8_ERR_INVALID_ARG, "unknown flag bits 0x%x (only FP8_SCALE_POW2 applies)",
+                    flags & ~FP8_SCALE_POW2);
+    fp8mi::MultiQuantArgs a;
+    for (int t = 0; t < count; ++t) {
+        const fp8_tensor& d = tensors[t];
+        if (d.rows < 0 || d.cols < 0)
+            return fail(FP8_ERR_INVALID_ARG, "tensor %d: negative size rows=%lld cols=%lld", t, (long long)d.rows,
+                        (long long)d.cols);
+        if (d.rows > (int64_t(1) << 31) || d.cols > (int64_t(1) << 31))
+            return fail(FP8_ERR_UNSUPPORTED_SHAPE, "tensor %d: rows and cols must each be <= 2^31", t);
+        const int64_t elems = d.rows * d.cols;
+        if (elems / 8 > fp8mi::kMaxUnits)
+            return fail(FP8_ERR_UNSUPPORTED_SHAPE, "tensor %d too large: more than 2^34 elements", t);
+        if (elems > 0 && d.x == nullptr) return fail(FP8_ERR_INVALID_ARG, "tensor %d: x is NULL", t);
+        if (elems > 0 && d.q == nullptr) return fail(FP8_ERR_INVALID_ARG, "tensor %d: q is NULL", t);
+        if (d.scale_inv == nullptr) return fail(FP8_ERR_INVALID_ARG, "tensor %d: scale_inv is NULL", t);
+        if (d.amax == nullptr) return fail(FP8_ERR_INVALID_ARG, "tensor %d: amax is NULL", t);
+        if (!is_aligned(d.x, 16)) return fail(FP8_ERR_MISALIGNED, "tensor %d: x must be 16-byte aligned", t);
+        if (!is_aligned(d.q, 8)) return fail(FP8_ERR_MISALIGNED, "tensor %d: q must be 8-byte aligned", t);
+        if (!is_aligned(d.scale_inv, 4) || !is_aligned(d.amax, 4))
+            return fail(FP8_ERR_MISALIGNED, "tensor %d: scale_inv and amax must be 4-byte aligned", t);
+        if (d.diag != nullptr && !is_aligned(d.diag, 4))
+            return fail(FP8_ERR_MISALIGNED, "tensor %d: diag must be 4-byte aligned", t);
+        a.x[t] = d.x; a.elems[t] = elems; a.q[t] = d.q;
+        a.scale_inv[t] = d.scale_inv; a.amax[t] = d.amax; a.diag[t] = d.diag;
+    }
+    uint32_t* scratch = nullptr;
+    fp8_status st = check_workspace(true, workspace, workspace_bytes, &scratch);
+    if (st != FP8_OK) return st;
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != FP8_OK) return st;
+    a.n = count; a.in_bf16 = in_dtype == FP8_IN_BF16; a.fmt = fmt; a.pow2 = (flags & FP8_SCALE_POW2) != 0;
+    a.scratch = scratch; a.stream = (hipStream_t)stream; a.num_cus = cus;
+    return launch_result(fp8mi::launch_quantize_multi(a), "fp8_quantize_tensors");
+}
+
 static fp8_status check_gemm_common(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, int64_t M,
                                     int64_t N, int64_t K, const float* sa, const float* sb, void* C,
                                     int out_dtype, int64_t ldc) {

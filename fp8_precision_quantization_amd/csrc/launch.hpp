@@ -32,6 +32,24 @@ struct QuantArgs {
     int num_cus = 256;
 };
 
+// fp8_quantize_tensors: just-in-time per-tensor quantization of up to
+// FP8_MAX_TENSORS contiguous tensors in one amax launch and one cast launch.
+struct MultiQuantArgs {
+    int n = 0;
+    bool in_bf16 = true;
+    int fmt = 0;
+    bool pow2 = false;
+    const void* x[FP8_MAX_TENSORS] = {};
+    int64_t elems[FP8_MAX_TENSORS] = {};
+    uint8_t* q[FP8_MAX_TENSORS] = {};
+    float* scale_inv[FP8_MAX_TENSORS] = {};
+    float* amax[FP8_MAX_TENSORS] = {};
+    fp8_diag* diag[FP8_MAX_TENSORS] = {};
+    uint32_t* scratch = nullptr;
+    hipStream_t stream = nullptr;
+    int num_cus = 256;
+};
+
 struct GemmArgs {
     const uint8_t* A = nullptr;
     const uint8_t* B = nullptr;
@@ -86,6 +104,7 @@ struct KvLoadArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a);
+hipError_t launch_quantize_multi(const MultiQuantArgs& a);
 // Address on the current device of the workspace fp8_quantize_noalloc uses
 // (a device array of kScratchWords words); taken once per device.
 hipError_t static_workspace(uint32_t** out);

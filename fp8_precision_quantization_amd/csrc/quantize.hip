@@ -26,6 +26,7 @@ namespace fp8mi {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMultiMax = FP8_MAX_TENSORS;
 // Transposed cast: workgroups per CU (a workgroup's 4 waves take one SIMD
 // each, so also the waves per SIMD its registers must allow).
 constexpr int kTBlocksPerCU = 4;
@@ -226,10 +227,14 @@ constexpr int kUnroll = 4;
 // consecutive loads in the same DRAM pages; measured on 1 GiB, contiguous
 // runs read at about 7.0 TB/s for 2 to 16 blocks per CU, where a
 // grid-stride loop over the same units falls to 5.2-5.9 TB/s at 4 to 8.
-__device__ __forceinline__ void flat_run(uint32_t whole, uint32_t chunk, uint32_t& beg, uint32_t& end) {
-    const uint64_t b = (uint64_t)blockIdx.x * chunk, e = b + chunk;
+__device__ __forceinline__ void flat_run_of(uint32_t blk, uint32_t whole, uint32_t chunk, uint32_t& beg,
+                                            uint32_t& end) {
+    const uint64_t b = (uint64_t)blk * chunk, e = b + chunk;
     beg = (uint32_t)(b < whole ? b : whole);
     end = (uint32_t)(e < whole ? e : whole);
+}
+__device__ __forceinline__ void flat_run(uint32_t whole, uint32_t chunk, uint32_t& beg, uint32_t& end) {
+    flat_run_of(blockIdx.x, whole, chunk, beg, end);
 }
 
 // The units [it + t, it + t + kThreads, ...) of one loop iteration of a flat
@@ -450,6 +455,93 @@ __global__ __launch_bounds__(kThreads) void k_cast_tensor(
     if constexpr (DELAYED) {
         const uint32_t bm = block_max(m, lds);
         if (threadIdx.x == 0) partials_out[blockIdx.x] = bm;
+    }
+}
+
+// Several contiguous tensors quantized just in time, each with its own
+// per-tensor scale, in one amax launch and one cast launch.  Each tensor
+// owns a run of consecutive blocks in both grids (first[t] .. first[t+1]),
+// at least one even when empty, and each of its blocks streams `chunk`
+// whole units of it exactly as the single-tensor flat kernels do; the
+// tensor's first block takes its ragged last unit.  The amax pass leaves
+// one partial per block; a cast block reduces its own tensor's partials.
+struct MultiSet {
+    const void* x[kMultiMax];
+    uint8_t* q[kMultiMax];
+    float* scale_inv[kMultiMax];
+    float* amax[kMultiMax];
+    fp8_diag* diag[kMultiMax];
+    uint32_t whole[kMultiMax];          // whole 8-element units
+    uint32_t tail[kMultiMax];           // elements of a ragged last unit, 0..7
+    uint32_t afirst[kMultiMax + 1];     // first amax-pass block of each tensor; afirst[n] = grid
+    uint32_t cfirst[kMultiMax + 1];     // first cast-pass block of each tensor; cfirst[n] = grid
+    uint32_t achunk, cchunk;
+    int n;
+};
+
+// The tensor whose block run holds block b (runs are non-empty and in order).
+__device__ __forceinline__ int multi_tensor_of(const uint32_t* first, int n, uint32_t b) {
+    int t = 0;
+    for (int i = 1; i < n; ++i) t += b >= first[i] ? 1 : 0;
+    return t;
+}
+
+template <typename InT>
+__global__ __launch_bounds__(kThreads) void k_amax_multi(MultiSet ms, uint32_t* __restrict__ partials) {
+    __shared__ uint32_t lds[16];
+    const int t = multi_tensor_of(ms.afirst, ms.n, blockIdx.x);
+    const uint32_t blk = blockIdx.x - ms.afirst[t];
+    const InT* __restrict__ x = static_cast<const InT*>(ms.x[t]);
+    const uint32_t whole = ms.whole[t];
+    uint32_t beg, end;
+    flat_run_of(blk, whole, ms.achunk, beg, end);
+    uint32_t m = 0;
+    for (uint32_t it = beg; it < end; it += kThreads * kUnroll) {
+        Pack<InT> p[kUnroll];
+        load_iteration(x, it, end, p);
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) m = max(m, p[i].abs_max());
+    }
+    if (blk == 0 && threadIdx.x == 0 && ms.tail[t] != 0)
+        m = max(m, load_unit<InT>(x, (int64_t)whole * 8, (int)ms.tail[t], false).abs_max());
+    const uint32_t bm = block_max(m, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = bm;
+}
+
+template <typename InT, int FMT, bool DIAG>
+__global__ __launch_bounds__(kThreads) void k_cast_multi(MultiSet ms, const uint32_t* __restrict__ partials,
+                                                         bool pow2) {
+    __shared__ uint32_t lds[16];
+    const int t = multi_tensor_of(ms.cfirst, ms.n, blockIdx.x);
+    const uint32_t blk = blockIdx.x - ms.cfirst[t];
+    const uint32_t am = reduce_partials(partials + ms.afirst[t], (int)(ms.afirst[t + 1] - ms.afirst[t]), lds);
+    const float s = scale_from_amax_bits<FMT>(am, pow2);
+    if (blk == 0 && threadIdx.x == 0) {
+        ms.amax[t][0] = __uint_as_float(am);
+        ms.scale_inv[t][0] = recip_rn(s);
+    }
+    const InT* __restrict__ x = static_cast<const InT*>(ms.x[t]);
+    uint8_t* __restrict__ q = ms.q[t];
+    const uint32_t whole = ms.whole[t];
+    uint32_t beg, end;
+    flat_run_of(blk, whole, ms.cchunk, beg, end);
+    Counters cnt;
+    for (uint32_t it = beg; it < end; it += kThreads * kUnroll) {
+        Pack<InT> p[kUnroll];
+        load_iteration(x, it, end, p);
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const uint32_t u = it + threadIdx.x + i * kThreads;
+            if (u < end) store_flat(q, u, encode_unit<FMT, DIAG>(p[i], s, cnt));
+        }
+    }
+    if (blk == 0 && threadIdx.x == 0 && ms.tail[t] != 0) {
+        const int64_t off = (int64_t)whole * 8;
+        const int nv = (int)ms.tail[t];
+        store_unit(q, off, nv, false, encode_unit<FMT, DIAG>(load_unit<InT>(x, off, nv, false), s, cnt));
+    }
+    if constexpr (DIAG) {
+        if (ms.diag[t] != nullptr) block_add_diag(cnt, lds, ms.diag[t]);
     }
 }
 
@@ -1018,6 +1110,57 @@ hipError_t launch_quantize(const QuantArgs& a) {
         return a.fmt == 0 ? quantize_typed<uint16_t, kE4M3>(a) : quantize_typed<uint16_t, kE5M2>(a);
     }
     return a.fmt == 0 ? quantize_typed<float, kE4M3>(a) : quantize_typed<float, kE5M2>(a);
+}
+
+// Grids of fp8_quantize_tensors: one chunk length per pass for all tensors
+// (the single-tensor flat grid's, taken over the tensors' total units), so
+// every block but a tensor's last streams the same number of units, and
+// each tensor gets the blocks its units need (at least one).
+template <typename InT, int FMT>
+hipError_t quantize_multi_typed(const MultiQuantArgs& a) {
+    MultiSet ms = {};
+    ms.n = a.n;
+    int64_t total = 0;
+    for (int t = 0; t < a.n; ++t) {
+        ms.x[t] = a.x[t];
+        ms.q[t] = a.q[t];
+        ms.scale_inv[t] = a.scale_inv[t];
+        ms.amax[t] = a.amax[t];
+        ms.diag[t] = a.diag[t];
+        ms.whole[t] = (uint32_t)(a.elems[t] / 8);
+        ms.tail[t] = (uint32_t)(a.elems[t] % 8);
+        total += a.elems[t] / 8;
+    }
+    const unsigned cap = (unsigned)std::min<int64_t>((int64_t)a.num_cus * 8, kMaxCastBlocks);
+    flat_grid(total, kMaxAmaxBlocks, &ms.achunk);
+    flat_grid(total, cap, &ms.cchunk);
+    ms.afirst[0] = ms.cfirst[0] = 0;
+    for (int t = 0; t < a.n; ++t) {
+        const uint32_t w = ms.whole[t];
+        ms.afirst[t + 1] = ms.afirst[t] + std::max<uint32_t>(1u, (w + ms.achunk - 1) / ms.achunk);
+        ms.cfirst[t + 1] = ms.cfirst[t] + std::max<uint32_t>(1u, (w + ms.cchunk - 1) / ms.cchunk);
+    }
+    // at most kMaxAmaxBlocks + kMultiMax partials: inside the workspace's partials region
+    static_assert(kMaxAmaxBlocks + kMultiMax <= kScratchDiag - kScratchAmaxPartials, "scratch layout");
+    uint32_t* partials = a.scratch + kScratchAmaxPartials;
+    hipStream_t st = a.stream;
+    hipLaunchKernelGGL((k_amax_multi<InT>), dim3(ms.afirst[a.n]), dim3(kThreads), 0, st, ms, partials);
+    bool diag = false;
+    for (int t = 0; t < a.n; ++t) diag = diag || a.diag[t] != nullptr;
+    if (diag)
+        hipLaunchKernelGGL((k_cast_multi<InT, FMT, true>), dim3(ms.cfirst[a.n]), dim3(kThreads), 0, st, ms,
+                           (const uint32_t*)partials, a.pow2);
+    else
+        hipLaunchKernelGGL((k_cast_multi<InT, FMT, false>), dim3(ms.cfirst[a.n]), dim3(kThreads), 0, st, ms,
+                           (const uint32_t*)partials, a.pow2);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_multi(const MultiQuantArgs& a) {
+    if (a.in_bf16) {
+        return a.fmt == 0 ? quantize_multi_typed<uint16_t, kE4M3>(a) : quantize_multi_typed<uint16_t, kE5M2>(a);
+    }
+    return a.fmt == 0 ? quantize_multi_typed<float, kE4M3>(a) : quantize_multi_typed<float, kE5M2>(a);
 }
 
 // The workspace of fp8_quantize_noalloc: 64 KiB of device memory in the

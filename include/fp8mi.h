@@ -29,14 +29,14 @@
  *     of the calls that need one.  The library never allocates, frees or
  *     synchronizes.
  *   - Workspace: the per-tensor reductions of fp8_amax / fp8_quantize /
- *     fp8_quantize_dual (FP8_GRAN_TENSOR) and the grouped GEMM's tile table
- *     need `workspace`, device memory of at least fp8_workspace_size() bytes,
- *     16-byte aligned (else FP8_ERR_INVALID_ARG / FP8_ERR_MISALIGNED).  It
- *     needs no initialization and holds nothing the caller reads; a call
- *     owns it from launch until its kernels finish, so calls in flight at
- *     the same time (different streams) need different workspaces, while
- *     calls ordered on one stream can share one.  Calls that do not need it
- *     accept NULL.
+ *     fp8_quantize_dual (FP8_GRAN_TENSOR) / fp8_quantize_tensors and the
+ *     grouped GEMM's tile table need `workspace`, device memory of at least
+ *     fp8_workspace_size() bytes, 16-byte aligned (else FP8_ERR_INVALID_ARG
+ *     / FP8_ERR_MISALIGNED).  It needs no initialization and holds nothing
+ *     the caller reads; a call owns it from launch until its kernels
+ *     finish, so calls in flight at the same time (different streams) need
+ *     different workspaces, while calls ordered on one stream can share one.
+ *     Calls that do not need it accept NULL.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call is asynchronous: it returns after host-side validation and
  *     the kernel launches.  A fault inside a kernel surfaces at the caller's
@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FP8MI_ABI_VERSION 6
+#define FP8MI_ABI_VERSION 7
 
 typedef enum {
     FP8_OK = 0,
@@ -234,6 +234,40 @@ fp8_status fp8_quantize_dual(const void* x, fp8_in_dtype in_dtype, int64_t rows,
                              fp8_format fmt, uint32_t flags, fp8_amax_history* hist, uint8_t* q, int64_t ldq,
                              uint8_t* qt, int64_t ldqt, float* scale_inv_out, float* amax_out, fp8_diag* diag,
                              void* workspace, int64_t workspace_bytes, void* stream);
+
+/* One tensor of fp8_quantize_tensors (a host-side descriptor; its pointers
+ * are device pointers).  x: [rows x cols] contiguous (no leading dimension),
+ * 16-byte aligned.  q: [rows x cols] uint8 codes, contiguous, 8-byte
+ * aligned.  scale_inv, amax: one fp32 each (4-byte aligned).  diag: optional
+ * counters (NULL to skip), as fp8_quantize. */
+typedef struct fp8_tensor {
+    const void* x;
+    int64_t rows;
+    int64_t cols;
+    uint8_t* q;
+    float* scale_inv;
+    float* amax;
+    fp8_diag* diag;
+} fp8_tensor;
+
+#define FP8_MAX_TENSORS 8
+
+/* Just-in-time per-tensor quantization of up to FP8_MAX_TENSORS tensors in
+ * two launches, whatever their number: one amax pass over all of them, then
+ * one cast pass.  A GEMM's operands are cast to FP8 together before it
+ * ([DeepL] 2.2; [Swift] dynamic per-tensor), each with its own factor
+ * ([DeepL] 2.3, tensor granularity), so the activation and the weight of a
+ * layer can share the launches.  Each tensor's amax, scale_inv and codes
+ * are those fp8_quantize gives it with FP8_GRAN_TENSOR and no history, bit
+ * for bit.
+ * tensors: HOST array of `count` descriptors (1..FP8_MAX_TENSORS), read
+ * during the call only.  All tensors share in_dtype and fmt; flags:
+ * FP8_SCALE_POW2 only.  Tensors may be empty (amax 0, scale_inv 1).  Each
+ * tensor's outputs must not overlap any input or another tensor's outputs.
+ * workspace: required (see the conventions above).  Errors name the tensor
+ * by its index. */
+fp8_status fp8_quantize_tensors(const fp8_tensor* tensors, int32_t count, fp8_in_dtype in_dtype, fp8_format fmt,
+                                uint32_t flags, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Scaled FP8 GEMM ([H100] FP8 matrix multiply-add in hardware; [Soup]
  * tensorwise and rowwise GEMMs; [DeepL] 2.2 results return to high

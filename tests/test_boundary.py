@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import shutil
 import subprocess
 
 import pytest
@@ -49,7 +50,7 @@ def test_library_is_gfx950_only_code_object():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.fp8_abi_version() == 6
+    assert lib.fp8_abi_version() == 7
     assert lib.fp8_workspace_size() == L.WORKSPACE_BYTES
     for code, name in [(0, "FP8_OK"), (1, "FP8_ERR_INVALID_ARG"), (2, "FP8_ERR_UNSUPPORTED_SHAPE"),
                        (3, "FP8_ERR_MISALIGNED"), (4, "FP8_ERR_UNSUPPORTED_DEVICE"), (5, "FP8_ERR_HIP")]:
@@ -128,6 +129,75 @@ def test_quantize_dual_validation(kw, status, needle):
     st, msg = qd(**kw)
     assert st == status, (st, msg)
     assert needle in msg
+
+
+def qt(descs=None, count=None, in_dt=L.FP8_IN_BF16, fmt=L.FP8_E4M3, flags=0, ws=FAKE,
+       ws_bytes=L.WORKSPACE_BYTES, **kw):
+    """fp8_quantize_tensors on two fake 64 x 96 tensors; kw overrides fields
+    of tensor 1 (the second), so errors must name index 1."""
+    if descs is None:
+        descs = [dict(x=FAKE, rows=64, cols=96, q=FAKE, scale_inv=FAKE, amax=FAKE, diag=None) for _ in range(2)]
+        descs[1].update(kw)
+    arr = (L.Fp8Tensor * max(len(descs), 1))(*[L.Fp8Tensor(**d) for d in descs])
+    ptr = ctypes.cast(arr, ctypes.c_void_p) if descs else None
+    st = L.lib().fp8_quantize_tensors(ptr, len(descs) if count is None else count, in_dt, fmt, flags, ws,
+                                      ws_bytes, None)
+    return st, L.lib().fp8_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), 1, "tensor 1: x is NULL"),
+    (dict(q=None), 1, "tensor 1: q is NULL"),
+    (dict(scale_inv=None), 1, "tensor 1: scale_inv is NULL"),
+    (dict(amax=None), 1, "tensor 1: amax is NULL"),
+    (dict(rows=-2), 1, "tensor 1: negative"),
+    (dict(cols=2 ** 31 + 1), 2, "tensor 1: rows and cols"),
+    (dict(rows=2 ** 31, cols=2 ** 31), 2, "tensor 1 too large"),
+    (dict(x=FAKE + 8), 3, "tensor 1: x must be 16-byte aligned"),
+    (dict(q=FAKE + 4), 3, "tensor 1: q must be 8-byte aligned"),
+    (dict(amax=FAKE + 2), 3, "tensor 1: scale_inv and amax"),
+    (dict(diag=FAKE + 2), 3, "tensor 1: diag"),
+    (dict(in_dt=9), 1, "in_dtype"),
+    (dict(fmt=4), 1, "format"),
+    (dict(flags=2), 1, "FP8_SCALE_POW2"),
+    (dict(flags=4), 1, "FP8_SCALE_POW2"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(ws_bytes=1024), 1, "workspace_bytes"),
+    (dict(ws=FAKE + 4), 3, "workspace"),
+    (dict(count=0), 1, "count=0"),
+    (dict(count=9), 1, "count=9"),
+])
+def test_quantize_tensors_validation(kw, status, needle):
+    top = {k: kw.pop(k) for k in ("in_dt", "fmt", "flags", "ws", "ws_bytes", "count") if k in kw}
+    st, msg = qt(**top, **kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_quantize_tensors_null_array_and_empty_tensors_validate():
+    st, msg = qt(descs=[], count=1)
+    assert st == 1 and "tensors is NULL" in msg
+    # empty tensors need no x or q; validation then reaches the device check
+    # (no GPU here), never a launch
+    st, msg = qt(x=None, q=None, rows=0)
+    assert st in (L.FP8_ERR_UNSUPPORTED_DEVICE, L.FP8_ERR_HIP), (st, msg)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc is not installed")
+def test_tensor_descriptor_layout_matches_header(tmp_path):
+    """The binding's fp8_tensor (ctypes) has the header's size and offsets."""
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fp8mi.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu %d\\n", sizeof(fp8_tensor), '
+                   'offsetof(fp8_tensor, x), offsetof(fp8_tensor, rows), offsetof(fp8_tensor, cols), '
+                   'offsetof(fp8_tensor, q), offsetof(fp8_tensor, scale_inv), offsetof(fp8_tensor, amax), '
+                   'offsetof(fp8_tensor, diag), FP8_MAX_TENSORS); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(L.HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    T = L.Fp8Tensor
+    want = [ctypes.sizeof(T)] + [getattr(T, f).offset for f, _ in T._fields_] + [L.MAX_TENSORS]
+    assert got == want
 
 
 def gg(**kw):
