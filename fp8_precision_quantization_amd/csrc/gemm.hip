@@ -224,20 +224,25 @@ struct DmaL {
     }
     // issue_full with the lane's offset formed here from an opaque copy of
     // its base, so that the compiler keeps two base registers live instead of
-    // one precomputed offset per instruction
+    // one precomputed offset per instruction.  Every DMA of the GEMM kernels
+    // goes through it: precomputed offsets are spilled across the epilogue,
+    // and each reload's wait (vector-memory operations complete in issue
+    // order) would also wait for the tile's stores of C and the DMA in flight.
     __device__ __forceinline__ void issue_full_lean(uint32_t slot, int k0, int i) const {
         uint32_t b = base[i & 1];
         asm volatile("" : "+v"(b));
         dma16(slot + lds0 + (uint32_t)(8 * i * kBK2), b + (uint32_t)i * ld8, rsrc, (uint32_t)k0);
     }
     __device__ __forceinline__ void issue_checked(uint32_t slot, int k0, int K, int i) const {
-        const uint32_t o = (k0 + col_of(i) < K) ? off(i) + (uint32_t)k0 : kOOB;
+        uint32_t b = base[i & 1];
+        asm volatile("" : "+v"(b));
+        const uint32_t o = (k0 + col_of(i) < K) ? b + (uint32_t)i * ld8 + (uint32_t)k0 : kOOB;
         dma16(slot + lds0 + (uint32_t)(8 * i * kBK2), o, rsrc, 0u);
     }
     __device__ __forceinline__ void issue(uint32_t slot, int k0, int K) const {
         if (k0 + kBK2 <= K) {
 #pragma unroll
-            for (int i = 0; i < kInst; ++i) issue_full(slot, k0, i);
+            for (int i = 0; i < kInst; ++i) issue_full_lean(slot, k0, i);
         } else {
 #pragma unroll
             for (int i = 0; i < kInst; ++i) issue_checked(slot, k0, K, i);
@@ -253,7 +258,7 @@ struct FullDma {
     const D* d;
     uint32_t slot;
     int k0;
-    __device__ __forceinline__ void operator()(int i) const { d->issue_full(slot, k0, i); }
+    __device__ __forceinline__ void operator()(int i) const { d->issue_full_lean(slot, k0, i); }
 };
 
 // The same for the last stages: `on` and `full` are wave-uniform.
@@ -266,7 +271,7 @@ struct TailDma {
     bool on, full;
     __device__ __forceinline__ void operator()(int i) const {
         if (on) {
-            if (full) d->issue_full(slot, k0, i);
+            if (full) d->issue_full_lean(slot, k0, i);
             else d->issue_checked(slot, k0, K, i);
         }
     }
@@ -495,11 +500,14 @@ template <bool OUT_BF16, int BM>
 __device__ __forceinline__ void epilogue_slot(const GemmParams& p, float sa0, float sb0,
                                               const v16f (&acc)[4][BM / 64], int m0, int n0, int wm, int wn, int wave,
                                               int lane_in, uint8_t* slot, bool interior) {
-    // an opaque copy of the lane id: the per-lane address arithmetic stays
-    // here instead of being hoisted out of the tile loop (where it would
-    // hold registers across the whole K loop)
-    int lane = lane_in;
-    asm volatile("" : "+v"(lane));
+    // the lane id formed here from the execution mask (every lane is
+    // active), opaquely: the per-lane address arithmetic stays here instead
+    // of being hoisted out of the tile loop, and no register keeps the id
+    // live across the K loop (a spilled id would come back through a
+    // scratch load, whose wait also waits for every DMA and store in flight)
+    (void)lane_in;
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
     const int mode = (p.sa_row ? 1 : 0) | (p.sb_row ? 2 : 0);
     if (mode == 0)
         epilogue_body<OUT_BF16, 0, BM>(p, p.sb, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, slot, interior);
