@@ -899,7 +899,6 @@ constexpr int kBQB = 2 * kBQSlot;                // LDS: A0 | A1 | B0 | B1 | sca
 constexpr int kBQScale = 8 * 256;                // 8 waves x 64 lanes x 4 bytes (32 rows used per wave)
 constexpr int kBQS = 4 * kBQSlot;
 constexpr int kBQLds = kBQS + 2 * kBQScale;
-constexpr int kBQPer = 2 * DmaL<256, 8>::kInst + 1;   // DMA instructions per wave per stage
 
 // One LDS fragment read at a per-lane address plus a constant offset.
 __device__ __forceinline__ uint4 lds_read16(uint32_t addr, int imm) {
@@ -911,19 +910,31 @@ __device__ __forceinline__ uint4 lds_read16(uint32_t addr, int imm) {
 // One stage of k_gemm_bq from buffer Q (the K loop is unrolled by two, so
 // every LDS offset is a constant): column blocks 0-2 with the next column
 // block's B streaming in, then the barrier, then column block 3 with the
-// DMA of stage s+2 into this buffer and the reads of stage s+1.
+// DMA of stage s+2 into this buffer and the reads of stage s+1.  RB: 32-row
+// blocks per wave (2 in a 256-row tile, 1 in a 128-row tile).
+template <int RB>
 struct BQState {
-    v16f acc[4][2];     // [column block j][row block i]
+    v16f acc[4][RB];    // [column block j][row block i]
     v16f part;          // partial sum of the latest output block
-    v8i a[2][2];        // A fragments of the stage: [row block][64-wide half]
+    v8i a[RB][2];       // A fragments of the stage: [row block][64-wide half]
     v8i bc[2], bn[2];   // B fragments of the current / next column block: [half]
-    float sc[2];        // promotion scales of this stage, per row block
+    float sc[RB];       // promotion scales of this stage, per row block
 };
 
-template <int Q, typename ISSUE>
-__device__ __forceinline__ void bq_stage(BQState& t, const uint32_t (&la)[2][2], const uint32_t (&lb)[2][2],
+// DMA instructions per wave per stage of a (128 RB)-row tile: A rows, B
+// rows, then one for the A-row scales.
+template <int RB>
+struct BQDma {
+    using DA = DmaL<128 * RB, 8>;
+    using DB = DmaL<256, 8>;
+    static constexpr int kA = DA::kInst, kB = DB::kInst, kPer = kA + kB + 1;
+};
+
+template <int Q, int RB, typename ISSUE>
+__device__ __forceinline__ void bq_stage(BQState<RB>& t, const uint32_t (&la)[2][2], const uint32_t (&lb)[2][2],
                                          uint32_t lsc, bool more, bool fill, float sbn,
                                          const ISSUE& issue) {
+    constexpr int kA = BQDma<RB>::kA, kB = BQDma<RB>::kB, kS = kA + kB;   // kS: the scale DMA
     auto read_b = [&](v8i (&b)[2], int q, int j) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -963,60 +974,80 @@ __device__ __forceinline__ void bq_stage(BQState& t, const uint32_t (&la)[2][2],
         block_mma(0);
         if (jj == 1 && fill) {
 #pragma unroll
-            for (int d = 0; d < 3; ++d) issue(d);
+            for (int d = 0; d < (RB == 2 ? kA - 1 : kA); ++d) issue(d);
+            if constexpr (RB == 1) issue(kS);
         }
         promote(jj, 0, t.sc[0]);
         __builtin_amdgcn_sched_barrier(0);
-        block_mma(1);
-        if (jj == 1 && fill) {
-            issue(3);
-            issue(8);
+        if constexpr (RB == 2) {
+            block_mma(1);
+            if (jj == 1 && fill) {
+                issue(kA - 1);
+                issue(kS);
+            }
+            promote(jj, 1, t.sc[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        promote(jj, 1, t.sc[1]);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) t.bc[h] = t.bn[h];
     }
     // column block 3: stage s+1 has landed (only this stage's A and scale
     // DMA may still fly) and every wave is done reading this buffer's B
     // (the last B reads were waited for here)
-    if (fill) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DmaL<256, 8>::kInst + 1) : "memory");
+    if (fill) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kA + 1) : "memory");
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     asm volatile("" : "+s"(sbn));
     block_mma(0);
     if (fill) {
 #pragma unroll
-        for (int d = 4; d < 6; ++d) issue(d);
+        for (int d = kA; d < kA + kB / 2; ++d) issue(d);
     }
     promote(3, 0, t.sc[0]);
     __builtin_amdgcn_sched_barrier(0);
-    float san0 = 0.0f, san1 = 0.0f;
+    float san[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) san[i] = 0.0f;
     if (more) {
         read_b(t.bn, Q ^ 1, 0);
         read_a(Q ^ 1, 0);
-        san0 = *reinterpret_cast<const LDS_AS float*>((uintptr_t)(lsc + (uint32_t)((Q ^ 1) * kBQScale)));
-        san1 = *reinterpret_cast<const LDS_AS float*>((uintptr_t)(lsc + (uint32_t)((Q ^ 1) * kBQScale + 256)));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    block_mma(1);
-    if (fill) {
 #pragma unroll
-        for (int d = 6; d < 8; ++d) issue(d);
+        for (int i = 0; i < RB; ++i)
+            san[i] = *reinterpret_cast<const LDS_AS float*>(
+                (uintptr_t)(lsc + (uint32_t)((Q ^ 1) * kBQScale + i * 256)));
     }
-    promote(3, 1, t.sc[1]);
     __builtin_amdgcn_sched_barrier(0);
-    if (more) read_a(Q ^ 1, 1);
+    if constexpr (RB == 2) {
+        block_mma(1);
+        if (fill) {
+#pragma unroll
+            for (int d = kA + kB / 2; d < kS; ++d) issue(d);
+        }
+        promote(3, 1, t.sc[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) read_a(Q ^ 1, 1);
+    } else {
+        if (fill) {
+#pragma unroll
+            for (int d = kA + kB / 2; d < kS; ++d) issue(d);
+        }
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) t.bc[h] = t.bn[h];
-    t.sc[0] = san0 * sbn;
-    t.sc[1] = san1 * sbn;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) t.sc[i] = san[i] * sbn;
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kBQThreads, 1) void k_gemm_bq(GemmParams p) {
-    using D = DmaL<256, 8>;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+// One (128 RB) x 256 tile of k_gemm_bq at rows m0, columns n0: eight waves
+// as 4 x 2, each (32 RB) rows x 128 columns.  RB = 1 serves the last round
+// of a grid whose remaining tiles fill at most half of it, as half tiles:
+// every output's K sum is the same chain of MFMAs and promotions as in a
+// whole tile.
+template <int RB, bool OUT_BF16>
+__device__ __forceinline__ void bq_tile(const GemmParams& p, int m0, int n0, int wave, int wm, int wn) {
+    using Dm = BQDma<RB>;
+    typename Dm::DA da;
+    typename Dm::DB db;
+    const int lane = threadIdx.x & 63;
     const int K = p.K;
     const int nks = K / kBK2;                    // stages (128-wide K blocks) per tile
     const int nbn = p.N / 128;                   // 128-row blocks of B
@@ -1033,89 +1064,113 @@ __global__ __launch_bounds__(kBQThreads, 1) void k_gemm_bq(GemmParams p) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int ra = wm * 64 + r32, rb = wn * 128 + r32;
+                const int ra = wm * (32 * RB) + r32, rb = wn * 128 + r32;
                 const int c = 4 * h + 2 * (lane >> 5) + e;
                 la[h][e] = ring + (uint32_t)(ra * kBK2 + ((c ^ swz2(ra)) << 4));
                 lb[h][e] = ring + (uint32_t)(kBQB + rb * kBK2 + ((c ^ swz2(rb)) << 4));
                 asm volatile("" : "+v"(la[h][e]), "+v"(lb[h][e]));
             }
     }
-    // this lane's A-row scale of row block 0 in buffer 0 (row block 1: +256 bytes)
-    uint32_t lsc = ring + (uint32_t)(kBQS + (wm * 2) * 256 + (lane & 31) * 4);
+    // this lane's A-row scale of row block 0 in buffer 0 (row block 1: +256
+    // bytes): wave w's scale DMA fills rows 32 w .. 32 w + 31
+    uint32_t lsc = ring + (uint32_t)(kBQS + (wm * RB) * 256 + (lane & 31) * 4);
     asm volatile("" : "+v"(lsc));
 
-    int tm, tn;
-    const int limit = p.tiles_m * p.tiles_n;
-    for (int r = 0; tile_of_round(p, p.tiles_m, p.group_m, limit, r, tm, tn); ++r) {
-        const int m0 = tm * 256, n0 = tn * 256;
-        D da, db;
-        da.init(p.A, p.lda, m0, p.M, wave);
-        db.init(p.B, p.ldb, n0, p.N, wave);
-        // this wave's DMA of A-row scales: rows 32 w + lane (lanes 0-31)
-        const int rows_here = max(0, min(256, p.M - m0));
-        const v4i sa_rsrc = make_rsrc(p.sa + (int64_t)m0 * nks, (uint32_t)((int64_t)rows_here * nks * 4));
-        const int srow = wave * 32 + lane;
-        const uint32_t sa_off0 = (lane < 32 && srow < rows_here) ? (uint32_t)(srow * nks * 4) : kOOB;
-        // the B scales of this wave's 128 columns (a block past N is never stored)
-        const float* sbw = p.sb + (int64_t)min((n0 + wn * 128) / 128, nbn - 1) * nks;
-        auto issue_one = [&](int st, int q, int d) {
-            if (d < D::kInst) da.issue_full_lean(ring + (uint32_t)(q * kBQSlot), st * kBK2, d);
-            else if (d < 2 * D::kInst) db.issue_full_lean(ring + (uint32_t)(kBQB + q * kBQSlot), st * kBK2, d - D::kInst);
-            else dma4(ring + (uint32_t)(kBQS + q * kBQScale + wave * 256),
-                      sa_off0 == kOOB ? kOOB : sa_off0 + (uint32_t)(st * 4), sa_rsrc);
-        };
+    da.init(p.A, p.lda, m0, p.M, wave);
+    db.init(p.B, p.ldb, n0, p.N, wave);
+    // this wave's DMA of A-row scales: rows 32 w + lane (lanes 0-31)
+    const int rows_here = max(0, min(128 * RB, p.M - m0));
+    const v4i sa_rsrc = make_rsrc(p.sa + (int64_t)m0 * nks, (uint32_t)((int64_t)rows_here * nks * 4));
+    const int srow = wave * 32 + lane;
+    const uint32_t sa_off0 = (lane < 32 && srow < rows_here) ? (uint32_t)(srow * nks * 4) : kOOB;
+    // the B scales of this wave's 128 columns (a block past N is never stored)
+    const float* sbw = p.sb + (int64_t)min((n0 + wn * 128) / 128, nbn - 1) * nks;
+    auto issue_one = [&](int st, int q, int d) {
+        if (d < Dm::kA) da.issue_full_lean(ring + (uint32_t)(q * kBQSlot), st * kBK2, d);
+        else if (d < Dm::kA + Dm::kB)
+            db.issue_full_lean(ring + (uint32_t)(kBQB + q * kBQSlot), st * kBK2, d - Dm::kA);
+        else dma4(ring + (uint32_t)(kBQS + q * kBQScale + wave * 256),
+                  sa_off0 == kOOB ? kOOB : sa_off0 + (uint32_t)(st * 4), sa_rsrc);
+    };
 
-        // prologue: stages 0 and 1 in flight, wait for stage 0
-        BQState t;
-        const float sb0 = load_uniform(sbw);
+    // prologue: stages 0 and 1 in flight, wait for stage 0
+    BQState<RB> t;
+    const float sb0 = load_uniform(sbw);
 #pragma unroll
-        for (int d = 0; d < kBQPer; ++d) issue_one(0, 0, d);
-        if (nks > 1) {
+    for (int d = 0; d < Dm::kPer; ++d) issue_one(0, 0, d);
+    if (nks > 1) {
 #pragma unroll
-            for (int d = 0; d < kBQPer; ++d) issue_one(1, 1, d);
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kBQPer) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        }
-        t.sc[0] = *reinterpret_cast<const LDS_AS float*>((uintptr_t)lsc) * sb0;
-        t.sc[1] = *reinterpret_cast<const LDS_AS float*>((uintptr_t)(lsc + 256u)) * sb0;
+        for (int d = 0; d < Dm::kPer; ++d) issue_one(1, 1, d);
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Dm::kPer) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RB; ++i)
+        t.sc[i] = *reinterpret_cast<const LDS_AS float*>((uintptr_t)(lsc + (uint32_t)(i * 256))) * sb0;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) set_half(t.a[i][h], e, lds_read16(la[h][e], i * 32 * kBK2));
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) set_half(t.bc[h], e, lds_read16(lb[h][e], 0));
+            for (int e = 0; e < 2; ++e) set_half(t.a[i][h], e, lds_read16(la[h][e], i * 32 * kBK2));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int e = 0; e < 2; ++e) set_half(t.bc[h], e, lds_read16(lb[h][e], 0));
 #pragma unroll
-                for (int q = 0; q < 16; ++q) t.acc[j][i][q] = 0.0f;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) t.acc[j][i][q] = 0.0f;
 
-        for (int s = 0; s < nks; s += 2) {
-            {
-                const float sbn = s + 1 < nks ? load_uniform(sbw + s + 1) : 0.0f;
-                auto iss = [&](int d) { issue_one(s + 2, 0, d); };
-                bq_stage<0>(t, la, lb, lsc, s + 1 < nks, s + 2 < nks, sbn, iss);
-            }
-            if (s + 1 < nks) {
-                const float sbn = s + 2 < nks ? load_uniform(sbw + s + 2) : 0.0f;
-                auto iss = [&](int d) { issue_one(s + 3, 1, d); };
-                bq_stage<1>(t, la, lb, lsc, s + 2 < nks, s + 3 < nks, sbn, iss);
-            }
+    for (int s = 0; s < nks; s += 2) {
+        {
+            const float sbn = s + 1 < nks ? load_uniform(sbw + s + 1) : 0.0f;
+            auto iss = [&](int d) { issue_one(s + 2, 0, d); };
+            bq_stage<0, RB>(t, la, lb, lsc, s + 1 < nks, s + 2 < nks, sbn, iss);
         }
-        __syncthreads();
-        // an opaque copy of the lane id: the epilogue's per-lane address
-        // arithmetic stays here instead of being hoisted out of the tile loop
-        int lane_e = lane;
-        asm volatile("" : "+v"(lane_e));
-        const bool interior = p.vec_out && m0 + 256 <= p.M && n0 + 256 <= p.N;
-        epilogue_body<OUT_BF16, 4, 128>(p, p.sb, 1.0f, 1.0f, t.acc, m0, n0, wm, wn, wave, lane_e, g_ring, interior);
-        __syncthreads();          // every wave is done with the staging area
+        if (s + 1 < nks) {
+            const float sbn = s + 2 < nks ? load_uniform(sbw + s + 2) : 0.0f;
+            auto iss = [&](int d) { issue_one(s + 3, 1, d); };
+            bq_stage<1, RB>(t, la, lb, lsc, s + 2 < nks, s + 3 < nks, sbn, iss);
+        }
+    }
+    __syncthreads();
+    // an opaque copy of the lane id: the epilogue's per-lane address
+    // arithmetic stays here instead of being hoisted out of the tile loop
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const bool interior = p.vec_out && m0 + 128 * RB <= p.M && n0 + 256 <= p.N;
+    epilogue_body<OUT_BF16, 4, 64 * RB>(p, p.sb, 1.0f, 1.0f, t.acc, m0, n0, wm, wn, wave, lane_e, g_ring,
+                                        interior);
+    __syncthreads();          // every wave is done with the staging area
+}
+
+// Persistent block-scaled GEMM over 256 x 256 tiles.  When the tiles leave
+// a last round that fills at most half of the grid, that round runs as
+// 128 x 256 halves over the whole grid (both halves of a tile on one XCD).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kBQThreads, 1) void k_gemm_bq(GemmParams p) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int G = gridDim.x;
+    const int T = p.tiles_m * p.tiles_n;
+    const int full = T / G, rem = T % G;
+    const bool halves = full > 0 && rem != 0 && 2 * rem <= G;
+    const int limit = halves ? full * G : T;
+    int tm, tn;
+    for (int r = 0; tile_of_round(p, p.tiles_m, p.group_m, limit, r, tm, tn); ++r)
+        bq_tile<2, OUT_BF16>(p, tm * 256, tn * 256, wave, wm, wn);
+    if (halves) {
+        int b = blockIdx.x;
+        if ((G & 7) == 0) b = (b & 7) * (G >> 3) + (b >> 3);
+        if (b < 2 * rem) {
+            tile_of_linear(p, p.tiles_m, p.group_m, full * G + (b >> 1), tm, tn);
+            const int m0 = tm * 256 + (b & 1) * 128;
+            if (m0 < p.M) bq_tile<1, OUT_BF16>(p, m0, tn * 256, wave, wm, wn);
+        }
     }
 }
 

@@ -304,6 +304,35 @@ def test_gemm_empty_shapes():
 BLOCK_SHAPES = [(1, 128, 128), (37, 256, 384), (300, 128, 128), (256, 384, 1024), (513, 640, 256)]
 
 
+def test_blockscaled_gemm_half_tile_last_round():
+    """300 x 38400 x 256: 300 tiles of 256 x 256 on a 256-workgroup grid
+    leave a last round of 44 tiles, which runs as 128 x 256 halves over the
+    whole grid.  Every output against the oracle, and bit for bit equal to
+    the same rows computed in launches with whole rounds only (256-row
+    slices: 150 tiles, one per workgroup)."""
+    M, N, K = 300, 38400, 256
+    rng = np.random.default_rng(4100)
+    X = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.015).astype(np.float32)
+    qa = oracle.quantize(X, 0, "1x128")
+    qb = oracle.quantize(W, 0, "128x128")
+    A, B = qa["q"], qb["q"]
+    a_inv, b_inv = qa["scale_inv"], qb["scale_inv"]
+    say("blockgemm half-tile last round", M, N, K)
+    dA, dB, dai, dbi = dev_u8(A), dev_u8(B), dev_f32(a_inv), dev_f32(b_inv)
+    y = host(fp8.blockscaled_gemm(dA, dB, dai, dbi, torch.bfloat16))
+    ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    y32, pr = oracle.blockgemm_sampled(A, B, a_inv, b_inv, ms.ravel(), ns.ravel())
+    rep = assert_gemm(y.reshape(-1), y32, pr, K, "bf16", what=f"block {M}x{N}x{K}",
+                      model=gemm_model_at(A, 0, B, 0, a_inv, b_inv, ms.ravel(), ns.ravel(), block=True))
+    print(rep)
+    for r0 in (0, 256):
+        r1 = min(M, r0 + 256)
+        say("blockgemm rows", r0, r1)
+        ys = host(fp8.blockscaled_gemm(dA[r0:r1].contiguous(), dB, dai[r0:r1].contiguous(), dbi, torch.bfloat16))
+        assert np.array_equal(ys, y[r0:r1]), (r0, np.argwhere(ys != y[r0:r1])[:5])
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_blockscaled_gemm_parity(out):
     for i, (M, N, K) in enumerate(BLOCK_SHAPES):
