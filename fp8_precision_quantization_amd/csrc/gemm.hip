@@ -86,6 +86,10 @@ struct GemmParams {
     const int4* gtab;
     int64_t b_gstride;
     int main_grid;        // grouped: the persistent grid, when k_gemm_h takes a last round split off (else 0)
+    // plain persistent launch: the problem's full N when columns [N, tail_N)
+    // run as 128-row half tiles after the whole rounds of columns [0, N)
+    // (else 0)
+    int tail_N;
 };
 
 template <int FX, int FY>
@@ -608,7 +612,7 @@ struct TileRef<true, 256> {
 // GROUPED: the M-tiles are those of the grouped GEMM's table, whose size
 // only the device knows.
 template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
+__device__ __forceinline__ void p_rounds(const GemmParams& p) {
     constexpr int BM = 256, TI = BM / 64;        // tile rows; 32-row MFMA blocks per wave
     int tiles_m = p.tiles_m, group_m = p.group_m;
     // scalar scales (per-tensor modes; the grouped B scale is the tile's)
@@ -756,43 +760,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
 constexpr int kHStage = 128 * kBK2 + 256 * kBK2;      // 48 KiB: A, then B
 constexpr int kHRing = 3 * kHStage;
 
-// GROUPED: the blocks take the grouped GEMM's tiles that the persistent
-// kernel left (its last round, when at most half full: grouped_main_tiles
-// with the grid p.main_grid), block b the half b % 2 of the b/2-th of them;
-// a tile's half past its group's end, and blocks past the tiles, exit.
+// One 128 x 256 tile at rows [m0, m_end) and columns n0.. (m_end: the
+// problem's M, or the end of the tile's group), with B operand Bp and the
+// tile's B scales sbp (per column) or sb0.
 template <int FA, int FB, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
+__device__ __forceinline__ void h_tile(const GemmParams& p, int m0, int m_end, int n0, const uint8_t* Bp,
+                                       const float* sbp, float sa0, float sb0) {
     using DA = DmaL<128>;
     constexpr int kVm1 = DA::kInst + Dma2::kInst;  // A(s+2) and B(s+2) may still fly
-    const float sa0 = load_uniform(p.sa);
-    float sb0;
-    int tm, tn, m0, m_end;
-    const uint8_t* Bp = p.B;
-    const float* sbp = p.sb;
-    if constexpr (GROUPED) {
-        const int tiles_m = min(p.gtab[0].x, p.tiles_m);
-        const int T = tiles_m * p.tiles_n;
-        const int t = grouped_main_tiles(T, p.main_grid) + (int)(blockIdx.x >> 1);
-        if (t >= T) return;
-        tile_of_linear(p, tiles_m, tiles_m < 4 ? tiles_m : 4, t, tm, tn);
-        const int4 e = p.gtab[1 + tm];
-        m0 = e.y + 128 * (int)(blockIdx.x & 1);
-        m_end = e.z;
-        if (m0 >= m_end) return;
-        Bp = p.B + (int64_t)e.x * p.b_gstride;
-        sbp = p.sb + (p.sb_row ? (int64_t)e.x * p.N : (int64_t)e.x);
-        sb0 = load_uniform(sbp);
-    } else {
-        sb0 = load_uniform(p.sb);
-        tile_coords(p, tm, tn);
-        m0 = tm * 128;
-        m_end = p.M;
-    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = p.K;
     const int nks = (K + kBK2 - 1) / kBK2;
-    const int n0 = tn * 256;
     const uint32_t ring = lds_addr(g_ring);
     auto addr = [&](int slot) { return ring + (uint32_t)(slot * kHStage); };
     auto aptr = [&](int slot) { return g_ring + slot * kHStage; };
@@ -865,6 +844,86 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
         epilogue_slot<OUT_BF16, 128>(pt, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
     } else {
         epilogue_slot<OUT_BF16, 128>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
+    }
+}
+
+// k_gemm_h: one 128-row tile per block, over p's tiles (problems with at
+// most half as many 256-row tiles as CUs, or at most 128 rows).  GROUPED:
+// the blocks take the grouped GEMM's tiles that the persistent kernel left
+// (its last round, when at most half full: grouped_main_tiles with the grid
+// p.main_grid), block b the half b % 2 of the b/2-th of them; a tile's half
+// past its group's end, and blocks past the tiles, exit.
+template <int FA, int FB, bool OUT_BF16, bool GROUPED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
+    int tm, tn;
+    if constexpr (GROUPED) {
+        const int tiles_m = min(p.gtab[0].x, p.tiles_m);
+        const int T = tiles_m * p.tiles_n;
+        const int t = grouped_main_tiles(T, p.main_grid) + (int)(blockIdx.x >> 1);
+        if (t >= T) return;
+        tile_of_linear(p, tiles_m, tiles_m < 4 ? tiles_m : 4, t, tm, tn);
+        const int4 e = p.gtab[1 + tm];
+        const int m0 = e.y + 128 * (int)(blockIdx.x & 1);
+        if (m0 >= e.z) return;
+        const uint8_t* Bp = p.B + (int64_t)e.x * p.b_gstride;
+        const float* sbp = p.sb + (p.sb_row ? (int64_t)e.x * p.N : (int64_t)e.x);
+        h_tile<FA, FB, OUT_BF16, true>(p, m0, e.z, tn * 256, Bp, sbp, load_uniform(p.sa), load_uniform(sbp));
+    } else {
+        tile_coords(p, tm, tn);
+        h_tile<FA, FB, OUT_BF16, false>(p, tm * 128, p.M, tn * 256, p.B, p.sb, load_uniform(p.sa),
+                                        load_uniform(p.sb));
+    }
+}
+
+// Which of T half tiles (T <= the grid) this block runs after its whole
+// rounds: every XCD (blocks are dealt to the 8 XCDs round robin) takes a
+// contiguous run of ceil(T / 8) of them, so that a tail smaller than the
+// grid still spreads over every XCD and neighbouring tiles share an XCD's
+// L2.  A result >= T: none.
+__device__ __forceinline__ int tail_slot(int T) {
+    const int G = gridDim.x, b = blockIdx.x;
+    if ((G & 7) != 0) return b;
+    const int c = (T + 7) >> 3;            // <= G / 8 since T <= G
+    return (b >> 3) < c ? (b & 7) * c + (b >> 3) : T;
+}
+
+// The half tiles of a plain persistent launch (p.tail_N > p.N): columns
+// [p.N, p.tail_N) as 128 x 256 tiles, at most one per block, which a block
+// runs once its whole rounds are done, in the order of tile_coords.
+template <int FA, int FB, bool OUT_BF16>
+__device__ __forceinline__ void p_tail(const GemmParams& p) {
+    constexpr int kEsz = OUT_BF16 ? 2 : 4;
+    const int n0 = p.N;
+    GemmParams t = p;
+    t.B = p.B + (int64_t)n0 * p.ldb;
+    t.C = reinterpret_cast<uint8_t*>(p.C) + (int64_t)n0 * kEsz;
+    if (p.sb_row) t.sb = p.sb + n0;
+    t.N = p.tail_N - n0;
+    t.tiles_m = (p.M + 127) / 128;
+    t.tiles_n = (t.N + 255) / 256;
+    t.group_m = t.tiles_m < 4 ? t.tiles_m : 4;
+    const int T = t.tiles_m * t.tiles_n;
+    const int b = tail_slot(T);
+    if (b >= T) return;
+    int tm, tn;
+    tile_of_linear(t, t.tiles_m, t.group_m, b, tm, tn);
+    h_tile<FA, FB, OUT_BF16, false>(t, tm * 128, t.M, tn * 256, t.B, t.sb, load_uniform(t.sa),
+                                    load_uniform(t.sb));
+}
+
+// Persistent scaled GEMM (p_rounds), then a plain launch's half tiles, if
+// any: each block takes its half tile once its whole rounds are done.  (The
+// grouped GEMM leaves its half tiles to a k_gemm_h launch: in the grouped
+// kernel, the tail's code raised the register spills of the main loop from
+// 4 to 22 and made the moe GEMM 2 % slower.)
+template <int FA, int FB, bool OUT_BF16, bool RAGGED, bool GROUPED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_p(GemmParams p) {
+    p_rounds<FA, FB, OUT_BF16, RAGGED, GROUPED>(p);
+    if constexpr (!GROUPED) {
+        if (p.tail_N > p.N) {
+            __syncthreads();     // every wave is done with the last epilogue's staging slot
+            p_tail<FA, FB, OUT_BF16>(p);
+        }
     }
 }
 
@@ -1219,14 +1278,16 @@ GemmParams make_params(const GemmArgs& a, int bm, int bn) {
     p.gtab = nullptr;
     p.b_gstride = 0;
     p.main_grid = 0;
+    p.tail_N = 0;
     return p;
 }
 
 // One launch of k_gemm_p over p: a persistent grid of one block per CU when
-// there are more tiles than CUs and K has at least three stages, else one
-// block per tile.
+// there are more tiles than CUs and K has at least three stages, or when
+// asked for (a launch with half tiles after its rounds), else one block per
+// tile.
 template <int FA, int FB, bool OUT_BF16>
-hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream) {
+hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream, bool persistent = false) {
     static PerDeviceOnce once;
     const hipError_t attr_err = once.run([] {
         const hipError_t e = set_lds(k_gemm_p<FA, FB, OUT_BF16, false, false>, lds_scaled<OUT_BF16>());
@@ -1234,7 +1295,7 @@ hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream) {
     });
     if (attr_err != hipSuccess) return attr_err;
     unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    if (grid > (unsigned)num_cus && p.K > 2 * kBK2) grid = (unsigned)num_cus;
+    if ((grid > (unsigned)num_cus && p.K > 2 * kBK2) || persistent) grid = (unsigned)num_cus;
     if (grid == 0) return hipSuccess;
     if (p.K % kBK2 != 0)
         hipLaunchKernelGGL((k_gemm_p<FA, FB, OUT_BF16, true, false>), dim3(grid), dim3(kGemmThreads),
@@ -1259,31 +1320,17 @@ hipError_t launch_half(const GemmParams& p, hipStream_t stream, unsigned grid_gr
     return hipGetLastError();
 }
 
-// Columns [n0, N) of the GEMM as a problem of its own: B's rows, C's
-// columns and the per-column B scales from n0 on.
-GemmParams column_range(const GemmParams& p, int n0, int esz, int bm) {
-    GemmParams q = p;
-    q.B = p.B + (int64_t)n0 * p.ldb;
-    q.C = reinterpret_cast<uint8_t*>(p.C) + (int64_t)n0 * esz;
-    if (p.sb_row) q.sb = p.sb + n0;
-    q.N = p.N - n0;
-    q.tiles_m = (p.M + bm - 1) / bm;
-    q.tiles_n = (q.N + 255) / 256;
-    q.group_m = q.tiles_m < 4 ? q.tiles_m : 4;
-    return q;
-}
-
 // Scaled GEMM.  A single tile takes about the same time whether one CU or
 // all of them are busy (its K loop), so a round of tiles that fills at most
 // half the CUs costs nearly a full round.  Such a round runs as 128 x 256
-// tiles of k_gemm_h instead, which halves each CU's share of it: a problem
-// with at most half as many 256 x 256 tiles as CUs, or with at most 128
-// rows, runs entirely on them; a persistent problem whose last round is at
-// most half full runs its last columns (enough 256-wide column tiles to hold
-// that round's tiles) as a second launch of 128-row tiles, one round of
-// them, after the other columns' whole rounds.  Every output's K sum is the
-// same chain of MFMAs in both kernels, so the result is bit-identical to
-// the 256-row tiling.
+// tiles instead, which halves each CU's share of it: a problem with at most
+// half as many 256 x 256 tiles as CUs, or with at most 128 rows, runs
+// entirely on them (k_gemm_h); a persistent problem whose last round is at
+// most half full runs its last columns (enough 256-wide column tiles to
+// hold that round's tiles) as one round of 128-row tiles that each block of
+// the persistent launch takes once its whole rounds of the other columns
+// are done.  Every output's K sum is the same chain of MFMAs in both tile
+// heights, so the result is bit-identical to the 256-row tiling.
 template <int FA, int FB, bool OUT_BF16>
 hipError_t launch_scaled_typed(const GemmArgs& a) {
     const GemmParams p = make_params(a, 256, 256);
@@ -1295,13 +1342,11 @@ hipError_t launch_scaled_typed(const GemmArgs& a) {
         const int tail_n = (int)((last + p.tiles_m - 1) / p.tiles_m);            // column tiles of the tail
         const int64_t half_tiles = (int64_t)((p.M + 127) / 128) * tail_n;
         if (tail_n < p.tiles_n && half_tiles <= cus) {
-            const int n0 = (p.tiles_n - tail_n) * 256;
             GemmParams head = p;
-            head.N = n0;
+            head.N = (p.tiles_n - tail_n) * 256;
             head.tiles_n = p.tiles_n - tail_n;
-            hipError_t e = launch_tiles<FA, FB, OUT_BF16>(head, a.num_cus, a.stream);
-            if (e != hipSuccess) return e;
-            return launch_half<FA, FB, OUT_BF16>(column_range(p, n0, a.out_bf16 ? 2 : 4, 128), a.stream);
+            head.tail_N = p.N;
+            return launch_tiles<FA, FB, OUT_BF16>(head, a.num_cus, a.stream, true);
         }
     }
     return launch_tiles<FA, FB, OUT_BF16>(p, a.num_cus, a.stream);

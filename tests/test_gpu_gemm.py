@@ -209,7 +209,8 @@ def test_gemm_column_ranges_bitwise():
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_split_last_round_parity_and_bitwise(out):
     """A persistent problem whose last round is at most half full: its last
-    column tiles run as 128-row tiles in a second launch.  M, N and K
+    column tiles run as 128-row tiles that the persistent blocks take after
+    their whole rounds (one launch).  M, N and K
     ragged, one scale per row of A and per column of B (the tail's scales
     start at its first column).  Sampled outputs against the oracle (the
     tail columns and the last rows included); then every output against the
@@ -241,6 +242,34 @@ def test_gemm_split_last_round_parity_and_bitwise(out):
     torch.cuda.synchronize()
     assert torch.equal(y[:, n_tail:], ref_tail[:M])
     assert torch.equal(y[:, :n_tail], ref_head)
+
+
+def test_gemm_split_last_round_blocks_without_whole_rounds():
+    """The split of the last round when the other columns hold fewer 256 x
+    256 tiles than CUs: 100 x 3 tiles on 256 CUs (a last round of 44), so
+    the launch's 256 blocks take the 200 tiles of the first two column
+    tiles, 56 of them none, and then the 200 half tiles of the last, ragged
+    column tile.  Sampled outputs (all of the last rows and columns
+    included) against the oracle; every output against separate calls on
+    the two column ranges, bit for bit."""
+    rng = np.random.default_rng(33)
+    M, N, K = 25500, 700, 384
+    A, B, sa, sb = _realistic_operands(rng, M, N, K, 0, 0, True)
+    say("gemm split last round, idle blocks", M, N, K)
+    y = _run_gemm(A, 0, B, 0, sa, sb, torch.bfloat16)
+    yh = host(y)
+    ms = np.concatenate([[0, M - 1, M - 1, 0, 25343, 25344], rng.integers(0, M, 2000), rng.integers(24000, M, 600)])
+    ns = np.concatenate([[0, N - 1, 512, 511, N - 1, 512], rng.integers(0, N, 2000), rng.integers(512, N, 600)])
+    y32, pp = oracle.gemm_sampled(A, 0, B, 0, sa, sb, ms, ns)
+    print(assert_gemm(yh[ms, ns], y32, pp, K, "bf16", what="split last round, idle blocks",
+                      model=gemm_model_at(A, 0, B, 0, sa, sb, ms, ns)))
+    a, b = dev_u8(A), dev_u8(B)
+    say("gemm split last round, idle blocks: column ranges alone")
+    ref_head = fp8.scaled_gemm(a, b[:512], dev_f32(sa), dev_f32(sb[:512]), out_dtype=torch.bfloat16)
+    ref_tail = fp8.scaled_gemm(a, b[512:], dev_f32(sa), dev_f32(sb[512:]), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :512], ref_head)
+    assert torch.equal(y[:, 512:], ref_tail)
 
 
 def test_gemm_128_row_tiles_bitwise_and_small_m_persistent():
