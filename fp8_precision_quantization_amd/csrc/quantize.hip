@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <mutex>
 
 #include "cast_unit.hpp"
@@ -334,26 +335,44 @@ __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h
                                                              bool pow2, float* amax_out, float* scale_inv_out,
                                                              fp8_diag* diag, fp8_diag* diag_tmp) {
     __shared__ uint32_t lds[16];
+    // The history as it stands before this call's update, one word per
+    // thread, read beside the partials' reduction: the ring update then
+    // waits for no load of its own (one round trip to memory instead of a
+    // chain of them).
+    constexpr int kWords = (int)(sizeof(fp8_amax_history) / 4);
+    constexpr int kLen = (int)(offsetof(fp8_amax_history, len) / 4);
+    constexpr int kPos = (int)(offsetof(fp8_amax_history, pos) / 4);
+    constexpr int kCount = (int)(offsetof(fp8_amax_history, count) / 4);
+    constexpr int kSteps = (int)(offsetof(fp8_amax_history, steps) / 4);
+    constexpr int kThr = (int)(offsetof(fp8_amax_history, spike_threshold) / 4);
+    constexpr int kSpikes = (int)(offsetof(fp8_amax_history, spikes) / 4);
+    static_assert(kWords <= kThreads && offsetof(fp8_amax_history, amax) == 0, "history layout");
+    __shared__ uint32_t hw[kWords];
+    uint32_t word = 0;
+    if (threadIdx.x < kWords) word = reinterpret_cast<const uint32_t*>(h)[threadIdx.x];
     const uint32_t cur = reduce_partials(partials, n, lds);
+    if (threadIdx.x < kWords) hw[threadIdx.x] = word;
+    __syncthreads();
     if (threadIdx.x != 0) return;
     const float amax_now = __uint_as_float(cur);
     amax_out[0] = amax_now;
-    int32_t len = h->len;
+    int32_t len = (int32_t)hw[kLen];
     len = len < 1 ? 1 : (len > 16 ? 16 : len);
-    int32_t pos = h->pos;
+    int32_t pos = (int32_t)hw[kPos];
     pos = (pos < 0 || pos >= len) ? 0 : pos;
+    const int32_t count_in = (int32_t)hw[kCount];
     if constexpr (GUARD) {
-        const int32_t count0 = h->count < 0 ? 0 : (h->count > len ? len : h->count);
+        const int32_t count0 = count_in < 0 ? 0 : (count_in > len ? len : count_in);
         uint32_t wbits = 0;
-        for (int i = 0; i < count0; ++i) wbits = max(wbits, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
-        const float thr = h->spike_threshold;
+        for (int i = 0; i < count0; ++i) wbits = max(wbits, hw[i] & 0x7FFFFFFFu);
+        const float thr = __uint_as_float(hw[kThr]);
         const bool spiked = count0 > 0 && thr > 0.0f && amax_now > thr * __uint_as_float(wbits);
         h->internal[0] = spiked ? 1u : 0u;
         if (spiked) {
             const float sj = scale_from_amax_bits<FMT>(cur, pow2);
             h->internal[1] = __float_as_uint(sj);
             scale_inv_out[0] = recip_rn(sj);
-            h->spikes = h->spikes + 1u;
+            h->spikes = hw[kSpikes] + 1u;
         }
         if (diag_tmp != nullptr && !spiked && diag != nullptr) {
             diag->sat_count += diag_tmp->sat_count;
@@ -363,14 +382,15 @@ __global__ __launch_bounds__(kThreads) void k_delayed_finish(fp8_amax_history* h
     }
     h->amax[pos] = amax_now;
     h->pos = (pos + 1) % len;
-    const int32_t count = h->count < len ? h->count + 1 : len;
+    const int32_t count = count_in < len ? count_in + 1 : len;
     h->count = count;
+    // the window after this step's entry: slot pos now holds amax_now
     uint32_t basis = 0;
-    for (int i = 0; i < count; ++i) basis = max(basis, __float_as_uint(h->amax[i]) & 0x7FFFFFFFu);
+    for (int i = 0; i < count; ++i) basis = max(basis, (i == pos ? cur : hw[i]) & 0x7FFFFFFFu);
     const float s = scale_from_amax_bits<FMT>(basis, pow2);
     h->scale = s;
     h->scale_inv = 1.0f / s;
-    h->steps = h->steps + 1;
+    h->steps = hw[kSteps] + 1u;
     for (int i = 0; i < 3; ++i) h->sync[i] = 0u;
 }
 
