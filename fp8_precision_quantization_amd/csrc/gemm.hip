@@ -757,47 +757,53 @@ __device__ __forceinline__ void p_rounds(const GemmParams& p) {
 // program, its fragment reads and the epilogue are those of k_gemm_p with
 // 128-row tiles, so every output's K sum is the same chain of MFMAs.
 // ------------------------------------------------------------------------
-constexpr int kHStage = 128 * kBK2 + 256 * kBK2;      // 48 KiB: A, then B
-constexpr int kHRing = 3 * kHStage;
+// One stage of a BM x 256 tile: A (BM x 128 B), then B (256 x 128 B).
+template <int BM>
+constexpr int h_stage() { return BM * kBK2 + 256 * kBK2; }
+constexpr int kHStage = h_stage<128>();               // 48 KiB
+constexpr int kHRing = 3 * kHStage;                   // the ring of the largest tile
 
-// One 128 x 256 tile at rows [m0, m_end) and columns n0.. (m_end: the
+// One BM x 256 tile (BM = 128, or 64 for the quarter tiles of a grouped
+// GEMM's last round) at rows [m0, m_end) and columns n0.. (m_end: the
 // problem's M, or the end of the tile's group), with B operand Bp and the
-// tile's B scales sbp (per column) or sb0.
-template <int FA, int FB, bool OUT_BF16, bool GROUPED>
+// tile's B scales sbp (per column) or sb0.  BM = 64: each wave covers 32
+// rows, one row block of the same MFMA program.
+template <int FA, int FB, bool OUT_BF16, bool GROUPED, int BM = 128>
 __device__ __forceinline__ void h_tile(const GemmParams& p, int m0, int m_end, int n0, const uint8_t* Bp,
                                        const float* sbp, float sa0, float sb0) {
-    using DA = DmaL<128>;
+    constexpr int kStage = h_stage<BM>();
+    using DA = DmaL<BM>;
     constexpr int kVm1 = DA::kInst + Dma2::kInst;  // A(s+2) and B(s+2) may still fly
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = p.K;
     const int nks = (K + kBK2 - 1) / kBK2;
     const uint32_t ring = lds_addr(g_ring);
-    auto addr = [&](int slot) { return ring + (uint32_t)(slot * kHStage); };
-    auto aptr = [&](int slot) { return g_ring + slot * kHStage; };
-    auto bptr = [&](int slot) { return g_ring + slot * kHStage + 128 * kBK2; };
+    auto addr = [&](int slot) { return ring + (uint32_t)(slot * kStage); };
+    auto aptr = [&](int slot) { return g_ring + slot * kStage; };
+    auto bptr = [&](int slot) { return g_ring + slot * kStage + BM * kBK2; };
 
     DA da;
     Dma2 db;
     da.init(p.A, p.lda, m0, m_end, wave);
     db.init(Bp, p.ldb, n0, p.N, wave);
 
-    v16f acc[4][2];
+    v16f acc[4][BM / 64];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < BM / 64; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-    Frags<128, 256> f0, f1;
+    Frags<BM, 256> f0, f1;
     if (nks > 0) {
         // A(0), B(0), A(1), B(1), B(2); A(2) comes with the first even step
         for (int i = 0; i < 2 && i < nks; ++i) {
             da.issue(addr(i), i * kBK2, K);
-            db.issue(addr(i) + (uint32_t)(128 * kBK2), i * kBK2, K);
+            db.issue(addr(i) + (uint32_t)(BM * kBK2), i * kBK2, K);
         }
-        if (nks > 2) db.issue(addr(2) + (uint32_t)(128 * kBK2), 2 * kBK2, K);
+        if (nks > 2) db.issue(addr(2) + (uint32_t)(BM * kBK2), 2 * kBK2, K);
         if (nks > 2) wait_and_barrier<DA::kInst + 2 * Dma2::kInst>();
         else if (nks == 2) wait_and_barrier<kVm1>();
         else wait_and_barrier<0>();
@@ -818,7 +824,7 @@ __device__ __forceinline__ void h_tile(const GemmParams& p, int m0, int m_end, i
         const int ps = ns == 2 ? 0 : ns + 1;       // slot of stage s+2 (stage s-1's)
         const FullDma<DA> dA{&da, addr(ps), (s + 2) * kBK2};
         mma_step<FA, FB, false, kVm1, kVm1>(acc, f0, f1, aptr(cs), bptr(cs), 1, wm, wn, dA, 0);
-        const FullDma<Dma2> dB{&db, addr(cs) + (uint32_t)(128 * kBK2), (s + 3) * kBK2};
+        const FullDma<Dma2> dB{&db, addr(cs) + (uint32_t)(BM * kBK2), (s + 3) * kBK2};
         mma_step<FA, FB, true, kVm1, kVm1>(acc, f1, f0, aptr(ns), bptr(ns), 0, wm, wn, dB, 1);
         cs = ns;
     }
@@ -827,7 +833,7 @@ __device__ __forceinline__ void h_tile(const GemmParams& p, int m0, int m_end, i
         const int ps = ns == 2 ? 0 : ns + 1;
         const TailDma<DA> dA{&da, addr(ps), (s + 2) * kBK2, K, s + 2 < nks, (s + 3) * kBK2 <= K};
         mma_step<FA, FB, false, kVm1, kVm1>(acc, f0, f1, aptr(cs), bptr(cs), 1, wm, wn, dA, 0);
-        const TailDma<Dma2> dB{&db, addr(cs) + (uint32_t)(128 * kBK2), (s + 3) * kBK2, K, s + 3 < nks,
+        const TailDma<Dma2> dB{&db, addr(cs) + (uint32_t)(BM * kBK2), (s + 3) * kBK2, K, s + 3 < nks,
                                (s + 4) * kBK2 <= K};
         mma_step<FA, FB, true, kVm1, kVm1>(acc, f1, f0, aptr(ns), bptr(ns), 0, wm, wn, dB, s + 2 < nks ? 1 : 0);
         cs = ns;
@@ -836,38 +842,56 @@ __device__ __forceinline__ void h_tile(const GemmParams& p, int m0, int m_end, i
     // epilogue stages its values through the ring
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __syncthreads();
-    const bool interior = p.vec_out && m0 + 128 <= m_end && n0 + 256 <= p.N;
+    const bool interior = p.vec_out && m0 + BM <= m_end && n0 + 256 <= p.N;
     if constexpr (GROUPED) {
         GemmParams pt = p;           // the tile's rows end at its group's end
         pt.M = m_end;
         pt.sb = sbp;
-        epilogue_slot<OUT_BF16, 128>(pt, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
+        epilogue_slot<OUT_BF16, BM>(pt, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
     } else {
-        epilogue_slot<OUT_BF16, 128>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
+        epilogue_slot<OUT_BF16, BM>(p, sa0, sb0, acc, m0, n0, wm, wn, wave, lane, g_ring, interior);
     }
 }
 
 // k_gemm_h: one 128-row tile per block, over p's tiles (problems with at
 // most half as many 256-row tiles as CUs, or at most 128 rows).  GROUPED:
-// the blocks take the grouped GEMM's tiles that the persistent kernel left
+// the blocks take the R grouped-GEMM tiles that the persistent kernel left
 // (its last round, when at most half full: grouped_main_tiles with the grid
-// p.main_grid), block b the half b % 2 of the b/2-th of them; a tile's half
-// past its group's end, and blocks past the tiles, exit.
+// p.main_grid), as 4 R quarters of 64 rows when they fit the grid, else as
+// 2 R halves of 128 rows: a quarter has a quarter of a tile's K loop, so
+// the round ends sooner while most CUs would idle anyway.  Pieces are dealt
+// so that every XCD takes an equal run of whole tiles (a tile's pieces
+// share its B panel in that XCD's L2); piece j of tile t covers rows
+// j * BM.. of the tile.  Pieces past their group's end, and blocks past the
+// pieces, exit.
 template <int FA, int FB, bool OUT_BF16, bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
     int tm, tn;
     if constexpr (GROUPED) {
         const int tiles_m = min(p.gtab[0].x, p.tiles_m);
         const int T = tiles_m * p.tiles_n;
-        const int t = grouped_main_tiles(T, p.main_grid) + (int)(blockIdx.x >> 1);
-        if (t >= T) return;
+        const int main = grouped_main_tiles(T, p.main_grid);
+        const int G = gridDim.x;
+        const bool quarters = 4 * (T - main) <= G;
+        const int sh = quarters ? 2 : 1;             // log2 of pieces per tile
+        const int np = (T - main) << sh;
+        int b = blockIdx.x;
+        if ((G & 7) == 0) {
+            const int c = ((np + (8 << sh) - 1) >> (3 + sh)) << sh;   // pieces per XCD, whole tiles
+            if (c <= (G >> 3)) b = (b >> 3) < c ? (b & 7) * c + (b >> 3) : np;
+        }
+        if (b >= np) return;
+        const int t = main + (b >> sh);
         tile_of_linear(p, tiles_m, tiles_m < 4 ? tiles_m : 4, t, tm, tn);
         const int4 e = p.gtab[1 + tm];
-        const int m0 = e.y + 128 * (int)(blockIdx.x & 1);
+        const int m0 = e.y + (quarters ? 64 : 128) * (b & ((1 << sh) - 1));
         if (m0 >= e.z) return;
         const uint8_t* Bp = p.B + (int64_t)e.x * p.b_gstride;
         const float* sbp = p.sb + (p.sb_row ? (int64_t)e.x * p.N : (int64_t)e.x);
-        h_tile<FA, FB, OUT_BF16, true>(p, m0, e.z, tn * 256, Bp, sbp, load_uniform(p.sa), load_uniform(sbp));
+        if (quarters)
+            h_tile<FA, FB, OUT_BF16, true, 64>(p, m0, e.z, tn * 256, Bp, sbp, load_uniform(p.sa), load_uniform(sbp));
+        else
+            h_tile<FA, FB, OUT_BF16, true>(p, m0, e.z, tn * 256, Bp, sbp, load_uniform(p.sa), load_uniform(sbp));
     } else {
         tile_coords(p, tm, tn);
         h_tile<FA, FB, OUT_BF16, false>(p, tm * 128, p.M, tn * 256, p.B, p.sb, load_uniform(p.sa),

@@ -128,8 +128,8 @@ def test_grouped_groups_equal_plain_gemm_bitwise():
 def test_grouped_split_last_round(out_dtype):
     """A persistent grouped GEMM whose last round is at most half full
     (13 M-tiles x 20 N-tiles = 260 tiles on 256 CUs): the last 4 tiles, all
-    of the last group's single tile of 129 rows, run as 128-row halves (the
-    second half one row).  K ragged, one scale per A row and per expert
+    of the last group's single tile of 129 rows, run as 64-row quarters (the
+    third quarter one row, the fourth past the group's end).  K ragged, one scale per A row and per expert
     row.  Every group against the oracle, and bit for bit against the plain
     scaled GEMM of its rows with its expert."""
     sizes, N, K = [300, 0, 513, 700, 1000, 129], 5120, 528
@@ -150,6 +150,27 @@ def test_grouped_split_last_round(out_dtype):
             assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), g
         else:
             assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), g
+
+
+def test_grouped_split_last_round_halves():
+    """A grouped GEMM whose last round is at most half full but too large
+    for quarters: 90 M-tiles x 4 N-tiles = 360 tiles on 256 CUs leave 104,
+    which run as 208 halves of 128 rows (4 x 104 quarters would not fit the
+    grid).  K ragged (400), per-row A and per-expert-row B scales.  Every
+    group against the oracle, and bit for bit against the plain scaled GEMM
+    of its rows with its expert."""
+    sizes, N, K = [10000, 12784], 1024, 400
+    A, B, a_inv, b_inv, offsets = _problem(sizes, N, K, 0, 0, 43, lead=3, b_rows=True)
+    say("grouped split last round, halves")
+    y = _run(A, B, a_inv, b_inv, offsets, 0, 0, torch.bfloat16)
+    _check(y, A, B, a_inv, b_inv, offsets, 0, 0, torch.bfloat16, np.random.default_rng(8), per_group=400,
+           what="split last round, halves")
+    for g in range(len(sizes)):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        say("grouped split last round, halves: plain GEMM of group", g)
+        ref = fp8.scaled_gemm(dev_u8(A[lo:hi]), dev_u8(B[g]), torch.from_numpy(a_inv[lo:hi]).cuda(),
+                              torch.from_numpy(b_inv[g]).cuda(), out_dtype=torch.bfloat16)
+        assert np.array_equal(y[lo:hi].view(np.uint16), host(ref).view(np.uint16)), g
 
 
 def test_grouped_one_group_is_plain_gemm_and_repeatable():
