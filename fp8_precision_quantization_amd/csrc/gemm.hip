@@ -853,8 +853,9 @@ __device__ __forceinline__ void h_tile(const GemmParams& p, int m0, int m_end, i
     }
 }
 
-// k_gemm_h: one 128-row tile per block, over p's tiles (problems with at
-// most half as many 256-row tiles as CUs, or at most 128 rows).  GROUPED:
+// k_gemm_h: one BM-row tile per block, over p's tiles (problems with at
+// most half as many 256-row tiles as CUs, or at most 128 rows; BM = 64 when
+// one round of 64-row tiles fits the grid).  GROUPED:
 // the blocks take the R grouped-GEMM tiles that the persistent kernel left
 // (its last round, when at most half full: grouped_main_tiles with the grid
 // p.main_grid), as 4 R quarters of 64 rows when they fit the grid, else as
@@ -864,7 +865,7 @@ __device__ __forceinline__ void h_tile(const GemmParams& p, int m0, int m_end, i
 // share its B panel in that XCD's L2); piece j of tile t covers rows
 // j * BM.. of the tile.  Pieces past their group's end, and blocks past the
 // pieces, exit.
-template <int FA, int FB, bool OUT_BF16, bool GROUPED>
+template <int FA, int FB, bool OUT_BF16, bool GROUPED, int BM = 128>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
     int tm, tn;
     if constexpr (GROUPED) {
@@ -894,8 +895,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_h(GemmParams p) {
             h_tile<FA, FB, OUT_BF16, true>(p, m0, e.z, tn * 256, Bp, sbp, load_uniform(p.sa), load_uniform(sbp));
     } else {
         tile_coords(p, tm, tn);
-        h_tile<FA, FB, OUT_BF16, false>(p, tm * 128, p.M, tn * 256, p.B, p.sb, load_uniform(p.sa),
-                                        load_uniform(p.sb));
+        h_tile<FA, FB, OUT_BF16, false, BM>(p, tm * BM, p.M, tn * 256, p.B, p.sb, load_uniform(p.sa),
+                                            load_uniform(p.sb));
     }
 }
 
@@ -1330,16 +1331,17 @@ hipError_t launch_tiles(const GemmParams& p, int num_cus, hipStream_t stream, bo
     return hipGetLastError();
 }
 
-// One launch of k_gemm_h: over p's tiles (128-row tiles, one block each),
+// One launch of k_gemm_h: over p's tiles (BM-row tiles, one block each),
 // or GROUPED over the grouped GEMM's split-off last round (`grid` blocks).
-template <int FA, int FB, bool OUT_BF16, bool GROUPED = false>
+template <int FA, int FB, bool OUT_BF16, bool GROUPED = false, int BM = 128>
 hipError_t launch_half(const GemmParams& p, hipStream_t stream, unsigned grid_grouped = 0) {
     static PerDeviceOnce once;
-    const hipError_t attr_err = once.run([] { return set_lds(k_gemm_h<FA, FB, OUT_BF16, GROUPED>, (size_t)kHRing); });
+    const hipError_t attr_err =
+        once.run([] { return set_lds(k_gemm_h<FA, FB, OUT_BF16, GROUPED, BM>, (size_t)kHRing); });
     if (attr_err != hipSuccess) return attr_err;
     const unsigned grid = GROUPED ? grid_grouped : (unsigned)(p.tiles_m * p.tiles_n);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm_h<FA, FB, OUT_BF16, GROUPED>), dim3(grid), dim3(kGemmThreads), (size_t)kHRing,
+    hipLaunchKernelGGL((k_gemm_h<FA, FB, OUT_BF16, GROUPED, BM>), dim3(grid), dim3(kGemmThreads), (size_t)kHRing,
                        stream, p);
     return hipGetLastError();
 }
@@ -1349,7 +1351,8 @@ hipError_t launch_half(const GemmParams& p, hipStream_t stream, unsigned grid_gr
 // half the CUs costs nearly a full round.  Such a round runs as 128 x 256
 // tiles instead, which halves each CU's share of it: a problem with at most
 // half as many 256 x 256 tiles as CUs, or with at most 128 rows, runs
-// entirely on them (k_gemm_h); a persistent problem whose last round is at
+// entirely on them (k_gemm_h), or on 64 x 256 tiles when one round of
+// those fits the grid; a persistent problem whose last round is at
 // most half full runs its last columns (enough 256-wide column tiles to
 // hold that round's tiles) as one round of 128-row tiles that each block of
 // the persistent launch takes once its whole rounds of the other columns
@@ -1360,7 +1363,13 @@ hipError_t launch_scaled_typed(const GemmArgs& a) {
     const GemmParams p = make_params(a, 256, 256);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n, cus = a.num_cus;
     if (tiles == 0) return hipSuccess;
-    if (2 * tiles <= cus || a.M <= 128) return launch_half<FA, FB, OUT_BF16>(make_params(a, 128, 256), a.stream);
+    if (2 * tiles <= cus || a.M <= 128) {
+        // 64-row tiles when one round of them fits the grid (each has a
+        // quarter of a 256-row tile's K loop, so more CUs share the work)
+        const GemmParams q = make_params(a, 64, 256);
+        if ((int64_t)q.tiles_m * q.tiles_n <= cus) return launch_half<FA, FB, OUT_BF16, false, 64>(q, a.stream);
+        return launch_half<FA, FB, OUT_BF16>(make_params(a, 128, 256), a.stream);
+    }
     const int64_t last = tiles % cus;
     if (tiles > cus && a.K > 2 * kBK2 && last != 0 && 2 * last <= cus) {
         const int tail_n = (int)((last + p.tiles_m - 1) / p.tiles_m);            // column tiles of the tail
