@@ -272,6 +272,32 @@ def test_gemm_split_last_round_blocks_without_whole_rounds():
     assert torch.equal(y[:, 512:], ref_tail)
 
 
+@pytest.mark.parametrize("M", [1, 64, 200])
+def test_gemm_64_row_tiles_decode_shapes(M):
+    """Decode-sized problems (M = 1, 64, 200 rows against a 14336 x 4096
+    weight) run as 64-row tiles (one round of them fits the grid): every
+    output against the oracle, and bit for bit against the same rows in a
+    problem padded to 1280 rows (the persistent kernel's 256-row tiles and
+    its 128-row tail)."""
+    rng = np.random.default_rng(34 + M)
+    N, K = 14336, 4096
+    A, B, sa, sb = _realistic_operands(rng, M, N, K, 0, 0, True)
+    say("gemm 64-row tiles, decode shape", M, N, K)
+    y = _run_gemm(A, 0, B, 0, sa, sb, torch.bfloat16)
+    y32, pp = oracle.gemm(A, 0, B, 0, sa, sb)
+    print(assert_gemm(host(y), y32, pp, K, "bf16", what="decode %d" % M,
+                      model=gemm_model_at(A, 0, B, 0, sa, sb)))
+    Mp = 5 * 256                         # 5 x 56 tiles: more than the CUs, persistent
+    a_pad = torch.zeros((Mp, K), dtype=torch.uint8, device="cuda")
+    a_pad[:M] = dev_u8(A)
+    sa_pad = torch.ones(Mp, dtype=torch.float32, device="cuda")
+    sa_pad[:M] = dev_f32(sa)
+    say("gemm 64-row tiles, decode shape: 256-row reference", M)
+    ref = fp8.scaled_gemm(a_pad, dev_u8(B), sa_pad, dev_f32(sb), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref[:M])
+
+
 def test_gemm_128_row_tiles_bitwise_and_small_m_persistent():
     """Problems with at most half as many 256-row tiles as CUs, and any with
     at most 128 rows, run as 128-row tiles: their outputs equal the 256-row
