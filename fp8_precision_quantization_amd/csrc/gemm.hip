@@ -1234,7 +1234,9 @@ __device__ __forceinline__ void bq_tile(const GemmParams& p, int m0, int n0, int
 
 // Persistent block-scaled GEMM over 256 x 256 tiles.  When the tiles leave
 // a last round that fills at most half of the grid, that round runs as
-// 128 x 256 halves over the whole grid (both halves of a tile on one XCD).
+// 128 x 256 halves over the whole grid (both halves of a tile on one XCD);
+// a problem with at most half as many tiles as the grid runs all of them
+// so (a half past M has nothing to do).
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kBQThreads, 1) void k_gemm_bq(GemmParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1242,7 +1244,7 @@ __global__ __launch_bounds__(kBQThreads, 1) void k_gemm_bq(GemmParams p) {
     const int G = gridDim.x;
     const int T = p.tiles_m * p.tiles_n;
     const int full = T / G, rem = T % G;
-    const bool halves = full > 0 && rem != 0 && 2 * rem <= G;
+    const bool halves = rem != 0 && 2 * rem <= G;    // (full == 0: a small problem, all halves)
     const int limit = halves ? full * G : T;
     int tm, tn;
     for (int r = 0; tile_of_round(p, p.tiles_m, p.group_m, limit, r, tm, tn); ++r)
@@ -1481,8 +1483,9 @@ hipError_t launch_block_typed(const GemmArgs& a) {
     GemmParams p = make_params(a, 256, 256);
     p.group_m = p.tiles_m < 8 ? p.tiles_m : 8;
     unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    if (grid > (unsigned)a.num_cus) grid = (unsigned)a.num_cus;
-    if (grid > 0)
+    // at most half as many tiles as CUs: one block per CU, the tiles as halves
+    if (grid > (unsigned)a.num_cus || 2 * grid <= (unsigned)a.num_cus) grid = (unsigned)a.num_cus;
+    if (p.tiles_m * p.tiles_n > 0)
         hipLaunchKernelGGL((k_gemm_bq<OUT_BF16>), dim3(grid), dim3(kBQThreads), (size_t)kBQLds, a.stream, p);
     return hipGetLastError();
 }

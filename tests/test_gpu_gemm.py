@@ -388,6 +388,39 @@ def test_blockscaled_gemm_half_tile_last_round():
         assert np.array_equal(ys, y[r0:r1]), (r0, np.argwhere(ys != y[r0:r1])[:5])
 
 
+@pytest.mark.parametrize("M,N,Mp", [(64, 28672, 768), (300, 8192, 1280)])
+def test_blockscaled_gemm_small_problem_halves(M, N, Mp):
+    """Block-scaled problems with at most half as many 256 x 256 tiles as
+    CUs (64 x 28672 and 300 x 8192, K = 1024: 112 and 64 tiles) run every
+    tile as 128 x 256 halves over the whole grid (a half past M does
+    nothing).  Every output against the oracle, and bit for bit equal to the
+    same rows of a problem padded to Mp rows, whose 256 x 256 tiles fill
+    more than half the grid (336 tiles: a whole round first; 160: one
+    round)."""
+    K = 1024
+    rng = np.random.default_rng(4200 + M)
+    X = rng.standard_t(4, size=(M, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.015).astype(np.float32)
+    qa = oracle.quantize(X, 0, "1x128")
+    qb = oracle.quantize(W, 0, "128x128")
+    A, B = qa["q"], qb["q"]
+    a_inv, b_inv = qa["scale_inv"], qb["scale_inv"]
+    say("blockgemm small problem, halves", M, N, K)
+    dA, dB, dai, dbi = dev_u8(A), dev_u8(B), dev_f32(a_inv), dev_f32(b_inv)
+    y = host(fp8.blockscaled_gemm(dA, dB, dai, dbi, torch.bfloat16))
+    ms, ns = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    y32, pr = oracle.blockgemm_sampled(A, B, a_inv, b_inv, ms.ravel(), ns.ravel())
+    print(assert_gemm(y.reshape(-1), y32, pr, K, "bf16", what=f"block {M}x{N}x{K}",
+                      model=gemm_model_at(A, 0, B, 0, a_inv, b_inv, ms.ravel(), ns.ravel(), block=True)))
+    a_pad = torch.zeros((Mp, K), dtype=torch.uint8, device="cuda")
+    a_pad[:M] = dA
+    ai_pad = torch.ones((Mp, K // 128), dtype=torch.float32, device="cuda")
+    ai_pad[:M] = dai
+    say("blockgemm small problem, halves: padded reference", M)
+    ref = host(fp8.blockscaled_gemm(a_pad, dB, ai_pad, dbi, torch.bfloat16))
+    assert np.array_equal(ref[:M], y), np.argwhere(ref[:M] != y)[:5]
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_blockscaled_gemm_parity(out):
     for i, (M, N, K) in enumerate(BLOCK_SHAPES):
