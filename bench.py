@@ -57,7 +57,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 #   mlp8b: one scaled-GEMM call (profiles/k_gemm_mlp8b_hbm_traffic.md)
 #   kv: one fp8_kv_load launch (profiles/kv_store_gather_8x128_paged_kernel_stats.md)
 TRAFFIC = {
-    "mlp8b": {"bytes": 504890556, "source": "csrc/gemm.hip", "sha16": "d793fc1fbcb8b61f"},
+    "mlp8b": {"bytes": 504843973, "source": "csrc/gemm.hip", "sha16": "0a8746efb4236bf4"},
     "kv": {"bytes": 104882176, "source": "csrc/kvcache.hip", "sha16": "119ccf3371e008a4"},
 }
 

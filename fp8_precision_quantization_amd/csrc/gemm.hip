@@ -33,6 +33,10 @@
 //     (one block per CU when tiles outnumber CUs): the next tile's first
 //     stages stream in during the current tile's last ones, and the
 //     epilogue's stores overlap the next tile's first stage.
+//   * A round of tiles that would leave CUs idle (a persistent launch's
+//     last round, a small problem, a grouped GEMM's leftover tiles) runs on
+//     128- or 64-row tiles of the same MFMA program, so every output is the
+//     same chain of MFMAs whatever tile computes it.
 //   * The block-scaled GEMM (k_gemm_bq, 256 x 256 tiles, eight waves) moves
 //     K in stages of 128 bytes, one stage per 128-wide scale block, through
 //     two buffers that carry the block's A-row scales too; the promotion of
